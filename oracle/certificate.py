@@ -1,0 +1,169 @@
+"""The DoSA pruning certificate in float64 (test infrastructure).
+
+Follows the DoSA pages (podcast transcript of "DOSA: Dots Sparse Attention",
+Method section; the zicq.com summary, "Technical Mechanism Analysis" items
+1-2; the picx.dev item, section 03):
+
+1. Seed threshold.  Score a subset of the visible keys exactly; the K-th
+   largest seed score tau lower-bounds the K-th largest score over all
+   visible keys (a subset's K-th largest can never exceed the full set's).
+2. Omitted positive heads.  A few positive-weight heads (proxies P) are
+   evaluated exactly.  Every other positive-weight head h is projected onto
+   the proxies with nonnegative coefficients that minimise the residual norm:
+   q_h = sum_p alpha_hp q_p + r_h, alpha >= 0.  Since ReLU is subadditive and
+   positively homogeneous, ReLU(q_h.k) <= sum_p alpha_hp ReLU(q_p.k) + ReLU(r_h.k),
+   so the proxies absorb these heads with weights c_p = w_p + sum_h w_h alpha_hp.
+3. Joint residual bound.  sum_h w_h ReLU(r_h.k) = (sum_{h active} w_h r_h).k
+   <= rho * ||k|| with rho^2 = sum_{h,j} w_h w_j max(0, <r_h, r_j>), which
+   covers every possible active subset at once (never larger than the
+   separable sum_h w_h ||r_h||, also provided).
+4. Negative heads.  For any subset A of the negative-weight heads,
+   sum_{h in H-} |w_h| ReLU(x_h) >= ReLU(a.k) with a = sum_{h in A} |w_h| q_h.
+   A is chosen from activation statistics: the negative heads that are
+   positive on at least half of the seed keys.
+5. Certificate: UB(t,s) = sum_p c_p ReLU(q_p.k_s) + rho ||k_s|| - ReLU(a.k_s)
+   >= S(t,s).  A key with UB < tau cannot enter the Top-K (K seed keys score
+   at least tau > S), whatever the tie rule, so it is pruned.
+
+None of the choices (seed set, proxy count, rho variant, support) affects the
+selected set as long as each bound is valid; they only change how much is
+pruned.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+
+from . import indexer
+
+
+def seed_keys(pos: int, K: int, prefix: int = 64, window: int | None = None) -> np.ndarray:
+    """Seed set: the first ``prefix`` keys and the last ``window`` visible keys (window defaults to K)."""
+    W = K if window is None else window
+    n = pos + 1
+    a = np.arange(min(prefix, n))
+    b = np.arange(max(0, n - W), n)
+    return np.union1d(a, b)
+
+
+def seed_threshold(S_seed: np.ndarray, K: int) -> float:
+    """K-th largest seed score, -inf when fewer than K seeds."""
+    if S_seed.size < K:
+        return -np.inf
+    return float(np.sort(S_seed)[::-1][K - 1])
+
+
+def nnls(Q: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """argmin_{alpha >= 0} ||v - Q alpha||_2 for a handful of columns.
+
+    Exhaustive over supports: for each subset of columns solve the
+    unconstrained least squares; among the feasible (nonnegative) solutions
+    keep the one of least residual.  Exact for the small column counts used.
+    """
+    p = Q.shape[1]
+    best = np.zeros(p)
+    best_r = float(v @ v)
+    for size in range(1, p + 1):
+        for sub in itertools.combinations(range(p), size):
+            Qs = Q[:, sub]
+            sol, *_ = np.linalg.lstsq(Qs, v, rcond=None)
+            if np.any(sol < 0):
+                continue
+            res = v - Qs @ sol
+            r = float(res @ res)
+            if r < best_r:
+                best_r = r
+                best = np.zeros(p)
+                best[list(sub)] = sol
+    return best
+
+
+def plan(q: np.ndarray, w: np.ndarray, x_seed: np.ndarray | None, num_proxies: int = 3,
+         support_frac: float = 0.5, rho_kind: str = "joint", use_negative: bool = True):
+    """Per-query certificate constants.
+
+    q [H, d], w [H] float64; x_seed [H, m] head dots on the seed keys (for
+    the negative support).  Returns a dict with proxies P, coefficients c,
+    alpha, residuals, rho, support A and aggregate a.
+    """
+    H = w.shape[0]
+    pos_h = np.nonzero(w > 0)[0]
+    neg_h = np.nonzero(w < 0)[0]
+    qn = np.linalg.norm(q, axis=1)
+    strength = w[pos_h] * qn[pos_h]
+    order = pos_h[np.lexsort((pos_h, -strength))]
+    P = np.sort(order[: min(num_proxies, order.size)])
+    O = np.setdiff1d(pos_h, P)
+    QP = q[P].T                                          # [d, p]
+    alpha = np.zeros((O.size, P.size))
+    R = np.zeros((O.size, q.shape[1]))
+    for i, h in enumerate(O):
+        al = nnls(QP, q[h]) if P.size else np.zeros(0)
+        alpha[i] = al
+        R[i] = q[h] - QP @ al if P.size else q[h]
+    c = w[P] + (w[O] @ alpha if O.size else 0.0)
+    if O.size == 0:
+        rho = 0.0
+    elif rho_kind == "joint":
+        G = R @ R.T
+        rho = float(np.sqrt(max(0.0, np.einsum("i,j,ij->", w[O], w[O], np.maximum(G, 0.0)))))
+    elif rho_kind == "separable":
+        rho = float(np.sum(w[O] * np.linalg.norm(R, axis=1)))
+    else:
+        raise ValueError(rho_kind)
+    if use_negative and neg_h.size and x_seed is not None and x_seed.shape[1] > 0:
+        active = np.mean(x_seed[neg_h] > 0, axis=1)
+        A = neg_h[active >= support_frac]
+    else:
+        A = np.zeros(0, dtype=np.int64)
+    a = (np.abs(w[A]) @ q[A]) if A.size else np.zeros(q.shape[1])
+    return {"P": P, "O": O, "alpha": alpha, "R": R, "c": np.asarray(c, dtype=np.float64),
+            "rho": rho, "A": A, "a": a, "qP": q[P]}
+
+
+def upper_bound(pl, k: np.ndarray) -> np.ndarray:
+    """UB[s] = sum_p c_p ReLU(q_p . k_s) + rho ||k_s|| - ReLU(a . k_s), float64."""
+    kn = np.linalg.norm(k, axis=1)
+    ub = pl["rho"] * kn
+    if pl["P"].size:
+        ub = ub + np.maximum(pl["qP"] @ k.T, 0.0).T @ pl["c"]
+    ub = ub - np.maximum(k @ pl["a"], 0.0)
+    return ub
+
+
+def query_certificate(q, w, k_vis, pos, K, num_proxies=3, prefix=64, window=None,
+                      support_frac=0.5, rho_kind="joint", use_negative=True):
+    """Everything the certificate says about one query.
+
+    k_vis: the query's visible keys [pos+1, d].  Returns dict with S (exact
+    scores), seed indices, tau, UB (all visible keys), pruned mask (non-seed
+    keys with UB < tau) and the plan.
+    """
+    S = indexer.scores(q[None], w[None], k_vis)[0]
+    seeds = seed_keys(pos, K, prefix, window)
+    tau = seed_threshold(S[seeds], K)
+    x_seed = q @ k_vis[seeds].T
+    pl = plan(q, w, x_seed, num_proxies, support_frac, rho_kind, use_negative)
+    UB = upper_bound(pl, k_vis)
+    is_seed = np.zeros(S.size, dtype=bool)
+    is_seed[seeds] = True
+    pruned = (~is_seed) & (UB < tau)
+    return {"S": S, "seeds": seeds, "tau": tau, "UB": UB, "pruned": pruned, "plan": pl}
+
+
+def filter_rate(wl, rows, **kw):
+    """Fraction of bounded (non-seed visible) pairs pruned, over the given query rows."""
+    seq, pos = indexer.query_positions(wl)
+    bounded = 0
+    pruned = 0
+    for r in np.asarray(rows, dtype=np.int64):
+        b, p = int(seq[r]), int(pos[r])
+        kv = indexer.seq_keys(wl, b, p + 1)
+        q = indexer.query_rows(wl, [r])[0]
+        w = indexer.weights(wl, [r])[0]
+        cert = query_certificate(q, w, kv, p, wl.topk, **kw)
+        nb = int(np.sum(~np.isin(np.arange(p + 1), cert["seeds"])))
+        bounded += nb
+        pruned += int(cert["pruned"].sum())
+    return pruned / max(bounded, 1), bounded, pruned
