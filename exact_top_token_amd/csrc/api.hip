@@ -1,0 +1,484 @@
+// C-ABI entry points: argument checks, work planning, workspace layout and
+// kernel launches on the caller's stream.  No allocation, no host sync.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "dosa_device.h"
+#include "dosa_internal.h"
+
+using namespace dosa;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail_hip(hipError_t e, const char* what) {
+  g_err = std::string(what) + ": " + hipGetErrorString(e);
+  return DOSA_ERR_HIP;
+}
+
+int combo_of(int qd, int kd) {
+  if (qd == DOSA_F32 && kd == DOSA_F32) return C_F32;
+  if (qd == DOSA_BF16 && kd == DOSA_BF16) return C_BF16;
+  if (qd == DOSA_FP8_E4M3FN && kd == DOSA_FP8_E4M3FN) return C_FP8;
+  if (qd == DOSA_BF16 && kd == DOSA_FP8_E4M3FN) return C_BF16Q_FP8K;
+  return -1;
+}
+
+int qbytes(int qd) { return qd == DOSA_F32 ? 4 : (qd == DOSA_BF16 ? 2 : 1); }
+
+size_t align_up(size_t x, size_t a = 256) { return (x + a - 1) / a * a; }
+
+// Everything the planner derives from the shapes.
+struct Plan {
+  int combo = -1, QW = 4, J = 1, R = 1, cap = 0, F = 0, W = 0;
+  bool dense = true;
+  int64_t total_q = 0, total_k = 0;
+  std::vector<GroupInfo> groups;
+  std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed items then main items
+  int n_seed_items = 0;
+  int mask_words = 0;
+  int64_t list_total = 0;
+  // workspace offsets
+  size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
+         o_norms = 0, o_normmin = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, total = 0;
+  uint64_t pairs_total = 0;
+};
+
+int check_shapes(int32_t batch, const int32_t* q_lens, const int32_t* kv_lens, int32_t H, int32_t d,
+                 int32_t topk, int32_t q_dtype, int32_t k_dtype) {
+  if (batch < 0 || (batch > 0 && (q_lens == nullptr || kv_lens == nullptr))) {
+    g_err = "batch < 0 or q_lens/kv_lens NULL";
+    return DOSA_ERR_INVALID_ARG;
+  }
+  if (H <= 0 || d <= 0 || topk <= 0) {
+    g_err = "H, d and topk must be positive";
+    return DOSA_ERR_INVALID_ARG;
+  }
+  for (int b = 0; b < batch; ++b) {
+    if (q_lens[b] < 0 || kv_lens[b] < 0 || q_lens[b] > kv_lens[b]) {
+      g_err = "sequence " + std::to_string(b) + ": need 0 <= q_len <= kv_len";
+      return DOSA_ERR_INVALID_ARG;
+    }
+  }
+  const int combo = combo_of(q_dtype, k_dtype);
+  if (combo < 0 || !combo_supported(combo, H, d) || topk > 4096) {
+    g_err = "unsupported dtype combination, H, d or topk";
+    return DOSA_ERR_UNSUPPORTED;
+  }
+  return DOSA_OK;
+}
+
+int resolve_cfg(const dosa_config* in, int32_t topk, dosa_config* out) {
+  dosa_default_config(topk, out);
+  if (in) {
+    *out = *in;
+    if (out->num_proxies < 0 || out->num_proxies > 3 || out->seed_window < 0 || out->seed_prefix < 0 ||
+        out->key_splits < 0 || !(out->neg_support_frac >= 0.f && out->neg_support_frac <= 1.f)) {
+      g_err = "config out of range";
+      return DOSA_ERR_INVALID_ARG;
+    }
+    if (out->buffer_cap == 0) out->buffer_cap = 2 * topk + 1024;
+    if (out->buffer_cap < topk + 64) {
+      g_err = "buffer_cap must be >= topk + 64";
+      return DOSA_ERR_INVALID_ARG;
+    }
+  }
+  return DOSA_OK;
+}
+
+void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv_lens, int32_t H, int32_t d,
+                int32_t topk, int32_t q_dtype, int32_t k_dtype, bool paged, bool dense,
+                const dosa_config& cfg) {
+  P.combo = combo_of(q_dtype, k_dtype);
+  P.QW = queries_per_wave(P.combo, H, d);
+  P.dense = dense;
+  P.cap = (cfg.buffer_cap + 63) / 64 * 64;
+  P.F = cfg.seed_prefix;
+  P.W = std::max(cfg.seed_window, 16);
+  int64_t cq = 0, ck = 0;
+  uint64_t pairs = 0;
+  int64_t max_kv = 0;
+  for (int b = 0; b < batch; ++b) {
+    const int m = q_lens[b], n = kv_lens[b];
+    max_kv = std::max<int64_t>(max_kv, n);
+    for (int i = 0; i < m; i += P.QW) {
+      GroupInfo g{};
+      g.seq = b;
+      g.q_row0 = (int32_t)(cq + i);
+      g.nq = std::min(P.QW, m - i);
+      g.pos0 = n - m + i;
+      g.key_base = paged ? 0 : (int32_t)ck;
+      g.norm_base = (int32_t)ck;
+      P.groups.push_back(g);
+    }
+    pairs += (uint64_t)m * (uint64_t)(n - m + 1) + (uint64_t)m * (uint64_t)(m - 1) / 2;
+    cq += m;
+    ck += n;
+  }
+  P.total_q = cq;
+  P.total_k = ck;
+  P.pairs_total = pairs;
+  const int G = (int)P.groups.size();
+  // Key splits: aim for ~2 wavefronts per SIMD (1024 SIMDs) with >= 2048 keys per split.
+  int J = cfg.key_splits;
+  if (J <= 0) {
+    int64_t work_keys = 0;
+    for (auto& g : P.groups) work_keys += g.pos0 + g.nq;
+    const int64_t avg = G ? work_keys / G : 0;
+    J = 1;
+    while ((int64_t)G * J < 2048 && avg / (2 * J) >= 2048 && J < 64) J *= 2;
+  }
+  P.J = J;
+  if (dense) {
+    P.R = J;
+    for (int gi = 0; gi < G; ++gi) {
+      const GroupInfo& g = P.groups[gi];
+      const int n = g.pos0 + g.nq;   // visible range [0, n) of the group's last query
+      for (int r = 0; r < J; ++r) {
+        int lo = (int)((int64_t)n * r / J) & ~15, hi = (r == J - 1) ? n : ((int)((int64_t)n * (r + 1) / J) & ~15);
+        WorkItem it{};
+        it.group = gi;
+        it.region = r;
+        if (lo == 0) {
+          // the attention-sink block first, then newest to oldest
+          it.a0 = 0; it.a1 = std::min(16, hi);
+          it.b0 = std::min(16, hi); it.b1 = hi;
+        } else {
+          it.a0 = it.a1 = lo;
+          it.b0 = lo; it.b1 = hi;
+        }
+        P.items.push_back(it);
+      }
+    }
+  } else {
+    P.R = 1 + J;
+    int64_t loff = 0;
+    int max_bounded = 0;
+    for (int gi = 0; gi < G; ++gi) {
+      GroupInfo& g = P.groups[gi];
+      const int n = g.pos0 + g.nq;                 // keys of the group's last query
+      const int wlo = std::max(0, n - P.W);        // seed window start
+      const int f = std::min(P.F, wlo);            // seed prefix end
+      WorkItem it{};
+      it.group = gi;
+      it.region = 0;
+      it.a0 = 0; it.a1 = f;
+      it.b0 = wlo; it.b1 = n;
+      P.items.push_back(it);
+      g.n_bounded = wlo - f;                       // bounded keys: [f, wlo), visible to every query of the group
+      g.bound_lo = f;
+      g.list_off = (int32_t)loff;
+      g.list_cap = (g.n_bounded + 15) / 16 * 16;
+      loff += g.list_cap;
+      max_bounded = std::max(max_bounded, g.n_bounded);
+    }
+    P.n_seed_items = G;
+    for (int gi = 0; gi < G; ++gi)
+      for (int r = 0; r < J; ++r) {
+        WorkItem it{};
+        it.group = gi;
+        it.region = 1 + r;
+        it.gather = 1;
+        it.a0 = r;        // split index; the list length is read on the device
+        it.a1 = J;
+        P.items.push_back(it);
+      }
+    P.list_total = loff;
+    P.mask_words = (max_bounded + 63) / 64;
+  }
+  // workspace layout
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
+  P.o_groups = take(sizeof(GroupInfo) * std::max(G, 1));
+  P.o_items = take(sizeof(WorkItem) * std::max<size_t>(P.items.size(), 1));
+  P.o_cand = take((size_t)P.total_q * P.R * P.cap * sizeof(u64));
+  P.o_counts = take((size_t)P.total_q * P.R * sizeof(uint32_t));
+  if (!dense) {
+    P.o_tau = take((size_t)P.total_q * sizeof(float));
+    P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
+    P.o_coef = take((size_t)P.total_q * 8 * sizeof(float));
+    P.o_norms = take((size_t)std::max<int64_t>(P.total_k, 1) * sizeof(float));
+    P.o_normmin = take((size_t)std::max(batch, 1) * sizeof(float));
+    P.o_seqinfo = take((size_t)(batch + 1) * sizeof(int32_t));
+    P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
+    P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
+    P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
+  }
+  P.total = o;
+  (void)max_kv;
+}
+
+bool valid_ptrs(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
+                int32_t q_dtype, int32_t k_dtype, const int32_t* page_table, int32_t page_size,
+                int32_t max_pages, int32_t* out_idx, int64_t total_q) {
+  if (total_q > 0 && (q == nullptr || w == nullptr || k == nullptr || out_idx == nullptr)) return false;
+  if (total_q > 0 && q_dtype == DOSA_FP8_E4M3FN && q_scale == nullptr) return false;
+  if (total_q > 0 && k_dtype == DOSA_FP8_E4M3FN && k_scale == nullptr) return false;
+  if (page_table != nullptr && (page_size <= 0 || (page_size % 16) != 0 || max_pages <= 0)) return false;
+  return true;
+}
+
+int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const float* w, const void* k,
+        int32_t k_dtype, const float* k_scale, const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+        const int32_t* page_table, int32_t page_size, int32_t max_pages, int32_t H, int32_t d, int32_t topk,
+        int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes, const dosa_config& cfg,
+        dosa_stats* stats, hipStream_t stream);
+
+}  // namespace
+
+extern "C" {
+
+int dosa_default_config(int32_t topk, dosa_config* cfg) {
+  if (cfg == nullptr) return DOSA_ERR_INVALID_ARG;
+  std::memset(cfg, 0, sizeof(*cfg));
+  cfg->num_proxies = 3;
+  cfg->seed_window = 4096;
+  cfg->seed_prefix = 64;
+  cfg->buffer_cap = 2 * (topk > 0 ? topk : 2048) + 1024;
+  cfg->key_splits = 0;
+  cfg->neg_support_frac = 0.5f;
+  cfg->flags = 0;
+  cfg->debug_ub = nullptr;
+  return DOSA_OK;
+}
+
+size_t dosa_workspace_size(int32_t batch, const int32_t* q_lens, const int32_t* kv_lens, int32_t H, int32_t d,
+                           int32_t topk, int32_t q_dtype, int32_t k_dtype, int32_t paged, int32_t dense,
+                           const dosa_config* cfg) {
+  if (check_shapes(batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype) != DOSA_OK) return 0;
+  dosa_config c;
+  if (resolve_cfg(cfg, topk, &c) != DOSA_OK) return 0;
+  Plan P;
+  build_plan(P, batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype, paged != 0, dense != 0, c);
+  return std::max<size_t>(P.total, 256);
+}
+
+int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w, const void* k,
+                     int32_t k_dtype, const float* k_scale, const int32_t* q_lens, const int32_t* kv_lens,
+                     int32_t batch, const int32_t* page_table, int32_t page_size, int32_t max_pages, int32_t H,
+                     int32_t d, int32_t topk, int32_t* out_idx, float* out_score, void* workspace,
+                     size_t workspace_bytes, uint32_t flags, int32_t key_splits, dosa_stats* stats,
+                     void* stream) {
+  try {
+    int st = check_shapes(batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype);
+    if (st != DOSA_OK) return st;
+    dosa_config c;
+    dosa_default_config(topk, &c);
+    if (key_splits < 0) {
+      g_err = "key_splits < 0";
+      return DOSA_ERR_INVALID_ARG;
+    }
+    c.key_splits = key_splits;
+    c.flags = flags & DOSA_SORTED;
+    return run(true, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, batch, page_table, page_size,
+               max_pages, H, d, topk, out_idx, out_score, workspace, workspace_bytes, c, stats,
+               static_cast<hipStream_t>(stream));
+  } catch (...) {
+    g_err = "internal error";
+    return DOSA_ERR_HIP;
+  }
+}
+
+int dosa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w, const void* k,
+                      int32_t k_dtype, const float* k_scale, const int32_t* q_lens, const int32_t* kv_lens,
+                      int32_t batch, const int32_t* page_table, int32_t page_size, int32_t max_pages, int32_t H,
+                      int32_t d, int32_t topk, int32_t* out_idx, float* out_score, void* workspace,
+                      size_t workspace_bytes, const dosa_config* cfg, dosa_stats* stats, void* stream) {
+  try {
+    int st = check_shapes(batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype);
+    if (st != DOSA_OK) return st;
+    dosa_config c;
+    st = resolve_cfg(cfg, topk, &c);
+    if (st != DOSA_OK) return st;
+    return run(false, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, batch, page_table, page_size,
+               max_pages, H, d, topk, out_idx, out_score, workspace, workspace_bytes, c, stats,
+               static_cast<hipStream_t>(stream));
+  } catch (...) {
+    g_err = "internal error";
+    return DOSA_ERR_HIP;
+  }
+}
+
+const char* dosa_status_string(int status) {
+  switch (status) {
+    case DOSA_OK: return "ok";
+    case DOSA_ERR_INVALID_ARG: return g_err.empty() ? "invalid argument" : g_err.c_str();
+    case DOSA_ERR_UNSUPPORTED: return g_err.empty() ? "unsupported shape or dtype" : g_err.c_str();
+    case DOSA_ERR_WORKSPACE: return g_err.empty() ? "workspace too small" : g_err.c_str();
+    case DOSA_ERR_HIP: return g_err.empty() ? "HIP error" : g_err.c_str();
+  }
+  return "unknown status";
+}
+
+const char* dosa_version(void) { return "dosa-indexer 0.1 (gfx950)"; }
+
+}  // extern "C"
+
+namespace {
+
+int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const float* w, const void* k,
+        int32_t k_dtype, const float* k_scale, const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+        const int32_t* page_table, int32_t page_size, int32_t max_pages, int32_t H, int32_t d, int32_t topk,
+        int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes, const dosa_config& cfg,
+        dosa_stats* stats, hipStream_t stream) {
+  Plan P;
+  build_plan(P, batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype, page_table != nullptr, dense, cfg);
+  if (!valid_ptrs(q, q_scale, w, k, k_scale, q_dtype, k_dtype, page_table, page_size, max_pages, out_idx,
+                  P.total_q)) {
+    g_err = "null input/output pointer, missing fp8 scale or bad page geometry";
+    return DOSA_ERR_INVALID_ARG;
+  }
+  if (workspace == nullptr || workspace_bytes < P.total) {
+    g_err = "workspace needs " + std::to_string(P.total) + " bytes";
+    return DOSA_ERR_WORKSPACE;
+  }
+  if (P.total_q == 0) return DOSA_OK;
+  char* ws = static_cast<char*>(workspace);
+  unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
+  hipError_t e;
+  e = hipMemcpyAsync(ws + P.o_groups, P.groups.data(), sizeof(GroupInfo) * P.groups.size(),
+                     hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(groups)");
+  e = hipMemcpyAsync(ws + P.o_items, P.items.data(), sizeof(WorkItem) * P.items.size(), hipMemcpyHostToDevice,
+                     stream);
+  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(items)");
+  if (st) {
+    unsigned long long add[8] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0};
+    e = launch_stats_add(st, add, stream);
+    if (e != hipSuccess) return fail_hip(e, "stats");
+  }
+  Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages};
+  CandBuf cb{reinterpret_cast<u64*>(ws + P.o_cand), reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R, P.cap};
+  const GroupInfo* dg = reinterpret_cast<const GroupInfo*>(ws + P.o_groups);
+  const WorkItem* di = reinterpret_cast<const WorkItem*>(ws + P.o_items);
+  if (dense) {
+    ScoreLaunch sl{};
+    sl.in = in;
+    sl.groups = dg;
+    sl.items = di;
+    sl.n_items = (int)P.items.size();
+    sl.cb = cb;
+    sl.theta_init = nullptr;
+    sl.topk = topk;
+    sl.stats = st;
+    sl.scored_slot = 4;
+    e = launch_score(P.combo, H, d, sl, stream);
+    if (e != hipSuccess) return fail_hip(e, "score kernel launch");
+  } else {
+    const int G = (int)P.groups.size();
+    std::vector<int32_t> cu(batch + 1, 0);
+    int32_t max_kv = 0;
+    for (int b = 0; b < batch; ++b) {
+      cu[b + 1] = cu[b] + kv_lens[b];
+      max_kv = std::max(max_kv, kv_lens[b]);
+    }
+    int32_t* cu_dev = reinterpret_cast<int32_t*>(ws + P.o_seqinfo);
+    e = hipMemcpyAsync(cu_dev, cu.data(), sizeof(int32_t) * cu.size(), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(cu_kv)");
+    float* tau = reinterpret_cast<float*>(ws + P.o_tau);
+    float* norms = reinterpret_cast<float*>(ws + P.o_norms);
+    float* norm_min = reinterpret_cast<float*>(ws + P.o_normmin);
+    float* coef = reinterpret_cast<float*>(ws + P.o_coef);
+    u64* masks = reinterpret_cast<u64*>(ws + P.o_masks);
+    int32_t* lists = reinterpret_cast<int32_t*>(ws + P.o_lists);
+    int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
+    // 1. per-key norms
+    NormLaunch nl{in, cu_dev, batch, P.total_k, norms, norm_min};
+    e = launch_key_norms(P.combo, d, nl, stream);
+    if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
+    // 2. seed pass: exact scores of the seed keys into region 0
+    ScoreLaunch sl{};
+    sl.in = in;
+    sl.groups = dg;
+    sl.items = di;
+    sl.n_items = P.n_seed_items;
+    sl.cb = cb;
+    sl.topk = topk;
+    sl.stats = st;
+    sl.scored_slot = 1;
+    e = launch_score(P.combo, H, d, sl, stream);
+    if (e != hipSuccess) return fail_hip(e, "seed score kernel launch");
+    // 3. tau = K-th largest seed score
+    SelectLaunch ts{};
+    ts.cb = cb;
+    ts.total_q = (int32_t)P.total_q;
+    ts.topk = topk;
+    ts.r0 = 0;
+    ts.r1 = 1;
+    ts.tau_out = tau;
+    e = launch_select(ts, stream);
+    if (e != hipSuccess) return fail_hip(e, "seed select kernel launch");
+    // 4. certificate plan per query
+    PlanLaunch pl{};
+    pl.in = in;
+    pl.groups = dg;
+    pl.n_groups = G;
+    pl.num_proxies = cfg.num_proxies;
+    pl.seed_window = P.W;
+    pl.neg_frac = cfg.neg_support_frac;
+    pl.flags = cfg.flags;
+    pl.tau = tau;
+    pl.norm_min = norm_min;
+    pl.rows = ws + P.o_rows;
+    pl.coef = coef;
+    e = launch_plan(P.combo, H, d, pl, stream);
+    if (e != hipSuccess) return fail_hip(e, "plan kernel launch");
+    // 5. bound pass -> survivor bitmasks
+    BoundLaunch bl{};
+    bl.in = in;
+    bl.groups = dg;
+    bl.n_groups = G;
+    bl.rows = ws + P.o_rows;
+    bl.coef = coef;
+    bl.norms = norms;
+    bl.masks = masks;
+    bl.mask_words = std::max(P.mask_words, 1);
+    bl.debug_ub = cfg.debug_ub;
+    bl.debug_ld = max_kv;
+    bl.stats = st;
+    e = launch_bound(P.combo, H, d, bl, stream);
+    if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
+    // 6. compaction -> survivor key lists
+    CompactLaunch cl{dg, G, masks, std::max(P.mask_words, 1), lists, list_len};
+    e = launch_compact(cl, stream);
+    if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
+    // 7. survivors scored with all heads into regions 1..J, threshold starts at tau
+    ScoreLaunch ml{};
+    ml.in = in;
+    ml.groups = dg;
+    ml.items = di + P.n_seed_items;
+    ml.n_items = (int)P.items.size() - P.n_seed_items;
+    ml.cb = cb;
+    ml.theta_init = tau;
+    ml.lists = lists;
+    ml.list_len = list_len;
+    ml.topk = topk;
+    ml.stats = st;
+    ml.scored_slot = 4;
+    e = launch_score(P.combo, H, d, ml, stream);
+    if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
+  }
+  SelectLaunch se{};
+  se.cb = cb;
+  se.total_q = (int32_t)P.total_q;
+  se.topk = topk;
+  se.r0 = 0;
+  se.r1 = P.R;
+  se.out_idx = out_idx;
+  se.out_score = out_score;
+  se.tau_out = nullptr;
+  se.sorted = (cfg.flags & DOSA_SORTED) ? 1 : 0;
+  se.stats = st;
+  e = launch_select(se, stream);
+  if (e != hipSuccess) return fail_hip(e, "select kernel launch");
+  return DOSA_OK;
+}
+
+}  // namespace

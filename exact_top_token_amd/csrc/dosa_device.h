@@ -1,0 +1,273 @@
+// Device-side building blocks for gfx950: MFMA operand fragments, ordered
+// 64-bit candidate keys and the wavefront radix select.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dosa_internal.h"
+
+namespace dosa {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+typedef unsigned long long u64;
+
+// ---------------------------------------------------------------------------
+// Candidate keys.  A candidate (score, key position) is packed into one u64
+// whose unsigned order is the selection order: score descending, then
+// position ascending.  High word: the float's bits mapped to an unsigned
+// total order; low word: ~position.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f2ord(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float ord2f(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ u64 make_key(float s, int pos) {
+  return ((u64)f2ord(s) << 32) | (u64)(uint32_t)(~(uint32_t)pos);
+}
+__device__ __forceinline__ int key_pos(u64 e) { return (int)(~(uint32_t)e); }
+__device__ __forceinline__ float key_score(u64 e) { return ord2f((uint32_t)(e >> 32)); }
+
+// fp8 E4M3FN code -> bf16 bits, exact.  Normal codes (exponent field e>0):
+// (1+m/8)*2^(e-7) -> bf16 exponent field e+120, mantissa m<<4.  Subnormal
+// codes m*2^-9 go through an exact float.
+__device__ __forceinline__ uint32_t fp8_to_bf16_bits(uint32_t x) {
+  const uint32_t s = (x & 0x80u) << 8;
+  const uint32_t em = x & 0x7Fu;
+  const uint32_t normal = (em + (120u << 3)) << 4;
+  const uint32_t sub = __float_as_uint((float)(em & 7u) * 0.001953125f) >> 16;
+  return s | ((em >> 3) ? normal : sub);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA operand fragments.  For a 16x16xK MFMA, lane l supplies row (A) or
+// column (B) l%16; lane group g = l/16 supplies its share of the reduction
+// dimension.  Both operands use the same assignment: lane group g owns the
+// contiguous elements [g*d/4, (g+1)*d/4) of every row, split into STEPS
+// instructions, so each MFMA output is a full-length dot product.
+// ---------------------------------------------------------------------------
+template <int C, int D>
+struct Ops;
+
+template <int D>
+struct Ops<C_F32, D> {
+  static constexpr int STEPS = D / 4;
+  static constexpr int QB = 4, KB = 4;
+  typedef float frag;
+  __device__ __forceinline__ static void load_q(const void* row, int g, frag* f) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(row) + g * (D / 4));
+#pragma unroll
+    for (int v = 0; v < D / 16; ++v) {
+      float4 t = p[v];
+      f[4 * v] = t.x; f[4 * v + 1] = t.y; f[4 * v + 2] = t.z; f[4 * v + 3] = t.w;
+    }
+  }
+  __device__ __forceinline__ static void load_k(const void* row, int g, frag* f) { load_q(row, g, f); }
+  __device__ __forceinline__ static void zero(frag* f) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) f[s] = 0.f;
+  }
+  __device__ __forceinline__ static v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int D>
+struct Ops<C_BF16, D> {
+  static constexpr int STEPS = D / 32;
+  static constexpr int QB = 2, KB = 2;
+  typedef v8bf frag;
+  __device__ __forceinline__ static void load_q(const void* row, int g, frag* f) {
+    const v4i* p = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(row) + g * (D / 4));
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) f[s] = __builtin_bit_cast(v8bf, p[s]);
+  }
+  __device__ __forceinline__ static void load_k(const void* row, int g, frag* f) { load_q(row, g, f); }
+  __device__ __forceinline__ static void zero(frag* f) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) f[s] = __builtin_bit_cast(v8bf, v4i{0, 0, 0, 0});
+  }
+  __device__ __forceinline__ static v4f mma(frag a, frag b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <int D>
+struct Ops<C_FP8, D> {
+  static constexpr int STEPS = 1;
+  static constexpr int QB = 1, KB = 1;
+  typedef v8i frag;
+  __device__ __forceinline__ static void load_q(const void* row, int g, frag* f) {
+    const uint8_t* b = static_cast<const uint8_t*>(row);
+    if constexpr (D == 128) {
+      const v4i* p = reinterpret_cast<const v4i*>(b + 32 * g);
+      v4i lo = p[0], hi = p[1];
+      f[0] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const v4i* p = reinterpret_cast<const v4i*>(b + 16 * g);
+      v4i lo = p[0];
+      f[0] = v8i{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ static void load_k(const void* row, int g, frag* f) { load_q(row, g, f); }
+  __device__ __forceinline__ static void zero(frag* f) { f[0] = v8i{0, 0, 0, 0, 0, 0, 0, 0}; }
+  __device__ __forceinline__ static v4f mma(frag a, frag b, v4f c) {
+    // operand formats 0/0 = fp8 E4M3 for A and B; scales 127 = 2^0
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+  }
+};
+
+// bf16 queries against fp8 keys: keys are widened to bf16 (exact) in registers.
+template <int D>
+struct Ops<C_BF16Q_FP8K, D> {
+  static constexpr int STEPS = D / 32;
+  static constexpr int QB = 2, KB = 1;
+  typedef v8bf frag;
+  __device__ __forceinline__ static void load_q(const void* row, int g, frag* f) {
+    Ops<C_BF16, D>::load_q(row, g, f);
+  }
+  __device__ __forceinline__ static void load_k(const void* row, int g, frag* f) {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(row) + g * (D / 4));
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      uint32_t w0 = p[2 * s], w1 = p[2 * s + 1];
+      v4i v;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t w = h ? w1 : w0;
+        uint32_t b0 = fp8_to_bf16_bits(w & 0xFFu), b1 = fp8_to_bf16_bits((w >> 8) & 0xFFu);
+        uint32_t b2 = fp8_to_bf16_bits((w >> 16) & 0xFFu), b3 = fp8_to_bf16_bits(w >> 24);
+        v[2 * h] = (int)(b0 | (b1 << 16));
+        v[2 * h + 1] = (int)(b2 | (b3 << 16));
+      }
+      f[s] = __builtin_bit_cast(v8bf, v);
+    }
+  }
+  __device__ __forceinline__ static void zero(frag* f) { Ops<C_BF16, D>::zero(f); }
+  __device__ __forceinline__ static v4f mma(frag a, frag b, v4f c) { return Ops<C_BF16, D>::mma(a, b, c); }
+};
+
+template <int C>
+struct HasQScale { static constexpr bool value = (C == C_FP8); };
+template <int C>
+struct HasKScale { static constexpr bool value = (C == C_FP8 || C == C_BF16Q_FP8K); };
+
+// Queries per wavefront for a (combo, H, d): the largest of 4/2/1 whose
+// register-resident query rows fit 128 VGPRs and whose head slots (16/QW)
+// divide H.  MFMA row r = (query r/(16/QW), head slot r%(16/QW)).
+__host__ __device__ constexpr int queries_per_wave(int C, int H, int D) {
+  int qb = (C == C_F32) ? 4 : (C == C_FP8 ? 1 : 2);
+  int per = H * D * qb;
+  if (4 * per <= 32768 && H % 4 == 0) return 4;
+  if (2 * per <= 32768 && H % 8 == 0) return 2;
+  return 1;
+}
+
+// ---------------------------------------------------------------------------
+// Key addressing (contiguous or paged storage)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t key_row(const Inputs& in, int key_base, int seq, int key) {
+  if (in.page_table == nullptr) return (int64_t)key_base + key;
+  const int pg = in.page_table[(int64_t)seq * in.max_pages + key / in.page_size];
+  return (int64_t)pg * in.page_size + key % in.page_size;
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront helpers (one 64-lane wavefront per workgroup)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t o = __shfl_down(v, off, 64);
+    if (lane + off < 64) v += o;
+  }
+  return v;
+}
+
+// Segmented view of a query's candidate regions.
+struct Segs {
+  const u64* base;   // region 0 of this query
+  const uint32_t* counts;
+  int cap;
+  int nseg;
+  __device__ __forceinline__ uint32_t n(int r) const { return counts[r]; }
+  __device__ __forceinline__ const u64* ptr(int r) const { return base + (int64_t)r * cap; }
+};
+
+// K-th largest of the (distinct) entries of the segments, K >= 1 and
+// K <= total.  Radix select on 11/11/10-bit digits from the top; stops as soon
+// as the digit bin holding the K-th entry is taken whole.  Returns T with
+// exactly K entries >= T.  hist: 2048 u32 of LDS.
+__device__ __noinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) {
+  const int lane = lane_id();
+  u64 prefix = 0;
+  uint32_t rem = (uint32_t)K;
+  __syncthreads();
+#pragma unroll 1
+  for (int p = 0; p < 6; ++p) {
+    const int sh = (p == 0) ? 53 : (p == 1) ? 42 : (p == 2) ? 32 : (p == 3) ? 21 : (p == 4) ? 10 : 0;
+    const int wd = (p == 2 || p == 5) ? 10 : 11;
+    const int nb = 1 << wd;
+    const int hs = sh + wd;
+    for (int b = lane; b < nb; b += 64) hist[b] = 0;
+    __syncthreads();
+    const u64 want = (p == 0) ? 0 : (prefix >> hs);
+    for (int r = 0; r < sg.nseg; ++r) {
+      const u64* ptr = sg.ptr(r);
+      const uint32_t n = sg.n(r);
+      for (uint32_t i = lane; i < n; i += 64) {
+        const u64 e = ptr[i];
+        if (p == 0 || (e >> hs) == want) atomicAdd(&hist[(uint32_t)(e >> sh) & (uint32_t)(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    const int per = nb >> 6;
+    uint32_t s = 0;
+    for (int t = 0; t < per; ++t) s += hist[lane * per + t];
+    const uint32_t suf = wave_suffix_sum(s);
+    const bool cross = (suf >= rem) && (suf - s < rem);
+    const u64 cm = __ballot(cross);
+    const int L = cm ? (__ffsll((long long)cm) - 1) : 0;
+    uint32_t acc = __shfl(suf - s, L, 64);
+    int b = L * per;
+    uint32_t cnt_b = 0;
+    for (int t = per - 1; t >= 0; --t) {
+      const uint32_t h = hist[L * per + t];
+      if (acc + h >= rem) { b = L * per + t; cnt_b = h; break; }
+      acc += h;
+    }
+    rem -= acc;
+    prefix |= ((u64)(uint32_t)b) << sh;
+    __syncthreads();
+    if (cnt_b == rem) break;
+  }
+  return prefix;
+}
+
+// Copy the entries >= T of src[0..n) to dst[out..] in order (dst may equal
+// src).  Returns the new end.
+__device__ __forceinline__ uint32_t compact_ge(const u64* src, uint32_t n, u64 T, u64* dst, uint32_t out) {
+  const int lane = lane_id();
+  for (uint32_t base = 0; base < n; base += 64) {
+    const uint32_t i = base + lane;
+    const u64 e = (i < n) ? src[i] : 0ull;
+    const bool keep = (i < n) && (e >= T);
+    const u64 m = __ballot(keep);
+    const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+    if (keep && out + before < n) dst[out + before] = e;
+    out += __popcll(m);
+  }
+  return out;
+}
+
+}  // namespace dosa

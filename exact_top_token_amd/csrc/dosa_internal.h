@@ -1,0 +1,153 @@
+// Internal declarations shared by the host planner and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dosa_indexer.h"
+
+namespace dosa {
+
+// Operand combinations the kernels are built for.
+enum Combo : int { C_F32 = 0, C_BF16 = 1, C_FP8 = 2, C_BF16Q_FP8K = 3 };
+
+// A query group: up to 4 consecutive queries of one sequence, scored together
+// by one wavefront (MFMA rows = group queries x head slots).
+struct GroupInfo {
+  int32_t seq;       // sequence index
+  int32_t q_row0;    // global row of the first query
+  int32_t nq;        // queries in the group
+  int32_t pos0;      // position of the first query (queries are consecutive)
+  int32_t key_base;  // contiguous storage: row of the sequence's key 0
+  int32_t list_off;  // start of the group's survivor list (DoSA)
+  int32_t list_cap;  // capacity of that list
+  int32_t n_bounded; // keys the bound pass covers: [bound_lo, bound_lo + n_bounded)
+  int32_t bound_lo;  // first bounded key (end of the seed prefix)
+  int32_t norm_base; // index of the sequence's key 0 in the per-key norm array
+};
+
+// One wavefront's share of scoring: a group, a candidate region and the keys
+// to score.  Range mode walks [a0,a1) then [b0,b1), each from the top block
+// down; gather mode walks entries [b0,b1) of the group's survivor list.
+struct WorkItem {
+  int32_t group;
+  int32_t region;
+  int32_t a0, a1;
+  int32_t b0, b1;
+  int32_t gather;
+  int32_t pad;
+};
+
+// Where the inputs live, as the kernels see them.
+struct Inputs {
+  const void* q;
+  const float* q_scale;
+  const float* w;
+  const void* k;
+  const float* k_scale;
+  const int32_t* page_table;  // NULL = contiguous
+  int32_t page_size;
+  int32_t max_pages;
+};
+
+// Candidate buffers: entry (q_row, region, i) at cand[(q_row*R + region)*cap + i];
+// counts[q_row*R + region].
+struct CandBuf {
+  unsigned long long* cand;
+  uint32_t* counts;
+  int32_t R;
+  int32_t cap;
+};
+
+struct ScoreLaunch {
+  Inputs in;
+  const GroupInfo* groups;
+  const WorkItem* items;
+  int32_t n_items;
+  CandBuf cb;
+  const float* theta_init;   // [total_q] or NULL (-inf)
+  const int32_t* lists;      // survivor lists (gather mode)
+  const int32_t* list_len;   // survivor list length per group (gather mode)
+  int32_t topk;
+  int32_t scored_slot;       // dosa_stats field (u64 index) that counts scored pairs
+  unsigned long long* stats; // dosa_stats as u64[8] or NULL
+};
+
+struct SelectLaunch {
+  CandBuf cb;
+  int32_t total_q;
+  int32_t topk;
+  int32_t r0, r1;            // regions merged: [r0, r1)
+  int32_t* out_idx;          // NULL: threshold-only mode
+  float* out_score;
+  float* tau_out;            // K-th score per query (-inf if fewer than K), or NULL
+  int32_t sorted;
+  unsigned long long* stats;
+};
+
+// Certificate plan: per query 4 operand rows of d elements in the query
+// storage type (proxy rows first, then terms of the negative aggregate) and 8
+// fp32 coefficients:
+//   coef[0..3] : per-row multiplier (proxy rows: c_p * q_scale; aggregate
+//                rows: sigma_j * q_scale)
+//   coef[4]    : rho' * q_scale (joint residual constant plus rounding margin)
+//   coef[5]    : tau (seed threshold)
+//   coef[6]    : number of proxy rows p (rows p..3 are aggregate terms)
+//   coef[7]    : 1 if the certificate cannot prune any key of this query
+struct PlanLaunch {
+  Inputs in;
+  const GroupInfo* groups;
+  int32_t n_groups;
+  int32_t num_proxies;
+  int32_t seed_window;
+  float neg_frac;
+  uint32_t flags;
+  const float* tau;          // [total_q]
+  const float* norm_min;     // [batch] smallest key norm per sequence
+  void* rows;                // [total_q, 4, d] query storage type
+  float* coef;               // [total_q, 8]
+};
+
+struct BoundLaunch {
+  Inputs in;
+  const GroupInfo* groups;
+  int32_t n_groups;
+  const void* rows;
+  const float* coef;
+  const float* norms;        // per logical key, sequences back to back
+  unsigned long long* masks; // [n_groups, mask_words]
+  int32_t mask_words;
+  float* debug_ub;           // [total_q, debug_ld] or NULL
+  int32_t debug_ld;
+  unsigned long long* stats;
+};
+
+struct CompactLaunch {
+  const GroupInfo* groups;
+  int32_t n_groups;
+  const unsigned long long* masks;
+  int32_t mask_words;
+  int32_t* lists;
+  int32_t* list_len;
+};
+
+struct NormLaunch {
+  Inputs in;
+  const int32_t* cu_kv;      // [batch+1] logical key offsets
+  int32_t batch;
+  int64_t total_k;
+  float* norms;              // [total_k]
+  float* norm_min;           // [batch]
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s);
+hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
+hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s);
+hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t s);
+hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream_t s);
+hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
+hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* host_vals, hipStream_t s);
+
+bool combo_supported(int combo, int H, int d);
+
+}  // namespace dosa

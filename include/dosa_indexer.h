@@ -1,0 +1,169 @@
+/*
+ * dosa_indexer.h -- exact Top-K selection for the DSA sparse-attention indexer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (DoSA pages: podcast transcript of "DOSA: Dots Sparse
+ * Attention", Method section, problem formulation; the DSA indexer score):
+ * every query t carries H indexer heads with query vectors q[t,h,:] and
+ * signed weights w[t,h]; all heads share one key k[s,:] per token.  The score
+ * of key s for query t is
+ *
+ *     S(t,s) = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:])
+ *
+ * and each query keeps the K visible keys of highest score.  Causality: query
+ * i of sequence b sits at position kv_lens[b] - q_lens[b] + i and sees the
+ * keys at positions 0..position.  Ties are broken towards the lower position.
+ * When fewer than K keys are visible, all of them are returned followed by -1.
+ *
+ * Two entry points compute the same set:
+ *   dsa_indexer_topk   scores every visible key (dense scoring with a
+ *                      streaming Top-K; the plain method).
+ *   dosa_indexer_topk  the DoSA way (same pages, Method section: seed subset
+ *                      threshold, certificate built from nonnegative head
+ *                      projections, a joint residual bound and an
+ *                      activation-informed negative-head aggregate; zicq.com
+ *                      summary, items 1-3; picx.dev item, sections 02-03):
+ *                      a seed pass scores a seed subset exactly and takes its
+ *                      K-th score as a threshold tau; a bound pass computes a
+ *                      conservative upper bound per key; keys whose bound is
+ *                      below tau are dropped; survivors are compacted and
+ *                      scored with all heads; then the exact Top-K.  The
+ *                      selected set is identical to dsa_indexer_topk's, bit
+ *                      for bit, for every configuration.
+ *
+ * Layouts (all row-major, all pointers below are DEVICE pointers unless said):
+ *   q        [total_q, H, d] of q_dtype; queries of the batch back to back
+ *            (total_q = sum q_lens).
+ *   q_scale  [total_q] fp32, required iff q_dtype == DOSA_FP8_E4M3FN (one
+ *            scale per query token across all heads); ignored otherwise.
+ *   w        [total_q, H] fp32 (any sign).
+ *   k        contiguous (page_table == NULL): [total_k, d] of k_dtype,
+ *            sequence b's keys at rows sum(kv_lens[0..b-1]) + position;
+ *            paged: [num_pages, page_size, d], logical key j of sequence b in
+ *            pool page page_table[b*max_pages + j/page_size], slot j%page_size.
+ *   k_scale  per key token fp32 ([total_k] or [num_pages, page_size]),
+ *            required iff k_dtype == DOSA_FP8_E4M3FN.
+ *   fp8 values are OCP E4M3FN; the value of a code is scale * decode(code).
+ *   q_lens, kv_lens  HOST int32 [batch], 0 <= q_lens[b] <= kv_lens[b].
+ *   out_idx  [total_q, topk] int32: logical key positions, -1 padding.
+ *   out_score [total_q, topk] fp32 or NULL: the fp32 score of each returned
+ *            key (-inf padding).
+ *   Row order inside out_idx is unspecified unless DOSA_SORTED is set (then
+ *   score descending, position ascending); it is deterministic run to run.
+ *
+ * Supported: d in {64, 128}; H in {8, 16, 32, 64}; 1 <= topk <= 4096;
+ * (q_dtype, k_dtype) in {(F32,F32), (BF16,BF16), (FP8,FP8), (BF16,FP8)}.
+ * Inputs must be finite.
+ *
+ * Ownership and synchronisation: the caller owns every buffer, including the
+ * workspace (size from dosa_workspace_size).  The library allocates nothing
+ * and keeps no state between calls; everything is enqueued on `stream`
+ * (a hipStream_t, NULL = default stream) and no call waits for the device.
+ * Outputs, workspace contents and stats are valid once the stream has
+ * completed.  Calls on distinct workspaces/streams may run concurrently.
+ *
+ * Errors: 0 on success or a negative dosa_status.  On error nothing has been
+ * enqueued.  No C++ exception crosses this interface.
+ */
+#ifndef DOSA_INDEXER_H_
+#define DOSA_INDEXER_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DOSA_F32 = 0,
+  DOSA_BF16 = 1,
+  DOSA_FP8_E4M3FN = 2
+} dosa_dtype;
+
+typedef enum {
+  DOSA_OK = 0,
+  DOSA_ERR_INVALID_ARG = -1,     /* null pointer, bad length, q_lens > kv_lens, ... */
+  DOSA_ERR_UNSUPPORTED = -2,     /* dtype combination, d, H or topk outside the supported set */
+  DOSA_ERR_WORKSPACE = -3,       /* workspace NULL or smaller than dosa_workspace_size */
+  DOSA_ERR_HIP = -4              /* a HIP runtime call or kernel launch failed */
+} dosa_status;
+
+/* flags */
+#define DOSA_NO_PRUNE 0x1u        /* dosa_indexer_topk: skip the bound pass (every key survives) */
+#define DOSA_SORTED 0x2u          /* rows of out_idx in (score desc, position asc) order */
+#define DOSA_SEPARABLE_RHO 0x4u   /* residual bound sum_h w_h ||r_h|| instead of the joint bound */
+#define DOSA_NO_NEGATIVE 0x8u     /* drop the negative-head aggregate from the bound */
+
+/* Knobs of dosa_indexer_topk.  None of them changes the selected set; they
+ * only change how much work the certificate saves. */
+typedef struct {
+  int32_t num_proxies;      /* positive heads evaluated exactly in the bound: 0..3 (default 3) */
+  int32_t seed_window;      /* seed = the last seed_window visible keys ... (default 4096) */
+  int32_t seed_prefix;      /* ... plus the first seed_prefix keys (default 64) */
+  int32_t buffer_cap;       /* per-query candidate buffer, entries; >= topk + 64 (default 2*topk + 1024) */
+  int32_t key_splits;       /* key ranges scored in parallel per query group; 0 = automatic */
+  float neg_support_frac;   /* negative head joins the aggregate if positive on >= this
+                               fraction of the sampled seed keys (default 0.5) */
+  uint32_t flags;           /* DOSA_* flags */
+  float* debug_ub;          /* optional DEVICE [total_q, max_kv] fp32: certificate value per
+                               bounded key (NaN elsewhere); for testing only */
+} dosa_config;
+
+/* Device-resident counters, accumulated (not reset) by each call that gets a
+ * non-NULL pointer.  Pairs are causal (query, visible key) pairs. */
+typedef struct {
+  uint64_t pairs_total;        /* all visible pairs */
+  uint64_t pairs_seed;         /* pairs scored exactly in the seed pass */
+  uint64_t pairs_bounded;      /* pairs given a certificate (non-seed) */
+  uint64_t pairs_survived;     /* bounded pairs whose certificate reached tau */
+  uint64_t pairs_scored;       /* pairs scored with all heads after the seed (incl. tile union) */
+  uint64_t candidates_written; /* entries appended to candidate buffers */
+  uint64_t reselects;          /* in-kernel buffer re-selections */
+  uint64_t groups_skipped;     /* query groups whose certificate could prune nothing */
+} dosa_stats;
+
+/* Fill *cfg with the defaults for a given topk. */
+int dosa_default_config(int32_t topk, dosa_config* cfg);
+
+/* Bytes of device workspace the call with these shapes needs. q_lens/kv_lens
+ * are HOST arrays.  paged != 0 if a page table will be passed.  cfg NULL =
+ * defaults.  dense != 0 sizes for dsa_indexer_topk, 0 for dosa_indexer_topk.
+ * Returns 0 for invalid arguments. */
+size_t dosa_workspace_size(int32_t batch, const int32_t* q_lens, const int32_t* kv_lens,
+                           int32_t H, int32_t d, int32_t topk, int32_t q_dtype, int32_t k_dtype,
+                           int32_t paged, int32_t dense, const dosa_config* cfg);
+
+/* DoSA path: certificate-pruned exact Top-K.  stats: DEVICE pointer or NULL. */
+int dosa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                      const void* k, int32_t k_dtype, const float* k_scale,
+                      const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+                      const int32_t* page_table, int32_t page_size, int32_t max_pages,
+                      int32_t H, int32_t d, int32_t topk,
+                      int32_t* out_idx, float* out_score,
+                      void* workspace, size_t workspace_bytes,
+                      const dosa_config* cfg, dosa_stats* stats, void* stream);
+
+/* Dense path: every visible key scored with all heads, streaming exact Top-K.
+ * flags: DOSA_SORTED or 0.  key_splits as in dosa_config (0 = automatic). */
+int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                     const void* k, int32_t k_dtype, const float* k_scale,
+                     const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+                     const int32_t* page_table, int32_t page_size, int32_t max_pages,
+                     int32_t H, int32_t d, int32_t topk,
+                     int32_t* out_idx, float* out_score,
+                     void* workspace, size_t workspace_bytes,
+                     uint32_t flags, int32_t key_splits, dosa_stats* stats, void* stream);
+
+/* Human-readable text for a status code (static storage; for DOSA_ERR_HIP it
+ * names the failing HIP call of the most recent error on this thread). */
+const char* dosa_status_string(int status);
+
+/* Library version string. */
+const char* dosa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DOSA_INDEXER_H_ */

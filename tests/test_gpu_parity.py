@@ -1,0 +1,188 @@
+"""GPU parity: both entry points against the oracle, and the pruned path
+against the dense path (bit-identical selection), through the C-ABI."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from parity_helpers import assert_same_selection, check_vs_oracle, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, path, **kw):
+    from exact_top_token_amd.runner import run_once
+
+    print(f"[gpu] {wl.name} {path} q={wl.total_q} H={wl.H} d={wl.d} K={wl.topk} {wl.q_dtype}/{wl.k_dtype} {kw}",
+          flush=True)
+    return run_once(wl, path, **kw)
+
+
+def _both(wl, rows=None, cfg=None, **kw):
+    di, ds, dst = _run(wl, "dsa", **kw)
+    pi, ps, pst = _run(wl, "dosa", cfg=cfg, **kw)
+    assert_same_selection(pi, ps, di, ds)
+    if rows is not None:
+        check_vs_oracle(wl, di, ds, rows)
+    return (di, ds, dst), (pi, ps, pst)
+
+
+def test_tiny_prefill_all_rows():
+    wl = synth.tiny_prefill()
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=np.arange(wl.total_q))
+    assert dst["pairs_total"] == wl.pairs() == dst["pairs_scored"]
+    assert pst["pairs_seed"] + pst["pairs_bounded"] == wl.pairs()
+
+
+def test_structured_bf16_4k():
+    wl = synth.dsa_prefill_32k(L=4096)
+    _both(wl, rows=sample_rows(wl, 40))
+
+
+def test_fp8_chunked_prefill():
+    import torch
+
+    from exact_top_token_amd.runner import Runner, slice_chunk, to_device
+
+    wl = synth.long_prefill_128k(L=8192, chunk=4096)
+    inp = to_device(wl)
+    outs = {}
+    for path in ("dsa", "dosa"):
+        idx = np.zeros((wl.total_q, wl.topk), np.int32)
+        sc = np.zeros((wl.total_q, wl.topk), np.float32)
+        for c in wl.chunk_calls():
+            print(f"[gpu] fp8 chunk {c} {path}", flush=True)
+            r = Runner(slice_chunk(inp, c["q0"], c["q_len"], c["kv_len"]), path)
+            a, b = r()
+            torch.cuda.synchronize()
+            idx[c["q0"]:c["q0"] + c["q_len"]] = a.cpu().numpy()
+            sc[c["q0"]:c["q0"] + c["q_len"]] = b.cpu().numpy()
+        outs[path] = (idx, sc)
+    assert_same_selection(*outs["dosa"], *outs["dsa"])
+    check_vs_oracle(wl, *outs["dsa"], sample_rows(wl, 24))
+
+
+def test_decode_paged_bf16q_fp8k():
+    wl = synth.decode_mtp(batch=6, kv_min=3000, kv_max=20000)
+    _both(wl, rows=np.arange(wl.total_q))
+
+
+@pytest.mark.parametrize("qd,kd", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
+@pytest.mark.parametrize("page", [0, 16])
+@pytest.mark.parametrize("K", [16, 300])
+def test_edge_shapes(qd, kd, page, K):
+    lens = [(1, 1), (3, 5), (0, 7), (17, 17), (5, 300), (2, 129), (33, 1000)]
+    wl = synth.custom(3, lens, H=8, d=64, topk=K, q_dtype=qd, k_dtype=kd, page_size=page)
+    _both(wl, rows=np.arange(wl.total_q))
+
+
+def test_h64_d64_and_h32_d128():
+    for H, d in ((64, 64), (32, 128), (16, 128)):
+        wl = synth.custom(4, [(9, 700), (4, 4)], H=H, d=d, topk=64, q_dtype="bf16", k_dtype="bf16")
+        _both(wl, rows=np.arange(wl.total_q))
+
+
+def test_correlated_heads_prunes_and_matches():
+    import exact_top_token_amd as E
+
+    wl = synth.correlated_heads(L=8192)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 2048
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 24), cfg=cfg)
+    assert pst["pairs_bounded"] > 0
+    print("correlated stats", pst, flush=True)
+    assert pst["pairs_survived"] < pst["pairs_bounded"], "certificate pruned nothing on the correlated recipe"
+
+
+@pytest.mark.parametrize("knob", ["p0", "p1", "p2", "w64", "w512", "cap", "noprune", "separable", "noneg",
+                                  "splits3", "frac0", "frac1"])
+def test_knob_invariance(knob):
+    import exact_top_token_amd as E
+    from exact_top_token_amd.runner import run_once
+
+    wl = synth.correlated_heads(L=3000, topk=128)
+    di, ds, _ = run_once(wl, "dsa")
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 512
+    ks = 0
+    if knob.startswith("p"):
+        cfg.num_proxies = int(knob[1])
+    elif knob == "w64":
+        cfg.seed_window = 64
+    elif knob == "w512":
+        cfg.seed_window = 512
+    elif knob == "cap":
+        cfg.buffer_cap = wl.topk + 64
+    elif knob == "noprune":
+        cfg.flags |= E.DOSA_NO_PRUNE
+    elif knob == "separable":
+        cfg.flags |= E.DOSA_SEPARABLE_RHO
+    elif knob == "noneg":
+        cfg.flags |= E.DOSA_NO_NEGATIVE
+    elif knob == "splits3":
+        ks = 3
+    elif knob == "frac0":
+        cfg.neg_support_frac = 0.0
+    elif knob == "frac1":
+        cfg.neg_support_frac = 1.0
+    print(f"[gpu] knob {knob}", flush=True)
+    pi, ps, _ = run_once(wl, "dosa", cfg=cfg, key_splits=ks)
+    assert_same_selection(pi, ps, di, ds)
+
+
+def test_dense_small_buffer_and_splits():
+    import torch
+
+    from exact_top_token_amd.runner import Runner, to_device
+
+    wl = synth.dsa_prefill_32k(L=3000, topk=256)
+    base = _run(wl, "dsa")
+    inp = to_device(wl)
+    for ks in (1, 2, 5):
+        # 3000 keys per query against a 2K+1024 buffer: every split re-selects in-kernel
+        r = Runner(inp, "dsa", key_splits=ks)
+        a, b = r()
+        torch.cuda.synchronize()
+        assert_same_selection(a.cpu().numpy(), b.cpu().numpy(), base[0], base[1])
+
+
+def test_determinism_and_sorted_rows():
+    wl = synth.dsa_prefill_32k(L=2500, topk=256)
+    a = _run(wl, "dosa")
+    b = _run(wl, "dosa")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    c = _run(wl, "dsa", sorted_rows=True)
+    assert_same_selection(c[0], c[1], a[0], a[1])
+    for r in range(wl.total_q):
+        v = c[0][r] >= 0
+        s, i = c[1][r][v], c[0][r][v]
+        assert np.all((s[:-1] > s[1:]) | ((s[:-1] == s[1:]) & (i[:-1] < i[1:]))), r
+
+
+def test_bound_dump_dominates_oracle_scores():
+    import torch
+
+    import exact_top_token_amd as E
+    from exact_top_token_amd.runner import Runner, to_device
+    from oracle import indexer
+
+    for wl in (synth.tiny_prefill(L=1024, topk=64), synth.correlated_heads(L=3000, topk=128)):
+        inp = to_device(wl)
+        maxkv = int(max(wl.kv_lens))
+        dbg = torch.full((wl.total_q, maxkv), float("nan"), dtype=torch.float32, device="cuda")
+        cfg = E.default_config(wl.topk)
+        cfg.seed_window = 256
+        cfg.debug_ub = dbg.data_ptr()
+        r = Runner(inp, "dosa", cfg)
+        r()
+        torch.cuda.synchronize()
+        ub = dbg.cpu().numpy()
+        rows = sample_rows(wl, 16)
+        _, sc, theta = indexer.topk_rows(wl, rows)
+        for j, q in enumerate(rows):
+            keys = np.nonzero(~np.isnan(ub[q]))[0]
+            if keys.size == 0:
+                continue
+            S, A = indexer.score_pairs(wl, np.full(keys.size, q), keys)
+            assert np.all(ub[q, keys] >= S - 1e-6 * A), f"{wl.name} row {q}: bound below score"
