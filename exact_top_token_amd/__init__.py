@@ -32,7 +32,7 @@ STATUS = {0: "DOSA_OK", -1: "DOSA_ERR_INVALID_ARG", -2: "DOSA_ERR_UNSUPPORTED", 
           -4: "DOSA_ERR_HIP"}
 
 EXPORTS = ("dosa_default_config", "dosa_workspace_size", "dosa_indexer_topk", "dsa_indexer_topk",
-           "dosa_status_string", "dosa_version")
+           "dosa_status_string", "dosa_version", "dosa_profile_begin", "dosa_profile_end")
 
 
 class DosaConfig(ctypes.Structure):
@@ -55,6 +55,10 @@ class DosaStats(ctypes.Structure):
 
 
 STAT_FIELDS = [f[0] for f in DosaStats._fields_]
+
+
+class DosaKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("total_ms", ctypes.c_double)]
 
 
 class DosaError(RuntimeError):
@@ -88,8 +92,26 @@ def lib():
         L.dosa_status_string.restype = ctypes.c_char_p
         L.dosa_version.argtypes = []
         L.dosa_version.restype = ctypes.c_char_p
+        L.dosa_profile_begin.argtypes = []
+        L.dosa_profile_begin.restype = ctypes.c_int
+        L.dosa_profile_end.argtypes = [ctypes.POINTER(DosaKernelTime), i32]
+        L.dosa_profile_end.restype = ctypes.c_int
         _lib = L
     return _lib
+
+
+def profile_begin() -> None:
+    """Start bracketing every kernel this thread enqueues with HIP events."""
+    lib().dosa_profile_begin()
+
+
+def profile_end() -> dict:
+    """Wait for the recorded events; {pass name: (launches, total ms)}."""
+    buf = (DosaKernelTime * 32)()
+    n = lib().dosa_profile_end(buf, 32)
+    if n < 0:
+        raise DosaError(n, status_string(n))
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}
 
 
 def status_string(status: int) -> str:

@@ -18,6 +18,47 @@ namespace {
 
 thread_local std::string g_err;
 
+// ---------------------------------------------------------------------------
+// optional per-pass event timing
+// ---------------------------------------------------------------------------
+enum PassId { P_NORMS = 0, P_SCORE_SEED, P_SELECT_SEED, P_PLAN, P_BOUND, P_COMPACT, P_SCORE_SURV, P_SCORE_DENSE,
+              P_SELECT_FINAL, P_COUNT };
+const char* const kPassNames[P_COUNT] = {"key_norms", "score_seed", "select_seed", "plan", "bound",
+                                         "compact", "score_survivors", "score_dense", "select_final"};
+
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  std::vector<std::pair<int, size_t>> recs;   // (pass, index of start event; stop = +1)
+  hipEvent_t next() {
+    if (used == pool.size()) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      pool.push_back(e);
+    }
+    return pool[used++];
+  }
+};
+thread_local Profiler g_prof;
+
+struct PassScope {
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  PassScope(int pass, hipStream_t st) : s(st) {
+    if (!g_prof.on) return;
+    const size_t at = g_prof.used;
+    hipEvent_t a = g_prof.next(), b = g_prof.next();
+    if (!a || !b) return;
+    hipEventRecord(a, s);
+    stop = b;
+    g_prof.recs.push_back({pass, at});
+  }
+  ~PassScope() {
+    if (stop) hipEventRecord(stop, s);
+  }
+};
+
 int fail_hip(hipError_t e, const char* what) {
   g_err = std::string(what) + ": " + hipGetErrorString(e);
   return DOSA_ERR_HIP;
@@ -319,6 +360,43 @@ const char* dosa_status_string(int status) {
 
 const char* dosa_version(void) { return "dosa-indexer 0.1 (gfx950)"; }
 
+int dosa_profile_begin(void) {
+  g_prof.on = true;
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  return DOSA_OK;
+}
+
+int dosa_profile_end(dosa_kernel_time* out, int32_t max_entries) {
+  if (!g_prof.on) return 0;
+  g_prof.on = false;
+  double ms[P_COUNT] = {0};
+  int n[P_COUNT] = {0};
+  for (auto& r : g_prof.recs) {
+    hipEvent_t a = g_prof.pool[r.second], b = g_prof.pool[r.second + 1];
+    hipError_t e = hipEventSynchronize(b);
+    if (e != hipSuccess) return fail_hip(e, "hipEventSynchronize");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, a, b);
+    if (e != hipSuccess) return fail_hip(e, "hipEventElapsedTime");
+    ms[r.first] += t;
+    n[r.first] += 1;
+  }
+  g_prof.recs.clear();
+  g_prof.used = 0;
+  int k = 0;
+  for (int i = 0; i < P_COUNT; ++i) {
+    if (n[i] == 0) continue;
+    if (out != nullptr && k < max_entries) {
+      out[k].name = kPassNames[i];
+      out[k].launches = n[i];
+      out[k].total_ms = ms[i];
+    }
+    ++k;
+  }
+  return std::min(k, max_entries);
+}
+
 }  // extern "C"
 
 namespace {
@@ -369,7 +447,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.topk = topk;
     sl.stats = st;
     sl.scored_slot = 4;
-    e = launch_score(P.combo, H, d, sl, stream);
+    {
+      PassScope ps(P_SCORE_DENSE, stream);
+      e = launch_score(P.combo, H, d, sl, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "score kernel launch");
   } else {
     const int G = (int)P.groups.size();
@@ -391,7 +472,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
     // 1. per-key norms
     NormLaunch nl{in, cu_dev, batch, P.total_k, norms, norm_min};
-    e = launch_key_norms(P.combo, d, nl, stream);
+    {
+      PassScope ps(P_NORMS, stream);
+      e = launch_key_norms(P.combo, d, nl, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
     // 2. seed pass: exact scores of the seed keys into region 0
     ScoreLaunch sl{};
@@ -403,7 +487,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.topk = topk;
     sl.stats = st;
     sl.scored_slot = 1;
-    e = launch_score(P.combo, H, d, sl, stream);
+    {
+      PassScope ps(P_SCORE_SEED, stream);
+      e = launch_score(P.combo, H, d, sl, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "seed score kernel launch");
     // 3. tau = K-th largest seed score
     SelectLaunch ts{};
@@ -413,7 +500,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ts.r0 = 0;
     ts.r1 = 1;
     ts.tau_out = tau;
-    e = launch_select(ts, stream);
+    {
+      PassScope ps(P_SELECT_SEED, stream);
+      e = launch_select(ts, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "seed select kernel launch");
     // 4. certificate plan per query
     PlanLaunch pl{};
@@ -428,7 +518,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     pl.norm_min = norm_min;
     pl.rows = ws + P.o_rows;
     pl.coef = coef;
-    e = launch_plan(P.combo, H, d, pl, stream);
+    {
+      PassScope ps(P_PLAN, stream);
+      e = launch_plan(P.combo, H, d, pl, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "plan kernel launch");
     // 5. bound pass -> survivor bitmasks
     BoundLaunch bl{};
@@ -443,11 +536,17 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.debug_ub = cfg.debug_ub;
     bl.debug_ld = max_kv;
     bl.stats = st;
-    e = launch_bound(P.combo, H, d, bl, stream);
+    {
+      PassScope ps(P_BOUND, stream);
+      e = launch_bound(P.combo, H, d, bl, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
     // 6. compaction -> survivor key lists
     CompactLaunch cl{dg, G, masks, std::max(P.mask_words, 1), lists, list_len};
-    e = launch_compact(cl, stream);
+    {
+      PassScope ps(P_COMPACT, stream);
+      e = launch_compact(cl, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
     // 7. survivors scored with all heads into regions 1..J, threshold starts at tau
     ScoreLaunch ml{};
@@ -462,7 +561,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ml.topk = topk;
     ml.stats = st;
     ml.scored_slot = 4;
-    e = launch_score(P.combo, H, d, ml, stream);
+    {
+      PassScope ps(P_SCORE_SURV, stream);
+      e = launch_score(P.combo, H, d, ml, stream);
+    }
     if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
   }
   SelectLaunch se{};
@@ -476,7 +578,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   se.tau_out = nullptr;
   se.sorted = (cfg.flags & DOSA_SORTED) ? 1 : 0;
   se.stats = st;
-  e = launch_select(se, stream);
+  {
+    PassScope ps(P_SELECT_FINAL, stream);
+    e = launch_select(se, stream);
+  }
   if (e != hipSuccess) return fail_hip(e, "select kernel launch");
   return DOSA_OK;
 }

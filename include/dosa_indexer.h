@@ -155,6 +155,24 @@ int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const
                      void* workspace, size_t workspace_bytes,
                      uint32_t flags, int32_t key_splits, dosa_stats* stats, void* stream);
 
+/* Per-pass timing (tracing for benchmarks).  Between dosa_profile_begin()
+ * and dosa_profile_end(), every kernel the calling thread enqueues through
+ * this library is bracketed by two HIP events recorded on the kernel's own
+ * stream.  dosa_profile_end() waits for those events, writes up to
+ * max_entries per-pass totals to out (HOST array) and returns the number of
+ * entries written, or a negative status.  Off by default; profiling creates
+ * HIP event objects (no device memory) and reuses them across sessions.
+ * Pass names: key_norms, score_seed, select_seed, plan, bound, compact,
+ * score_survivors, score_dense, select_final. */
+typedef struct {
+  const char* name;   /* static string */
+  int32_t launches;
+  double total_ms;    /* sum of the launches' event-to-event durations */
+} dosa_kernel_time;
+
+int dosa_profile_begin(void);
+int dosa_profile_end(dosa_kernel_time* out, int32_t max_entries);
+
 /* Human-readable text for a status code (static storage; for DOSA_ERR_HIP it
  * names the failing HIP call of the most recent error on this thread). */
 const char* dosa_status_string(int status);
