@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--paths", default="dosa,dsa")
+    ap.add_argument("--buffer-cap", type=int, default=0, help="candidate buffer entries per query (0 = default)")
+    ap.add_argument("--key-splits", type=int, default=0)
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (queries shard across GPUs "
@@ -109,6 +111,10 @@ def main():
     outs = {}
     for path in a.paths.split(","):
         cfg = E.default_config(K)
+        if a.buffer_cap:
+            cfg.buffer_cap = a.buffer_cap
+        if a.key_splits:
+            cfg.key_splits = a.key_splits
         ws_bytes = max(E.workspace_size(c.q_lens, c.kv_lens, c.H, c.d, K, c.q_dtype, c.k_dtype,
                                         c.page_table is not None, path == "dsa", cfg) for _, c in calls)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -121,7 +127,7 @@ def main():
                 if path == "dsa":
                     E.dsa_indexer_topk(c.q, c.q_dtype, c.q_scale, c.w, c.k, c.k_dtype, c.k_scale, c.q_lens,
                                        c.kv_lens, c.page_table, c.page_size, c.H, c.d, K, oi, None, ws,
-                                       stats=stats)
+                                       cfg=cfg, stats=stats)
                 else:
                     E.dosa_indexer_topk(c.q, c.q_dtype, c.q_scale, c.w, c.k, c.k_dtype, c.k_scale, c.q_lens,
                                         c.kv_lens, c.page_table, c.page_size, c.H, c.d, K, oi, None, ws,

@@ -86,7 +86,7 @@ def lib():
         common = [vp, i32, vp, vp, vp, i32, vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp, vp, vp, sz]
         L.dosa_indexer_topk.argtypes = common + [ctypes.POINTER(DosaConfig), vp, vp]
         L.dosa_indexer_topk.restype = ctypes.c_int
-        L.dsa_indexer_topk.argtypes = common + [u32, i32, vp, vp]
+        L.dsa_indexer_topk.argtypes = common + [ctypes.POINTER(DosaConfig), vp, vp]
         L.dsa_indexer_topk.restype = ctypes.c_int
         L.dosa_status_string.argtypes = [ctypes.c_int]
         L.dosa_status_string.restype = ctypes.c_char_p
@@ -180,9 +180,10 @@ def dosa_indexer_topk(q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_le
 
 
 def dsa_indexer_topk(q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, page_table, page_size,
-                     H, d, topk, out_idx, out_score, workspace, flags: int = 0, key_splits: int = 0,
+                     H, d, topk, out_idx, out_score, workspace, cfg: Optional[DosaConfig] = None,
                      stats=None, stream=None):
-    """Dense scoring of every visible key with streaming exact Top-K."""
-    tail = [int(flags), int(key_splits), _ptr(stats), _stream(stream)]
+    """Dense scoring of every visible key with streaming exact Top-K (uses cfg's
+    buffer_cap, key_splits and DOSA_SORTED)."""
+    tail = [ctypes.byref(cfg) if cfg is not None else None, _ptr(stats), _stream(stream)]
     return _call(lib().dsa_indexer_topk, tail, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens,
                  page_table, page_size, H, d, topk, out_idx, out_score, workspace)

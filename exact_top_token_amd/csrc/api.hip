@@ -22,9 +22,9 @@ thread_local std::string g_err;
 // optional per-pass event timing
 // ---------------------------------------------------------------------------
 enum PassId { P_NORMS = 0, P_SCORE_SEED, P_SELECT_SEED, P_PLAN, P_BOUND, P_COMPACT, P_SCORE_SURV, P_SCORE_DENSE,
-              P_SELECT_FINAL, P_COUNT };
+              P_SELECT_FINAL, P_PREP, P_COUNT };
 const char* const kPassNames[P_COUNT] = {"key_norms", "score_seed", "select_seed", "plan", "bound",
-                                         "compact", "score_survivors", "score_dense", "select_final"};
+                                         "compact", "score_survivors", "score_dense", "select_final", "prep"};
 
 struct Profiler {
   bool on = false;
@@ -82,13 +82,16 @@ struct Plan {
   bool dense = true;
   int64_t total_q = 0, total_k = 0;
   std::vector<GroupInfo> groups;
-  std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed items then main items
-  int n_seed_items = 0;
+  std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed, tiled-survivor, list-survivor items
+  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items;
+  bool tiled = true;
+  int bound_splits = 1;
   int mask_words = 0;
   int64_t list_total = 0;
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
-         o_norms = 0, o_normmin = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, total = 0;
+         o_norms = 0, o_normmin = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0,
+         o_lrows = 0, o_lsig = 0, o_lerr = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -134,6 +137,18 @@ int resolve_cfg(const dosa_config* in, int32_t topk, dosa_config* out) {
   return DOSA_OK;
 }
 
+struct TileInfo {
+  int first, n, n_last, seq;
+};
+
+// Split choice: enough work items to fill the GPU (target items), keeping at
+// least min_keys keys per split.
+int choose_splits(int64_t n_units, int64_t avg_keys, int64_t target, int64_t min_keys) {
+  int J = 1;
+  while (n_units * J < target && avg_keys / (2 * J) >= min_keys && J < 64) J *= 2;
+  return J;
+}
+
 void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv_lens, int32_t H, int32_t d,
                 int32_t topk, int32_t q_dtype, int32_t k_dtype, bool paged, bool dense,
                 const dosa_config& cfg) {
@@ -142,13 +157,13 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.dense = dense;
   P.cap = (cfg.buffer_cap + 63) / 64 * 64;
   P.F = cfg.seed_prefix;
-  P.W = std::max(cfg.seed_window, 16);
+  P.W = std::max(cfg.seed_window, 64);
+  const int TW = tile_waves();
   int64_t cq = 0, ck = 0;
   uint64_t pairs = 0;
-  int64_t max_kv = 0;
+  std::vector<TileInfo> tiles;
   for (int b = 0; b < batch; ++b) {
     const int m = q_lens[b], n = kv_lens[b];
-    max_kv = std::max<int64_t>(max_kv, n);
     for (int i = 0; i < m; i += P.QW) {
       GroupInfo g{};
       g.seq = b;
@@ -157,82 +172,145 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       g.pos0 = n - m + i;
       g.key_base = paged ? 0 : (int32_t)ck;
       g.norm_base = (int32_t)ck;
+      const int gi = (int)P.groups.size();
+      if (tiles.empty() || tiles.back().seq != b || tiles.back().n == TW) tiles.push_back({gi, 0, 0, b});
+      tiles.back().n += 1;
+      tiles.back().n_last = g.pos0 + g.nq;
       P.groups.push_back(g);
     }
     pairs += (uint64_t)m * (uint64_t)(n - m + 1) + (uint64_t)m * (uint64_t)(m - 1) / 2;
     cq += m;
     ck += n;
   }
+  for (auto& t : tiles)
+    for (int i = 0; i < t.n; ++i) {
+      P.groups[t.first + i].tile_first = t.first;
+      P.groups[t.first + i].tile_n = t.n;
+    }
   P.total_q = cq;
   P.total_k = ck;
   P.pairs_total = pairs;
   const int G = (int)P.groups.size();
-  // Key splits: aim for ~2 wavefronts per SIMD (1024 SIMDs) with >= 2048 keys per split.
-  int J = cfg.key_splits;
-  if (J <= 0) {
-    int64_t work_keys = 0;
-    for (auto& g : P.groups) work_keys += g.pos0 + g.nq;
-    const int64_t avg = G ? work_keys / G : 0;
-    J = 1;
-    while ((int64_t)G * J < 2048 && avg / (2 * J) >= 2048 && J < 64) J *= 2;
-  }
-  P.J = J;
+  const int NT = (int)tiles.size();
+  int64_t key_sum = 0;
+  for (auto& t : tiles) key_sum += t.n_last;
+  const int64_t avg_keys = NT ? key_sum / NT : 0;
+  // Tiles that hold few groups waste the tiled kernel's wavefronts: use one
+  // wavefront per group there (decode-like batches).
+  P.tiled = (NT > 0) && (G >= 4 * NT);
+  auto range_split = [](int lo_all, int hi_all, int r, int J, int align, int& lo, int& hi) {
+    const int64_t len = hi_all - lo_all;
+    lo = lo_all + (int)((len * r / J) / align * align);
+    hi = (r == J - 1) ? hi_all : lo_all + (int)((len * (r + 1) / J) / align * align);
+  };
   if (dense) {
-    P.R = J;
-    for (int gi = 0; gi < G; ++gi) {
-      const GroupInfo& g = P.groups[gi];
-      const int n = g.pos0 + g.nq;   // visible range [0, n) of the group's last query
-      for (int r = 0; r < J; ++r) {
-        int lo = (int)((int64_t)n * r / J) & ~15, hi = (r == J - 1) ? n : ((int)((int64_t)n * (r + 1) / J) & ~15);
-        WorkItem it{};
-        it.group = gi;
-        it.region = r;
-        if (lo == 0) {
-          // the attention-sink block first, then newest to oldest
-          it.a0 = 0; it.a1 = std::min(16, hi);
-          it.b0 = std::min(16, hi); it.b1 = hi;
-        } else {
-          it.a0 = it.a1 = lo;
-          it.b0 = lo; it.b1 = hi;
+    if (P.tiled) {
+      int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(NT, avg_keys, 256, 1024);
+      P.J = J;
+      for (const auto& t : tiles)
+        for (int r = 0; r < J; ++r) {
+          int lo, hi;
+          range_split(0, t.n_last, r, J, 64, lo, hi);
+          WorkItem it{};
+          it.group = t.first;
+          it.pad = t.n;
+          it.region = r;
+          if (lo == 0) {
+            it.a0 = 0; it.a1 = std::min(64, hi);   // the attention-sink tile first, then newest to oldest
+            it.b0 = it.a1; it.b1 = hi;
+          } else {
+            it.a0 = it.a1 = lo;
+            it.b0 = lo; it.b1 = hi;
+          }
+          P.items.push_back(it);
         }
-        P.items.push_back(it);
+    } else {
+      int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
+      P.J = J;
+      for (int gi = 0; gi < G; ++gi) {
+        const GroupInfo& g = P.groups[gi];
+        const int n = g.pos0 + g.nq;
+        for (int r = 0; r < J; ++r) {
+          int lo, hi;
+          range_split(0, n, r, J, 16, lo, hi);
+          WorkItem it{};
+          it.group = gi;
+          it.region = r;
+          if (lo == 0) {
+            it.a0 = 0; it.a1 = std::min(16, hi);
+            it.b0 = it.a1; it.b1 = hi;
+          } else {
+            it.a0 = it.a1 = lo;
+            it.b0 = lo; it.b1 = hi;
+          }
+          P.items.push_back(it);
+        }
       }
     }
+    P.R = P.J;
   } else {
-    P.R = 1 + J;
+    // seed pass per tile: the first F keys and the last W keys of the tile's
+    // last query; the keys in between get a certificate
     int64_t loff = 0;
     int max_bounded = 0;
-    for (int gi = 0; gi < G; ++gi) {
-      GroupInfo& g = P.groups[gi];
-      const int n = g.pos0 + g.nq;                 // keys of the group's last query
-      const int wlo = std::max(0, n - P.W);        // seed window start
-      const int f = std::min(P.F, wlo);            // seed prefix end
+    for (const auto& t : tiles) {
+      const int wlo = std::max(0, t.n_last - P.W);
+      const int f = std::min(P.F, wlo);
       WorkItem it{};
-      it.group = gi;
+      it.group = t.first;
+      it.pad = t.n;
       it.region = 0;
       it.a0 = 0; it.a1 = f;
-      it.b0 = wlo; it.b1 = n;
-      P.items.push_back(it);
-      g.n_bounded = wlo - f;                       // bounded keys: [f, wlo), visible to every query of the group
-      g.bound_lo = f;
-      g.list_off = (int32_t)loff;
-      g.list_cap = (g.n_bounded + 15) / 16 * 16;
-      loff += g.list_cap;
-      max_bounded = std::max(max_bounded, g.n_bounded);
+      it.b0 = wlo; it.b1 = t.n_last;
+      it.gather = 0;
+      P.seed_items.push_back(it);
+      for (int i = 0; i < t.n; ++i) {
+        GroupInfo& g = P.groups[t.first + i];
+        g.bound_lo = f;
+        g.n_bounded = wlo - f;
+        g.list_off = (int32_t)loff;
+        g.list_cap = (g.n_bounded + 15) / 16 * 16;
+        loff += g.list_cap;
+        max_bounded = std::max(max_bounded, g.n_bounded);
+      }
     }
-    P.n_seed_items = G;
+    const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
+    P.J = J;
+    P.R = 1 + J;
+    // survivors of tiles whose certificate can prune nothing: tiled kernel over the bounded range
+    for (const auto& t : tiles) {
+      const GroupInfo& g = P.groups[t.first];
+      for (int r = 0; r < J; ++r) {
+        int lo, hi;
+        range_split(g.bound_lo, g.bound_lo + g.n_bounded, r, J, 64, lo, hi);
+        WorkItem it{};
+        it.group = t.first;
+        it.pad = t.n;
+        it.region = 1 + r;
+        it.a0 = it.a1 = lo;
+        it.b0 = lo; it.b1 = hi;
+        P.surv_tiled_items.push_back(it);
+      }
+    }
+    // everything else: one wavefront per group over its compacted survivor list
     for (int gi = 0; gi < G; ++gi)
       for (int r = 0; r < J; ++r) {
         WorkItem it{};
         it.group = gi;
         it.region = 1 + r;
         it.gather = 1;
-        it.a0 = r;        // split index; the list length is read on the device
+        it.a0 = r;
         it.a1 = J;
-        P.items.push_back(it);
+        P.surv_list_items.push_back(it);
       }
+    P.items = P.seed_items;
+    P.items.insert(P.items.end(), P.surv_tiled_items.begin(), P.surv_tiled_items.end());
+    P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
     P.list_total = loff;
     P.mask_words = (max_bounded + 63) / 64;
+    int64_t bsum = 0;
+    for (auto& g : P.groups) bsum += g.n_bounded;
+    P.bound_splits = choose_splits(G, G ? bsum / G : 0, 4096, 4096);
   }
   // workspace layout
   size_t o = 0;
@@ -241,6 +319,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.o_items = take(sizeof(WorkItem) * std::max<size_t>(P.items.size(), 1));
   P.o_cand = take((size_t)P.total_q * P.R * P.cap * sizeof(u64));
   P.o_counts = take((size_t)P.total_q * P.R * sizeof(uint32_t));
+  const int LS = 16 / P.QW;   // weighted-query terms per query
+  P.o_lrows = take((size_t)P.total_q * LS * d * qbytes(q_dtype));
+  P.o_lsig = take((size_t)P.total_q * LS * sizeof(float));
+  P.o_lerr = take((size_t)P.total_q * 2 * sizeof(float));
   if (!dense) {
     P.o_tau = take((size_t)P.total_q * sizeof(float));
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
@@ -251,9 +333,9 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
+    P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
   }
   P.total = o;
-  (void)max_kv;
 }
 
 bool valid_ptrs(const void* q, const float* q_scale, const float* w, const void* k, const float* k_scale,
@@ -305,19 +387,14 @@ int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const
                      int32_t k_dtype, const float* k_scale, const int32_t* q_lens, const int32_t* kv_lens,
                      int32_t batch, const int32_t* page_table, int32_t page_size, int32_t max_pages, int32_t H,
                      int32_t d, int32_t topk, int32_t* out_idx, float* out_score, void* workspace,
-                     size_t workspace_bytes, uint32_t flags, int32_t key_splits, dosa_stats* stats,
-                     void* stream) {
+                     size_t workspace_bytes, const dosa_config* cfg, dosa_stats* stats, void* stream) {
   try {
     int st = check_shapes(batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype);
     if (st != DOSA_OK) return st;
     dosa_config c;
-    dosa_default_config(topk, &c);
-    if (key_splits < 0) {
-      g_err = "key_splits < 0";
-      return DOSA_ERR_INVALID_ARG;
-    }
-    c.key_splits = key_splits;
-    c.flags = flags & DOSA_SORTED;
+    st = resolve_cfg(cfg, topk, &c);
+    if (st != DOSA_OK) return st;
+    c.flags &= DOSA_SORTED;
     return run(true, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, batch, page_table, page_size,
                max_pages, H, d, topk, out_idx, out_score, workspace, workspace_bytes, c, stats,
                static_cast<hipStream_t>(stream));
@@ -433,12 +510,21 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "stats");
   }
   Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages};
+  PrepLaunch pr{q, w, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
+                reinterpret_cast<float*>(ws + P.o_lerr)};
+  {
+    PassScope ps(P_PREP, stream);
+    e = launch_prep(P.combo, H, d, pr, stream);
+  }
+  if (e != hipSuccess) return fail_hip(e, "prep kernel launch");
   CandBuf cb{reinterpret_cast<u64*>(ws + P.o_cand), reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R, P.cap};
   const GroupInfo* dg = reinterpret_cast<const GroupInfo*>(ws + P.o_groups);
   const WorkItem* di = reinterpret_cast<const WorkItem*>(ws + P.o_items);
   if (dense) {
     ScoreLaunch sl{};
     sl.in = in;
+    sl.lrows = pr.rows;
+    sl.lsig = pr.sig;
     sl.groups = dg;
     sl.items = di;
     sl.n_items = (int)P.items.size();
@@ -447,6 +533,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.topk = topk;
     sl.stats = st;
     sl.scored_slot = 4;
+    sl.tiled = P.tiled ? 1 : 0;
     {
       PassScope ps(P_SCORE_DENSE, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -470,6 +557,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     u64* masks = reinterpret_cast<u64*>(ws + P.o_masks);
     int32_t* lists = reinterpret_cast<int32_t*>(ws + P.o_lists);
     int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
+    int32_t* gflags = reinterpret_cast<int32_t*>(ws + P.o_gflags);
     // 1. per-key norms
     NormLaunch nl{in, cu_dev, batch, P.total_k, norms, norm_min};
     {
@@ -480,13 +568,16 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     // 2. seed pass: exact scores of the seed keys into region 0
     ScoreLaunch sl{};
     sl.in = in;
+    sl.lrows = pr.rows;
+    sl.lsig = pr.sig;
     sl.groups = dg;
     sl.items = di;
-    sl.n_items = P.n_seed_items;
+    sl.n_items = (int)P.seed_items.size();
     sl.cb = cb;
     sl.topk = topk;
     sl.stats = st;
     sl.scored_slot = 1;
+    sl.tiled = 1;
     {
       PassScope ps(P_SCORE_SEED, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -516,6 +607,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     pl.flags = cfg.flags;
     pl.tau = tau;
     pl.norm_min = norm_min;
+    pl.lerr = pr.err;
     pl.rows = ws + P.o_rows;
     pl.coef = coef;
     {
@@ -535,6 +627,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.mask_words = std::max(P.mask_words, 1);
     bl.debug_ub = cfg.debug_ub;
     bl.debug_ld = max_kv;
+    bl.splits = P.bound_splits;
+    bl.group_flags = gflags;
     bl.stats = st;
     {
       PassScope ps(P_BOUND, stream);
@@ -542,18 +636,20 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
     // 6. compaction -> survivor key lists
-    CompactLaunch cl{dg, G, masks, std::max(P.mask_words, 1), lists, list_len};
+    CompactLaunch cl{dg, G, masks, std::max(P.mask_words, 1), lists, list_len, gflags};
     {
       PassScope ps(P_COMPACT, stream);
       e = launch_compact(cl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
-    // 7. survivors scored with all heads into regions 1..J, threshold starts at tau
+    // 7. survivors scored with all heads into regions 1..J, threshold starts at tau:
+    //    tiles whose certificate prunes nothing take the tiled kernel over the
+    //    bounded range, the other groups walk their compacted lists
     ScoreLaunch ml{};
     ml.in = in;
+    ml.lrows = pr.rows;
+    ml.lsig = pr.sig;
     ml.groups = dg;
-    ml.items = di + P.n_seed_items;
-    ml.n_items = (int)P.items.size() - P.n_seed_items;
     ml.cb = cb;
     ml.theta_init = tau;
     ml.lists = lists;
@@ -561,9 +657,21 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ml.topk = topk;
     ml.stats = st;
     ml.scored_slot = 4;
+    ml.tile_flags = gflags;
     {
       PassScope ps(P_SCORE_SURV, stream);
+      ml.items = di + P.seed_items.size();
+      ml.n_items = (int)P.surv_tiled_items.size();
+      ml.tiled = 1;
+      ml.flag_mode = 1;
       e = launch_score(P.combo, H, d, ml, stream);
+      if (e == hipSuccess) {
+        ml.items = di + P.seed_items.size() + P.surv_tiled_items.size();
+        ml.n_items = (int)P.surv_list_items.size();
+        ml.tiled = 0;
+        ml.flag_mode = 2;
+        e = launch_score(P.combo, H, d, ml, stream);
+      }
     }
     if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
   }

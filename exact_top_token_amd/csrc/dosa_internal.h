@@ -23,11 +23,14 @@ struct GroupInfo {
   int32_t n_bounded; // keys the bound pass covers: [bound_lo, bound_lo + n_bounded)
   int32_t bound_lo;  // first bounded key (end of the seed prefix)
   int32_t norm_base; // index of the sequence's key 0 in the per-key norm array
+  int32_t tile_first;// first group of the tile (<= 8 consecutive groups) this group belongs to
+  int32_t tile_n;    // groups in that tile
 };
 
-// One wavefront's share of scoring: a group, a candidate region and the keys
-// to score.  Range mode walks [a0,a1) then [b0,b1), each from the top block
-// down; gather mode walks entries [b0,b1) of the group's survivor list.
+// A share of scoring: a group (list kernel) or a tile of up to 8 groups
+// starting at `group` (tiled kernel, `pad` = groups in the tile), a candidate
+// region and the keys.  Range mode walks [a0,a1) then [b0,b1), each from the
+// top down; gather mode walks split a0 of a1 of the group's survivor list.
 struct WorkItem {
   int32_t group;
   int32_t region;
@@ -58,8 +61,22 @@ struct CandBuf {
   int32_t cap;
 };
 
+// Weighted query sums (see prep.hip): rows [total_q, 16/QW, d] in the query
+// operand type, sig [total_q, 16/QW] term scales, err [total_q, 2] =
+// (||qbar - represented qbar||, sum_j sigma_j ||f_j||), unscaled units.
+struct PrepLaunch {
+  const void* q;
+  const float* w;
+  int64_t total_q;
+  void* rows;
+  float* sig;
+  float* err;
+};
+
 struct ScoreLaunch {
   Inputs in;
+  const void* lrows;         // weighted-query rows (PrepLaunch::rows)
+  const float* lsig;         // their scales (PrepLaunch::sig)
   const GroupInfo* groups;
   const WorkItem* items;
   int32_t n_items;
@@ -69,6 +86,9 @@ struct ScoreLaunch {
   const int32_t* list_len;   // survivor list length per group (gather mode)
   int32_t topk;
   int32_t scored_slot;       // dosa_stats field (u64 index) that counts scored pairs
+  int32_t tiled;             // 1: score_tiled_kernel, 0: score_list_kernel
+  const int32_t* tile_flags; // per group: 1 if the certificate prunes nothing in its tile (or NULL)
+  int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not
   unsigned long long* stats; // dosa_stats as u64[8] or NULL
 };
 
@@ -103,6 +123,7 @@ struct PlanLaunch {
   uint32_t flags;
   const float* tau;          // [total_q]
   const float* norm_min;     // [batch] smallest key norm per sequence
+  const float* lerr;         // [total_q, 2] weighted-query representation error and magnitude
   void* rows;                // [total_q, 4, d] query storage type
   float* coef;               // [total_q, 8]
 };
@@ -118,6 +139,8 @@ struct BoundLaunch {
   int32_t mask_words;
   float* debug_ub;           // [total_q, debug_ld] or NULL
   int32_t debug_ld;
+  int32_t splits;            // key splits per group (grid = n_groups * splits)
+  int32_t* group_flags;      // out: 1 if no query of the group can prune anything
   unsigned long long* stats;
 };
 
@@ -128,6 +151,7 @@ struct CompactLaunch {
   int32_t mask_words;
   int32_t* lists;
   int32_t* list_len;
+  const int32_t* group_flags;
 };
 
 struct NormLaunch {
@@ -141,6 +165,7 @@ struct NormLaunch {
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s);
+hipError_t launch_prep(int combo, int H, int d, const PrepLaunch& p, hipStream_t s);
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
 hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s);
 hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t s);
@@ -149,5 +174,6 @@ hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* host_vals, hipStream_t s);
 
 bool combo_supported(int combo, int H, int d);
+int tile_waves();
 
 }  // namespace dosa

@@ -79,29 +79,56 @@ __global__ void fill_f32(float* p, int n, float v) {
   if (i < n) p[i] = v;
 }
 
+// 16 lanes per key (coalesced row reads), 16 keys per pass of a 256-thread
+// block, kNormKeys consecutive logical keys per block.  The per-sequence
+// minimum is kept per lane group and flushed with one atomic per sequence
+// change.
+constexpr int kNormKeys = 1024;
+
 template <int C, int D>
 __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= p.total_k) return;
-  int lo = 0, hi = p.batch;                  // last b with cu_kv[b] <= i
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.cu_kv[mid] <= i) lo = mid; else hi = mid;
+  constexpr int PER = D / 16;   // elements per lane
+  const int t = threadIdx.x;
+  const int grp = t >> 4, l16 = t & 15;
+  const int64_t k0 = (int64_t)blockIdx.x * kNormKeys;
+  const int64_t k1 = min<int64_t>(k0 + kNormKeys, p.total_k);
+  int cur_seq = -1;
+  float cur_min = INFINITY;
+  int b = 0;
+  {
+    int lo = 0, hi = p.batch;   // last b with cu_kv[b] <= k0
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.cu_kv[mid] <= k0) lo = mid; else hi = mid;
+    }
+    b = lo;
   }
-  const int b = lo;
-  const int key = (int)(i - p.cu_kv[b]);
-  const int64_t row = key_row(p.in, p.cu_kv[b], b, key);
-  float acc = 0.f;
-  for (int e = 0; e < D; ++e) {
-    const float v = k_elem<C>(p.in.k, row * D + e);
-    acc = fmaf(v, v, acc);
+  for (int64_t i = k0 + grp; i < k1; i += 16) {
+    while (b + 1 < p.batch && p.cu_kv[b + 1] <= i) ++b;
+    const int key = (int)(i - p.cu_kv[b]);
+    const int64_t row = key_row(p.in, p.cu_kv[b], b, key);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float v = k_elem<C>(p.in.k, row * D + l16 * PER + e);
+      acc = fmaf(v, v, acc);
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 16);
+    float n = sqrtf(acc);
+    if constexpr (HasKScale<C>::value) n *= p.in.k_scale[row];
+    n *= 1.0000153f;                           // covers the fp32 sum/sqrt/scale rounding (<< 2^-16)
+    if (l16 == 0) p.norms[i] = n;
+    if (b != cur_seq) {
+      if (cur_seq >= 0 && l16 == 0)
+        atomicMin(reinterpret_cast<unsigned int*>(p.norm_min) + cur_seq, __float_as_uint(cur_min));
+      cur_seq = b;
+      cur_min = INFINITY;
+    }
+    cur_min = fminf(cur_min, n * 0.9999695f);
   }
-  float n = sqrtf(acc);
-  if constexpr (HasKScale<C>::value) n *= p.in.k_scale[row];
-  n *= 1.0000153f;                           // covers the fp32 sum/sqrt/scale rounding (<< 2^-16)
-  p.norms[i] = n;
-  const float nd = n * 0.9999695f;
-  atomicMin(reinterpret_cast<unsigned int*>(p.norm_min) + b, __float_as_uint(nd));
+  if (cur_seq >= 0 && l16 == 0)
+    atomicMin(reinterpret_cast<unsigned int*>(p.norm_min) + cur_seq, __float_as_uint(cur_min));
 }
 
 // ---------------------------------------------------------------------------
@@ -202,7 +229,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   const int t = threadIdx.x;
 
   __shared__ float qf[H][D + 1];     // decoded, unscaled (exact in fp32)
-  __shared__ double G[H][H];         // head Gram matrix
+  constexpr int SCR = (H * H > 32 * D) ? H * H : 32 * D;   // doubles
+  __shared__ double scratch[SCR];    // head Gram matrix, later the sampled seed keys
+  double (*G)[H] = reinterpret_cast<double (*)[H]>(scratch);
+  __shared__ double qn[H];           // ||q_h||
   __shared__ double wd[H];
   __shared__ double alpha[H][3];
   __shared__ int prox[3];
@@ -299,25 +329,34 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   double rho = block_sum(part, red);
   rho = separable ? rho : sqrt(fmax(rho, 0.0));
   __syncthreads();
-  // activation statistics of the negative heads on sampled seed-window keys
+  for (int h = t; h < H; h += 256) qn[h] = sqrt(G[h][h]);
+  __syncthreads();
+  // activation statistics of the negative heads on up to 64 keys sampled
+  // from the seed window (staged in LDS over the Gram storage)
   const int n_last = gr.pos0 + gr.nq;
   const int wlo = max(0, n_last - p.seed_window);
   const int span = pos - wlo + 1;
   const int ns = min(64, max(span, 0));
   const bool use_neg = (p.flags & DOSA_NO_NEGATIVE) == 0;
+  float* kf = reinterpret_cast<float*>(scratch);   // [64][D]
   if (use_neg && ns > 0) {
+    const int step = max(1, span / ns);
+    for (int e = t; e < ns * D; e += 256) {
+      const int i = e / D, c = e % D;
+      const int key = pos - i * step;
+      const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
+      kf[i * D + c] = k_elem<C>(p.in.k, row * D + c);
+    }
+    __syncthreads();
     const int h = t & (H - 1);
     const int part_id = t / H;
     const int nparts = 256 / H;
-    const int step = max(1, span / ns);
     if (wd[h] < 0.0) {
       int c = 0;
       for (int i = part_id; i < ns; i += nparts) {
-        const int key = pos - i * step;
-        const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
-        float s = 0.f;
-        for (int e = 0; e < D; ++e) s = fmaf(qf[h][e], k_elem<C>(p.in.k, row * D + e), s);
-        c += (s > 0.f) ? 1 : 0;
+        float sacc = 0.f;
+        for (int e = 0; e < D; ++e) sacc = fmaf(qf[h][e], kf[i * D + e], sacc);
+        c += (sacc > 0.f) ? 1 : 0;
       }
       atomicAdd(&act[h], c);
     }
@@ -383,7 +422,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   for (int i = t; i < D; i += 256) an += avec[i] * avec[i];
   an = sqrt(block_sum(an, red));
   double wq = 0.0;
-  for (int h = t; h < H; h += 256) wq += fabs(wd[h]) * sqrt(G[h][h]);
+  for (int h = t; h < H; h += 256) wq += fabs(wd[h]) * qn[h];
   wq = block_sum(wq, red);
   if (t == 0) {
     const double qs = HasQScale<C>::value ? (double)p.in.q_scale[qrow] : 1.0;
@@ -394,9 +433,12 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     const double n = (double)(D + H + 16);
     const double gam = n * u / (1.0 - n * u);
     double cq = 0.0, sf = 0.0;
-    for (int r = 0; r < np; ++r) cq += cvec[r] * sqrt(G[prox[r]][prox[r]]);
+    for (int r = 0; r < np; ++r) cq += cvec[r] * qn[prox[r]];
     for (int r = np; r < 4; ++r) sf += sig[r] * fnorm[r];
-    const double margin = 2.0 * gam * (wq + cq + sf + rho) + ea;
+    // the score kernels evaluate sum_h w_h ReLU(x_h) as sum_h (w_h/2)|x_h| + qbar.k/2
+    // with qbar held as a few terms; their error and magnitude (unscaled) enter here
+    const double l_err = (double)p.lerr[(int64_t)qrow * 2], l_mag = (double)p.lerr[(int64_t)qrow * 2 + 1];
+    const double margin = 2.0 * gam * (wq + cq + sf + rho + 0.5 * l_mag) + ea + 0.5 * l_err;
     const double rho_p = (rho + margin) * qs;
     float* cf = p.coef + (int64_t)qrow * 8;
     for (int r = 0; r < 4; ++r) cf[r] = (r < np) ? (float)(cvec[r] * qs) : (float)(sig[r] * qs);
@@ -415,17 +457,22 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// bound pass: one wavefront per query group streams the group's bounded keys
+// bound pass: wavefront (group, split) streams a 64-key-aligned share of the
+// group's bounded keys; MFMA rows = 4 certificate rows x 4 queries
 // ---------------------------------------------------------------------------
 template <int C, int D>
 __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
   using O = Ops<C, D>;
   constexpr int STEPS = O::STEPS;
+  constexpr int KBYTES = D * O::KB;
   const int lane = lane_id();
-  const int gi = blockIdx.x;
+  const int gi = blockIdx.x / p.splits, sp = blockIdx.x % p.splits;
   const GroupInfo gr = p.groups[gi];
   const int col = lane & 15, g = lane >> 4;
-  const int lo = gr.bound_lo, n = gr.n_bounded;
+  const int lo_all = gr.bound_lo, n_all = gr.n_bounded;
+  const int nw = (n_all + 63) / 64;
+  const int w0 = (int)((int64_t)nw * sp / p.splits), w1 = (int)((int64_t)nw * (sp + 1) / p.splits);
+  const int lo = lo_all + 64 * w0, hi = min(lo_all + 64 * w1, lo_all + n_all);
   unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
   // this lane's output rows 4g..4g+3 = the 4 certificate rows of query slot g
   const bool qok = g < gr.nq;
@@ -438,17 +485,17 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
   const u64 hm = __ballot(qok && hopeless);
   const u64 okm = __ballot(qok);
   const bool all_hopeless = (hm == okm);
-  u64 n_surv = 0;
+  if (sp == 0 && lane == 0) p.group_flags[gi] = all_hopeless ? 1 : 0;
+  const u64 nbounded = (u64)max(hi - lo, 0) * (u64)gr.nq;
   if (all_hopeless) {
-    const int nw = (n + 63) / 64;
-    for (int wd = lane; wd < nw; wd += 64) {
-      const int rem = n - wd * 64;
+    for (int wd = w0 + lane; wd < w1; wd += 64) {
+      const int rem = n_all - wd * 64;
       mw[wd] = rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
     }
     if (p.stats != nullptr && lane == 0) {
-      atomicAdd(&p.stats[2], (u64)n * (u64)gr.nq);
-      atomicAdd(&p.stats[3], (u64)n * (u64)gr.nq);
-      atomicAdd(&p.stats[7], 1ull);
+      atomicAdd(&p.stats[2], nbounded);
+      atomicAdd(&p.stats[3], nbounded);
+      if (sp == 0) atomicAdd(&p.stats[7], 1ull);
     }
     if (p.debug_ub == nullptr) return;
   }
@@ -462,21 +509,21 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
       O::zero(A);
   }
   const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
-  u64 word = 0;
-#pragma unroll 1
-  for (int kb = lo; kb < lo + n; kb += 16) {
-    const int key = kb + col;
-    const bool kvalid = key < lo + n;
-    typename O::frag B[STEPS];
-    float ks = 1.f, kn = 0.f;
-    if (kvalid) {
+  u64 word = 0, n_surv = 0;
+  auto load = [&](int key, typename O::frag* B, float& ks, float& kn) {
+    if (key < hi) {
       const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
-      O::load_k(kbytes + row * D * O::KB, g, B);
-      if constexpr (HasKScale<C>::value) ks = p.in.k_scale[row];
+      O::load_k(kbytes + row * KBYTES, g, B);
+      ks = HasKScale<C>::value ? p.in.k_scale[row] : 1.f;
       kn = p.norms[(int64_t)gr.norm_base + key];
     } else {
       O::zero(B);
+      ks = 1.f;
+      kn = 0.f;
     }
+  };
+  auto bound = [&](int kb, const typename O::frag* B, float ks, float kn) {
+    const int key = kb + col;
     v4f c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < STEPS; ++s) c = O::mma(A[s], B[s], c);
@@ -487,22 +534,31 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
       else neg += cf[i] * c[i];
     }
     const float ub = ks * (pos - fmaxf(neg, 0.f)) + cf[4] * kn;
-    const bool valid = qok && kvalid;
+    const bool valid = qok && key < hi;
     const bool surv = valid && (hopeless || ub >= cf[5]);
     if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
-    if (all_hopeless) continue;
+    if (all_hopeless) return;
     const u64 m = __ballot(surv);
     const uint32_t u = (uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu;
     n_surv += __popcll(m);
-    const int bi = (kb - lo) >> 4;
+    const int bi = (kb - lo_all) >> 4;
     word |= (u64)u << (16 * (bi & 3));
-    if ((bi & 3) == 3 || kb + 16 >= lo + n) {
+    if ((bi & 3) == 3 || kb + 16 >= hi) {
       if (lane == 0) mw[bi >> 2] = word;
       word = 0;
     }
+  };
+#pragma unroll 1
+  for (int kb = lo; kb < hi; kb += 32) {
+    typename O::frag B0[STEPS], B1[STEPS];
+    float ks0, kn0, ks1, kn1;
+    load(kb + col, B0, ks0, kn0);
+    load(kb + 16 + col, B1, ks1, kn1);
+    bound(kb, B0, ks0, kn0);
+    if (kb + 16 < hi) bound(kb + 16, B1, ks1, kn1);
   }
   if (!all_hopeless && p.stats != nullptr && lane == 0) {
-    atomicAdd(&p.stats[2], (u64)n * (u64)gr.nq);
+    atomicAdd(&p.stats[2], nbounded);
     atomicAdd(&p.stats[3], n_surv);
   }
 }
@@ -515,6 +571,12 @@ __global__ __launch_bounds__(64) void compact_kernel(const CompactLaunch p) {
   const int lane = lane_id();
   const int gi = blockIdx.x;
   const GroupInfo gr = p.groups[gi];
+  bool all = true;
+  for (int i = 0; i < gr.tile_n; ++i) all = all && (p.group_flags[gr.tile_first + i] != 0);
+  if (all) {                 // the tiled kernel walks this tile's bounded range directly
+    if (lane == 0) p.list_len[gi] = 0;
+    return;
+  }
   const int nw = (gr.n_bounded + 63) / 64;
   const unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
   int32_t* out = p.lists + gr.list_off;
@@ -563,7 +625,7 @@ hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long*
 
 template <int C>
 static hipError_t norms_c(int d, const NormLaunch& p, hipStream_t s) {
-  const int nb = (int)((p.total_k + 255) / 256);
+  const int nb = (int)((p.total_k + kNormKeys - 1) / kNormKeys);
   if (d == 64) hipLaunchKernelGGL((key_norm_kernel<C, 64>), dim3(nb), dim3(256), 0, s, p);
   else hipLaunchKernelGGL((key_norm_kernel<C, 128>), dim3(nb), dim3(256), 0, s, p);
   return hipGetLastError();
@@ -609,8 +671,9 @@ hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t
 
 template <int C>
 static hipError_t bound_c(int d, const BoundLaunch& p, hipStream_t s) {
-  if (d == 64) hipLaunchKernelGGL((bound_kernel<C, 64>), dim3(p.n_groups), dim3(64), 0, s, p);
-  else hipLaunchKernelGGL((bound_kernel<C, 128>), dim3(p.n_groups), dim3(64), 0, s, p);
+  const int nb = p.n_groups * p.splits;
+  if (d == 64) hipLaunchKernelGGL((bound_kernel<C, 64>), dim3(nb), dim3(64), 0, s, p);
+  else hipLaunchKernelGGL((bound_kernel<C, 128>), dim3(nb), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -1,133 +1,404 @@
 // Exact all-head scoring on MFMA with a streaming per-query candidate buffer.
 //
-// One wavefront scores one query group (QW consecutive queries of a sequence)
-// against a list of keys.  MFMA rows are (query, head slot) pairs, columns are
-// 16 keys, the reduction runs over the head dimension d:
+// A wavefront scores a query group (QW consecutive queries of a sequence).
+// MFMA rows are (query, head slot) pairs, columns are 16 keys, the reduction
+// runs over the head dimension d:
 //     x[(t,h), s] = q[t,h,:] . k[s,:]            (fp32 accumulation)
-// and each lane folds its 4 output rows -- 4 heads of one query -- into
-//     S(t,s) = sum_h w[t,h] * max(0, x)           (then x q_scale * k_scale)
-// so after all head groups every lane holds a finished score with no
-// cross-lane reduction (QW = 4; QW = 2/1 need one/two lane exchanges).
+// and each lane folds its 4 output rows -- 4 heads of one query -- into the
+// score through the identity w max(0,x) = w x/2 + w |x|/2:
+//     S(t,s) = sum_h (w_h/2) |x_h|  +  (1/2) qbar_t . k_s   (then x q_scale * k_scale)
+// with qbar_t = sum_h w_h q_h evaluated by one more MFMA row group (its terms
+// come from prep.hip), so each head value costs one fused multiply-add with
+// a free |.| operand modifier.  After all head groups every lane holds a
+// finished score with no cross-lane reduction (QW = 4; QW = 2/1 need one/two
+// lane exchanges).
+//
+// Two kernels share that arithmetic, so a (query, key) pair gets the same
+// fp32 score whichever kernel computes it:
+//   score_tiled_kernel  8 wavefronts (8 query groups) share key tiles staged
+//                       through LDS, double-buffered with register prefetch;
+//                       used for key ranges (dense path, seed pass).
+//   score_list_kernel   one wavefront per query group walking a key range or a
+//                       survivor list with its own loads (pruned path).
 //
 // Scores at or above the query's running threshold theta are appended to the
-// query's candidate region as packed (score, position) keys.  When a region
-// nears its capacity the wavefront runs an exact radix select over it,
-// keeps the current K best and raises theta to the K-th score (prior art named
-// by the DoSA pages, Related Work: radix selection and bounded-buffer
-// streaming; DoSA Method section: fuse full scoring with threshold filtering
-// and pack scores for selection).
+// query's candidate region as packed (score, position) keys (DoSA pages,
+// Method section: full scoring fused with threshold filtering, scores packed
+// for selection; Related Work: radix selection, bounded-buffer streaming).
+// theta comes from a per-query LDS histogram of every score seen so far: 256
+// bins of 1/32 octave on the order-preserving integer image of the float,
+// anchored below the first block's maximum.  The lower edge of the highest
+// bin with at least K scores at or above it never exceeds the K-th largest
+// score seen, so it is a valid filter at all times.  A full region is
+// compacted at theta in one pass; only if that frees too little does the
+// wavefront run an exact radix select.
 #include "dosa_device.h"
 
 namespace dosa {
 
-template <int C, int H, int D>
-__global__ __launch_bounds__(64) void score_kernel(const ScoreLaunch p) {
-  using O = Ops<C, D>;
-  constexpr int QW = queries_per_wave(C, H, D);
-  constexpr int S = 16 / QW;   // head slots per query in one MFMA
-  constexpr int HG = H / S;    // head groups
-  constexpr int STEPS = O::STEPS;
-  __shared__ uint32_t hist[2048];
+constexpr int kTileKeys = 64;   // keys per LDS tile
+constexpr int kTileWaves = 8;   // wavefronts (query groups) per tiled workgroup
 
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// K-th largest of the n distinct entries at ptr, by one wavefront with a
+// private 256-bin LDS histogram (8-bit digits from the top; no workgroup
+// barrier, so the other wavefronts keep working).  Returns T with exactly K
+// entries >= T.
+__device__ __noinline__ u64 select_kth_wave(const u64* ptr, uint32_t n, int K, uint32_t* hist) {
   const int lane = lane_id();
-  const WorkItem it = p.items[blockIdx.x];
-  const GroupInfo gr = p.groups[it.group];
-  const int col = lane & 15;   // key column (B operand and outputs)
-  const int g = lane >> 4;     // lane group
+  u64 prefix = 0;
+  uint32_t rem = (uint32_t)K;
+  wave_sync();
+#pragma unroll 1
+  for (int p = 0; p < 8; ++p) {
+    const int sh = 56 - 8 * p;
+    const int hs = sh + 8;
+    for (int b = lane; b < 256; b += 64) hist[b] = 0;
+    wave_sync();
+    const u64 want = (p == 0) ? 0 : (prefix >> hs);
+    for (uint32_t i = lane; i < n; i += 64) {
+      const u64 e = ptr[i];
+      if (p == 0 || (e >> hs) == want) atomicAdd(&hist[(uint32_t)(e >> sh) & 255u], 1u);
+    }
+    wave_sync();
+    uint32_t s = 0;
+    for (int t = 0; t < 4; ++t) s += hist[lane * 4 + t];
+    const uint32_t suf = wave_suffix_sum(s);
+    const bool cross = (suf >= rem) && (suf - s < rem);
+    const u64 cm = __ballot(cross);
+    const int L = cm ? (__ffsll((long long)cm) - 1) : 0;
+    uint32_t acc = __shfl(suf - s, L, 64);
+    int b = L * 4;
+    uint32_t cnt_b = 0;
+    for (int t = 3; t >= 0; --t) {
+      const uint32_t h = hist[L * 4 + t];
+      if (acc + h >= rem) { b = L * 4 + t; cnt_b = h; break; }
+      acc += h;
+    }
+    rem -= acc;
+    prefix |= ((u64)(uint32_t)b) << sh;
+    wave_sync();
+    if (cnt_b == rem) break;
+  }
+  return prefix;
+}
 
-  // Query rows of this group, kept in registers for the whole key sweep.
+constexpr int kHistBins = 256;          // running-threshold histogram bins per query
+constexpr int kHistShift = 18;          // 2^18 ord units per bin: 32 bins per octave
+constexpr int kHistAnchor = 192;        // the first block's maximum lands in this bin
+
+template <int C, int H, int D>
+struct Scorer {
+  using O = Ops<C, D>;
+  static constexpr int QW = queries_per_wave(C, H, D);
+  static constexpr int S = 16 / QW;   // head slots per query in one MFMA
+  static constexpr int HG = H / S;    // head groups
+  static constexpr int STEPS = O::STEPS;
+  static constexpr int KBYTES = D * O::KB;
+
   typename O::frag A[HG][STEPS];
-  {
-    const int ra = lane & 15;
-    const int qa = ra / S, hs = ra % S;
-    const bool ok = qa < gr.nq;
-    const uint8_t* qb = static_cast<const uint8_t*>(p.in.q);
+  typename O::frag AL[STEPS];       // weighted-query terms of the group's queries
+  float sl[4];                      // their scales / 2, for this lane's 4 output rows
+  int lane, col, g, qi, qrow, pos, owner_lane0;
+  bool qok, owner;
+  float qs, theta;
+  uint32_t count;
+  u64* buf;
+  const float* wq;   // LDS: this lane's query weights / 2 [H]
+  uint32_t wq_lds;   // the same as an LDS byte address
+  uint32_t* qh;      // LDS: this wavefront's query histograms [QW][kHistBins]
+  uint32_t hbase;    // ord value of the lower edge of bin 0 (0 = not anchored yet)
+  uint32_t n_written, n_reselect, n_scored;
+
+  // wl: LDS [QW][H] weights of this wavefront's queries (filled here, halved);
+  // hq: LDS [QW][kHistBins] running-threshold histograms (zeroed here).
+  __device__ __forceinline__ void init(const ScoreLaunch& p, const GroupInfo& gr, int region, float* wl,
+                                       uint32_t* hq, bool active) {
+    lane = lane_id();
+    col = lane & 15;
+    g = lane >> 4;
+    const int nq = active ? gr.nq : 0;
+    {
+      const int ra = lane & 15;
+      const int qa = ra / S, hs = ra % S;
+      const bool ok = qa < nq;
+      const uint8_t* qb = static_cast<const uint8_t*>(p.in.q);
 #pragma unroll
-    for (int j = 0; j < HG; ++j) {
-      const int head = S * j + hs;
+      for (int j = 0; j < HG; ++j) {
+        const int head = S * j + hs;
+        if (ok)
+          O::load_q(qb + ((int64_t)(gr.q_row0 + qa) * H + head) * D * O::QB, g, A[j]);
+        else
+          O::zero(A[j]);
+      }
       if (ok)
-        O::load_q(qb + ((int64_t)(gr.q_row0 + qa) * H + head) * D * O::QB, g, A[j]);
+        O::load_q(static_cast<const uint8_t*>(p.lrows) + ((int64_t)(gr.q_row0 + qa) * S + hs) * D * O::QB, g, AL);
       else
-        O::zero(A[j]);
+        O::zero(AL);
+    }
+    for (int e = lane; e < QW * H; e += 64) {
+      const int q = e / H;
+      wl[e] = (q < nq) ? 0.5f * p.in.w[(int64_t)(gr.q_row0 + q) * H + (e % H)] : 0.f;
+    }
+    qi = (4 * g) / S;
+    qok = qi < nq;
+    qrow = gr.q_row0 + qi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sl[i] = qok ? 0.5f * p.lsig[(int64_t)qrow * S + ((4 * g + i) % S)] : 0.f;
+    wq = wl + qi * H;
+    wq_lds = (uint32_t)(uintptr_t)wq;   // low 32 bits of a generic LDS address = the LDS offset
+    qs = (HasQScale<C>::value && qok) ? p.in.q_scale[qrow] : 1.f;
+    pos = gr.pos0 + qi;
+    theta = (p.theta_init != nullptr && qok) ? p.theta_init[qrow] : -INFINITY;
+    count = 0;
+    owner_lane0 = 16 * (qi * (4 / QW));
+    owner = (lane >> 4) == (owner_lane0 >> 4);
+    buf = qok ? p.cb.cand + ((int64_t)qrow * p.cb.R + region) * p.cb.cap : nullptr;
+    qh = hq;
+    for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
+    hbase = 0;
+    n_written = n_reselect = n_scored = 0;
+  }
+
+  // Raise theta of every query of the wavefront to the lower edge of the
+  // highest histogram bin that has at least K scores at or above it.
+  __device__ __forceinline__ void refresh_theta(int K) {
+    wave_sync();
+#pragma unroll 1
+    for (int qq = 0; qq < QW; ++qq) {
+      const uint32_t* h = qh + qq * kHistBins;
+      const uint32_t b0 = __shfl(hbase, 16 * (qq * (4 / QW)), 64);
+      if (b0 == 0) continue;
+      uint32_t s4 = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) s4 += h[lane * 4 + t];
+      const uint32_t suf = wave_suffix_sum(s4);
+      const bool cross = (suf >= (uint32_t)K) && (suf - s4 < (uint32_t)K);
+      const u64 cm = __ballot(cross);
+      if (cm == 0) continue;                       // fewer than K scores counted so far
+      const int L = __ffsll((long long)cm) - 1;
+      uint32_t acc = __shfl(suf - s4, L, 64);
+      int b = L * 4;
+      for (int t = 3; t >= 0; --t) {
+        const uint32_t hv = h[L * 4 + t];
+        if (acc + hv >= (uint32_t)K) { b = L * 4 + t; break; }
+        acc += hv;
+      }
+      uint32_t edge = b0 + ((uint32_t)b << kHistShift);
+      if (edge < b0 || edge > 0xFF7FFFFFu) edge = 0xFF7FFFFFu;   // stay on finite floats
+      const float th = ord2f(edge);
+      if (qi == qq && th > theta) theta = th;
     }
   }
-  // Weights of this lane's output rows: rows 4g..4g+3 belong to query qi.
-  const int qi = (4 * g) / S;
-  const bool qok = qi < gr.nq;
-  const int qrow = gr.q_row0 + qi;
-  float wv[HG][4];
-#pragma unroll
-  for (int j = 0; j < HG; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int head = S * j + ((4 * g + i) % S);
-      wv[j][i] = qok ? p.in.w[(int64_t)qrow * H + head] : 0.f;
-    }
-  const float qs = (HasQScale<C>::value && qok) ? p.in.q_scale[qrow] : 1.f;
-  const int pos = gr.pos0 + qi;
-  float theta = (p.theta_init != nullptr && qok) ? p.theta_init[qrow] : -INFINITY;
-  uint32_t count = 0;
-  const int owner_lane0 = 16 * (qi * (4 / QW));
-  const bool owner = (lane >> 4) == (owner_lane0 >> 4);
-  const int R = p.cb.R, cap = p.cb.cap;
-  u64* const cand_base = p.cb.cand;
-  u64* const buf = qok ? cand_base + ((int64_t)qrow * R + it.region) * cap : nullptr;
-  const uint32_t hi_water = (uint32_t)(cap - 16);
-  uint32_t n_written = 0, n_reselect = 0, n_scored = 0;
 
-  const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
-
-  auto block = [&](int key, bool kvalid) {
-    typename O::frag B[STEPS];
-    float ks = 1.f;
-    if (kvalid) {
-      const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
-      O::load_k(kbytes + row * D * O::KB, g, B);
-      if constexpr (HasKScale<C>::value) ks = p.in.k_scale[row];
-    } else {
-      O::zero(B);
+  // Compact the region of query qq to the entries >= its theta; if that
+  // leaves it more than half full, select the exact K-th and keep K.
+  __device__ __forceinline__ void shrink(const ScoreLaunch& p, const GroupInfo& gr, int region, int qq,
+                                         uint32_t* shist) {
+    const int cap = p.cb.cap;
+    const uint32_t cq = __shfl(count, 16 * (qq * (4 / QW)), 64);
+    const float tq = __shfl(theta, 16 * (qq * (4 / QW)), 64);
+    u64* bq = p.cb.cand + ((int64_t)(gr.q_row0 + qq) * p.cb.R + region) * cap;
+    uint32_t nk = cq;
+    float th = tq;
+    if (tq > -INFINITY) {
+      nk = compact_ge(bq, cq, (u64)f2ord(tq) << 32, bq, 0);
+      wave_sync();
     }
-    float o = 0.f;
+    if (nk > (uint32_t)(cap / 2) && nk > (uint32_t)p.topk) {
+      const u64 T = select_kth_wave(bq, nk, p.topk, shist);
+      compact_ge(bq, nk, T, bq, 0);
+      wave_sync();
+      nk = (uint32_t)p.topk;
+      th = fmaxf(th, key_score(T));
+      ++n_reselect;
+    }
+    if (qi == qq) {
+      count = nk;
+      theta = th;
+    }
+  }
+
+  __device__ __forceinline__ static v4f mma_all(const typename O::frag* a, const typename O::frag* B) {
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) c = O::mma(a[s], B[s], c);
+    return c;
+  }
+
+  // Unscaled scores of this lane's (query, key column) for NB 16-key blocks
+  // whose fragments are in B[0..NB).  Head groups run in the outer loop, so
+  // one LDS read of a group's weights serves all NB blocks and the NB MFMAs
+  // of a group are independent of each other.  A block's value is the same
+  // sequence of operations whatever NB is, so a (query, key) score does not
+  // depend on which kernel computes it or on the other keys of the step.
+  template <int NB>
+  __device__ __forceinline__ void scoreN(const typename O::frag (*Bin)[STEPS], float* out) const {
+    // Software pipeline pinned with empty volatile asm statements (which the
+    // compiler keeps in program order): iteration j issues the MFMAs of head
+    // group j+1 -- their key fragments are re-versioned at the start of the
+    // iteration so they cannot be hoisted earlier -- then folds group j, whose
+    // MFMAs were issued one iteration before; the accumulators are pinned at
+    // the end of the iteration so the FMAs cannot sink later.
+    typename O::frag B[NB][STEPS];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) B[b][s] = Bin[b][s];
+    float o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] = 0.f;
+    uint32_t wa = wq_lds + 4u * (uint32_t)((4 * g) % S);
+    asm volatile("" : "+v"(wa));
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    v4f cur[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cur[b] = mma_all(A[0], B[b]);
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
-      v4f c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) c = O::mma(A[j][s], B[s], c);
+      for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o += wv[j][i] * fmaxf(c[i], 0.f);
+        for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(B[b][s]));
+      const v4f w4 = *reinterpret_cast<lds_v4f*>((uintptr_t)(wa + 4u * (uint32_t)(S * j)));
+      v4f nxt[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) nxt[b] = (j + 1 < HG) ? mma_all(A[j + 1 < HG ? j + 1 : 0], B[b]) : mma_all(AL, B[b]);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        o[b] = fmaf(w4[0], fabsf(cur[b][0]), o[b]);
+        o[b] = fmaf(w4[1], fabsf(cur[b][1]), o[b]);
+        o[b] = fmaf(w4[2], fabsf(cur[b][2]), o[b]);
+        o[b] = fmaf(w4[3], fabsf(cur[b][3]), o[b]);
+        asm volatile("" : "+v"(o[b]));
+        cur[b] = nxt[b];
+      }
     }
-    if constexpr (QW <= 2) o += __shfl_xor(o, 16, 64);
-    if constexpr (QW == 1) o += __shfl_xor(o, 32, 64);
-    const float score = o * qs * ks;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[b] = fmaf(sl[i], cur[b][i], o[b]);
+      if constexpr (QW <= 2) o[b] += __shfl_xor(o[b], 16, 64);
+      if constexpr (QW == 1) o[b] += __shfl_xor(o[b], 32, 64);
+      out[b] = o[b];
+    }
+  }
+
+  // Count this lane's score in its query's histogram, append it if it
+  // reaches theta, and shrink regions that are about to overflow.  Called by
+  // all 64 lanes of the wavefront.
+  __device__ __forceinline__ void append(const ScoreLaunch& p, const GroupInfo& gr, int region, float o,
+                                         float ks, int key, bool kvalid, uint32_t* shist) {
+    const float sc = o * qs * ks;
     const bool valid = owner && qok && kvalid && key <= pos;
-    const bool take = valid && score >= theta;
+    const uint32_t so = f2ord(sc);
+    if (__any(hbase == 0)) {
+      // anchor each query's histogram below the maximum of its first scores
+      // (all lanes take part in the exchanges; only unanchored queries update)
+      uint32_t mx = valid ? so : 0u;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+      mx = __shfl(mx, owner_lane0 + col, 64);
+      if (hbase == 0 && mx != 0u) {
+        const uint32_t lo = (uint32_t)kHistAnchor << kHistShift;
+        hbase = (mx > 0x00800000u + lo) ? mx - lo : 0x00800000u;
+      }
+    }
+    if (valid && hbase != 0 && so >= hbase) {
+      const uint32_t bin = min((so - hbase) >> kHistShift, (uint32_t)(kHistBins - 1));
+      atomicAdd(&qh[qi * kHistBins + bin], 1u);
+    }
+    const bool take = valid && sc >= theta;
     const u64 m = __ballot(take);
     n_scored += __popcll(__ballot(valid));
     const uint32_t slice = (uint32_t)(m >> owner_lane0) & 0xFFFFu;
     const uint32_t before = __popc(slice & ((1u << col) - 1u));
-    if (take) buf[count + before] = make_key(score, key);
+    if (take) buf[count + before] = make_key(sc, key);
     count += __popc(slice);
     n_written += __popcll(m);
+    const uint32_t hi_water = (uint32_t)(p.cb.cap - 16);
     if (__any(count > hi_water)) {
+      refresh_theta(p.topk);
 #pragma unroll 1
-      for (int qq = 0; qq < QW; ++qq) {
-        const int src = 16 * (qq * (4 / QW));
-        const uint32_t cq = __shfl(count, src, 64);
-        if (cq > hi_water) {
-          u64* bq = cand_base + ((int64_t)(gr.q_row0 + qq) * R + it.region) * cap;
-          uint32_t one = cq;
-          Segs s1{bq, &one, cap, 1};
-          const u64 T = select_kth(s1, p.topk, hist);
-          compact_ge(bq, cq, T, bq, 0);
-          __syncthreads();
-          if (qi == qq) {
-            count = (uint32_t)p.topk;
-            theta = key_score(T);
-          }
-          ++n_reselect;
-        }
+      for (int qq = 0; qq < QW; ++qq)
+        if (__shfl(count, 16 * (qq * (4 / QW)), 64) > hi_water) shrink(p, gr, region, qq, shist);
+    }
+  }
+
+  // End of the sweep: bring every region down to its final theta.
+  __device__ __forceinline__ void close(const ScoreLaunch& p, const GroupInfo& gr, int region, uint32_t* shist) {
+    refresh_theta(p.topk);
+#pragma unroll 1
+    for (int qq = 0; qq < QW; ++qq) {
+      const uint32_t cq = __shfl(count, 16 * (qq * (4 / QW)), 64);
+      const float tq = __shfl(theta, 16 * (qq * (4 / QW)), 64);
+      if (cq > (uint32_t)p.topk && tq > -INFINITY) {
+        u64* bq = p.cb.cand + ((int64_t)(gr.q_row0 + qq) * p.cb.R + region) * p.cb.cap;
+        const uint32_t nk = compact_ge(bq, cq, (u64)f2ord(tq) << 32, bq, 0);
+        if (qi == qq) count = nk;
       }
     }
+    wave_sync();
+  }
+
+  __device__ __forceinline__ void finish(const ScoreLaunch& p, int region) {
+    if (qok && lane == owner_lane0) p.cb.counts[(int64_t)qrow * p.cb.R + region] = count;
+    if (p.stats != nullptr && lane == 0) {
+      atomicAdd(&p.stats[p.scored_slot], (u64)n_scored);
+      atomicAdd(&p.stats[5], (u64)n_written);
+      atomicAdd(&p.stats[6], (u64)n_reselect);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// one wavefront per query group: key range (two sub-ranges walked top-down)
+// or survivor list (ascending)
+// ---------------------------------------------------------------------------
+template <int C, int H, int D>
+__global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
+  using SC = Scorer<C, H, D>;
+  using O = typename SC::O;
+  __shared__ uint32_t hist[256];
+  __shared__ __attribute__((aligned(16))) float wl[SC::QW * H];
+  __shared__ uint32_t qhist[SC::QW * kHistBins];
+  const WorkItem it = p.items[blockIdx.x];
+  const GroupInfo gr = p.groups[it.group];
+  if (p.flag_mode == 2) {
+    bool all = true;
+    for (int i = 0; i < gr.tile_n; ++i) all = all && (p.tile_flags[gr.tile_first + i] != 0);
+    if (all) return;   // the tiled kernel scores this tile
+  }
+  SC sc;
+  sc.init(p, gr, it.region, wl, qhist, true);
+  __syncthreads();
+  int nblk = 0;
+  const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
+
+  auto load = [&](int key, bool kvalid, typename O::frag* B, float& ks) {
+    ks = 1.f;
+    if (kvalid) {
+      const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
+      O::load_k(kbytes + row * SC::KBYTES, sc.g, B);
+      if constexpr (HasKScale<C>::value) ks = p.in.k_scale[row];
+    } else {
+      O::zero(B);
+    }
+  };
+  // four 16-key blocks per step
+  auto step4 = [&](const int* keys, const bool* v) {
+    typename O::frag B[4][SC::STEPS];
+    float ks[4], o[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) load(keys[b], v[b], B[b], ks[b]);
+    sc.template scoreN<4>(B, o);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) sc.append(p, gr, it.region, o[b], ks[b], keys[b], v[b], hist);
+    if ((++nblk & 1) == 0) sc.refresh_theta(p.topk);
   };
 
   if (!it.gather) {
@@ -135,9 +406,15 @@ __global__ __launch_bounds__(64) void score_kernel(const ScoreLaunch p) {
     for (int r = 0; r < 2; ++r) {
       const int lo = r ? it.b0 : it.a0, hi = r ? it.b1 : it.a1;
 #pragma unroll 1
-      for (int kb = hi - 16; kb > lo - 16; kb -= 16) {
-        const int key = kb + col;
-        block(key, key >= lo && key < hi);
+      for (int kb = hi - 16; kb > lo - 16; kb -= 64) {
+        int keys[4];
+        bool v[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          keys[b] = kb - 16 * b + sc.col;
+          v[b] = keys[b] >= lo && keys[b] < hi;
+        }
+        step4(keys, v);
       }
     }
   } else {
@@ -146,23 +423,131 @@ __global__ __launch_bounds__(64) void score_kernel(const ScoreLaunch p) {
     const int e0 = (int)(((int64_t)len * it.a0 / it.a1) & ~15LL);
     const int e1 = (it.a0 == it.a1 - 1) ? len : (int)(((int64_t)len * (it.a0 + 1) / it.a1) & ~15LL);
 #pragma unroll 1
-    for (int e = e0; e < e1; e += 16) {
-      const int idx = e + col;
-      const bool kv = idx < e1;
-      const int key = kv ? lst[idx] : 0;
-      block(key, kv);
+    for (int e = e0; e < e1; e += 64) {
+      int keys[4];
+      bool v[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i0 = e + 16 * b + sc.col;
+        v[b] = i0 < e1;
+        keys[b] = v[b] ? lst[i0] : 0;
+      }
+      step4(keys, v);
     }
   }
+  sc.close(p, gr, it.region, hist);
+  sc.finish(p, it.region);
+}
 
-  if (qok && lane == owner_lane0) p.cb.counts[(int64_t)qrow * R + it.region] = count;
-  if (p.stats != nullptr && lane == 0) {
-    atomicAdd(&p.stats[p.scored_slot], (u64)n_scored);
-    atomicAdd(&p.stats[5], (u64)n_written);
-    atomicAdd(&p.stats[6], (u64)n_reselect);
+// ---------------------------------------------------------------------------
+// 8 wavefronts (consecutive query groups of one sequence) share LDS key tiles
+// (range mode: [a0,a1) then [b0,b1), each from the top tile down)
+// ---------------------------------------------------------------------------
+template <int C, int H, int D>
+__global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const ScoreLaunch p) {
+  using SC = Scorer<C, H, D>;
+  using O = typename SC::O;
+  constexpr int KB = SC::KBYTES;
+  constexpr int ROW = KB + 16;                       // padded LDS row: conflict-free 16-byte reads
+  constexpr int CPK = KB / 16;                       // 16-byte chunks per key
+  constexpr int NCH = (kTileKeys * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileKeys * ROW];
+  __shared__ float kscale[2][kTileKeys];
+  __shared__ __attribute__((aligned(16))) float wl[kTileWaves][SC::QW * H];
+  __shared__ uint32_t hist[kTileWaves][256];
+  __shared__ uint32_t qhist[kTileWaves][SC::QW * kHistBins];
+
+  const int wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const WorkItem it = p.items[blockIdx.x];
+  const int ngroups = it.pad;                        // query groups in this tile
+  if (p.flag_mode == 1) {
+    bool all = true;
+    for (int i = 0; i < ngroups; ++i) all = all && (p.tile_flags[it.group + i] != 0);
+    if (!all) return;  // the list kernel scores this tile's survivors
+  }
+  const bool active = wave < ngroups;
+  const GroupInfo gr = p.groups[it.group + (active ? wave : 0)];
+  const GroupInfo g0 = p.groups[it.group];
+  SC sc;
+  sc.init(p, gr, it.region, wl[wave], qhist[wave], active);
+
+  const int na = (it.a1 > it.a0) ? (it.a1 - it.a0 + kTileKeys - 1) / kTileKeys : 0;
+  const int nbt = (it.b1 > it.b0) ? (it.b1 - it.b0 + kTileKeys - 1) / kTileKeys : 0;
+  const int ntiles = na + nbt;
+  const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
+
+  v4i stage[NCH];
+  float stage_s = 1.f;
+  auto fetch = [&](int t) {
+    const bool ra = t < na;
+    const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
+    const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * 64 * kTileWaves;
+      const int slot = ch / CPK, part = ch % CPK;
+      const int key = kb + slot;
+      if (slot < kTileKeys && key >= lo && key < hi) {
+        const int64_t row = key_row(p.in, g0.key_base, g0.seq, key);
+        stage[c] = *reinterpret_cast<const v4i*>(kbytes + row * KB + part * 16);
+      } else {
+        stage[c] = v4i{0, 0, 0, 0};
+      }
+    }
+    if constexpr (HasKScale<C>::value) {
+      if (tid < kTileKeys) {
+        const int key = kb + tid;
+        stage_s = (key >= lo && key < hi) ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, key)] : 0.f;
+      }
+    }
+  };
+  auto commit = [&](int bufi) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * 64 * kTileWaves;
+      const int slot = ch / CPK, part = ch % CPK;
+      if (slot < kTileKeys) *reinterpret_cast<v4i*>(&ktile[bufi][slot * ROW + part * 16]) = stage[c];
+    }
+    if (tid < kTileKeys) kscale[bufi][tid] = stage_s;
+  };
+
+  if (ntiles > 0) fetch(0);
+#pragma unroll 1
+  for (int t = 0; t < ntiles; ++t) {
+    const int bufi = t & 1;
+    commit(bufi);
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
+    const bool ra = t < na;
+    const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
+    const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
+    if (active) {
+      typename O::frag B[4][SC::STEPS];
+      float ks[4], o[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        O::load_k(&ktile[bufi][(b * 16 + sc.col) * ROW], sc.g, B[b]);
+        ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + sc.col] : 1.f;
+      }
+      sc.template scoreN<4>(B, o);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int key = kb + b * 16 + sc.col;
+        sc.append(p, gr, it.region, o[b], ks[b], key, key >= lo && key < hi, hist[wave]);
+      }
+      if ((t & 1) == 1) sc.refresh_theta(p.topk);
+    }
+  }
+  if (active) {
+    sc.close(p, gr, it.region, hist[wave]);
+    sc.finish(p, it.region);
   }
 }
 
-// Final merge: the exact Top-K of each query over regions [r0, r1).
+// ---------------------------------------------------------------------------
+// final merge: the exact Top-K of each query over regions [r0, r1)
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
   const int q = blockIdx.x;
@@ -178,7 +563,7 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
   if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
   if (p.out_idx == nullptr) return;
-  // Exactly min(K, total) entries are >= T; write them in region order.
+  // exactly min(K, total) entries are >= T; write them in region order
   int32_t* oi = p.out_idx + (int64_t)q * K;
   float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
   uint32_t out = 0;
@@ -264,10 +649,16 @@ __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p)
   }
 }
 
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
 template <int C, int H, int D>
 static hipError_t launch_score_t(const ScoreLaunch& p, hipStream_t s) {
   if (p.n_items == 0) return hipSuccess;
-  hipLaunchKernelGGL((score_kernel<C, H, D>), dim3(p.n_items), dim3(64), 0, s, p);
+  if (p.tiled)
+    hipLaunchKernelGGL((score_tiled_kernel<C, H, D>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+  else
+    hipLaunchKernelGGL((score_list_kernel<C, H, D>), dim3(p.n_items), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -299,6 +690,8 @@ hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {
     hipLaunchKernelGGL(select_kernel, dim3(p.total_q), dim3(64), 0, s, p);
   return hipGetLastError();
 }
+
+int tile_waves() { return kTileWaves; }
 
 bool combo_supported(int combo, int H, int d) {
   if (combo < 0 || combo > 3) return false;

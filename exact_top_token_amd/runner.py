@@ -88,8 +88,7 @@ class Runner:
         if self.path == "dsa":
             dsa_indexer_topk(i.q, i.q_dtype, i.q_scale, i.w, i.k, i.k_dtype, i.k_scale, i.q_lens, i.kv_lens,
                              i.page_table, i.page_size, i.H, i.d, i.topk, self.out_idx, self.out_score,
-                             self.workspace, flags=self.flags, key_splits=self.key_splits, stats=self.stats,
-                             stream=stream)
+                             self.workspace, cfg=self.cfg, stats=self.stats, stream=stream)
         else:
             dosa_indexer_topk(i.q, i.q_dtype, i.q_scale, i.w, i.k, i.k_dtype, i.k_scale, i.q_lens, i.kv_lens,
                               i.page_table, i.page_size, i.H, i.d, i.topk, self.out_idx, self.out_score,

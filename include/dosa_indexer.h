@@ -145,7 +145,7 @@ int dosa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, cons
                       const dosa_config* cfg, dosa_stats* stats, void* stream);
 
 /* Dense path: every visible key scored with all heads, streaming exact Top-K.
- * flags: DOSA_SORTED or 0.  key_splits as in dosa_config (0 = automatic). */
+ * Of cfg (NULL = defaults) it uses buffer_cap, key_splits and DOSA_SORTED. */
 int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
                      const void* k, int32_t k_dtype, const float* k_scale,
                      const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
@@ -153,7 +153,7 @@ int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const
                      int32_t H, int32_t d, int32_t topk,
                      int32_t* out_idx, float* out_score,
                      void* workspace, size_t workspace_bytes,
-                     uint32_t flags, int32_t key_splits, dosa_stats* stats, void* stream);
+                     const dosa_config* cfg, dosa_stats* stats, void* stream);
 
 /* Per-pass timing (tracing for benchmarks).  Between dosa_profile_begin()
  * and dosa_profile_end(), every kernel the calling thread enqueues through

@@ -186,3 +186,20 @@ def test_bound_dump_dominates_oracle_scores():
                 continue
             S, A = indexer.score_pairs(wl, np.full(keys.size, q), keys)
             assert np.all(ub[q, keys] >= S - 1e-6 * A), f"{wl.name} row {q}: bound below score"
+
+
+@pytest.mark.parametrize("case", ["all_negative_w", "zero_queries", "huge_scale"])
+def test_degenerate_score_distributions(case):
+    """Massive exact ties and extreme magnitudes: the answer is still the oracle's."""
+    wl = synth.custom(11, [(37, 3000), (5, 700)], H=8, d=64, topk=128, q_dtype="f32", k_dtype="f32")
+    if case == "all_negative_w":
+        wl.w = -np.abs(wl.w)                 # every score <= 0, most keys exactly 0
+    elif case == "zero_queries":
+        wl.q = np.zeros_like(wl.q)           # every score is 0: Top-K = the lowest positions
+    else:
+        wl.k = wl.k * np.float32(1e15)       # scores ~1e16..1e17
+    (di, ds, _), _ = _both(wl, rows=np.arange(wl.total_q))
+    if case == "zero_queries":
+        for r in range(wl.total_q):
+            v = np.sort(di[r][di[r] >= 0])
+            assert np.array_equal(v, np.arange(v.size)), r
