@@ -628,7 +628,6 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.debug_ub = cfg.debug_ub;
     bl.debug_ld = max_kv;
     bl.splits = P.bound_splits;
-    bl.group_flags = gflags;
     bl.stats = st;
     {
       PassScope ps(P_BOUND, stream);

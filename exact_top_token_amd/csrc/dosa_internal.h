@@ -140,7 +140,6 @@ struct BoundLaunch {
   float* debug_ub;           // [total_q, debug_ld] or NULL
   int32_t debug_ld;
   int32_t splits;            // key splits per group (grid = n_groups * splits)
-  int32_t* group_flags;      // out: 1 if no query of the group can prune anything
   unsigned long long* stats;
 };
 
@@ -151,7 +150,7 @@ struct CompactLaunch {
   int32_t mask_words;
   int32_t* lists;
   int32_t* list_len;
-  const int32_t* group_flags;
+  int32_t* group_flags;      // out: 1 if the group's tile is scored over its whole bounded range
 };
 
 struct NormLaunch {

@@ -218,6 +218,8 @@ __device__ void nnls3(int p, const double Gp[3][3], const double b[3], double ou
   }
 }
 
+constexpr float kSkipFrac = 0.7f;   // sampled survival above which the bound pass is skipped
+
 template <int C, int H, int D>
 __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   constexpr int QB = (C == C_F32) ? 4 : (C == C_FP8 ? 1 : 2);
@@ -230,11 +232,13 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
 
   __shared__ float qf[H][D + 1];     // decoded, unscaled (exact in fp32)
   constexpr int SCR = (H * H > 32 * D) ? H * H : 32 * D;   // doubles
-  __shared__ double scratch[SCR];    // head Gram matrix, later the sampled seed keys
+  __shared__ double scratch[SCR];    // sampled seed keys, later the head Gram matrix
   double (*G)[H] = reinterpret_cast<double (*)[H]>(scratch);
-  __shared__ double qn[H];           // ||q_h||
   __shared__ double wd[H];
+  __shared__ double qn2[H];          // ||q_h||^2
+  __shared__ double gph[3][H];       // <q_p, q_h> for the proxies
   __shared__ double alpha[H][3];
+  __shared__ double rn2[H];          // ||r_h||^2
   __shared__ int prox[3];
   __shared__ int np_s;
   __shared__ int act[H];
@@ -251,20 +255,16 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     act[h] = 0;
   }
   __syncthreads();
-  for (int pr = t; pr < H * H; pr += 256) {
-    const int h = pr / H, j = pr % H;
-    if (j < h) continue;
-    double s = 0.0;
-    for (int i = 0; i < D; ++i) s += (double)qf[h][i] * (double)qf[j][i];
-    G[h][j] = s;
-    G[j][h] = s;
+  for (int h = t; h < H; h += 256) {
+    double s2 = 0.0;
+    for (int i = 0; i < D; ++i) s2 += (double)qf[h][i] * (double)qf[h][i];
+    qn2[h] = s2;
   }
   __syncthreads();
   // proxies: positive heads of largest w_h ||q_h|| (lower head index on ties)
   if (t == 0) {
     int n = 0;
-    const int want = p.num_proxies;
-    for (int r = 0; r < want; ++r) {
+    for (int r = 0; r < p.num_proxies; ++r) {
       int best = -1;
       double bv = -1.0;
       for (int h = 0; h < H; ++h) {
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
         bool used = false;
         for (int u = 0; u < n; ++u) used = used || (prox[u] == h);
         if (used) continue;
-        const double v = wd[h] * sqrt(G[h][h]);
+        const double v = wd[h] * sqrt(qn2[h]);
         if (v > bv) { bv = v; best = h; }
       }
       if (best < 0) break;
@@ -282,20 +282,11 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   }
   __syncthreads();
   const int np = np_s;
-  // nonnegative projections of the other positive heads
-  for (int h = t; h < H; h += 256) {
-    bool is_p = false;
-    for (int u = 0; u < np; ++u) is_p = is_p || (prox[u] == h);
-    double a[3] = {0, 0, 0};
-    if (wd[h] > 0.0 && !is_p && np > 0) {
-      double Gp[3][3], b[3];
-      for (int r = 0; r < 3; ++r) {
-        b[r] = (r < np) ? G[prox[r]][h] : 0.0;
-        for (int c = 0; c < 3; ++c) Gp[r][c] = (r < np && c < np) ? G[prox[r]][prox[c]] : 0.0;
-      }
-      nnls3(np, Gp, b, a);
-    }
-    alpha[h][0] = a[0]; alpha[h][1] = a[1]; alpha[h][2] = a[2];
+  for (int e = t; e < np * H; e += 256) {
+    const int r = e / H, h = e % H;
+    double s2 = 0.0;
+    for (int i = 0; i < D; ++i) s2 += (double)qf[prox[r]][i] * (double)qf[h][i];
+    gph[r][h] = s2;
   }
   __syncthreads();
   auto in_O = [&](int h) {
@@ -304,6 +295,23 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
       if (prox[u] == h) return false;
     return true;
   };
+  // nonnegative projections of the other positive heads; residual norms
+  for (int h = t; h < H; h += 256) {
+    double a[3] = {0, 0, 0};
+    double Gp[3][3], b[3];
+    for (int r = 0; r < 3; ++r) {
+      b[r] = (r < np) ? gph[r][h] : 0.0;
+      for (int c = 0; c < 3; ++c) Gp[r][c] = (r < np && c < np) ? gph[r][prox[c]] : 0.0;
+    }
+    if (in_O(h) && np > 0) nnls3(np, Gp, b, a);
+    alpha[h][0] = a[0]; alpha[h][1] = a[1]; alpha[h][2] = a[2];
+    double r2 = qn2[h];
+    for (int u = 0; u < np; ++u) r2 -= 2.0 * a[u] * b[u];
+    for (int u = 0; u < np; ++u)
+      for (int v = 0; v < np; ++v) r2 += a[u] * Gp[u][v] * a[v];
+    rn2[h] = fmax(r2, 0.0);
+  }
+  __syncthreads();
   // c_p = w_p + sum_{h in O} w_h alpha_hp
   for (int u = 0; u < np; ++u) {
     double v = 0.0;
@@ -312,27 +320,18 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     v = block_sum(v, red);
     if (t == 0) cvec[u] = wd[prox[u]] + v;
   }
-  // residual Gram <r_h, r_j> and the joint (or separable) constant
-  double part = 0.0;
-  const bool separable = (p.flags & DOSA_SEPARABLE_RHO) != 0;
-  for (int pr = t; pr < H * H; pr += 256) {
-    const int h = pr / H, j = pr % H;
-    if (!in_O(h) || !in_O(j)) continue;
-    if (separable && h != j) continue;
-    double r = G[h][j];
-    for (int u = 0; u < np; ++u) r -= alpha[h][u] * G[prox[u]][j] + alpha[j][u] * G[prox[u]][h];
-    for (int u = 0; u < np; ++u)
-      for (int v = 0; v < np; ++v) r += alpha[h][u] * alpha[j][v] * G[prox[u]][prox[v]];
-    if (separable) part += wd[h] * sqrt(fmax(r, 0.0));
-    else part += wd[h] * wd[j] * fmax(r, 0.0);
-  }
-  double rho = block_sum(part, red);
-  rho = separable ? rho : sqrt(fmax(rho, 0.0));
-  __syncthreads();
-  for (int h = t; h < H; h += 256) qn[h] = sqrt(G[h][h]);
-  __syncthreads();
+  // separable residual constant (an upper bound of the joint one) and the
+  // diagonal of the joint sum (a lower bound of it)
+  double ps = 0.0, pl = 0.0;
+  for (int h = t; h < H; h += 256)
+    if (in_O(h)) {
+      ps += wd[h] * sqrt(rn2[h]);
+      pl += wd[h] * wd[h] * rn2[h];
+    }
+  const double rho_sep = block_sum(ps, red);
+  const double rho_lo = sqrt(fmax(block_sum(pl, red), 0.0));
   // activation statistics of the negative heads on up to 64 keys sampled
-  // from the seed window (staged in LDS over the Gram storage)
+  // from the seed window (staged in LDS)
   const int n_last = gr.pos0 + gr.nq;
   const int wlo = max(0, n_last - p.seed_window);
   const int span = pos - wlo + 1;
@@ -365,12 +364,12 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   // aggregate a = sum_{h in A} |w_h| q_h, in fp64, unscaled units
   const double need = (double)p.neg_frac * (double)ns;
   for (int i = t; i < D; i += 256) {
-    double s = 0.0;
+    double sacc = 0.0;
     if (use_neg)
       for (int h = 0; h < H; ++h)
-        if (wd[h] < 0.0 && (ns > 0 ? (double)act[h] >= need : p.neg_frac <= 0.f)) s += -wd[h] * (double)qf[h][i];
-    avec[i] = s;
-    res[i] = s;
+        if (wd[h] < 0.0 && (ns > 0 ? (double)act[h] >= need : p.neg_frac <= 0.f)) sacc += -wd[h] * (double)qf[h][i];
+    avec[i] = sacc;
+    res[i] = sacc;
   }
   __syncthreads();
   // operand rows: proxies verbatim, then terms of the aggregate
@@ -422,36 +421,97 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   for (int i = t; i < D; i += 256) an += avec[i] * avec[i];
   an = sqrt(block_sum(an, red));
   double wq = 0.0;
-  for (int h = t; h < H; h += 256) wq += fabs(wd[h]) * qn[h];
+  for (int h = t; h < H; h += 256) wq += fabs(wd[h]) * sqrt(qn2[h]);
   wq = block_sum(wq, red);
+  const double qs = HasQScale<C>::value ? (double)p.in.q_scale[qrow] : 1.0;
+  // rounding margin: forward error of the fp32 dot products and sums in the
+  // score and bound kernels (Higham, dot-product error gamma_n), with
+  // u = 2^-22 (4x the fp32 unit roundoff) and n = d + H + 16; rho enters via
+  // its separable upper bound.  The score kernels evaluate
+  // sum_h w_h ReLU(x_h) as sum_h (w_h/2)|x_h| + qbar.k/2 with qbar held as a
+  // few terms; their error and magnitude (unscaled) enter as well.
+  const double u = 1.0 / 4194304.0;
+  const double nn = (double)(D + H + 16);
+  const double gam = nn * u / (1.0 - nn * u);
+  double cq = 0.0, sf = 0.0;
+  for (int r = 0; r < np; ++r) cq += cvec[r] * sqrt(qn2[prox[r]]);
+  for (int r = np; r < 4; ++r) sf += sig[r] * fnorm[r];
+  const double l_err = (double)p.lerr[(int64_t)qrow * 2], l_mag = (double)p.lerr[(int64_t)qrow * 2 + 1];
+  const double margin = 2.0 * gam * (wq + cq + sf + rho_sep + 0.5 * l_mag) + ea + 0.5 * l_err;
+  const float tau = p.tau[qrow];
+  // Whether the bound pass is worth running for this query.  Skipping it
+  // (every key survives) is always correct, so this is a cost decision: with
+  // an optimistic certificate (rho replaced by its diagonal lower bound),
+  // evaluate up to 64 keys sampled evenly from the bounded range; if at least
+  // kSkipFrac of them would still survive, the query is scored densely.
+  __shared__ int n_surv_s;
+  if (t == 0) n_surv_s = 0;
+  const int nb = gr.n_bounded;
+  const int nsb = min(64, nb);
+  bool skip = !(tau > -INFINITY) || (p.flags & DOSA_NO_PRUNE) || nsb == 0;
+  if (!skip) {
+    __syncthreads();
+    for (int e = t; e < nsb * D; e += 256) {
+      const int i = e / D, c = e % D;
+      const int key = gr.bound_lo + (int)(((int64_t)i * nb) / nsb);
+      const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
+      kf[i * D + c] = k_elem<C>(p.in.k, row * D + c);
+    }
+    __syncthreads();
+    if (t < nsb) {
+      const int key = gr.bound_lo + (int)(((int64_t)t * nb) / nsb);
+      const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
+      const double ks = HasKScale<C>::value ? (double)p.in.k_scale[row] : 1.0;
+      double ub = 0.0, ad = 0.0, kn2 = 0.0;
+      for (int r = 0; r < np; ++r) {
+        double xd = 0.0;
+        for (int e = 0; e < D; ++e) xd += (double)qf[prox[r]][e] * (double)kf[t * D + e];
+        ub += cvec[r] * fmax(xd, 0.0);
+      }
+      for (int e = 0; e < D; ++e) {
+        ad += avec[e] * (double)kf[t * D + e];
+        kn2 += (double)kf[t * D + e] * (double)kf[t * D + e];
+      }
+      ub = (ub - fmax(ad, 0.0) + rho_lo * sqrt(kn2)) * qs * ks;
+      if (ub >= (double)tau) atomicAdd(&n_surv_s, 1);
+    }
+    __syncthreads();
+    skip = (float)n_surv_s >= kSkipFrac * (float)nsb;
+  }
+  const bool hopeless = skip;
+  double rho = rho_sep;
+  const bool separable = (p.flags & DOSA_SEPARABLE_RHO) != 0;
+  if (!hopeless && !separable) {
+    // joint constant: rho^2 = sum_{h,j in O} w_h w_j max(0, <r_h, r_j>) from the head Gram matrix
+    __syncthreads();
+    for (int pr = t; pr < H * H; pr += 256) {
+      const int h = pr / H, j = pr % H;
+      if (j < h || !in_O(h) || !in_O(j)) continue;
+      double s2 = 0.0;
+      for (int i = 0; i < D; ++i) s2 += (double)qf[h][i] * (double)qf[j][i];
+      G[h][j] = s2;
+      G[j][h] = s2;
+    }
+    __syncthreads();
+    double part = 0.0;
+    for (int pr = t; pr < H * H; pr += 256) {
+      const int h = pr / H, j = pr % H;
+      if (!in_O(h) || !in_O(j)) continue;
+      double r = G[h][j];
+      for (int uu = 0; uu < np; ++uu) r -= alpha[h][uu] * gph[uu][j] + alpha[j][uu] * gph[uu][h];
+      for (int uu = 0; uu < np; ++uu)
+        for (int vv = 0; vv < np; ++vv) r += alpha[h][uu] * alpha[j][vv] * gph[uu][prox[vv]];
+      part += wd[h] * wd[j] * fmax(r, 0.0);
+    }
+    rho = sqrt(fmax(block_sum(part, red), 0.0));
+  }
   if (t == 0) {
-    const double qs = HasQScale<C>::value ? (double)p.in.q_scale[qrow] : 1.0;
-    // rounding margin: forward error of the fp32 dot products and sums in the
-    // score and bound kernels (Higham, dot-product error gamma_n), with
-    // u = 2^-22 (4x the fp32 unit roundoff) and n = d + H + 16
-    const double u = 1.0 / 4194304.0;
-    const double n = (double)(D + H + 16);
-    const double gam = n * u / (1.0 - n * u);
-    double cq = 0.0, sf = 0.0;
-    for (int r = 0; r < np; ++r) cq += cvec[r] * qn[prox[r]];
-    for (int r = np; r < 4; ++r) sf += sig[r] * fnorm[r];
-    // the score kernels evaluate sum_h w_h ReLU(x_h) as sum_h (w_h/2)|x_h| + qbar.k/2
-    // with qbar held as a few terms; their error and magnitude (unscaled) enter here
-    const double l_err = (double)p.lerr[(int64_t)qrow * 2], l_mag = (double)p.lerr[(int64_t)qrow * 2 + 1];
-    const double margin = 2.0 * gam * (wq + cq + sf + rho + 0.5 * l_mag) + ea + 0.5 * l_err;
     const double rho_p = (rho + margin) * qs;
     float* cf = p.coef + (int64_t)qrow * 8;
     for (int r = 0; r < 4; ++r) cf[r] = (r < np) ? (float)(cvec[r] * qs) : (float)(sig[r] * qs);
     cf[4] = (float)rho_p * 1.0000005f;
-    const float tau = p.tau[qrow];
     cf[5] = tau;
     cf[6] = (float)np;
-    // If even the most favourable key cannot drop below tau, nothing is
-    // prunable: UB >= (rho' - ||a'||) ||k|| >= (rho' - ||a'||) min ||k||.
-    const double a_rep = (an + ea) * qs;
-    const double floor_ub = (rho_p - a_rep) * (double)p.norm_min[gr.seq];
-    const bool hopeless = !(tau > -INFINITY) || (p.flags & DOSA_NO_PRUNE) ||
-                          (rho_p - a_rep > 0.0 && floor_ub >= (double)tau);
     cf[7] = hopeless ? 1.f : 0.f;
   }
 }
@@ -485,7 +545,6 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
   const u64 hm = __ballot(qok && hopeless);
   const u64 okm = __ballot(qok);
   const bool all_hopeless = (hm == okm);
-  if (sp == 0 && lane == 0) p.group_flags[gi] = all_hopeless ? 1 : 0;
   const u64 nbounded = (u64)max(hi - lo, 0) * (u64)gr.nq;
   if (all_hopeless) {
     for (int wd = w0 + lane; wd < w1; wd += 64) {
@@ -564,35 +623,62 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// compaction: survivor bitmask -> ascending key list, by ballot-free
-// per-lane popcounts and a wavefront prefix sum
+// compaction: one workgroup per tile, one wavefront per query group.  Each
+// wavefront counts its group's union survivors (popcounts of the bitmask);
+// if the tile's survivors are at least kDenseFrac of its bounded keys, the
+// tile is flagged for the tiled kernel, which walks the bounded range
+// directly.  Otherwise each wavefront turns its bitmask into an ascending key
+// list: per-lane popcounts, a wavefront prefix sum for the write offsets,
+// then each lane expands its word.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void compact_kernel(const CompactLaunch p) {
+constexpr float kDenseFrac = 0.4f;
+
+__global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
+  const int gi0 = blockIdx.x;
+  const GroupInfo head = p.groups[gi0];
+  if (head.tile_first != gi0) return;          // one workgroup per tile
+  const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  const int gi = blockIdx.x;
+  __shared__ uint32_t surv[8];
+  __shared__ uint32_t bounded[8];
+  const bool active = wave < head.tile_n;
+  const int gi = gi0 + (active ? wave : 0);
   const GroupInfo gr = p.groups[gi];
-  bool all = true;
-  for (int i = 0; i < gr.tile_n; ++i) all = all && (p.group_flags[gr.tile_first + i] != 0);
-  if (all) {                 // the tiled kernel walks this tile's bounded range directly
+  const int nw = active ? (gr.n_bounded + 63) / 64 : 0;
+  const unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
+  uint32_t c = 0;
+  for (int wd = lane; wd < nw; wd += 64) c += __popcll(mw[wd]);
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  if (lane == 0) {
+    surv[wave] = active ? c : 0u;
+    bounded[wave] = active ? (uint32_t)gr.n_bounded : 0u;
+  }
+  __syncthreads();
+  uint64_t ts = 0, tb = 0;
+  for (int i = 0; i < 8; ++i) {
+    ts += surv[i];
+    tb += bounded[i];
+  }
+  const bool dense = (float)ts >= kDenseFrac * (float)tb;
+  if (!active) return;
+  if (lane == 0) p.group_flags[gi] = dense ? 1 : 0;
+  if (dense) {
     if (lane == 0) p.list_len[gi] = 0;
     return;
   }
-  const int nw = (gr.n_bounded + 63) / 64;
-  const unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
   int32_t* out = p.lists + gr.list_off;
   uint32_t base = 0;
   for (int w0 = 0; w0 < nw; w0 += 64) {
     const int wd = w0 + lane;
     u64 m = (wd < nw) ? mw[wd] : 0ull;
-    const uint32_t c = __popcll(m);
-    // exclusive prefix over lanes
-    uint32_t incl = c;
+    const uint32_t cnt = __popcll(m);
+    uint32_t incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t v = __shfl_up(incl, off, 64);
       if (lane >= off) incl += v;
     }
-    uint32_t at = base + incl - c;
+    uint32_t at = base + incl - cnt;
     const int k0 = gr.bound_lo + 64 * wd;
     while (m) {
       const int b = __ffsll((long long)m) - 1;
@@ -691,7 +777,7 @@ hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream
 
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s) {
   if (p.n_groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3(p.n_groups), dim3(64), 0, s, p);
+  hipLaunchKernelGGL(compact_kernel, dim3(p.n_groups), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -360,40 +360,56 @@ def decode_mtp(seed: int = 0, batch: int = 64, q_per_seq: int = 2, kv_min: int =
 
 
 def correlated_heads(seed: int = 0, L: int = 32768, H: int = 64, d: int = 128, topk: int = 2048,
-                     dtype: str = "bf16", basis: int = 3, head_noise: float = 0.05,
-                     q_len: Optional[int] = None, chunk: int = 0):
+                     dtype: str = "bf16", corr: float = 0.9995, head_noise: float = 0.05,
+                     topic_window: int = 64, q_len: Optional[int] = None, chunk: int = 0):
     """Supplementary recipe with cross-head structure (not one of the headline workloads).
 
-    Keys: k_s = mu + U c_s + eps_s (rank-16 + noise as above, plus a common
-    offset mu with ||mu|| = sqrt(d)/2 shared by every key; sinks x4).
-    Queries: for each token, ``basis`` directions b_r are anchored to recent
-    keys as in the structured recipe; a positive-weight head is a nonnegative
-    mix of them, q_h = sum_r a_hr b_r + head_noise*n_h; a negative-weight head
-    additionally carries a component along mu, so it fires on most keys.
-    This is the shape of indexer the certificate is designed for: heads that
-    are close to a few others, and negative heads active on broad support.
+    Keys drift slowly through topics: k_s = mu + U c_s + eps_s, where the
+    rank-16 coordinates follow c_s = corr c_{s-1} + sqrt(1-corr^2) xi_s
+    (correlation length ~1/(1-corr) tokens), mu is a common offset with
+    ||mu|| = 0.6 sqrt(d), eps ~ N(0, 0.3^2), sinks 0..3 x4.
+    Queries: every head of token t points along the current topic (the mean
+    of U c over the previous ``topic_window`` keys, scaled to norm sqrt(d))
+    plus ``head_noise`` sqrt(d) of its own random direction, times a per-head
+    gain in [0.5, inf); a negative-weight head instead points mostly along mu
+    (0.8 sqrt(d)) with 0.3 of the topic, so it fires on nearly every key.
+    Heads are then close to one another and the negative heads are active on
+    broad support: the indexer shape the certificate is designed for, and one
+    where the recent-window seed holds most of the true Top-K.
     """
+    from scipy.signal import lfilter
+
     m = L if q_len is None else q_len
     r = _streams(seed, 7, 8)
     U = _low_rank_basis(r[0], d)
     mu = r[1].standard_normal(d).astype(np.float32)
-    mu *= np.float32(0.5 * math.sqrt(d)) / np.linalg.norm(mu)
-    k32 = _structured_keys(L, d, U, r[2])
-    k32[SINKS:] += mu
+    mu *= np.float32(0.6 * math.sqrt(d)) / np.linalg.norm(mu)
+    xi = r[2].standard_normal((L, RANK)).astype(np.float64)
+    xi[1:] *= math.sqrt(1.0 - corr * corr)
+    c = lfilter([1.0], [1.0, -corr], xi, axis=0).astype(np.float32)
+    z = c @ U.T                                                 # [L, d] topic part
+    k32 = mu + z + r[3].standard_normal((L, d)).astype(np.float32) * np.float32(0.3)
+    k32[:SINKS] *= np.float32(4.0)
     pos = np.arange(L - m, L, dtype=np.int64)
-    w = _mixed_sign_weights(m, H, r[3])
-    b = _anchored_queries(pos, basis, d, k32, r[4])          # [m, basis, d]
-    mix = np.abs(r[5].standard_normal((m, H, basis), dtype=np.float32))
-    q32 = np.einsum("thr,trd->thd", mix, b, optimize=True).astype(np.float32)
-    q32 /= np.maximum(np.linalg.norm(q32, axis=-1, keepdims=True), 1e-6) / np.float32(math.sqrt(d))
-    noise = _iid((m, H, d), r[6], 1024) * np.float32(head_noise)
-    q32 += noise
+    w = _mixed_sign_weights(m, H, r[4])
+    cs = np.concatenate([np.zeros((1, d), np.float64), np.cumsum(z, axis=0, dtype=np.float64)])
+    lo = np.maximum(pos - topic_window, 0)
+    hi = np.maximum(pos, 1)
+    topic = ((cs[hi] - cs[lo]) / (hi - lo)[:, None]).astype(np.float32)
+    topic *= np.float32(math.sqrt(d)) / np.maximum(np.linalg.norm(topic, axis=1, keepdims=True), 1e-6)
+    n = _iid((m, H, d), r[5], 1024)
+    n *= np.float32(head_noise * math.sqrt(d)) / np.maximum(np.linalg.norm(n, axis=-1, keepdims=True), 1e-6)
+    gain = np.abs(r[6].standard_normal((m, H))).astype(np.float32) * np.float32(0.5) + np.float32(0.5)
     mu_hat = mu / np.linalg.norm(mu)
-    neg = w < 0
-    q32 += np.where(neg[..., None], np.float32(0.8 * math.sqrt(d)) * mu_hat, np.float32(0.0))
-    return _contig("correlated_heads", H, d, topk, dtype, dtype, q32, w, k32, [m], [L], chunk=chunk,
-                   recipe=f"supplementary: heads = nonnegative mixes of {basis} anchored directions "
-                          f"+ {head_noise} noise; negative heads aligned with a common key offset")
+    neg = (w < 0)[..., None]
+    q32 = np.where(neg, np.float32(0.8 * math.sqrt(d)) * mu_hat + np.float32(0.3) * topic[:, None, :],
+                   topic[:, None, :]) + n
+    q32 *= gain[..., None]
+    return _contig("correlated_heads", H, d, topk, dtype, dtype, q32.astype(np.float32), w, k32, [m], [L],
+                   chunk=chunk,
+                   recipe=f"supplementary: AR({corr}) topic-drift keys + common offset; heads along the "
+                          f"topic of the last {topic_window} keys + {head_noise} noise; negative heads "
+                          f"along the offset")
 
 
 def custom(seed: int, lens, H: int, d: int, topk: int, q_dtype: str = "f32", k_dtype: str = "f32",
