@@ -28,10 +28,51 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0, "f32": 157.3}
 PEAK_HBM_GBS = 8000.0
+COMBO_ID = {("f32", "f32"): 0, ("bf16", "bf16"): 1, ("fp8", "fp8"): 2, ("bf16", "fp8"): 3}
+ROLE_ID = {"score_dense": 0, "score_seed": 1, "score_survivor_tiles": 2, "score_survivor_lists": 2}
+# HBM traffic per launch measured with rocprofv3 counters, valid while the
+# kernel's sources are unchanged (sha256 over KERNEL_SOURCES)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["exact_top_token_amd/csrc/score_kernels.h", "exact_top_token_amd/csrc/dosa_device.h",
+                  "exact_top_token_amd/csrc/dosa_internal.h"]
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_name(pass_name, wl):
+    """Name of the kernel instantiation a pass launches, as profilers print it."""
+    c = COMBO_ID[(wl.q_dtype, wl.k_dtype)]
+    if pass_name in ROLE_ID:
+        k = "score_list_kernel" if pass_name == "score_survivor_lists" else "score_tiled_kernel"
+        return f"{k}<{c}, {wl.H}, {wl.d}, {ROLE_ID[pass_name]}>"
+    return {"plan": "plan_kernel", "bound": "bound_kernel", "compact": "compact_kernel",
+            "key_norms": "key_norm_kernel", "select_seed": "select_kernel", "select_final": "select_kernel",
+            "prep": "qbar_kernel"}.get(pass_name, pass_name)
+
+
+def sources_digest():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kname, workload):
+    """HBM bytes per launch of `kname` from the committed counter summary, or
+    None if there is none for this kernel and workload or the sources changed."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kname or t.get("workload") != workload or t.get("sources_sha256") != sources_digest():
+        return None
+    return t.get("bytes_per_launch")
 
 
 def build_calls(wl, inp):
@@ -82,6 +123,8 @@ def main():
     ap.add_argument("--paths", default="dosa,dsa")
     ap.add_argument("--buffer-cap", type=int, default=0, help="candidate buffer entries per query (0 = default)")
     ap.add_argument("--key-splits", type=int, default=0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run one plain copy of this size first (calibrates HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (queries shard across GPUs "
@@ -105,6 +148,13 @@ def main():
     torch.cuda.set_device(dev)
     inp = to_device(wl, dev)
     calls = build_calls(wl, inp)
+    if a.calib_copy_mib:
+        # a plain copy kernel of known size: reads and writes calib_copy_mib MiB
+        x = torch.ones(a.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        y = torch.empty_like(x)
+        torch.neg(x, out=y)
+        torch.cuda.synchronize()
+        del x, y
     K = wl.topk
     pairs = wl.pairs()
     results = {}
@@ -119,7 +169,7 @@ def main():
                                         c.page_table is not None, path == "dsa", cfg) for _, c in calls)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         out_idx = torch.empty((wl.total_q, K), dtype=torch.int32, device=dev)
-        stats = torch.zeros(8, dtype=torch.int64, device=dev)
+        stats = torch.zeros(len(E.STAT_FIELDS), dtype=torch.int64, device=dev)
 
         def step():
             for q0, c in calls:
@@ -175,23 +225,29 @@ def main():
     # dominant kernel of the main path, by time
     kern = R["kernel_ms_per_step"]
     dom = max(kern, key=kern.get)
-    if dom.startswith("score"):
-        units = {"score_seed": st["pairs_seed"], "score_survivors": st["pairs_scored"],
-                 "score_dense": st["pairs_scored"]}[dom]
-        ach = units * flop_pair / (kern[dom] / 1e3) / 1e12
-        roof = {"kernel": f"{dom} (score_kernel)", "bound": "mfma", "achieved": ach,
-                "peak": PEAK_TFLOPS[wl.q_dtype if wl.q_dtype == wl.k_dtype else "bf16"], "unit": "TFLOP/s"}
+    launches = max(R["launches_per_step"].get(dom, 1), 1)
+    avg_ms = kern[dom] / launches
+    kname = kernel_name(dom, wl)
+    if dom in ROLE_ID:
+        units = {"score_seed": st["pairs_seed"],
+                 "score_survivor_tiles": st["pairs_scored"] - st["pairs_scored_list"],
+                 "score_survivor_lists": st["pairs_scored_list"], "score_dense": st["pairs_scored"]}[dom]
+        per_launch = units * flop_pair / launches
+        roof = {"kernel": kname, "bound": "mfma", "achieved": per_launch / (avg_ms / 1e3) / 1e12,
+                "peak": PEAK_TFLOPS[wl.q_dtype if wl.q_dtype == wl.k_dtype else "bf16"], "unit": "TFLOP/s",
+                "flop_per_launch": per_launch}
     elif dom == "bound":
-        qw = 4
-        units = st["pairs_bounded"] // qw
         kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.k_dtype] * wl.d + 8
-        ach = units * kb / (kern[dom] / 1e3) / 1e9
-        roof = {"kernel": "bound", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        per_launch = st["pairs_bounded"] / 4 * kb / launches
+        roof = {"kernel": kname, "bound": "hbm", "achieved": per_launch / (avg_ms / 1e3) / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "bytes_per_launch": per_launch}
     else:
-        roof = {"kernel": dom, "bound": "alu", "achieved": None, "peak": None, "unit": None}
+        roof = {"kernel": kname, "bound": "alu", "achieved": None, "peak": None, "unit": None}
     if roof.get("achieved") is not None:
         roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["launches_per_step"] = launches
+    roof["avg_launch_ms"] = avg_ms
+    roof["traffic"] = measured_traffic(kname, wl.name)
     bounded = max(st["pairs_bounded"], 1)
     extra = {
         "dense_path_scores_per_s": results.get("dsa", {}).get("scores_per_s"),

@@ -21,10 +21,11 @@ thread_local std::string g_err;
 // ---------------------------------------------------------------------------
 // optional per-pass event timing
 // ---------------------------------------------------------------------------
-enum PassId { P_NORMS = 0, P_SCORE_SEED, P_SELECT_SEED, P_PLAN, P_BOUND, P_COMPACT, P_SCORE_SURV, P_SCORE_DENSE,
-              P_SELECT_FINAL, P_PREP, P_COUNT };
-const char* const kPassNames[P_COUNT] = {"key_norms", "score_seed", "select_seed", "plan", "bound",
-                                         "compact", "score_survivors", "score_dense", "select_final", "prep"};
+enum PassId { P_NORMS = 0, P_SCORE_SEED, P_SELECT_SEED, P_PLAN, P_BOUND, P_COMPACT, P_SURV_TILES, P_SURV_LISTS,
+              P_SCORE_DENSE, P_SELECT_FINAL, P_PREP, P_COUNT };
+const char* const kPassNames[P_COUNT] = {"key_norms", "score_seed", "select_seed", "plan", "bound", "compact",
+                                         "score_survivor_tiles", "score_survivor_lists", "score_dense",
+                                         "select_final", "prep"};
 
 struct Profiler {
   bool on = false;
@@ -90,7 +91,7 @@ struct Plan {
   int64_t list_total = 0;
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
-         o_norms = 0, o_normmin = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0,
+         o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0,
          o_lrows = 0, o_lsig = 0, o_lerr = 0, total = 0;
   uint64_t pairs_total = 0;
 };
@@ -328,7 +329,6 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
     P.o_coef = take((size_t)P.total_q * 8 * sizeof(float));
     P.o_norms = take((size_t)std::max<int64_t>(P.total_k, 1) * sizeof(float));
-    P.o_normmin = take((size_t)std::max(batch, 1) * sizeof(float));
     P.o_seqinfo = take((size_t)(batch + 1) * sizeof(int32_t));
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
@@ -505,7 +505,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
                      stream);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(items)");
   if (st) {
-    unsigned long long add[8] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0};
+    unsigned long long add[9] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0};
     e = launch_stats_add(st, add, stream);
     if (e != hipSuccess) return fail_hip(e, "stats");
   }
@@ -534,6 +534,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.stats = st;
     sl.scored_slot = 4;
     sl.tiled = P.tiled ? 1 : 0;
+    sl.role = ROLE_DENSE;
     {
       PassScope ps(P_SCORE_DENSE, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -552,14 +553,13 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(cu_kv)");
     float* tau = reinterpret_cast<float*>(ws + P.o_tau);
     float* norms = reinterpret_cast<float*>(ws + P.o_norms);
-    float* norm_min = reinterpret_cast<float*>(ws + P.o_normmin);
     float* coef = reinterpret_cast<float*>(ws + P.o_coef);
     u64* masks = reinterpret_cast<u64*>(ws + P.o_masks);
     int32_t* lists = reinterpret_cast<int32_t*>(ws + P.o_lists);
     int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
     int32_t* gflags = reinterpret_cast<int32_t*>(ws + P.o_gflags);
     // 1. per-key norms
-    NormLaunch nl{in, cu_dev, batch, P.total_k, norms, norm_min};
+    NormLaunch nl{in, cu_dev, batch, P.total_k, norms};
     {
       PassScope ps(P_NORMS, stream);
       e = launch_key_norms(P.combo, d, nl, stream);
@@ -578,6 +578,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.stats = st;
     sl.scored_slot = 1;
     sl.tiled = 1;
+    sl.role = ROLE_SEED;
     {
       PassScope ps(P_SCORE_SEED, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -606,8 +607,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     pl.neg_frac = cfg.neg_support_frac;
     pl.flags = cfg.flags;
     pl.tau = tau;
-    pl.norm_min = norm_min;
     pl.lerr = pr.err;
+    pl.norms = norms;
     pl.rows = ws + P.o_rows;
     pl.coef = coef;
     {
@@ -635,7 +636,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
     // 6. compaction -> survivor key lists
-    CompactLaunch cl{dg, G, masks, std::max(P.mask_words, 1), lists, list_len, gflags};
+    CompactLaunch cl{dg, G, coef, masks, std::max(P.mask_words, 1), lists, list_len, gflags};
     {
       PassScope ps(P_COMPACT, stream);
       e = launch_compact(cl, stream);
@@ -657,20 +658,23 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ml.stats = st;
     ml.scored_slot = 4;
     ml.tile_flags = gflags;
+    ml.role = ROLE_SURVIVORS;
     {
-      PassScope ps(P_SCORE_SURV, stream);
+      PassScope ps(P_SURV_TILES, stream);
       ml.items = di + P.seed_items.size();
       ml.n_items = (int)P.surv_tiled_items.size();
       ml.tiled = 1;
       ml.flag_mode = 1;
       e = launch_score(P.combo, H, d, ml, stream);
-      if (e == hipSuccess) {
-        ml.items = di + P.seed_items.size() + P.surv_tiled_items.size();
-        ml.n_items = (int)P.surv_list_items.size();
-        ml.tiled = 0;
-        ml.flag_mode = 2;
-        e = launch_score(P.combo, H, d, ml, stream);
-      }
+    }
+    if (e == hipSuccess) {
+      PassScope ps(P_SURV_LISTS, stream);
+      ml.items = di + P.seed_items.size() + P.surv_tiled_items.size();
+      ml.n_items = (int)P.surv_list_items.size();
+      ml.tiled = 0;
+      ml.flag_mode = 2;
+      ml.scored_slot2 = 8;
+      e = launch_score(P.combo, H, d, ml, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
   }

@@ -10,6 +10,11 @@ namespace dosa {
 // Operand combinations the kernels are built for.
 enum Combo : int { C_F32 = 0, C_BF16 = 1, C_FP8 = 2, C_BF16Q_FP8K = 3 };
 
+// Which pass a scoring launch belongs to (selects a kernel of its own name).
+enum Role : int { ROLE_DENSE = 0, ROLE_SEED = 1, ROLE_SURVIVORS = 2 };
+
+constexpr int kTileWaves = 8;   // wavefronts (query groups) per tiled scoring workgroup
+
 // A query group: up to 4 consecutive queries of one sequence, scored together
 // by one wavefront (MFMA rows = group queries x head slots).
 struct GroupInfo {
@@ -86,10 +91,12 @@ struct ScoreLaunch {
   const int32_t* list_len;   // survivor list length per group (gather mode)
   int32_t topk;
   int32_t scored_slot;       // dosa_stats field (u64 index) that counts scored pairs
+  int32_t scored_slot2;      // a second field that counts them too (0 = none)
   int32_t tiled;             // 1: score_tiled_kernel, 0: score_list_kernel
   const int32_t* tile_flags; // per group: 1 if the certificate prunes nothing in its tile (or NULL)
   int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not
-  unsigned long long* stats; // dosa_stats as u64[8] or NULL
+  int32_t role;              // Role
+  unsigned long long* stats; // dosa_stats as u64[9] or NULL
 };
 
 struct SelectLaunch {
@@ -122,8 +129,8 @@ struct PlanLaunch {
   float neg_frac;
   uint32_t flags;
   const float* tau;          // [total_q]
-  const float* norm_min;     // [batch] smallest key norm per sequence
   const float* lerr;         // [total_q, 2] weighted-query representation error and magnitude
+  const float* norms;        // per logical key (as BoundLaunch::norms)
   void* rows;                // [total_q, 4, d] query storage type
   float* coef;               // [total_q, 8]
 };
@@ -146,6 +153,7 @@ struct BoundLaunch {
 struct CompactLaunch {
   const GroupInfo* groups;
   int32_t n_groups;
+  const float* coef;         // plan coefficients (coef[7]: hopeless flag per query)
   const unsigned long long* masks;
   int32_t mask_words;
   int32_t* lists;
@@ -159,7 +167,6 @@ struct NormLaunch {
   int32_t batch;
   int64_t total_k;
   float* norms;              // [total_k]
-  float* norm_min;           // [batch]
 };
 
 // Launchers (return hipError_t of the launch).

@@ -20,24 +20,30 @@
 //                       used for key ranges (dense path, seed pass).
 //   score_list_kernel   one wavefront per query group walking a key range or a
 //                       survivor list with its own loads (pruned path).
+// Both carry a ROLE template argument (dense path, seed pass, survivor pass)
+// that changes nothing in the code: each pass gets kernels of its own name,
+// so profiles attribute time per pass.  Each operand combination's kernels
+// are instantiated in a source file of their own (score_<combo>.hip).
 //
 // Scores at or above the query's running threshold theta are appended to the
 // query's candidate region as packed (score, position) keys (DoSA pages,
 // Method section: full scoring fused with threshold filtering, scores packed
 // for selection; Related Work: radix selection, bounded-buffer streaming).
-// theta comes from a per-query LDS histogram of every score seen so far: 256
-// bins of 1/32 octave on the order-preserving integer image of the float,
-// anchored below the first block's maximum.  The lower edge of the highest
-// bin with at least K scores at or above it never exceeds the K-th largest
-// score seen, so it is a valid filter at all times.  A full region is
+// theta comes from a per-query LDS histogram of the scores that reached
+// theta: 256 bins of 1/32 octave on the order-preserving integer image of the
+// float, anchored below the first block's maximum.  The lower edge of the
+// highest bin with at least K counted scores at or above it never exceeds
+// the K-th largest score seen, so it is a valid filter at all times (scores
+// below theta are left out: they can only lie in bins at or below theta's,
+// so leaving them out can delay a raise but never make one wrong).  A full region is
 // compacted at theta in one pass; only if that frees too little does the
 // wavefront run an exact radix select.
+#pragma once
 #include "dosa_device.h"
 
 namespace dosa {
 
 constexpr int kTileKeys = 64;   // keys per LDS tile
-constexpr int kTileWaves = 8;   // wavefronts (query groups) per tiled workgroup
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
@@ -308,11 +314,11 @@ struct Scorer {
         hbase = (mx > 0x00800000u + lo) ? mx - lo : 0x00800000u;
       }
     }
-    if (valid && hbase != 0 && so >= hbase) {
+    const bool take = valid && sc >= theta;
+    if (take && hbase != 0 && so >= hbase) {
       const uint32_t bin = min((so - hbase) >> kHistShift, (uint32_t)(kHistBins - 1));
       atomicAdd(&qh[qi * kHistBins + bin], 1u);
     }
-    const bool take = valid && sc >= theta;
     const u64 m = __ballot(take);
     n_scored += __popcll(__ballot(valid));
     const uint32_t slice = (uint32_t)(m >> owner_lane0) & 0xFFFFu;
@@ -349,6 +355,7 @@ struct Scorer {
     if (qok && lane == owner_lane0) p.cb.counts[(int64_t)qrow * p.cb.R + region] = count;
     if (p.stats != nullptr && lane == 0) {
       atomicAdd(&p.stats[p.scored_slot], (u64)n_scored);
+      if (p.scored_slot2 > 0) atomicAdd(&p.stats[p.scored_slot2], (u64)n_scored);
       atomicAdd(&p.stats[5], (u64)n_written);
       atomicAdd(&p.stats[6], (u64)n_reselect);
     }
@@ -359,7 +366,7 @@ struct Scorer {
 // one wavefront per query group: key range (two sub-ranges walked top-down)
 // or survivor list (ascending)
 // ---------------------------------------------------------------------------
-template <int C, int H, int D>
+template <int C, int H, int D, int ROLE>
 __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
   using SC = Scorer<C, H, D>;
   using O = typename SC::O;
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
     sc.template scoreN<4>(B, o);
 #pragma unroll
     for (int b = 0; b < 4; ++b) sc.append(p, gr, it.region, o[b], ks[b], keys[b], v[b], hist);
-    if ((++nblk & 1) == 0) sc.refresh_theta(p.topk);
+    if ((++nblk & 3) == 0) sc.refresh_theta(p.topk);
   };
 
   if (!it.gather) {
@@ -443,7 +450,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
 // 8 wavefronts (consecutive query groups of one sequence) share LDS key tiles
 // (range mode: [a0,a1) then [b0,b1), each from the top tile down)
 // ---------------------------------------------------------------------------
-template <int C, int H, int D>
+template <int C, int H, int D, int ROLE>
 __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const ScoreLaunch p) {
   using SC = Scorer<C, H, D>;
   using O = typename SC::O;
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
         const int key = kb + b * 16 + sc.col;
         sc.append(p, gr, it.region, o[b], ks[b], key, key >= lo && key < hi, hist[wave]);
       }
-      if ((t & 1) == 1) sc.refresh_theta(p.topk);
+      if ((t & 3) == 3) sc.refresh_theta(p.topk);
     }
   }
   if (active) {
@@ -546,158 +553,35 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
 }
 
 // ---------------------------------------------------------------------------
-// final merge: the exact Top-K of each query over regions [r0, r1)
+// launcher for one operand combination (instantiated per score_<combo>.hip)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
-  __shared__ uint32_t hist[2048];
-  const int q = blockIdx.x;
-  const int lane = lane_id();
-  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
-  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
-  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
-  const int nseg = p.r1 - p.r0;
-  uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += cnt[r];
-  Segs sg{base, cnt, cap, nseg};
-  u64 T = 0;
-  if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
-  if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
-  if (p.out_idx == nullptr) return;
-  // exactly min(K, total) entries are >= T; write them in region order
-  int32_t* oi = p.out_idx + (int64_t)q * K;
-  float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
-  uint32_t out = 0;
-  for (int r = 0; r < nseg; ++r) {
-    const u64* src = sg.ptr(r);
-    const uint32_t n = cnt[r];
-    for (uint32_t b0 = 0; b0 < n; b0 += 64) {
-      const uint32_t i = b0 + lane;
-      const u64 e = (i < n) ? src[i] : 0ull;
-      const bool keep = (i < n) && (e >= T);
-      const u64 m = __ballot(keep);
-      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-      if (keep && out + before < (uint32_t)K) {
-        oi[out + before] = key_pos(e);
-        if (os) os[out + before] = key_score(e);
-      }
-      out += __popcll(m);
-    }
-  }
-  out = min(out, (uint32_t)K);
-  for (uint32_t i = out + lane; i < (uint32_t)K; i += 64) {
-    oi[i] = -1;
-    if (os) os[i] = -INFINITY;
-  }
-}
-
-// Same merge, rows ordered by (score desc, position asc): the kept keys are
-// gathered into LDS and bitonic-sorted (K <= 4096 -> 32 KiB).
-__global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p) {
-  __shared__ uint32_t hist[2048];
-  __shared__ u64 keys[4096];
-  const int q = blockIdx.x;
-  const int lane = lane_id();
-  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
-  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
-  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
-  const int nseg = p.r1 - p.r0;
-  uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += cnt[r];
-  Segs sg{base, cnt, cap, nseg};
-  u64 T = 0;
-  if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
-  if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
-  int N = 1;
-  while (N < K) N <<= 1;
-  for (int i = lane; i < N; i += 64) keys[i] = 0ull;
-  __syncthreads();
-  uint32_t out = 0;
-  for (int r = 0; r < nseg; ++r) {
-    const u64* src = sg.ptr(r);
-    const uint32_t n = cnt[r];
-    for (uint32_t b0 = 0; b0 < n; b0 += 64) {
-      const uint32_t i = b0 + lane;
-      const u64 e = (i < n) ? src[i] : 0ull;
-      const bool keep = (i < n) && (e >= T);
-      const u64 m = __ballot(keep);
-      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-      if (keep && out + before < (uint32_t)K) keys[out + before] = e;
-      out += __popcll(m);
-    }
-  }
-  __syncthreads();
-  for (int size = 2; size <= N; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = lane; i < (N >> 1); i += 64) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const u64 a = keys[lo], b = keys[hi];
-        if (desc ? (a < b) : (a > b)) { keys[lo] = b; keys[hi] = a; }
-      }
-      __syncthreads();
-    }
-  }
-  int32_t* oi = p.out_idx + (int64_t)q * K;
-  float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
-  out = min(out, (uint32_t)K);
-  for (int i = lane; i < K; i += 64) {
-    const bool real = (uint32_t)i < out;
-    const u64 e = keys[i];
-    oi[i] = real ? key_pos(e) : -1;
-    if (os) os[i] = real ? key_score(e) : -INFINITY;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// launchers
-// ---------------------------------------------------------------------------
-template <int C, int H, int D>
-static hipError_t launch_score_t(const ScoreLaunch& p, hipStream_t s) {
-  if (p.n_items == 0) return hipSuccess;
+template <int C, int H, int D, int ROLE>
+static hipError_t launch_score_r(const ScoreLaunch& p, hipStream_t s) {
   if (p.tiled)
-    hipLaunchKernelGGL((score_tiled_kernel<C, H, D>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+    hipLaunchKernelGGL((score_tiled_kernel<C, H, D, ROLE>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
   else
-    hipLaunchKernelGGL((score_list_kernel<C, H, D>), dim3(p.n_items), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((score_list_kernel<C, H, D, ROLE>), dim3(p.n_items), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
+template <int C, int H, int D>
+static hipError_t launch_score_t(const ScoreLaunch& p, hipStream_t s) {
+  if (p.n_items == 0) return hipSuccess;
+  switch (p.role) {
+    case ROLE_SEED: return launch_score_r<C, H, D, ROLE_SEED>(p, s);
+    case ROLE_SURVIVORS: return launch_score_r<C, H, D, ROLE_SURVIVORS>(p, s);
+    default: return launch_score_r<C, H, D, ROLE_DENSE>(p, s);
+  }
+}
+
 template <int C>
-static hipError_t dispatch_hd(int H, int d, const ScoreLaunch& p, hipStream_t s) {
+static hipError_t launch_score_c(int H, int d, const ScoreLaunch& p, hipStream_t s) {
 #define DOSA_HD(HH, DD) \
   if (H == HH && d == DD) return launch_score_t<C, HH, DD>(p, s);
   DOSA_HD(8, 64) DOSA_HD(16, 64) DOSA_HD(32, 64) DOSA_HD(64, 64)
   DOSA_HD(8, 128) DOSA_HD(16, 128) DOSA_HD(32, 128) DOSA_HD(64, 128)
 #undef DOSA_HD
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s) {
-  switch (combo) {
-    case C_F32: return dispatch_hd<C_F32>(H, d, p, s);
-    case C_BF16: return dispatch_hd<C_BF16>(H, d, p, s);
-    case C_FP8: return dispatch_hd<C_FP8>(H, d, p, s);
-    case C_BF16Q_FP8K: return dispatch_hd<C_BF16Q_FP8K>(H, d, p, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {
-  if (p.total_q == 0) return hipSuccess;
-  if (p.sorted && p.out_idx != nullptr)
-    hipLaunchKernelGGL(select_sorted_kernel, dim3(p.total_q), dim3(64), 0, s, p);
-  else
-    hipLaunchKernelGGL(select_kernel, dim3(p.total_q), dim3(64), 0, s, p);
-  return hipGetLastError();
-}
-
-int tile_waves() { return kTileWaves; }
-
-bool combo_supported(int combo, int H, int d) {
-  if (combo < 0 || combo > 3) return false;
-  if (!(d == 64 || d == 128)) return false;
-  if (!(H == 8 || H == 16 || H == 32 || H == 64)) return false;
-  return true;
 }
 
 }  // namespace dosa

@@ -1,0 +1,147 @@
+// Final merge of the candidate regions: the exact Top-K per query, and the
+// dispatch of the scoring launchers by operand combination.
+#include "dosa_device.h"
+
+namespace dosa {
+
+// ---------------------------------------------------------------------------
+// final merge: the exact Top-K of each query over regions [r0, r1)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
+  __shared__ uint32_t hist[2048];
+  const int q = blockIdx.x;
+  const int lane = lane_id();
+  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
+  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
+  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
+  const int nseg = p.r1 - p.r0;
+  uint32_t total = 0;
+  for (int r = 0; r < nseg; ++r) total += cnt[r];
+  Segs sg{base, cnt, cap, nseg};
+  u64 T = 0;
+  if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
+  if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
+  if (p.out_idx == nullptr) return;
+  // exactly min(K, total) entries are >= T; write them in region order
+  int32_t* oi = p.out_idx + (int64_t)q * K;
+  float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
+  uint32_t out = 0;
+  for (int r = 0; r < nseg; ++r) {
+    const u64* src = sg.ptr(r);
+    const uint32_t n = cnt[r];
+    for (uint32_t b0 = 0; b0 < n; b0 += 64) {
+      const uint32_t i = b0 + lane;
+      const u64 e = (i < n) ? src[i] : 0ull;
+      const bool keep = (i < n) && (e >= T);
+      const u64 m = __ballot(keep);
+      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+      if (keep && out + before < (uint32_t)K) {
+        oi[out + before] = key_pos(e);
+        if (os) os[out + before] = key_score(e);
+      }
+      out += __popcll(m);
+    }
+  }
+  out = min(out, (uint32_t)K);
+  for (uint32_t i = out + lane; i < (uint32_t)K; i += 64) {
+    oi[i] = -1;
+    if (os) os[i] = -INFINITY;
+  }
+}
+
+// Same merge, rows ordered by (score desc, position asc): the kept keys are
+// gathered into LDS and bitonic-sorted (K <= 4096 -> 32 KiB).
+__global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p) {
+  __shared__ uint32_t hist[2048];
+  __shared__ u64 keys[4096];
+  const int q = blockIdx.x;
+  const int lane = lane_id();
+  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
+  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
+  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
+  const int nseg = p.r1 - p.r0;
+  uint32_t total = 0;
+  for (int r = 0; r < nseg; ++r) total += cnt[r];
+  Segs sg{base, cnt, cap, nseg};
+  u64 T = 0;
+  if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
+  if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
+  int N = 1;
+  while (N < K) N <<= 1;
+  for (int i = lane; i < N; i += 64) keys[i] = 0ull;
+  __syncthreads();
+  uint32_t out = 0;
+  for (int r = 0; r < nseg; ++r) {
+    const u64* src = sg.ptr(r);
+    const uint32_t n = cnt[r];
+    for (uint32_t b0 = 0; b0 < n; b0 += 64) {
+      const uint32_t i = b0 + lane;
+      const u64 e = (i < n) ? src[i] : 0ull;
+      const bool keep = (i < n) && (e >= T);
+      const u64 m = __ballot(keep);
+      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+      if (keep && out + before < (uint32_t)K) keys[out + before] = e;
+      out += __popcll(m);
+    }
+  }
+  __syncthreads();
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = lane; i < (N >> 1); i += 64) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const u64 a = keys[lo], b = keys[hi];
+        if (desc ? (a < b) : (a > b)) { keys[lo] = b; keys[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+  int32_t* oi = p.out_idx + (int64_t)q * K;
+  float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
+  out = min(out, (uint32_t)K);
+  for (int i = lane; i < K; i += 64) {
+    const bool real = (uint32_t)i < out;
+    const u64 e = keys[i];
+    oi[i] = real ? key_pos(e) : -1;
+    if (os) os[i] = real ? key_score(e) : -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_score_f32(int H, int d, const ScoreLaunch& p, hipStream_t s);
+hipError_t launch_score_bf16(int H, int d, const ScoreLaunch& p, hipStream_t s);
+hipError_t launch_score_fp8(int H, int d, const ScoreLaunch& p, hipStream_t s);
+hipError_t launch_score_bf16fp8(int H, int d, const ScoreLaunch& p, hipStream_t s);
+
+hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s) {
+  switch (combo) {
+    case C_F32: return launch_score_f32(H, d, p, s);
+    case C_BF16: return launch_score_bf16(H, d, p, s);
+    case C_FP8: return launch_score_fp8(H, d, p, s);
+    case C_BF16Q_FP8K: return launch_score_bf16fp8(H, d, p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {
+  if (p.total_q == 0) return hipSuccess;
+  if (p.sorted && p.out_idx != nullptr)
+    hipLaunchKernelGGL(select_sorted_kernel, dim3(p.total_q), dim3(64), 0, s, p);
+  else
+    hipLaunchKernelGGL(select_kernel, dim3(p.total_q), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+int tile_waves() { return kTileWaves; }
+
+bool combo_supported(int combo, int H, int d) {
+  if (combo < 0 || combo > 3) return false;
+  if (!(d == 64 || d == 128)) return false;
+  if (!(H == 8 || H == 16 || H == 32 || H == 64)) return false;
+  return true;
+}
+
+}  // namespace dosa

@@ -121,6 +121,7 @@ typedef struct {
   uint64_t candidates_written; /* entries appended to candidate buffers */
   uint64_t reselects;          /* in-kernel buffer re-selections */
   uint64_t groups_skipped;     /* query groups whose certificate could prune nothing */
+  uint64_t pairs_scored_list;  /* the part of pairs_scored scored from compacted survivor lists */
 } dosa_stats;
 
 /* Fill *cfg with the defaults for a given topk. */
@@ -162,8 +163,8 @@ int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const
  * max_entries per-pass totals to out (HOST array) and returns the number of
  * entries written, or a negative status.  Off by default; profiling creates
  * HIP event objects (no device memory) and reuses them across sessions.
- * Pass names: key_norms, score_seed, select_seed, plan, bound, compact,
- * score_survivors, score_dense, select_final. */
+ * Pass names: prep, key_norms, score_seed, select_seed, plan, bound, compact,
+ * score_survivor_tiles, score_survivor_lists, score_dense, select_final. */
 typedef struct {
   const char* name;   /* static string */
   int32_t launches;
