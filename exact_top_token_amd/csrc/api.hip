@@ -87,6 +87,7 @@ struct Plan {
   std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items;
   bool tiled = true;
   int bound_splits = 1;
+  int Js = 1;                        // DoSA: regions of the seed pass
   int mask_words = 0;
   int64_t list_total = 0;
   // workspace offsets
@@ -129,8 +130,7 @@ int resolve_cfg(const dosa_config* in, int32_t topk, dosa_config* out) {
       g_err = "config out of range";
       return DOSA_ERR_INVALID_ARG;
     }
-    if (out->buffer_cap == 0) out->buffer_cap = 2 * topk + 1024;
-    if (out->buffer_cap < topk + 64) {
+    if (out->buffer_cap != 0 && out->buffer_cap < topk + 64) {
       g_err = "buffer_cap must be >= topk + 64";
       return DOSA_ERR_INVALID_ARG;
     }
@@ -156,7 +156,6 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.combo = combo_of(q_dtype, k_dtype);
   P.QW = queries_per_wave(P.combo, H, d);
   P.dense = dense;
-  P.cap = (cfg.buffer_cap + 63) / 64 * 64;
   P.F = cfg.seed_prefix;
   P.W = std::max(cfg.seed_window, 64);
   const int TW = tile_waves();
@@ -251,20 +250,27 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.R = P.J;
   } else {
     // seed pass per tile: the first F keys and the last W keys of the tile's
-    // last query; the keys in between get a certificate
+    // last query, the window split Js ways (regions 0..Js-1) so that the
+    // launch fills the GPU; the keys in between get a certificate
     int64_t loff = 0;
     int max_bounded = 0;
+    const int Js = choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), 256, 1024);
+    P.Js = Js;
     for (const auto& t : tiles) {
       const int wlo = std::max(0, t.n_last - P.W);
       const int f = std::min(P.F, wlo);
-      WorkItem it{};
-      it.group = t.first;
-      it.pad = t.n;
-      it.region = 0;
-      it.a0 = 0; it.a1 = f;
-      it.b0 = wlo; it.b1 = t.n_last;
-      it.gather = 0;
-      P.seed_items.push_back(it);
+      for (int r = 0; r < Js; ++r) {
+        int lo, hi;
+        range_split(wlo, t.n_last, r, Js, 64, lo, hi);
+        WorkItem it{};
+        it.group = t.first;
+        it.pad = t.n;
+        it.region = r;
+        it.a0 = 0; it.a1 = (r == 0) ? f : 0;
+        it.b0 = lo; it.b1 = hi;
+        it.gather = 0;
+        P.seed_items.push_back(it);
+      }
       for (int i = 0; i < t.n; ++i) {
         GroupInfo& g = P.groups[t.first + i];
         g.bound_lo = f;
@@ -277,7 +283,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     }
     const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
     P.J = J;
-    P.R = 1 + J;
+    P.R = Js + J;
     // survivors of tiles whose certificate can prune nothing: tiled kernel over the bounded range
     for (const auto& t : tiles) {
       const GroupInfo& g = P.groups[t.first];
@@ -287,7 +293,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         WorkItem it{};
         it.group = t.first;
         it.pad = t.n;
-        it.region = 1 + r;
+        it.region = Js + r;
         it.a0 = it.a1 = lo;
         it.b0 = lo; it.b1 = hi;
         P.surv_tiled_items.push_back(it);
@@ -298,7 +304,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       for (int r = 0; r < J; ++r) {
         WorkItem it{};
         it.group = gi;
-        it.region = 1 + r;
+        it.region = Js + r;
         it.gather = 1;
         it.a0 = r;
         it.a1 = J;
@@ -312,6 +318,25 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     int64_t bsum = 0;
     for (auto& g : P.groups) bsum += g.n_bounded;
     P.bound_splits = choose_splits(G, G ? bsum / G : 0, 4096, 4096);
+  }
+  // Candidate region capacity.  A region scoring n keys against a running
+  // threshold receives about K (1 + ln(n / K)) entries (the expected number of
+  // records among n draws); automatic sizing takes 1.3x that plus slack, so a
+  // region rarely has to be compacted mid-sweep, and never more than n + 64.
+  if (cfg.buffer_cap == 0) {
+    int64_t max_n = 0;
+    for (const auto& it : P.items) {
+      int64_t n = (int64_t)(it.a1 - it.a0) + (it.b1 - it.b0);
+      if (it.gather) n = (P.groups[it.group].n_bounded + it.a1 - 1) / it.a1 + 16;
+      max_n = std::max(max_n, n);
+    }
+    const double k = (double)topk;
+    const double est = 1.3 * k * (1.0 + std::log(std::max((double)max_n, k) / k)) + 256.0;
+    int64_t cap = std::min<int64_t>((int64_t)est, max_n + 64);
+    cap = std::max<int64_t>(cap, topk + 64);
+    P.cap = (int)((cap + 63) / 64 * 64);
+  } else {
+    P.cap = (cfg.buffer_cap + 63) / 64 * 64;
   }
   // workspace layout
   size_t o = 0;
@@ -364,7 +389,7 @@ int dosa_default_config(int32_t topk, dosa_config* cfg) {
   cfg->num_proxies = 3;
   cfg->seed_window = 4096;
   cfg->seed_prefix = 64;
-  cfg->buffer_cap = 2 * (topk > 0 ? topk : 2048) + 1024;
+  cfg->buffer_cap = 0;   // automatic
   cfg->key_splits = 0;
   cfg->neg_support_frac = 0.5f;
   cfg->flags = 0;
@@ -565,7 +590,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_key_norms(P.combo, d, nl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
-    // 2. seed pass: exact scores of the seed keys into region 0
+    // 2. seed pass: exact scores of the seed keys into regions 0..Js-1
     ScoreLaunch sl{};
     sl.in = in;
     sl.lrows = pr.rows;
@@ -590,7 +615,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ts.total_q = (int32_t)P.total_q;
     ts.topk = topk;
     ts.r0 = 0;
-    ts.r1 = 1;
+    ts.r1 = P.Js;
     ts.tau_out = tau;
     {
       PassScope ps(P_SELECT_SEED, stream);
@@ -642,7 +667,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_compact(cl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
-    // 7. survivors scored with all heads into regions 1..J, threshold starts at tau:
+    // 7. survivors scored with all heads into regions Js..Js+J-1, threshold starts at tau:
     //    tiles whose certificate prunes nothing take the tiled kernel over the
     //    bounded range, the other groups walk their compacted lists
     ScoreLaunch ml{};

@@ -184,6 +184,15 @@ __device__ __forceinline__ int64_t key_row(const Inputs& in, int key_base, int s
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// The lane id computed afresh where it is used.  Values derived from it are
+// then recomputed in place instead of being hoisted out of the scoring loops
+// and held in registers (two VALU instructions instead of a spill).
+__device__ __forceinline__ int lane_fresh() {
+  int v;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+  return v;
+}
+
 __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   const int lane = lane_id();
 #pragma unroll
@@ -193,6 +202,9 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   }
   return v;
 }
+
+// Wavefront-rows of 64 candidates loaded together by the streaming loops.
+constexpr int kBatch = 8;
 
 // Segmented view of a query's candidate regions.
 struct Segs {
@@ -225,9 +237,19 @@ __device__ __noinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) {
     for (int r = 0; r < sg.nseg; ++r) {
       const u64* ptr = sg.ptr(r);
       const uint32_t n = sg.n(r);
-      for (uint32_t i = lane; i < n; i += 64) {
-        const u64 e = ptr[i];
-        if (p == 0 || (e >> hs) == want) atomicAdd(&hist[(uint32_t)(e >> sh) & (uint32_t)(nb - 1)], 1u);
+      for (uint32_t b = 0; b < n; b += 64 * kBatch) {
+        u64 e[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {     // all loads of the batch in flight together
+          const uint32_t i = b + 64u * u + lane;
+          e[u] = (i < n) ? ptr[i] : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const uint32_t i = b + 64u * u + lane;
+          if (i < n && (p == 0 || (e[u] >> hs) == want))
+            atomicAdd(&hist[(uint32_t)(e[u] >> sh) & (uint32_t)(nb - 1)], 1u);
+        }
       }
     }
     __syncthreads();
@@ -255,17 +277,27 @@ __device__ __noinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) {
 }
 
 // Copy the entries >= T of src[0..n) to dst[out..] in order (dst may equal
-// src).  Returns the new end.
+// src, with out <= 0 then).  Returns the new end.  Entries are read kBatch
+// wavefront-rows at a time before any is written: in place, every write
+// lands below the first unread entry, so the batch cannot clobber its input.
 __device__ __forceinline__ uint32_t compact_ge(const u64* src, uint32_t n, u64 T, u64* dst, uint32_t out) {
   const int lane = lane_id();
-  for (uint32_t base = 0; base < n; base += 64) {
-    const uint32_t i = base + lane;
-    const u64 e = (i < n) ? src[i] : 0ull;
-    const bool keep = (i < n) && (e >= T);
-    const u64 m = __ballot(keep);
-    const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-    if (keep && out + before < n) dst[out + before] = e;
-    out += __popcll(m);
+  for (uint32_t base = 0; base < n; base += 64 * kBatch) {
+    u64 e[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = base + 64u * u + lane;
+      e[u] = (i < n) ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = base + 64u * u + lane;
+      const bool keep = (i < n) && (e[u] >= T);
+      const u64 m = __ballot(keep);
+      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+      if (keep) dst[out + before] = e[u];
+      out += __popcll(m);
+    }
   }
   return out;
 }

@@ -66,9 +66,18 @@ __device__ __noinline__ u64 select_kth_wave(const u64* ptr, uint32_t n, int K, u
     for (int b = lane; b < 256; b += 64) hist[b] = 0;
     wave_sync();
     const u64 want = (p == 0) ? 0 : (prefix >> hs);
-    for (uint32_t i = lane; i < n; i += 64) {
-      const u64 e = ptr[i];
-      if (p == 0 || (e >> hs) == want) atomicAdd(&hist[(uint32_t)(e >> sh) & 255u], 1u);
+    for (uint32_t b = 0; b < n; b += 64 * kBatch) {
+      u64 e[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = b + 64u * u + lane;
+        e[u] = (i < n) ? ptr[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = b + 64u * u + lane;
+        if (i < n && (p == 0 || (e[u] >> hs) == want)) atomicAdd(&hist[(uint32_t)(e[u] >> sh) & 255u], 1u);
+      }
     }
     wave_sync();
     uint32_t s = 0;
@@ -93,6 +102,29 @@ __device__ __noinline__ u64 select_kth_wave(const u64* ptr, uint32_t n, int K, u
   return prefix;
 }
 
+// Region compaction for the streaming select: keep the entries >= tq of
+// the n at bq; if more than half the region is still in use, select the
+// exact K-th and keep K.  Returns the new count in the low 31 bits, bit 31
+// set if a select ran, and the new threshold's bits in the high word.
+__device__ __noinline__ u64 shrink_region(u64* bq, uint32_t n, float tq, int cap, int K, uint32_t* shist) {
+  uint32_t nk = n;
+  float th = tq;
+  uint32_t sel = 0;
+  if (tq > -INFINITY) {
+    nk = compact_ge(bq, n, (u64)f2ord(tq) << 32, bq, 0);
+    wave_sync();
+  }
+  if (nk > (uint32_t)(cap / 2) && nk > (uint32_t)K) {
+    const u64 T = select_kth_wave(bq, nk, K, shist);
+    compact_ge(bq, nk, T, bq, 0);
+    wave_sync();
+    nk = (uint32_t)K;
+    th = fmaxf(th, key_score(T));
+    sel = 1u;
+  }
+  return ((u64)__float_as_uint(th) << 32) | (u64)(nk | (sel << 31));
+}
+
 constexpr int kHistBins = 256;          // running-threshold histogram bins per query
 constexpr int kHistShift = 18;          // 2^18 ord units per bin: 32 bins per octave
 constexpr int kHistAnchor = 192;        // the first block's maximum lands in this bin
@@ -108,26 +140,34 @@ struct Scorer {
 
   typename O::frag A[HG][STEPS];
   typename O::frag AL[STEPS];       // weighted-query terms of the group's queries
-  float sl[4];                      // their scales / 2, for this lane's 4 output rows
-  int lane, col, g, qi, qrow, pos, owner_lane0;
-  bool qok, owner;
+  int q_row0, pos0, nq;   // the group's first query row and position, its query count (wavefront-uniform)
+  // Lane roles, recomputed from the lane id where used (cheaper than holding
+  // them in registers across the scoring loop).
+  __device__ __forceinline__ int col() const { return lane_fresh() & 15; }
+  __device__ __forceinline__ int g() const { return lane_fresh() >> 4; }
+  __device__ __forceinline__ int qi() const { return (4 * g()) / S; }
+  __device__ __forceinline__ int qrow() const { return q_row0 + qi(); }
+  __device__ __forceinline__ int pos() const { return pos0 + qi(); }
+  __device__ __forceinline__ int owner_lane0() const { return 16 * (qi() * (4 / QW)); }
+  __device__ __forceinline__ bool qok() const { return qi() < nq; }
+  __device__ __forceinline__ bool owner() const { return g() == (owner_lane0() >> 4); }
   float qs, theta;
   uint32_t count;
   u64* buf;
-  const float* wq;   // LDS: this lane's query weights / 2 [H]
-  uint32_t wq_lds;   // the same as an LDS byte address
+  uint32_t wq_lds;   // LDS byte address of this lane's query's weights / 2, then its term scales / 2
   uint32_t* qh;      // LDS: this wavefront's query histograms [QW][kHistBins]
   uint32_t hbase;    // ord value of the lower edge of bin 0 (0 = not anchored yet)
   uint32_t n_written, n_reselect, n_scored;
 
-  // wl: LDS [QW][H] weights of this wavefront's queries (filled here, halved);
+  // wl: LDS [QW][H + S]: per query the head weights / 2, then the scales / 2
+  // of its weighted-query terms (filled here);
   // hq: LDS [QW][kHistBins] running-threshold histograms (zeroed here).
   __device__ __forceinline__ void init(const ScoreLaunch& p, const GroupInfo& gr, int region, float* wl,
                                        uint32_t* hq, bool active) {
-    lane = lane_id();
-    col = lane & 15;
-    g = lane >> 4;
-    const int nq = active ? gr.nq : 0;
+    const int lane = lane_id(), g = lane >> 4;
+    nq = active ? gr.nq : 0;
+    q_row0 = gr.q_row0;
+    pos0 = gr.pos0;
     {
       const int ra = lane & 15;
       const int qa = ra / S, hs = ra % S;
@@ -146,24 +186,17 @@ struct Scorer {
       else
         O::zero(AL);
     }
-    for (int e = lane; e < QW * H; e += 64) {
-      const int q = e / H;
-      wl[e] = (q < nq) ? 0.5f * p.in.w[(int64_t)(gr.q_row0 + q) * H + (e % H)] : 0.f;
+    for (int e = lane; e < QW * (H + S); e += 64) {
+      const int q = e / (H + S), h = e % (H + S);
+      float v = 0.f;
+      if (q < nq) v = 0.5f * (h < H ? p.in.w[(int64_t)(gr.q_row0 + q) * H + h] : p.lsig[(int64_t)(gr.q_row0 + q) * S + (h - H)]);
+      wl[e] = v;
     }
-    qi = (4 * g) / S;
-    qok = qi < nq;
-    qrow = gr.q_row0 + qi;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sl[i] = qok ? 0.5f * p.lsig[(int64_t)qrow * S + ((4 * g + i) % S)] : 0.f;
-    wq = wl + qi * H;
-    wq_lds = (uint32_t)(uintptr_t)wq;   // low 32 bits of a generic LDS address = the LDS offset
-    qs = (HasQScale<C>::value && qok) ? p.in.q_scale[qrow] : 1.f;
-    pos = gr.pos0 + qi;
-    theta = (p.theta_init != nullptr && qok) ? p.theta_init[qrow] : -INFINITY;
+    wq_lds = (uint32_t)(uintptr_t)(wl + qi() * (H + S));   // low 32 bits of a generic LDS address = the LDS offset
+    qs = (HasQScale<C>::value && qok()) ? p.in.q_scale[qrow()] : 1.f;
+    theta = (p.theta_init != nullptr && qok()) ? p.theta_init[qrow()] : -INFINITY;
     count = 0;
-    owner_lane0 = 16 * (qi * (4 / QW));
-    owner = (lane >> 4) == (owner_lane0 >> 4);
-    buf = qok ? p.cb.cand + ((int64_t)qrow * p.cb.R + region) * p.cb.cap : nullptr;
+    buf = qok() ? p.cb.cand + ((int64_t)qrow() * p.cb.R + region) * p.cb.cap : nullptr;
     qh = hq;
     for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
     hbase = 0;
@@ -181,7 +214,7 @@ struct Scorer {
       if (b0 == 0) continue;
       uint32_t s4 = 0;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s4 += h[lane * 4 + t];
+      for (int t = 0; t < 4; ++t) s4 += h[lane_id() * 4 + t];
       const uint32_t suf = wave_suffix_sum(s4);
       const bool cross = (suf >= (uint32_t)K) && (suf - s4 < (uint32_t)K);
       const u64 cm = __ballot(cross);
@@ -197,35 +230,26 @@ struct Scorer {
       uint32_t edge = b0 + ((uint32_t)b << kHistShift);
       if (edge < b0 || edge > 0xFF7FFFFFu) edge = 0xFF7FFFFFu;   // stay on finite floats
       const float th = ord2f(edge);
-      if (qi == qq && th > theta) theta = th;
+      if (qi() == qq && th > theta) theta = th;
     }
   }
 
   // Compact the region of query qq to the entries >= its theta; if that
-  // leaves it more than half full, select the exact K-th and keep K.
+  // leaves it more than half full, select the exact K-th and keep K.  The
+  // work is a call (shrink_region), so its registers do not weigh on the
+  // scoring loop around it.
   __device__ __forceinline__ void shrink(const ScoreLaunch& p, const GroupInfo& gr, int region, int qq,
                                          uint32_t* shist) {
     const int cap = p.cb.cap;
     const uint32_t cq = __shfl(count, 16 * (qq * (4 / QW)), 64);
     const float tq = __shfl(theta, 16 * (qq * (4 / QW)), 64);
     u64* bq = p.cb.cand + ((int64_t)(gr.q_row0 + qq) * p.cb.R + region) * cap;
-    uint32_t nk = cq;
-    float th = tq;
-    if (tq > -INFINITY) {
-      nk = compact_ge(bq, cq, (u64)f2ord(tq) << 32, bq, 0);
-      wave_sync();
-    }
-    if (nk > (uint32_t)(cap / 2) && nk > (uint32_t)p.topk) {
-      const u64 T = select_kth_wave(bq, nk, p.topk, shist);
-      compact_ge(bq, nk, T, bq, 0);
-      wave_sync();
-      nk = (uint32_t)p.topk;
-      th = fmaxf(th, key_score(T));
-      ++n_reselect;
-    }
-    if (qi == qq) {
+    const u64 r = shrink_region(bq, cq, tq, cap, p.topk, shist);
+    const uint32_t nk = (uint32_t)r & 0x7FFFFFFFu;
+    if ((uint32_t)r >> 31) ++n_reselect;
+    if (qi() == qq) {
       count = nk;
-      theta = th;
+      theta = __uint_as_float((uint32_t)(r >> 32));
     }
   }
 
@@ -258,7 +282,7 @@ struct Scorer {
     float o[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) o[b] = 0.f;
-    uint32_t wa = wq_lds + 4u * (uint32_t)((4 * g) % S);
+    uint32_t wa = wq_lds + 4u * (uint32_t)((4 * g()) % S);
     asm volatile("" : "+v"(wa));
     typedef __attribute__((address_space(3))) const v4f lds_v4f;
     v4f cur[NB];
@@ -284,6 +308,7 @@ struct Scorer {
         cur[b] = nxt[b];
       }
     }
+    const v4f sl = *reinterpret_cast<lds_v4f*>((uintptr_t)(wa + 4u * (uint32_t)(S * HG)));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
@@ -300,7 +325,7 @@ struct Scorer {
   __device__ __forceinline__ void append(const ScoreLaunch& p, const GroupInfo& gr, int region, float o,
                                          float ks, int key, bool kvalid, uint32_t* shist) {
     const float sc = o * qs * ks;
-    const bool valid = owner && qok && kvalid && key <= pos;
+    const bool valid = owner() && qok() && kvalid && key <= pos();
     const uint32_t so = f2ord(sc);
     if (__any(hbase == 0)) {
       // anchor each query's histogram below the maximum of its first scores
@@ -308,7 +333,7 @@ struct Scorer {
       uint32_t mx = valid ? so : 0u;
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-      mx = __shfl(mx, owner_lane0 + col, 64);
+      mx = __shfl(mx, owner_lane0() + col(), 64);
       if (hbase == 0 && mx != 0u) {
         const uint32_t lo = (uint32_t)kHistAnchor << kHistShift;
         hbase = (mx > 0x00800000u + lo) ? mx - lo : 0x00800000u;
@@ -317,12 +342,12 @@ struct Scorer {
     const bool take = valid && sc >= theta;
     if (take && hbase != 0 && so >= hbase) {
       const uint32_t bin = min((so - hbase) >> kHistShift, (uint32_t)(kHistBins - 1));
-      atomicAdd(&qh[qi * kHistBins + bin], 1u);
+      atomicAdd(&qh[qi() * kHistBins + bin], 1u);
     }
     const u64 m = __ballot(take);
     n_scored += __popcll(__ballot(valid));
-    const uint32_t slice = (uint32_t)(m >> owner_lane0) & 0xFFFFu;
-    const uint32_t before = __popc(slice & ((1u << col) - 1u));
+    const uint32_t slice = (uint32_t)(m >> owner_lane0()) & 0xFFFFu;
+    const uint32_t before = __popc(slice & ((1u << col()) - 1u));
     if (take) buf[count + before] = make_key(sc, key);
     count += __popc(slice);
     n_written += __popcll(m);
@@ -345,15 +370,15 @@ struct Scorer {
       if (cq > (uint32_t)p.topk && tq > -INFINITY) {
         u64* bq = p.cb.cand + ((int64_t)(gr.q_row0 + qq) * p.cb.R + region) * p.cb.cap;
         const uint32_t nk = compact_ge(bq, cq, (u64)f2ord(tq) << 32, bq, 0);
-        if (qi == qq) count = nk;
+        if (qi() == qq) count = nk;
       }
     }
     wave_sync();
   }
 
   __device__ __forceinline__ void finish(const ScoreLaunch& p, int region) {
-    if (qok && lane == owner_lane0) p.cb.counts[(int64_t)qrow * p.cb.R + region] = count;
-    if (p.stats != nullptr && lane == 0) {
+    if (qok() && lane_id() == owner_lane0()) p.cb.counts[(int64_t)qrow() * p.cb.R + region] = count;
+    if (p.stats != nullptr && lane_id() == 0) {
       atomicAdd(&p.stats[p.scored_slot], (u64)n_scored);
       if (p.scored_slot2 > 0) atomicAdd(&p.stats[p.scored_slot2], (u64)n_scored);
       atomicAdd(&p.stats[5], (u64)n_written);
@@ -371,7 +396,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
   using SC = Scorer<C, H, D>;
   using O = typename SC::O;
   __shared__ uint32_t hist[256];
-  __shared__ __attribute__((aligned(16))) float wl[SC::QW * H];
+  __shared__ __attribute__((aligned(16))) float wl[SC::QW * (H + SC::S)];
   __shared__ uint32_t qhist[SC::QW * kHistBins];
   const WorkItem it = p.items[blockIdx.x];
   const GroupInfo gr = p.groups[it.group];
@@ -390,7 +415,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
     ks = 1.f;
     if (kvalid) {
       const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
-      O::load_k(kbytes + row * SC::KBYTES, sc.g, B);
+      O::load_k(kbytes + row * SC::KBYTES, sc.g(), B);
       if constexpr (HasKScale<C>::value) ks = p.in.k_scale[row];
     } else {
       O::zero(B);
@@ -405,7 +430,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
     sc.template scoreN<4>(B, o);
 #pragma unroll
     for (int b = 0; b < 4; ++b) sc.append(p, gr, it.region, o[b], ks[b], keys[b], v[b], hist);
-    if ((++nblk & 3) == 0) sc.refresh_theta(p.topk);
+    if ((++nblk & 7) == 0) sc.refresh_theta(p.topk);
   };
 
   if (!it.gather) {
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
         bool v[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          keys[b] = kb - 16 * b + sc.col;
+          keys[b] = kb - 16 * b + sc.col();
           v[b] = keys[b] >= lo && keys[b] < hi;
         }
         step4(keys, v);
@@ -435,7 +460,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
       bool v[4];
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int i0 = e + 16 * b + sc.col;
+        const int i0 = e + 16 * b + sc.col();
         v[b] = i0 < e1;
         keys[b] = v[b] ? lst[i0] : 0;
       }
@@ -458,14 +483,16 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   constexpr int ROW = KB + 16;                       // padded LDS row: conflict-free 16-byte reads
   constexpr int CPK = KB / 16;                       // 16-byte chunks per key
   constexpr int NCH = (kTileKeys * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
+  // 16-key blocks per scoring step: as many as the key fragments' registers allow
+  constexpr int FB = (int)sizeof(typename O::frag) * SC::STEPS;   // bytes of one block's key fragment per lane
+  constexpr int NBK = FB <= 32 ? 4 : (FB <= 64 ? 2 : 1);
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileKeys * ROW];
   __shared__ float kscale[2][kTileKeys];
-  __shared__ __attribute__((aligned(16))) float wl[kTileWaves][SC::QW * H];
+  __shared__ __attribute__((aligned(16))) float wl[kTileWaves][SC::QW * (H + SC::S)];
   __shared__ uint32_t hist[kTileWaves][256];
   __shared__ uint32_t qhist[kTileWaves][SC::QW * kHistBins];
 
-  const int wave = threadIdx.x >> 6;
-  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;   // wavefront-uniform
   const WorkItem it = p.items[blockIdx.x];
   const int ngroups = it.pad;                        // query groups in this tile
   if (p.flag_mode == 1) {
@@ -487,6 +514,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   v4i stage[NCH];
   float stage_s = 1.f;
   auto fetch = [&](int t) {
+    const int tid = lane_fresh() + 64 * wave;
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
     const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
@@ -510,6 +538,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     }
   };
   auto commit = [&](int bufi) {
+    const int tid = lane_fresh() + 64 * wave;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 64 * kTileWaves;
@@ -530,20 +559,22 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
     const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
     if (active) {
-      typename O::frag B[4][SC::STEPS];
-      float ks[4], o[4];
+      float o[4];
+#pragma unroll
+      for (int hb = 0; hb < 4 / NBK; ++hb) {
+        typename O::frag B[NBK][SC::STEPS];
+#pragma unroll
+        for (int b = 0; b < NBK; ++b)
+          O::load_k(&ktile[bufi][((NBK * hb + b) * 16 + sc.col()) * ROW], sc.g(), B[b]);
+        sc.template scoreN<NBK>(B, o + NBK * hb);
+      }
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        O::load_k(&ktile[bufi][(b * 16 + sc.col) * ROW], sc.g, B[b]);
-        ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + sc.col] : 1.f;
+        const int key = kb + b * 16 + sc.col();
+        const float ks = HasKScale<C>::value ? kscale[bufi][b * 16 + sc.col()] : 1.f;
+        sc.append(p, gr, it.region, o[b], ks, key, key >= lo && key < hi, hist[wave]);
       }
-      sc.template scoreN<4>(B, o);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int key = kb + b * 16 + sc.col;
-        sc.append(p, gr, it.region, o[b], ks[b], key, key >= lo && key < hi, hist[wave]);
-      }
-      if ((t & 3) == 3) sc.refresh_theta(p.topk);
+      if ((t & 7) == 7) sc.refresh_theta(p.topk);
     }
   }
   if (active) {

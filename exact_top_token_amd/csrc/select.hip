@@ -29,17 +29,25 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   for (int r = 0; r < nseg; ++r) {
     const u64* src = sg.ptr(r);
     const uint32_t n = cnt[r];
-    for (uint32_t b0 = 0; b0 < n; b0 += 64) {
-      const uint32_t i = b0 + lane;
-      const u64 e = (i < n) ? src[i] : 0ull;
-      const bool keep = (i < n) && (e >= T);
-      const u64 m = __ballot(keep);
-      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-      if (keep && out + before < (uint32_t)K) {
-        oi[out + before] = key_pos(e);
-        if (os) os[out + before] = key_score(e);
+    for (uint32_t b0 = 0; b0 < n; b0 += 64 * kBatch) {
+      u64 e[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = b0 + 64u * u + lane;
+        e[u] = (i < n) ? src[i] : 0ull;
       }
-      out += __popcll(m);
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = b0 + 64u * u + lane;
+        const bool keep = (i < n) && (e[u] >= T);
+        const u64 m = __ballot(keep);
+        const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+        if (keep && out + before < (uint32_t)K) {
+          oi[out + before] = key_pos(e[u]);
+          if (os) os[out + before] = key_score(e[u]);
+        }
+        out += __popcll(m);
+      }
     }
   }
   out = min(out, (uint32_t)K);
@@ -74,14 +82,22 @@ __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p)
   for (int r = 0; r < nseg; ++r) {
     const u64* src = sg.ptr(r);
     const uint32_t n = cnt[r];
-    for (uint32_t b0 = 0; b0 < n; b0 += 64) {
-      const uint32_t i = b0 + lane;
-      const u64 e = (i < n) ? src[i] : 0ull;
-      const bool keep = (i < n) && (e >= T);
-      const u64 m = __ballot(keep);
-      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-      if (keep && out + before < (uint32_t)K) keys[out + before] = e;
-      out += __popcll(m);
+    for (uint32_t b0 = 0; b0 < n; b0 += 64 * kBatch) {
+      u64 e[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = b0 + 64u * u + lane;
+        e[u] = (i < n) ? src[i] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const uint32_t i = b0 + 64u * u + lane;
+        const bool keep = (i < n) && (e[u] >= T);
+        const u64 m = __ballot(keep);
+        const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+        if (keep && out + before < (uint32_t)K) keys[out + before] = e[u];
+        out += __popcll(m);
+      }
     }
   }
   __syncthreads();

@@ -101,7 +101,10 @@ typedef struct {
   int32_t num_proxies;      /* positive heads evaluated exactly in the bound: 0..3 (default 3) */
   int32_t seed_window;      /* seed = the last seed_window visible keys ... (default 4096) */
   int32_t seed_prefix;      /* ... plus the first seed_prefix keys (default 64) */
-  int32_t buffer_cap;       /* per-query candidate buffer, entries; >= topk + 64 (default 2*topk + 1024) */
+  int32_t buffer_cap;       /* entries per candidate region (each query has one region per key
+                               range scored in parallel); 0 = automatic (default): about
+                               1.3*topk*(1 + ln(range/topk)) + 256 for the longest range, so
+                               that regions rarely overflow; else >= topk + 64 */
   int32_t key_splits;       /* key ranges scored in parallel per query group; 0 = automatic */
   float neg_support_frac;   /* negative head joins the aggregate if positive on >= this
                                fraction of the sampled seed keys (default 0.5) */
