@@ -21,7 +21,19 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
   if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
-  if (p.out_idx == nullptr) return;
+  if (p.out_idx == nullptr) {
+    // threshold mode: keep only the K entries >= T in the merged regions, so
+    // a later merge reads K of them instead of all
+    if (total > (uint32_t)K) {
+      for (int r = 0; r < nseg; ++r) {
+        u64* ptr = p.cb.cand + ((int64_t)q * R + p.r0 + r) * cap;
+        const uint32_t nk = compact_ge(ptr, cnt[r], T, ptr, 0);
+        __syncthreads();
+        if (lane == 0) p.cb.counts[(int64_t)q * R + p.r0 + r] = nk;
+      }
+    }
+    return;
+  }
   // exactly min(K, total) entries are >= T; write them in region order
   int32_t* oi = p.out_idx + (int64_t)q * K;
   float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
