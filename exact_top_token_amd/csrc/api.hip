@@ -84,7 +84,7 @@ struct Plan {
   int64_t total_q = 0, total_k = 0;
   std::vector<GroupInfo> groups;
   std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed, tiled-survivor, list-survivor items
-  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items;
+  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items;
   bool tiled = true;
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
@@ -311,8 +311,30 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         P.surv_list_items.push_back(it);
       }
     P.items = P.seed_items;
+    // bound pass over LDS key tiles when tiles hold enough groups: one item per
+    // (tile, 64-key-aligned share of its bounded range)
+    if (P.tiled) {
+      int64_t bsum_t = 0;
+      for (const auto& t : tiles) bsum_t += P.groups[t.first].n_bounded;
+      const int Jb = choose_splits(NT, NT ? bsum_t / NT : 0, 512, 2048);
+      for (const auto& t : tiles) {
+        const GroupInfo& g = P.groups[t.first];
+        for (int r = 0; r < Jb; ++r) {
+          int lo, hi;
+          range_split(g.bound_lo, g.bound_lo + g.n_bounded, r, Jb, 64, lo, hi);
+          if (hi <= lo && r > 0) continue;
+          WorkItem it{};
+          it.group = t.first;
+          it.pad = t.n;
+          it.a0 = lo; it.a1 = hi;
+          it.b0 = r;
+          P.bound_items.push_back(it);
+        }
+      }
+    }
     P.items.insert(P.items.end(), P.surv_tiled_items.begin(), P.surv_tiled_items.end());
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
+    P.items.insert(P.items.end(), P.bound_items.begin(), P.bound_items.end());
     P.list_total = loff;
     P.mask_words = (max_bounded + 63) / 64;
     int64_t bsum = 0;
@@ -654,6 +676,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.debug_ub = cfg.debug_ub;
     bl.debug_ld = max_kv;
     bl.splits = P.bound_splits;
+    if (!P.bound_items.empty()) {
+      bl.items = di + P.seed_items.size() + P.surv_tiled_items.size() + P.surv_list_items.size();
+      bl.n_items = (int)P.bound_items.size();
+    }
     bl.stats = st;
     {
       PassScope ps(P_BOUND, stream);

@@ -146,7 +146,10 @@ struct BoundLaunch {
   int32_t mask_words;
   float* debug_ub;           // [total_q, debug_ld] or NULL
   int32_t debug_ld;
-  int32_t splits;            // key splits per group (grid = n_groups * splits)
+  int32_t splits;            // key splits per group (grid = n_groups * splits; per-group kernel)
+  const WorkItem* items;     // tiled kernel: one per (tile, key share): group = first group,
+                             // pad = groups, [a0, a1) keys, b0 = share index; NULL = per-group kernel
+  int32_t n_items;
   unsigned long long* stats;
 };
 

@@ -730,6 +730,142 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
+// bound pass over LDS key tiles: a workgroup takes one query tile (up to 8
+// groups, one wavefront each; the groups of a tile share their bounded range)
+// and a 64-key-aligned share of that range.  Keys, their scales and norms are
+// staged through LDS (double-buffered, register prefetch), so every key is
+// read once per tile instead of once per group.  Each wavefront evaluates the
+// certificate of its 4 queries on MFMA (16 rows = 4 rows x 4 queries) and
+// writes one 64-bit union-survivor word per 64 keys.
+// ---------------------------------------------------------------------------
+template <int C, int D>
+__global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const BoundLaunch p) {
+  using O = Ops<C, D>;
+  constexpr int STEPS = O::STEPS;
+  constexpr int KBYTES = D * O::KB;
+  constexpr int ROW = KBYTES + 16;                   // padded LDS row
+  constexpr int CPK = KBYTES / 16;
+  constexpr int NCH = (64 * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][64 * ROW];
+  __shared__ float kinfo[2][2][64];                  // [buffer][scale, norm][key]
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;
+  const int lane = lane_id();
+  const WorkItem it = p.items[blockIdx.x];
+  const GroupInfo g0 = p.groups[it.group];
+  const bool active = wave < it.pad;
+  const int gi = it.group + (active ? wave : 0);
+  const GroupInfo gr = p.groups[gi];
+  const int col = lane & 15, g = lane >> 4;
+  const int lo = it.a0, hi = it.a1;                  // keys [lo, hi), lo - bound_lo a multiple of 64
+  unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
+  const bool qok = active && g < gr.nq;
+  const int qrow = gr.q_row0 + g;
+  float cf[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cf[i] = qok ? p.coef[(int64_t)qrow * 8 + i] : 0.f;
+  const int npx = (int)cf[6];
+  const bool hopeless = !qok || cf[7] != 0.f;
+  const bool all_hopeless = __ballot(qok && !hopeless) == 0ull;    // this wavefront's group
+  const u64 nbounded = (u64)max(hi - lo, 0) * (u64)(active ? gr.nq : 0);
+  if (p.stats != nullptr && lane == 0 && active && all_hopeless && it.b0 == 0) {
+    const u64 all = (u64)gr.n_bounded * (u64)gr.nq;   // the group's first share counts the whole group
+    atomicAdd(&p.stats[2], all);
+    atomicAdd(&p.stats[3], all);
+    atomicAdd(&p.stats[7], 1ull);
+  }
+  // the whole workgroup leaves if no wavefront has work (and no dump is asked for)
+  if (__syncthreads_and(!active || all_hopeless) && p.debug_ub == nullptr) return;
+  typename O::frag A[STEPS];
+  {
+    const int ra = lane & 15;
+    const int qa = ra >> 2, rr = ra & 3;
+    if (active && qa < gr.nq)
+      O::load_q(static_cast<const uint8_t*>(p.rows) + ((int64_t)(gr.q_row0 + qa) * 4 + rr) * D * O::QB, g, A);
+    else
+      O::zero(A);
+  }
+  const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
+  const int ntiles = (hi - lo + 63) / 64;
+  v4i stage[NCH];
+  float st_s = 1.f, st_n = 0.f;
+  auto fetch = [&](int t) {
+    const int tid = lane_fresh() + 64 * wave;
+    const int kb = lo + 64 * t;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * 64 * kTileWaves;
+      const int slot = ch / CPK, part = ch % CPK;
+      const int key = kb + slot;
+      if (slot < 64 && key < hi) {
+        const int64_t row = key_row(p.in, g0.key_base, g0.seq, key);
+        stage[c] = *reinterpret_cast<const v4i*>(kbytes + row * KBYTES + part * 16);
+      } else {
+        stage[c] = v4i{0, 0, 0, 0};
+      }
+    }
+    if (tid < 64) {
+      const int key = kb + tid;
+      const bool v = key < hi;
+      st_s = (HasKScale<C>::value && v) ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, key)] : 1.f;
+      st_n = v ? p.norms[(int64_t)g0.norm_base + key] : 0.f;
+    }
+  };
+  auto commit = [&](int bufi) {
+    const int tid = lane_fresh() + 64 * wave;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * 64 * kTileWaves;
+      const int slot = ch / CPK, part = ch % CPK;
+      if (slot < 64) *reinterpret_cast<v4i*>(&ktile[bufi][slot * ROW + part * 16]) = stage[c];
+    }
+    if (tid < 64) {
+      kinfo[bufi][0][tid] = st_s;
+      kinfo[bufi][1][tid] = st_n;
+    }
+  };
+  u64 n_surv = 0;
+  if (ntiles > 0) fetch(0);
+#pragma unroll 1
+  for (int t = 0; t < ntiles; ++t) {
+    const int bufi = t & 1;
+    commit(bufi);
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
+    if (!active || (all_hopeless && p.debug_ub == nullptr)) continue;
+    const int kb = lo + 64 * t;
+    u64 word = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int kslot = b * 16 + col;
+      const int key = kb + kslot;
+      typename O::frag B[STEPS];
+      O::load_k(&ktile[bufi][kslot * ROW], g, B);
+      v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < STEPS; ++s) c = O::mma(A[s], B[s], c);
+      float pos = 0.f, neg = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < npx) pos += cf[i] * fmaxf(c[i], 0.f);
+        else neg += cf[i] * c[i];
+      }
+      const float ub = kinfo[bufi][0][kslot] * (pos - fmaxf(neg, 0.f)) + cf[4] * kinfo[bufi][1][kslot];
+      const bool valid = qok && key < hi;
+      if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
+      const bool surv = valid && (hopeless || ub >= cf[5]);
+      const u64 m = __ballot(surv);
+      n_surv += __popcll(m);
+      word |= (u64)((uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu) << (16 * b);
+    }
+    if (!all_hopeless && lane == 0) mw[(kb - gr.bound_lo) >> 6] = word;
+  }
+  if (active && !all_hopeless && p.stats != nullptr && lane == 0) {
+    atomicAdd(&p.stats[2], nbounded);
+    atomicAdd(&p.stats[3], n_surv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // compaction: one workgroup per tile, one wavefront per query group.  Each
 // wavefront counts its group's union survivors (popcounts of the bitmask; a
 // group whose every query the plan marked hopeless has no bitmask and keeps
@@ -878,6 +1014,12 @@ hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t
 
 template <int C>
 static hipError_t bound_c(int d, const BoundLaunch& p, hipStream_t s) {
+  if (p.items != nullptr) {
+    if (p.n_items == 0) return hipSuccess;
+    if (d == 64) hipLaunchKernelGGL((bound_tiled_kernel<C, 64>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+    else hipLaunchKernelGGL((bound_tiled_kernel<C, 128>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+    return hipGetLastError();
+  }
   const int nb = p.n_groups * p.splits;
   if (d == 64) hipLaunchKernelGGL((bound_kernel<C, 64>), dim3(nb), dim3(64), 0, s, p);
   else hipLaunchKernelGGL((bound_kernel<C, 128>), dim3(nb), dim3(64), 0, s, p);
