@@ -210,6 +210,7 @@ __device__ __forceinline__ void nnls3(int p, const double Gp[3][3], const double
 
 constexpr float kSkipFrac = 0.7f;   // sampled survival above which the bound pass is skipped
 constexpr int kSampleKeys = 64;     // keys sampled for activations and for the skip test
+constexpr float kJointGain = 0.1f;  // sampled extra pruning that pays for the joint constant
 
 // Sum over the P consecutive lanes that share one head (P a power of two <= 64).
 template <int P, typename T>
@@ -250,17 +251,18 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   const int hh = t / PARTS, part = t % PARTS;
   const int g = lane >> 4, col = lane & 15;
 
-  __shared__ float qf[H * D];                      // decoded, unscaled (exact in fp32)
+  constexpr int QS = D + 4;                        // LDS row stride of the decoded query (floats)
+  __shared__ float qf[H * QS];                     // decoded, unscaled (exact in fp32)
   __shared__ __align__(16) uint8_t kraw[kSampleKeys * KRS];   // staged keys, stored type
   __shared__ __align__(16) uint8_t rowl[4 * D * QB];          // the certificate rows
   __shared__ double wd[H], qn2[H], alpha[H][3], gph[3][H];
   __shared__ double avec[D];
   __shared__ float ksc[kSampleKeys], knm[kSampleKeys];        // skip-test keys: scale, norm
   __shared__ int prox[3], act[H], inO[H];
-  __shared__ double hsum[8];                       // c_0..c_2, rho_sep, rho_lo, sum |w_h| ||q_h||
-  __shared__ float cfs[6];                         // row multipliers, rho_lo (scaled)
+  __shared__ double hsum[8];                       // c_0..c_2, rho_sep, rho_lo, sum |w_h| ||q_h||, margin
+  __shared__ float cfs[6];                         // row multipliers, rho_lo, rho_sep + margin (scaled)
   __shared__ double red4[4];
-  __shared__ int np_s, nsurv_s;
+  __shared__ int np_s, nsurv_s, nsep_s;
 
   // ---- 0. issue the loads
   const uint8_t* qrow_raw = static_cast<const uint8_t*>(p.in.q) + (int64_t)qrow * H * D * QB;
@@ -317,7 +319,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
       float f[16 / QB];
       dec16<QB>(qv[j], f);
 #pragma unroll
-      for (int m = 0; m < 16 / QB; ++m) qf[c * (16 / QB) + m] = f[m];
+      for (int m = 0; m < 16 / QB; ++m) {
+        const int e = c * (16 / QB) + m;
+        qf[(e / D) * QS + e % D] = f[m];
+      }
     }
   }
 #pragma unroll
@@ -361,7 +366,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   // ---- 3. squared norms, proxies, proxy inner products (fp64 of exact values)
   float qr[EL];
 #pragma unroll
-  for (int e = 0; e < EL; ++e) qr[e] = qf[hh * D + part + PARTS * e];
+  for (int e = 0; e < EL; ++e) qr[e] = qf[hh * QS + part + PARTS * e];
   {
     double s2 = 0.0;
 #pragma unroll
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __syncthreads();
   const int np = np_s;
   for (int r = 0; r < np; ++r) {
-    const float* pr = qf + prox[r] * D + part;
+    const float* pr = qf + prox[r] * QS + part;
     double dsum = 0.0;
 #pragma unroll
     for (int e = 0; e < EL; ++e) dsum = fma((double)qr[e], (double)pr[PARTS * e], dsum);
@@ -455,7 +460,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
 #pragma unroll 8
         for (int h = 0; h < H; ++h) {
           const bool in_a = wd[h] < 0.0 && (ns > 0 ? (double)act[h] >= need : p.neg_frac <= 0.f);
-          if (in_a) sacc = fma(-wd[h], (double)qf[h * D + i], sacc);
+          if (in_a) sacc = fma(-wd[h], (double)qf[h * QS + i], sacc);
         }
       }
       avec[i] = sacc;
@@ -478,7 +483,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   if (wave == 0) {
     for (int e = lane; e < np * D; e += 64) {
       const int r = e / D, i = e % D;
-      const float v = qf[prox[r] * D + i];
+      const float v = qf[prox[r] * QS + i];
       if constexpr (QB == 1) rowl[r * D + i] = (uint8_t)enc_fp8(v);
       else if constexpr (QB == 4) reinterpret_cast<float*>(rowl)[r * D + i] = v;
       else reinterpret_cast<uint16_t*>(rowl)[r * D + i] = (uint16_t)enc_bf16(v);
@@ -529,25 +534,45 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     for (int v = 0; v < PER; ++v) e2 += res[v] * res[v];
     ea = sqrt(wave_sum(e2));
     if (lane == 0) {
+      // Rounding margin: forward error of the fp32 dot products and sums in
+      // the score and bound kernels (Higham, dot-product error gamma_n), with
+      // u = 2^-22 (4x the fp32 unit roundoff) and n = d + H + 16; rho enters
+      // via its separable upper bound.  The score kernels evaluate
+      // sum_h w_h ReLU(x_h) as sum_h (w_h/2)|x_h| + qbar.k/2 with qbar held as
+      // a few terms; their error and magnitude (unscaled) enter too.
+      const double u = 1.0 / 4194304.0;
+      const double nn = (double)(D + H + 16);
+      const double gam = nn * u / (1.0 - nn * u);
+      double cq = 0.0, sf = 0.0;
+      for (int r = 0; r < np; ++r) cq += hsum[r] * sqrt(qn2[prox[r]]);
+      for (int r = np; r < 4; ++r) sf += sig[r] * fnorm[r];
+      const double margin =
+          2.0 * gam * (hsum[5] + cq + sf + hsum[3] + 0.5 * (double)l_mag_f) + ea + 0.5 * (double)l_err_f;
+      hsum[6] = margin;
       const double qs = (double)qscale;
       for (int r = 0; r < 4; ++r) cfs[r] = (r < np) ? (float)(hsum[r] * qs) : (float)(sig[r] * qs);
       cfs[4] = (float)(hsum[4] * qs);
+      cfs[5] = (float)((hsum[3] + margin) * qs);
     }
   }
   __syncthreads();
   for (int c = t; c < 4 * D * QB / 16; c += 256)
     reinterpret_cast<uint4*>(rows)[c] = reinterpret_cast<const uint4*>(rowl)[c];
 
-  // ---- 6. skip test (wavefront 0): the bound pass's arithmetic with rho
-  // replaced by its diagonal lower bound (an optimistic certificate) on the
-  // sampled bounded keys; if at least kSkipFrac of them would survive, the
-  // bound pass is not worth running.  Skipping (every key survives) is always
-  // correct, so this is a cost decision only.
+  // ---- 6. skip test (wavefront 0): the bound pass's arithmetic on the
+  // sampled bounded keys, once with rho replaced by its diagonal lower bound
+  // (an optimistic certificate) and once with the separable constant (the
+  // valid certificate without the joint term).  If at least kSkipFrac of the
+  // sample would survive even the optimistic one, the bound pass is not worth
+  // running; the joint constant is worked out only where it would prune a
+  // clearly larger part of the sample than the separable one.  Skipping
+  // either is always correct, so these are cost decisions only.
+  if (t == 0) nsep_s = 0;
   if (wave == 0 && nsb > 0) {
     typename O::frag A[O::STEPS];
     if (col < 4) O::load_q(rowl + col * D * QB, g, A);
     else O::zero(A);
-    int n_surv = 0;
+    int n_surv = 0, n_sep = 0;
     for (int tile = 0; tile * 16 < nsb; ++tile) {
       const int i = tile * 16 + col;
       typename O::frag B[O::STEPS];
@@ -561,36 +586,60 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
         if (r < np) pz += cfs[r] * fmaxf(c[r], 0.f);
         else nz += cfs[r] * c[r];
       }
-      const bool surv = g == 0 && i < nsb && ksc[i] * (pz - fmaxf(nz, 0.f)) + cfs[4] * knm[i] >= tau;
-      n_surv += (int)__popcll(__ballot(surv));
+      const bool ok = g == 0 && i < nsb;
+      const float base = ok ? ksc[i] * (pz - fmaxf(nz, 0.f)) : 0.f;
+      const float kn = ok ? knm[i] : 0.f;
+      n_surv += (int)__popcll(__ballot(ok && base + cfs[4] * kn >= tau));
+      n_sep += (int)__popcll(__ballot(ok && base + cfs[5] * kn >= tau));
     }
-    if (lane == 0) nsurv_s = n_surv;
+    if (lane == 0) {
+      nsurv_s = n_surv;
+      nsep_s = n_sep;
+    }
   }
   __syncthreads();
   const bool hopeless = nsb == 0 || (float)nsurv_s >= kSkipFrac * (float)nsb;
+  const bool joint = !hopeless && (p.flags & DOSA_SEPARABLE_RHO) == 0 &&
+                     (nsb < 16 || (float)(nsep_s - nsurv_s) >= fmaxf(2.f, kJointGain * (float)nsb));
 
   // ---- 7. joint residual constant rho^2 = sum_{h,j in O} w_h w_j max(0, <r_h, r_j>)
+  // from the head Gram matrix on fp64 MFMA (16x16x4: lane l feeds row l%16,
+  // k l/16 of both operands and holds rows l/16 + 4i of column l%16 of the
+  // result; products and sums of the decoded fp8/bf16 values are exact or
+  // nearly so in fp64).  Wavefront w takes tiles (bi, bj), bi <= bj, round
+  // robin; off-diagonal tiles count twice.
   double rho = hsum[3];
-  const bool separable = (p.flags & DOSA_SEPARABLE_RHO) != 0;
-  if (!hopeless && !separable) {
-    double qd[EL];
-#pragma unroll
-    for (int e = 0; e < EL; ++e) qd[e] = (double)qr[e];
-    const bool ho = inO[hh] != 0;
+  if (joint) {
+    constexpr int NBLK = (H + 15) / 16;
+    constexpr int NT = NBLK * (NBLK + 1) / 2;
     double acc = 0.0;
-    for (int j = 0; j < H; ++j) {
-      if (!inO[j]) continue;                 // uniform
-      const float* qj = qf + j * D + part;
-      double gg = 0.0;
+    const int lr = lane & 15, lk = lane >> 4;
+    for (int tt = wave; tt < NT; tt += 4) {
+      int bi = 0, rem = tt;
+      while (rem >= NBLK - bi) { rem -= NBLK - bi; ++bi; }
+      const int bj = bi + rem;
+      const int ha = 16 * bi + lr, hb = 16 * bj + lr;       // operand rows of this lane
+      const float* pa = qf + (ha < H ? ha : 0) * QS + lk;
+      const float* pb = qf + (hb < H ? hb : 0) * QS + lk;
+      typedef double v4d __attribute__((ext_vector_type(4)));
+      v4d gacc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 8
+      for (int k = 0; k < D / 4; ++k) {
+        const double a = (ha < H) ? (double)pa[4 * k] : 0.0;
+        const double b = (hb < H) ? (double)pb[4 * k] : 0.0;
+        gacc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, gacc, 0, 0, 0);
+      }
+      const int j = 16 * bj + lr;                          // column of this lane's results
 #pragma unroll
-      for (int e = 0; e < EL; ++e) gg = fma(qd[e], (double)qj[PARTS * e], gg);
-      gg = part_sum<PARTS>(gg);
-      if (ho && part == (j % PARTS)) {
-        double r = gg;
-        for (int u = 0; u < np; ++u) r -= alpha[hh][u] * gph[u][j] + alpha[j][u] * gph[u][hh];
-        for (int u = 0; u < np; ++u)
-          for (int v = 0; v < np; ++v) r += alpha[hh][u] * alpha[j][v] * gph[u][prox[v]];
-        acc += wd[hh] * wd[j] * fmax(r, 0.0);
+      for (int i = 0; i < 4; ++i) {
+        const int h = 16 * bi + lk + 4 * i;
+        if (h < H && j < H && inO[h] && inO[j]) {
+          double r = gacc[i];
+          for (int u = 0; u < np; ++u) r -= alpha[h][u] * gph[u][j] + alpha[j][u] * gph[u][h];
+          for (int u = 0; u < np; ++u)
+            for (int v = 0; v < np; ++v) r += alpha[h][u] * alpha[j][v] * gph[u][prox[v]];
+          acc += (bi == bj ? 1.0 : 2.0) * wd[h] * wd[j] * fmax(r, 0.0);
+        }
       }
     }
     acc = wave_sum(acc);
@@ -599,22 +648,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     rho = sqrt(fmax(red4[0] + red4[1] + red4[2] + red4[3], 0.0));
   }
 
-  // ---- 8. coefficients.  Rounding margin: forward error of the fp32 dot
-  // products and sums in the score and bound kernels (Higham, dot-product
-  // error gamma_n), with u = 2^-22 (4x the fp32 unit roundoff) and
-  // n = d + H + 16; rho enters via its separable upper bound.  The score
-  // kernels evaluate sum_h w_h ReLU(x_h) as sum_h (w_h/2)|x_h| + qbar.k/2 with
-  // qbar held as a few terms; their error and magnitude (unscaled) enter too.
+  // ---- 8. coefficients
   if (t == 0) {
-    const double u = 1.0 / 4194304.0;
-    const double nn = (double)(D + H + 16);
-    const double gam = nn * u / (1.0 - nn * u);
-    double cq = 0.0, sf = 0.0;
-    for (int r = 0; r < np; ++r) cq += hsum[r] * sqrt(qn2[prox[r]]);
-    for (int r = np; r < 4; ++r) sf += sig[r] * fnorm[r];
-    const double margin = 2.0 * gam * (hsum[5] + cq + sf + hsum[3] + 0.5 * (double)l_mag_f) + ea + 0.5 * (double)l_err_f;
     const double qs = (double)qscale;
-    const double rho_p = (rho + margin) * qs;
+    const double rho_p = (rho + hsum[6]) * qs;
     float* cf = p.coef + (int64_t)qrow * 8;
     for (int r = 0; r < 4; ++r) cf[r] = (r < np) ? (float)(hsum[r] * qs) : (float)(sig[r] * qs);
     cf[4] = (float)rho_p * 1.0000005f;
