@@ -319,39 +319,57 @@ struct Scorer {
     }
   }
 
-  // Count this lane's score in its query's histogram, append it if it
-  // reaches theta, and shrink regions that are about to overflow.  Called by
-  // all 64 lanes of the wavefront.
-  __device__ __forceinline__ void append(const ScoreLaunch& p, const GroupInfo& gr, int region, float o,
-                                         float ks, int key, bool kvalid, uint32_t* shist) {
-    const float sc = o * qs * ks;
-    const bool valid = owner() && qok() && kvalid && key <= pos();
-    const uint32_t so = f2ord(sc);
+  // Count the scores of one step (4 blocks of 16 keys) in their queries'
+  // histograms, append those that reach theta, and shrink regions that are
+  // about to overflow.  Called by all 64 lanes of the wavefront.  Lane roles
+  // are derived once per step; a step adds at most 64 entries per query, so
+  // regions are checked against cap - 64 once per step.
+  __device__ __forceinline__ void append4(const ScoreLaunch& p, const GroupInfo& gr, int region, const float* o,
+                                          const float* ks, const int* key, const bool* kvalid, uint32_t* shist) {
+    const int ln = lane_fresh();
+    const int c = ln & 15, gg = ln >> 4;
+    const int q_i = (4 * gg) / S;
+    const int ol0 = 16 * (q_i * (4 / QW));
+    const bool own = (gg == (ol0 >> 4)) && q_i < nq;
+    const int last = pos0 + q_i;                         // the query sees keys <= last
+    const uint32_t below = (1u << c) - 1u;
+    float sc[4];
+    uint32_t so[4];
+    bool valid[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sc[b] = o[b] * qs * ks[b];
+      so[b] = f2ord(sc[b]);
+      valid[b] = own && kvalid[b] && key[b] <= last;
+    }
     if (__any(hbase == 0)) {
       // anchor each query's histogram below the maximum of its first scores
       // (all lanes take part in the exchanges; only unanchored queries update)
-      uint32_t mx = valid ? so : 0u;
+      uint32_t mx = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) mx = max(mx, valid[b] ? so[b] : 0u);
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-      mx = __shfl(mx, owner_lane0() + col(), 64);
+      mx = __shfl(mx, ol0 + c, 64);
       if (hbase == 0 && mx != 0u) {
         const uint32_t lo = (uint32_t)kHistAnchor << kHistShift;
         hbase = (mx > 0x00800000u + lo) ? mx - lo : 0x00800000u;
       }
     }
-    const bool take = valid && sc >= theta;
-    if (take && hbase != 0 && so >= hbase) {
-      const uint32_t bin = min((so - hbase) >> kHistShift, (uint32_t)(kHistBins - 1));
-      atomicAdd(&qh[qi() * kHistBins + bin], 1u);
+    uint32_t* hq = qh + q_i * kHistBins;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bool take = valid[b] && sc[b] >= theta;
+      if (take && hbase != 0 && so[b] >= hbase)
+        atomicAdd(&hq[min((so[b] - hbase) >> kHistShift, (uint32_t)(kHistBins - 1))], 1u);
+      const u64 m = __ballot(take);
+      n_scored += __popcll(__ballot(valid[b]));
+      const uint32_t slice = (uint32_t)(m >> ol0) & 0xFFFFu;
+      if (take) buf[count + __popc(slice & below)] = ((u64)so[b] << 32) | (u64)(uint32_t)(~(uint32_t)key[b]);
+      count += __popc(slice);
+      n_written += __popcll(m);
     }
-    const u64 m = __ballot(take);
-    n_scored += __popcll(__ballot(valid));
-    const uint32_t slice = (uint32_t)(m >> owner_lane0()) & 0xFFFFu;
-    const uint32_t before = __popc(slice & ((1u << col()) - 1u));
-    if (take) buf[count + before] = make_key(sc, key);
-    count += __popc(slice);
-    n_written += __popcll(m);
-    const uint32_t hi_water = (uint32_t)(p.cb.cap - 16);
+    const uint32_t hi_water = (uint32_t)(p.cb.cap - 64);
     if (__any(count > hi_water)) {
       refresh_theta(p.topk);
 #pragma unroll 1
@@ -359,6 +377,7 @@ struct Scorer {
         if (__shfl(count, 16 * (qq * (4 / QW)), 64) > hi_water) shrink(p, gr, region, qq, shist);
     }
   }
+
 
   // End of the sweep: bring every region down to its final theta.
   __device__ __forceinline__ void close(const ScoreLaunch& p, const GroupInfo& gr, int region, uint32_t* shist) {
@@ -428,8 +447,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) load(keys[b], v[b], B[b], ks[b]);
     sc.template scoreN<4>(B, o);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) sc.append(p, gr, it.region, o[b], ks[b], keys[b], v[b], hist);
+    sc.append4(p, gr, it.region, o, ks, keys, v, hist);
     if ((++nblk & 7) == 0) sc.refresh_theta(p.topk);
   };
 
@@ -568,11 +586,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
           O::load_k(&ktile[bufi][((NBK * hb + b) * 16 + sc.col()) * ROW], sc.g(), B[b]);
         sc.template scoreN<NBK>(B, o + NBK * hb);
       }
+      {
+        const int cl = sc.col();
+        float ks[4];
+        int keys[4];
+        bool kv[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int key = kb + b * 16 + sc.col();
-        const float ks = HasKScale<C>::value ? kscale[bufi][b * 16 + sc.col()] : 1.f;
-        sc.append(p, gr, it.region, o[b], ks, key, key >= lo && key < hi, hist[wave]);
+        for (int b = 0; b < 4; ++b) {
+          keys[b] = kb + b * 16 + cl;
+          ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + cl] : 1.f;
+          kv[b] = keys[b] >= lo && keys[b] < hi;
+        }
+        sc.append4(p, gr, it.region, o, ks, keys, kv, hist[wave]);
       }
       if ((t & 7) == 7) sc.refresh_theta(p.topk);
     }
