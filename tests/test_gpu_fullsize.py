@@ -1,0 +1,105 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py
+times (chunked prefill as one call per chunk on shared device inputs).
+
+Every row: the pruned path returns exactly the dense path's keys with
+bit-identical scores (compared on the device).  Sampled rows (first and last
+query of several chunks plus random ones): both paths against the oracle,
+which scores those rows one by one over all their visible keys.
+"""
+import numpy as np
+import pytest
+
+import synth
+from parity_helpers import check_vs_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_calls(wl, inp, path):
+    import torch
+
+    import exact_top_token_amd as E
+    from exact_top_token_amd.runner import slice_chunk
+
+    calls = ([(c["q0"], slice_chunk(inp, c["q0"], c["q_len"], c["kv_len"])) for c in wl.chunk_calls()]
+             if wl.chunk else [(0, inp)])
+    K = wl.topk
+    cfg = E.default_config(K)
+    ws = torch.empty(max(E.workspace_size(c.q_lens, c.kv_lens, c.H, c.d, K, c.q_dtype, c.k_dtype,
+                                          c.page_table is not None, path == "dsa", cfg) for _, c in calls),
+                     dtype=torch.uint8, device="cuda")
+    idx = torch.empty((wl.total_q, K), dtype=torch.int32, device="cuda")
+    sc = torch.empty((wl.total_q, K), dtype=torch.float32, device="cuda")
+    st = torch.zeros(len(E.STAT_FIELDS), dtype=torch.int64, device="cuda")
+    f = E.dsa_indexer_topk if path == "dsa" else E.dosa_indexer_topk
+    for q0, c in calls:
+        f(c.q, c.q_dtype, c.q_scale, c.w, c.k, c.k_dtype, c.k_scale, c.q_lens, c.kv_lens, c.page_table,
+          c.page_size, c.H, c.d, K, idx[q0:q0 + c.total_q], sc[q0:q0 + c.total_q], ws, cfg=cfg, stats=st)
+    torch.cuda.synchronize()
+    return idx, sc, {k: int(v) for k, v in zip(E.STAT_FIELDS, st.cpu().numpy().tolist())}
+
+
+def _same_on_device(ia, sa, ib, sb, block=8192):
+    import torch
+
+    for r0 in range(0, ia.shape[0], block):
+        xa, oa = torch.sort(ia[r0:r0 + block], dim=1)
+        xb, ob = torch.sort(ib[r0:r0 + block], dim=1)
+        assert torch.equal(xa, xb), f"key sets differ in rows {r0}..{r0 + block}"
+        va = torch.gather(sa[r0:r0 + block], 1, oa).view(torch.int32)
+        vb = torch.gather(sb[r0:r0 + block], 1, ob).view(torch.int32)
+        assert torch.equal(va, vb), f"scores of the same keys differ in rows {r0}..{r0 + block}"
+
+
+def _rows(wl, n_random, seed=0):
+    picks = set()
+    if wl.chunk:
+        calls = list(wl.chunk_calls())
+        for c in (calls[0], calls[len(calls) // 2], calls[-1]):
+            picks.update([c["q0"], c["q0"] + c["q_len"] - 1])
+    else:
+        cu = wl.cu_q()
+        for b in (0, wl.batch // 2, wl.batch - 1):
+            if cu[b + 1] > cu[b]:
+                picks.update([int(cu[b]), int(cu[b + 1] - 1)])
+    rng = np.random.default_rng(seed)
+    picks.update(rng.choice(wl.total_q, size=n_random, replace=False).tolist())
+    return np.array(sorted(picks), dtype=np.int64)
+
+
+def _check(wl, n_random):
+    from exact_top_token_amd.runner import to_device
+
+    print(f"[gpu] full size {wl.name}: q={wl.total_q} H={wl.H} d={wl.d} K={wl.topk} "
+          f"{wl.q_dtype}/{wl.k_dtype} pairs={wl.pairs()}", flush=True)
+    inp = to_device(wl)
+    di, ds, dst = _run_calls(wl, inp, "dsa")
+    pi, ps, pst = _run_calls(wl, inp, "dosa")
+    assert dst["pairs_total"] == wl.pairs() == pst["pairs_total"]
+    assert pst["pairs_seed"] + pst["pairs_bounded"] == wl.pairs()
+    _same_on_device(pi, ps, di, ds)
+    rows = _rows(wl, n_random)
+    print(f"[gpu] oracle rows {rows.tolist()}", flush=True)
+    ri = di[rows].cpu().numpy()
+    rs = ds[rows].cpu().numpy()
+    worst, swaps = check_vs_oracle(wl, {int(r): ri[j] for j, r in enumerate(rows)},
+                                   {int(r): rs[j] for j, r in enumerate(rows)}, rows)
+    print(f"[gpu] {wl.name}: max |S_gpu - S_ref| / A = {worst:.3g}, boundary swaps {swaps}, "
+          f"filtered {1 - pst['pairs_survived'] / max(pst['pairs_bounded'], 1):.3f}", flush=True)
+
+
+def test_full_long_prefill_128k_fp8_chunked():
+    _check(synth.long_prefill_128k(), 4)
+
+
+def test_full_dsa_prefill_32k_bf16():
+    _check(synth.dsa_prefill_32k(), 6)
+
+
+def test_full_decode_mtp_paged():
+    _check(synth.decode_mtp(), 8)
+
+
+@pytest.mark.parametrize("iid", [False, True])
+def test_full_million_chunk(iid):
+    _check(synth.make_workload("million_chunk_iid") if iid else synth.million_chunk(), 3)
