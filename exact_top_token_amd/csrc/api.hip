@@ -284,8 +284,25 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
     P.J = J;
     P.R = Js + J;
-    // survivors of tiles whose certificate can prune nothing: tiled kernel over the bounded range
+    // survivors of tiles whose certificate can prune nothing: the tiled kernel
+    // over the bounded range (one wavefront per group when tiles are small)
+    if (!P.tiled) {
+      for (int gi = 0; gi < G; ++gi) {
+        const GroupInfo& g = P.groups[gi];
+        for (int r = 0; r < J; ++r) {
+          int lo, hi;
+          range_split(g.bound_lo, g.bound_lo + g.n_bounded, r, J, 16, lo, hi);
+          WorkItem it{};
+          it.group = gi;
+          it.region = Js + r;
+          it.a0 = it.a1 = lo;
+          it.b0 = lo; it.b1 = hi;
+          P.surv_tiled_items.push_back(it);
+        }
+      }
+    }
     for (const auto& t : tiles) {
+      if (!P.tiled) break;
       const GroupInfo& g = P.groups[t.first];
       for (int r = 0; r < J; ++r) {
         int lo, hi;
@@ -606,7 +623,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
     int32_t* gflags = reinterpret_cast<int32_t*>(ws + P.o_gflags);
     // 1. per-key norms
-    NormLaunch nl{in, cu_dev, batch, P.total_k, norms};
+    NormLaunch nl{in, cu_dev, batch, P.total_k, max_kv, norms};
     {
       PassScope ps(P_NORMS, stream);
       e = launch_key_norms(P.combo, d, nl, stream);
@@ -714,7 +731,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       PassScope ps(P_SURV_TILES, stream);
       ml.items = di + P.seed_items.size();
       ml.n_items = (int)P.surv_tiled_items.size();
-      ml.tiled = 1;
+      ml.tiled = P.tiled ? 1 : 0;
       ml.flag_mode = 1;
       e = launch_score(P.combo, H, d, ml, stream);
     }

@@ -169,6 +169,7 @@ struct NormLaunch {
   const int32_t* cu_kv;      // [batch+1] logical key offsets
   int32_t batch;
   int64_t total_k;
+  int32_t max_kv;            // longest sequence
   float* norms;              // [total_k]
 };
 

@@ -98,7 +98,9 @@ __device__ __forceinline__ void dec16(const uint4 v, float* o) {
 }
 
 // CH = d*bytes/16 lanes per key, one 16-byte chunk each (coalesced rows); the
-// partial sums of squares meet by shuffles.  kNormIter keys per lane group.
+// partial sums of squares meet by shuffles.  Grid: (key blocks, sequences), so
+// a block knows its sequence and every key row costs at most one page-table
+// read; blocks past a sequence's end exit.  kNormIter keys per lane group.
 constexpr int kNormIter = 4;
 
 template <int C, int D>
@@ -109,21 +111,21 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
   constexpr int VPC = 16 / KBY;               // values per chunk
   const int t = threadIdx.x;
   const int sub = t % CH;
-  const int64_t first = (int64_t)blockIdx.x * KPB * kNormIter + t / CH;
+  const int first = blockIdx.x * KPB * kNormIter + t / CH;
+#pragma unroll 1
+  for (int b = blockIdx.y; b < p.batch; b += gridDim.y) {   // grid.y is capped at 65535
+  const int base = p.cu_kv[b];
+  const int n = p.cu_kv[b + 1] - base;
+  if (blockIdx.x * KPB * kNormIter >= n) continue;
   uint4 v[kNormIter];
   int64_t rows[kNormIter];
 #pragma unroll
   for (int it = 0; it < kNormIter; ++it) {
-    const int64_t i = first + (int64_t)it * KPB;
+    const int key = first + it * KPB;
     rows[it] = -1;
     v[it] = make_uint4(0u, 0u, 0u, 0u);
-    if (i < p.total_k) {
-      int lo = 0, hi = p.batch;                 // sequence of logical key i: last b with cu_kv[b] <= i
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.cu_kv[mid] <= i) lo = mid; else hi = mid;
-      }
-      rows[it] = key_row(p.in, p.cu_kv[lo], lo, (int)(i - p.cu_kv[lo]));
+    if (key < n) {
+      rows[it] = key_row(p.in, base, b, key);
       v[it] = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.in.k) + rows[it] * D * KBY)[sub];
     }
   }
@@ -136,12 +138,12 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
     for (int j = 0; j < VPC; ++j) acc = fmaf(f[j], f[j], acc);
 #pragma unroll
     for (int off = CH / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, CH);
-    const int64_t i = first + (int64_t)it * KPB;
     if (sub == 0 && rows[it] >= 0) {
-      float n = sqrtf(acc);
-      if constexpr (HasKScale<C>::value) n *= p.in.k_scale[rows[it]];
-      p.norms[i] = n * 1.0000153f;             // covers the fp32 sum/sqrt/scale rounding (<< 2^-16)
+      float nv = sqrtf(acc);
+      if constexpr (HasKScale<C>::value) nv *= p.in.k_scale[rows[it]];
+      p.norms[(int64_t)base + first + it * KPB] = nv * 1.0000153f;   // covers the fp32 sum/sqrt/scale rounding (<< 2^-16)
     }
+  }
   }
 }
 
@@ -1003,8 +1005,9 @@ hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long*
 template <int C, int D>
 static hipError_t norms_t(const NormLaunch& p, hipStream_t s) {
   constexpr int per_block = 256 / (D * KBytes<C>::value / 16) * kNormIter;
-  const int nb = (int)((p.total_k + per_block - 1) / per_block);
-  hipLaunchKernelGGL((key_norm_kernel<C, D>), dim3(nb), dim3(256), 0, s, p);
+  const int nb = (int)((p.max_kv + per_block - 1) / per_block);
+  if (nb == 0 || p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL((key_norm_kernel<C, D>), dim3(nb, p.batch < 65535 ? p.batch : 65535), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -234,6 +234,8 @@ struct Scorer {
     }
   }
 
+
+
   // Compact the region of query qq to the entries >= its theta; if that
   // leaves it more than half full, select the exact K-th and keep K.  The
   // work is a call (shrink_region), so its registers do not weigh on the
@@ -419,10 +421,11 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
   __shared__ uint32_t qhist[SC::QW * kHistBins];
   const WorkItem it = p.items[blockIdx.x];
   const GroupInfo gr = p.groups[it.group];
-  if (p.flag_mode == 2) {
+  if (p.flag_mode != 0) {
     bool all = true;
     for (int i = 0; i < gr.tile_n; ++i) all = all && (p.tile_flags[gr.tile_first + i] != 0);
-    if (all) return;   // the tiled kernel scores this tile
+    if (p.flag_mode == 2 && all) return;    // this tile's bounded range is scored whole
+    if (p.flag_mode == 1 && !all) return;   // this group's survivor list is scored instead
   }
   SC sc;
   sc.init(p, gr, it.region, wl, qhist, true);
