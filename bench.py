@@ -52,6 +52,21 @@ def kernel_name(pass_name, wl):
             "prep": "qbar_kernel"}.get(pass_name, pass_name)
 
 
+def bound_bytes(wl, pairs_bounded):
+    """Algorithmic HBM bytes of the bound pass: every bounded key row (plus its
+    scale and norm, 8 B) streamed once per query tile of 32 queries (8 groups
+    of 4 sharing LDS key tiles), or once per group of QW queries when the
+    batch's tiles are too small for the tiled kernel."""
+    kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.k_dtype] * wl.d + 8
+    qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_dtype]
+    per = wl.H * wl.d * qb
+    qw = 4 if (4 * per <= 32768 and wl.H % 4 == 0) else (2 if 2 * per <= 32768 else 1)
+    groups = sum((int(m) + qw - 1) // qw for m in wl.q_lens)
+    tiles = sum((((int(m) + qw - 1) // qw) + 7) // 8 for m in wl.q_lens if m > 0)
+    per_tile_q = 8 * qw if groups >= 4 * tiles else qw
+    return pairs_bounded / per_tile_q * kb
+
+
 def sources_digest():
     import hashlib
 
@@ -237,8 +252,7 @@ def main():
                 "peak": PEAK_TFLOPS[wl.q_dtype if wl.q_dtype == wl.k_dtype else "bf16"], "unit": "TFLOP/s",
                 "flop_per_launch": per_launch}
     elif dom == "bound":
-        kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.k_dtype] * wl.d + 8
-        per_launch = st["pairs_bounded"] / 4 * kb / launches
+        per_launch = bound_bytes(wl, st["pairs_bounded"]) / launches
         roof = {"kernel": kname, "bound": "hbm", "achieved": per_launch / (avg_ms / 1e3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "bytes_per_launch": per_launch}
     else:
@@ -248,6 +262,19 @@ def main():
     roof["launches_per_step"] = launches
     roof["avg_launch_ms"] = avg_ms
     roof["traffic"] = measured_traffic(kname, wl.name)
+    bound_ms = kern.get("bound", 0.0)
+    bound_line = None
+    qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_dtype]
+    qw = 4 if (4 * wl.H * wl.d * qb <= 32768 and wl.H % 4 == 0) else (2 if 2 * wl.H * wl.d * qb <= 32768 else 1)
+    n_groups = sum((int(m) + qw - 1) // qw for m in wl.q_lens) if not wl.chunk else wl.total_q // qw
+    if bound_ms > 0 and st["pairs_bounded"] > 0 and st["groups_skipped"] >= n_groups:
+        bound_line = {"note": "the plan skipped every group: no keys were streamed"}
+    elif bound_ms > 0 and st["pairs_bounded"] > 0:
+        bb = bound_bytes(wl, st["pairs_bounded"])
+        bound_line = {"kernel": "bound_tiled_kernel or bound_kernel", "bound": "hbm",
+                      "achieved": bb / (bound_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": bb / (bound_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                      "note": "groups the plan skips stream no keys; their pairs still count"}
     bounded = max(st["pairs_bounded"], 1)
     extra = {
         "dense_path_scores_per_s": results.get("dsa", {}).get("scores_per_s"),
@@ -257,6 +284,7 @@ def main():
         "pct_filtered": 100.0 * (1.0 - st["pairs_survived"] / bounded) if st["pairs_bounded"] else 0.0,
         "pct_pairs_exactly_scored": 100.0 * (st["pairs_seed"] + st["pairs_scored"]) / max(pairs, 1),
         "selection_identical_to_dense": same,
+        "bound_pass_roofline": bound_line,
         "kernel_ms_per_step": {p: r["kernel_ms_per_step"] for p, r in results.items()},
         "stats_per_step": {p: r["stats"] for p, r in results.items()},
     }
