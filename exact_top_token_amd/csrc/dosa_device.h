@@ -193,6 +193,17 @@ __device__ __forceinline__ int lane_fresh() {
   return v;
 }
 
+// Wait until every memory operation this wavefront has issued is complete.
+// Placed after the loads that set up a prefetching loop, it keeps the
+// compiler from merging their pending state into the loop, where its wait
+// for them would also wait for each iteration's own prefetch.
+__device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// Wait for this wavefront's vector memory operations only (vmcnt(0); the LDS
+// and export counters at their maxima).  Unconditional, so the compiler knows
+// afterwards that no load is pending on any path.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   const int lane = lane_id();
 #pragma unroll

@@ -851,6 +851,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   };
   auto commit = [&](int bufi) {
     const int tid = lane_fresh() + 64 * wave;
+    wait_vmem();
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 64 * kTileWaves;
@@ -863,40 +864,50 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
     }
   };
   u64 n_surv = 0;
-  if (ntiles > 0) fetch(0);
+  drain_memory();   // the certificate rows and coefficients, before the prefetching loop
+  // Tile t+1 is loaded while tile t is bounded and written to LDS before the
+  // tile's survivor word is stored; the last iteration reloads its own tile
+  // into the idle buffer, so no load stays pending across the back edge.
+  if (ntiles > 0) {
+    fetch(0);
+    commit(0);
+  }
+  __syncthreads();
+  const bool work = active && !(all_hopeless && p.debug_ub == nullptr);
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
     const int bufi = t & 1;
-    commit(bufi);
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
-    if (!active || (all_hopeless && p.debug_ub == nullptr)) continue;
+    fetch(min(t + 1, ntiles - 1));
     const int kb = lo + 64 * t;
     u64 word = 0;
+    if (work) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int kslot = b * 16 + col;
-      const int key = kb + kslot;
-      typename O::frag B[STEPS];
-      O::load_k(&ktile[bufi][kslot * ROW], g, B);
-      v4f c = {0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < 4; ++b) {
+        const int kslot = b * 16 + col;
+        const int key = kb + kslot;
+        typename O::frag B[STEPS];
+        O::load_k(&ktile[bufi][kslot * ROW], g, B);
+        v4f c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < STEPS; ++s) c = O::mma(A[s], B[s], c);
-      float pos = 0.f, neg = 0.f;
+        for (int s = 0; s < STEPS; ++s) c = O::mma(A[s], B[s], c);
+        float pos = 0.f, neg = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < npx) pos += cf[i] * fmaxf(c[i], 0.f);
-        else neg += cf[i] * c[i];
+        for (int i = 0; i < 4; ++i) {
+          if (i < npx) pos += cf[i] * fmaxf(c[i], 0.f);
+          else neg += cf[i] * c[i];
+        }
+        const float ub = kinfo[bufi][0][kslot] * (pos - fmaxf(neg, 0.f)) + cf[4] * kinfo[bufi][1][kslot];
+        const bool valid = qok && key < hi;
+        if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
+        const bool surv = valid && (hopeless || ub >= cf[5]);
+        const u64 m = __ballot(surv);
+        n_surv += __popcll(m);
+        word |= (u64)((uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu) << (16 * b);
       }
-      const float ub = kinfo[bufi][0][kslot] * (pos - fmaxf(neg, 0.f)) + cf[4] * kinfo[bufi][1][kslot];
-      const bool valid = qok && key < hi;
-      if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
-      const bool surv = valid && (hopeless || ub >= cf[5]);
-      const u64 m = __ballot(surv);
-      n_surv += __popcll(m);
-      word |= (u64)((uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu) << (16 * b);
     }
-    if (!all_hopeless && lane == 0) mw[(kb - gr.bound_lo) >> 6] = word;
+    commit(bufi ^ 1);
+    if (work && !all_hopeless && lane == 0) mw[(kb - gr.bound_lo) >> 6] = word;
+    __syncthreads();
   }
   if (active && !all_hopeless && p.stats != nullptr && lane == 0) {
     atomicAdd(&p.stats[2], nbounded);

@@ -560,6 +560,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   };
   auto commit = [&](int bufi) {
     const int tid = lane_fresh() + 64 * wave;
+    wait_vmem();
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 64 * kTileWaves;
@@ -569,18 +570,26 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     if (tid < kTileKeys) kscale[bufi][tid] = stage_s;
   };
 
-  if (ntiles > 0) fetch(0);
+  drain_memory();   // the query fragments of init, before the prefetching loop
+  // Tile t+1 is loaded while tile t is scored and is written to LDS before
+  // tile t's candidates are appended, so the wait for the loads never
+  // includes candidate stores just issued (one counter covers both).  The
+  // last iteration reloads its own tile into the idle buffer: an unconditional
+  // load and wait leave nothing pending into the next iteration on any path.
+  if (ntiles > 0) {
+    fetch(0);
+    commit(0);
+  }
+  __syncthreads();
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
     const int bufi = t & 1;
-    commit(bufi);
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
+    fetch(min(t + 1, ntiles - 1));
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
     const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
+    float o[4];
     if (active) {
-      float o[4];
 #pragma unroll
       for (int hb = 0; hb < 4 / NBK; ++hb) {
         typename O::frag B[NBK][SC::STEPS];
@@ -589,21 +598,23 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
           O::load_k(&ktile[bufi][((NBK * hb + b) * 16 + sc.col()) * ROW], sc.g(), B[b]);
         sc.template scoreN<NBK>(B, o + NBK * hb);
       }
-      {
-        const int cl = sc.col();
-        float ks[4];
-        int keys[4];
-        bool kv[4];
+    }
+    commit(bufi ^ 1);
+    if (active) {
+      const int cl = sc.col();
+      float ks[4];
+      int keys[4];
+      bool kv[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          keys[b] = kb + b * 16 + cl;
-          ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + cl] : 1.f;
-          kv[b] = keys[b] >= lo && keys[b] < hi;
-        }
-        sc.append4(p, gr, it.region, o, ks, keys, kv, hist[wave]);
+      for (int b = 0; b < 4; ++b) {
+        keys[b] = kb + b * 16 + cl;
+        ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + cl] : 1.f;
+        kv[b] = keys[b] >= lo && keys[b] < hi;
       }
+      sc.append4(p, gr, it.region, o, ks, keys, kv, hist[wave]);
       if ((t & 7) == 7) sc.refresh_theta(p.topk);
     }
+    __syncthreads();
   }
   if (active) {
     sc.close(p, gr, it.region, hist[wave]);
