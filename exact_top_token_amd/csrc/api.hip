@@ -197,7 +197,9 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   const int64_t avg_keys = NT ? key_sum / NT : 0;
   // Tiles that hold few groups waste the tiled kernel's wavefronts: use one
   // wavefront per group there (decode-like batches).
-  P.tiled = (NT > 0) && (G >= 4 * NT);
+  P.tiled = (NT > 0) && (2 * G >= TW * NT);
+  // work items that give every SIMD two wavefronts of tiled scoring
+  const int64_t tiled_target = 2048 / TW;
   auto range_split = [](int lo_all, int hi_all, int r, int J, int align, int& lo, int& hi) {
     const int64_t len = hi_all - lo_all;
     lo = lo_all + (int)((len * r / J) / align * align);
@@ -205,7 +207,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   };
   if (dense) {
     if (P.tiled) {
-      int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(NT, avg_keys, 256, 1024);
+      int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(NT, avg_keys, tiled_target, 1024);
       P.J = J;
       for (const auto& t : tiles)
         for (int r = 0; r < J; ++r) {
@@ -254,7 +256,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     // launch fills the GPU; the keys in between get a certificate
     int64_t loff = 0;
     int max_bounded = 0;
-    const int Js = choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), 256, 1024);
+    const int Js = choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), tiled_target, 1024);
     P.Js = Js;
     for (const auto& t : tiles) {
       const int wlo = std::max(0, t.n_last - P.W);
@@ -333,7 +335,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     if (P.tiled) {
       int64_t bsum_t = 0;
       for (const auto& t : tiles) bsum_t += P.groups[t.first].n_bounded;
-      const int Jb = choose_splits(NT, NT ? bsum_t / NT : 0, 512, 2048);
+      const int Jb = choose_splits(NT, NT ? bsum_t / NT : 0, 2 * tiled_target, 2048);
       for (const auto& t : tiles) {
         const GroupInfo& g = P.groups[t.first];
         for (int r = 0; r < Jb; ++r) {

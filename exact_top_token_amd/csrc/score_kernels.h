@@ -128,6 +128,10 @@ __device__ __noinline__ u64 shrink_region(u64* bq, uint32_t n, float tq, int cap
 constexpr int kHistBins = 256;          // running-threshold histogram bins per query
 constexpr int kHistShift = 18;          // 2^18 ord units per bin: 32 bins per octave
 constexpr int kHistAnchor = 192;        // the first block's maximum lands in this bin
+// 64-key tiles between two threshold refreshes of the tiled kernel.  A
+// refresh costs about as much as appending a tile's candidates; every 16
+// tiles measured fastest (8 appends 3% fewer candidates and runs slower).
+constexpr int kRefreshTiles = 16;
 
 template <int C, int H, int D>
 struct Scorer {
@@ -158,6 +162,7 @@ struct Scorer {
   uint32_t* qh;      // LDS: this wavefront's query histograms [QW][kHistBins]
   uint32_t hbase;    // ord value of the lower edge of bin 0 (0 = not anchored yet)
   uint32_t n_written, n_reselect, n_scored;
+  bool dirty;        // something was appended since the last refresh (wavefront-uniform)
 
   // wl: LDS [QW][H + S]: per query the head weights / 2, then the scales / 2
   // of its weighted-query terms (filled here);
@@ -194,47 +199,67 @@ struct Scorer {
     }
     wq_lds = (uint32_t)(uintptr_t)(wl + qi() * (H + S));   // low 32 bits of a generic LDS address = the LDS offset
     qs = (HasQScale<C>::value && qok()) ? p.in.q_scale[qrow()] : 1.f;
-    theta = (p.theta_init != nullptr && qok()) ? p.theta_init[qrow()] : -INFINITY;
+    // lanes of absent queries get an unreachable threshold, so they never append
+    theta = qok() ? (p.theta_init != nullptr ? p.theta_init[qrow()] : -INFINITY) : INFINITY;
     count = 0;
     buf = qok() ? p.cb.cand + ((int64_t)qrow() * p.cb.R + region) * p.cb.cap : nullptr;
     qh = hq;
     for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
     hbase = 0;
     n_written = n_reselect = n_scored = 0;
+    dirty = false;
   }
 
   // Raise theta of every query of the wavefront to the lower edge of the
-  // highest histogram bin that has at least K scores at or above it.
+  // highest histogram bin that has at least K scores at or above it.  The
+  // queries are handled side by side: each owns 64/QW lanes, each lane 4*QW
+  // consecutive bins; a segmented suffix sum over the query's lanes finds the
+  // lane whose bins hold the K-th count, which walks its own bins.
   __device__ __forceinline__ void refresh_theta(int K) {
+    constexpr int LPQ = 64 / QW;                 // lanes per query
+    constexpr int BPL = kHistBins / LPQ;         // bins per lane
     wave_sync();
-#pragma unroll 1
-    for (int qq = 0; qq < QW; ++qq) {
-      const uint32_t* h = qh + qq * kHistBins;
-      const uint32_t b0 = __shfl(hbase, 16 * (qq * (4 / QW)), 64);
-      if (b0 == 0) continue;
-      uint32_t s4 = 0;
+    const int ln = lane_fresh();
+    const int j = ln % LPQ, q = ln / LPQ;        // q == qi()
+    const uint32_t* h = qh + q * kHistBins + j * BPL;
+    uint32_t hv[BPL];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) s4 += h[lane_id() * 4 + t];
-      const uint32_t suf = wave_suffix_sum(s4);
-      const bool cross = (suf >= (uint32_t)K) && (suf - s4 < (uint32_t)K);
-      const u64 cm = __ballot(cross);
-      if (cm == 0) continue;                       // fewer than K scores counted so far
-      const int L = __ffsll((long long)cm) - 1;
-      uint32_t acc = __shfl(suf - s4, L, 64);
-      int b = L * 4;
-      for (int t = 3; t >= 0; --t) {
-        const uint32_t hv = h[L * 4 + t];
-        if (acc + hv >= (uint32_t)K) { b = L * 4 + t; break; }
-        acc += hv;
-      }
-      uint32_t edge = b0 + ((uint32_t)b << kHistShift);
-      if (edge < b0 || edge > 0xFF7FFFFFu) edge = 0xFF7FFFFFu;   // stay on finite floats
-      const float th = ord2f(edge);
-      if (qi() == qq && th > theta) theta = th;
+    for (int t = 0; t < BPL; t += 4) {
+      const v4i v = *reinterpret_cast<const v4i*>(h + t);
+      hv[t] = (uint32_t)v[0]; hv[t + 1] = (uint32_t)v[1]; hv[t + 2] = (uint32_t)v[2]; hv[t + 3] = (uint32_t)v[3];
     }
+    uint32_t s = 0;
+#pragma unroll
+    for (int t = 0; t < BPL; ++t) s += hv[t];
+    uint32_t suf = s;
+#pragma unroll
+    for (int off = 1; off < LPQ; off <<= 1) {
+      const uint32_t o = (uint32_t)__shfl_down((int)suf, off, LPQ);
+      if (j + off < LPQ) suf += o;
+    }
+    const bool cross = hbase != 0u && suf >= (uint32_t)K && suf - s < (uint32_t)K;
+    uint32_t a = suf - s;
+    int bt = 0;
+    bool found = false;
+#pragma unroll
+    for (int t = BPL - 1; t >= 0; --t) {
+      const bool hit = !found && a + hv[t] >= (uint32_t)K;
+      bt = hit ? t : bt;
+      found = found || hit;
+      a += hv[t];
+    }
+    uint32_t edge = hbase + ((uint32_t)(j * BPL + bt) << kHistShift);
+    if (edge < hbase || edge > 0xFF7FFFFFu) edge = 0xFF7FFFFFu;   // stay on finite floats
+    const u64 cm = __ballot(cross);
+    const u64 segm = (cm >> (q * LPQ)) & (LPQ == 64 ? ~0ull : ((1ull << (LPQ & 63)) - 1ull));
+    const int L = segm ? q * LPQ + (__ffsll((long long)segm) - 1) : ln;
+    const uint32_t e = (uint32_t)__shfl((int)edge, L, 64);
+    if (segm != 0ull) {
+      const float th = ord2f(e);
+      if (th > theta) theta = th;
+    }
+    dirty = false;
   }
-
-
 
   // Compact the region of query qq to the entries >= its theta; if that
   // leaves it more than half full, select the exact K-th and keep K.  The
@@ -323,33 +348,48 @@ struct Scorer {
 
   // Count the scores of one step (4 blocks of 16 keys) in their queries'
   // histograms, append those that reach theta, and shrink regions that are
-  // about to overflow.  Called by all 64 lanes of the wavefront.  Lane roles
-  // are derived once per step; a step adds at most 64 entries per query, so
-  // regions are checked against cap - 64 once per step.
+  // about to overflow.  Called by all 64 lanes of the wavefront.  CHECK: some
+  // keys of the step may lie outside the range (kvalid) or after a query's
+  // position; without it every key of the step is visible to every query of
+  // the group.  Lanes of absent queries hold theta = +inf and never take.  A
+  // step whose scores all stay below theta costs a few instructions.  A step
+  // adds at most 64 entries per query, so regions are checked against
+  // cap - 64 once per step.
+  template <bool CHECK>
   __device__ __forceinline__ void append4(const ScoreLaunch& p, const GroupInfo& gr, int region, const float* o,
                                           const float* ks, const int* key, const bool* kvalid, uint32_t* shist) {
     const int ln = lane_fresh();
     const int c = ln & 15, gg = ln >> 4;
     const int q_i = (4 * gg) / S;
     const int ol0 = 16 * (q_i * (4 / QW));
-    const bool own = (gg == (ol0 >> 4)) && q_i < nq;
-    const int last = pos0 + q_i;                         // the query sees keys <= last
-    const uint32_t below = (1u << c) - 1u;
+    const bool own = (QW == 4) || (gg == (ol0 >> 4));
     float sc[4];
-    uint32_t so[4];
-    bool valid[4];
+    bool take[4];
+    bool anyt = false;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       sc[b] = o[b] * qs * ks[b];
-      so[b] = f2ord(sc[b]);
-      valid[b] = own && kvalid[b] && key[b] <= last;
+      bool v = own;
+      if constexpr (CHECK) {
+        v = v && kvalid[b] && key[b] <= pos0 + q_i && q_i < nq;
+        n_scored += __popcll(__ballot(v));
+      }
+      take[b] = v && sc[b] >= theta;
+      anyt = anyt || take[b];
     }
+    if constexpr (!CHECK) n_scored += 64u * (uint32_t)nq;
+    if (__ballot(anyt) == 0ull) return;
+    dirty = true;
+    uint32_t so[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) so[b] = f2ord(sc[b]);
     if (__any(hbase == 0)) {
-      // anchor each query's histogram below the maximum of its first scores
-      // (all lanes take part in the exchanges; only unanchored queries update)
+      // anchor each query's histogram below the maximum of the first scores
+      // it takes (all lanes take part in the exchanges; only unanchored
+      // queries update)
       uint32_t mx = 0u;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) mx = max(mx, valid[b] ? so[b] : 0u);
+      for (int b = 0; b < 4; ++b) mx = max(mx, take[b] ? so[b] : 0u);
 #pragma unroll
       for (int off = 1; off < 16; off <<= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
       mx = __shfl(mx, ol0 + c, 64);
@@ -359,15 +399,15 @@ struct Scorer {
       }
     }
     uint32_t* hq = qh + q_i * kHistBins;
+    const uint32_t below = (1u << c) - 1u;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const bool take = valid[b] && sc[b] >= theta;
-      if (take && hbase != 0 && so[b] >= hbase)
+      const u64 m = __ballot(take[b]);
+      if (m == 0ull) continue;
+      if (take[b] && hbase != 0 && so[b] >= hbase)
         atomicAdd(&hq[min((so[b] - hbase) >> kHistShift, (uint32_t)(kHistBins - 1))], 1u);
-      const u64 m = __ballot(take);
-      n_scored += __popcll(__ballot(valid[b]));
       const uint32_t slice = (uint32_t)(m >> ol0) & 0xFFFFu;
-      if (take) buf[count + __popc(slice & below)] = ((u64)so[b] << 32) | (u64)(uint32_t)(~(uint32_t)key[b]);
+      if (take[b]) buf[count + __popc(slice & below)] = ((u64)so[b] << 32) | (u64)(uint32_t)(~(uint32_t)key[b]);
       count += __popc(slice);
       n_written += __popcll(m);
     }
@@ -450,8 +490,8 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) load(keys[b], v[b], B[b], ks[b]);
     sc.template scoreN<4>(B, o);
-    sc.append4(p, gr, it.region, o, ks, keys, v, hist);
-    if ((++nblk & 7) == 0) sc.refresh_theta(p.topk);
+    sc.template append4<true>(p, gr, it.region, o, ks, keys, v, hist);
+    if ((++nblk & 7) == 0 && sc.dirty) sc.refresh_theta(p.topk);
   };
 
   if (!it.gather) {
@@ -494,21 +534,27 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
 
 // ---------------------------------------------------------------------------
 // 8 wavefronts (consecutive query groups of one sequence) share LDS key tiles
-// (range mode: [a0,a1) then [b0,b1), each from the top tile down)
+// (range mode: [a0,a1) then [b0,b1), each from the top tile down).  PAGED:
+// keys go through the page table; otherwise a tile is one contiguous run of
+// rows addressed from a single base.
 // ---------------------------------------------------------------------------
-template <int C, int H, int D, int ROLE>
+template <int C, int H, int D, int ROLE, bool PAGED>
 __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const ScoreLaunch p) {
   using SC = Scorer<C, H, D>;
   using O = typename SC::O;
   constexpr int KB = SC::KBYTES;
   constexpr int ROW = KB + 16;                       // padded LDS row: conflict-free 16-byte reads
   constexpr int CPK = KB / 16;                       // 16-byte chunks per key
-  constexpr int NCH = (kTileKeys * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
+  // 64-key scoring steps per LDS tile.  One: with two (128-key tiles, half
+  // the barriers) the kernel measured slower on MI355X.
+  constexpr int TS = 1;
+  constexpr int TK = kTileKeys * TS;                 // keys per LDS tile
+  constexpr int NCH = (TK * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
   // 16-key blocks per scoring step: as many as the key fragments' registers allow
   constexpr int FB = (int)sizeof(typename O::frag) * SC::STEPS;   // bytes of one block's key fragment per lane
   constexpr int NBK = FB <= 32 ? 4 : (FB <= 64 ? 2 : 1);
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kTileKeys * ROW];
-  __shared__ float kscale[2][kTileKeys];
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][TK * ROW];
+  __shared__ float kscale[2][TK];
   __shared__ __attribute__((aligned(16))) float wl[kTileWaves][SC::QW * (H + SC::S)];
   __shared__ uint32_t hist[kTileWaves][256];
   __shared__ uint32_t qhist[kTileWaves][SC::QW * kHistBins];
@@ -527,10 +573,13 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   SC sc;
   sc.init(p, gr, it.region, wl[wave], qhist[wave], active);
 
-  const int na = (it.a1 > it.a0) ? (it.a1 - it.a0 + kTileKeys - 1) / kTileKeys : 0;
-  const int nbt = (it.b1 > it.b0) ? (it.b1 - it.b0 + kTileKeys - 1) / kTileKeys : 0;
+  const int na = (it.a1 > it.a0) ? (it.a1 - it.a0 + TK - 1) / TK : 0;
+  const int nbt = (it.b1 > it.b0) ? (it.b1 - it.b0 + TK - 1) / TK : 0;
   const int ntiles = na + nbt;
-  const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
+  // contiguous storage: row r of the sequence's keys at kseq + r * KB
+  const uint8_t* kseq = static_cast<const uint8_t*>(p.in.k) + (PAGED ? 0 : (int64_t)g0.key_base * KB);
+  const float* sseq = p.in.k_scale + (PAGED ? 0 : (int64_t)g0.key_base);
+  const int last0 = gr.pos0;                         // every query of the group sees keys <= last0
 
   v4i stage[NCH];
   float stage_s = 1.f;
@@ -538,23 +587,30 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     const int tid = lane_fresh() + 64 * wave;
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
-    const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
+    const int kb = hi - TK * ((ra ? t : t - na) + 1);
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 64 * kTileWaves;
       const int slot = ch / CPK, part = ch % CPK;
       const int key = kb + slot;
-      if (slot < kTileKeys && key >= lo && key < hi) {
-        const int64_t row = key_row(p.in, g0.key_base, g0.seq, key);
-        stage[c] = *reinterpret_cast<const v4i*>(kbytes + row * KB + part * 16);
+      if (slot < TK && key >= lo && key < hi) {
+        if constexpr (PAGED) {
+          const int64_t row = key_row(p.in, g0.key_base, g0.seq, key);
+          stage[c] = *reinterpret_cast<const v4i*>(kseq + row * KB + part * 16);
+        } else {
+          stage[c] = *reinterpret_cast<const v4i*>(kseq + ((uint32_t)key * (uint32_t)KB + (uint32_t)(part * 16)));
+        }
       } else {
         stage[c] = v4i{0, 0, 0, 0};
       }
     }
     if constexpr (HasKScale<C>::value) {
-      if (tid < kTileKeys) {
+      if (tid < TK) {
         const int key = kb + tid;
-        stage_s = (key >= lo && key < hi) ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, key)] : 0.f;
+        if (key >= lo && key < hi)
+          stage_s = PAGED ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, key)] : sseq[(uint32_t)key];
+        else
+          stage_s = 0.f;
       }
     }
   };
@@ -565,9 +621,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 64 * kTileWaves;
       const int slot = ch / CPK, part = ch % CPK;
-      if (slot < kTileKeys) *reinterpret_cast<v4i*>(&ktile[bufi][slot * ROW + part * 16]) = stage[c];
+      if (slot < TK) *reinterpret_cast<v4i*>(&ktile[bufi][slot * ROW + part * 16]) = stage[c];
     }
-    if (tid < kTileKeys) kscale[bufi][tid] = stage_s;
+    if (tid < TK) kscale[bufi][tid] = stage_s;
   };
 
   drain_memory();   // the query fragments of init, before the prefetching loop
@@ -587,32 +643,48 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     fetch(min(t + 1, ntiles - 1));
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
-    const int kb = hi - kTileKeys * ((ra ? t : t - na) + 1);
-    float o[4];
+    const int kb = hi - TK * ((ra ? t : t - na) + 1);
+    float o[TS][4];
     if (active) {
 #pragma unroll
-      for (int hb = 0; hb < 4 / NBK; ++hb) {
-        typename O::frag B[NBK][SC::STEPS];
+      for (int hh = 0; hh < TS; ++hh) {
 #pragma unroll
-        for (int b = 0; b < NBK; ++b)
-          O::load_k(&ktile[bufi][((NBK * hb + b) * 16 + sc.col()) * ROW], sc.g(), B[b]);
-        sc.template scoreN<NBK>(B, o + NBK * hb);
+        for (int hb = 0; hb < 4 / NBK; ++hb) {
+          typename O::frag B[NBK][SC::STEPS];
+#pragma unroll
+          for (int b = 0; b < NBK; ++b)
+            O::load_k(&ktile[bufi][(kTileKeys * hh + (NBK * hb + b) * 16 + sc.col()) * ROW], sc.g(), B[b]);
+          // all blocks' fragments in flight together: one LDS wait, not one per block
+#pragma unroll
+          for (int b = 0; b < NBK; ++b)
+#pragma unroll
+            for (int s = 0; s < SC::STEPS; ++s) asm volatile("" : "+v"(B[b][s]));
+          sc.template scoreN<NBK>(B, o[hh] + NBK * hb);
+        }
       }
     }
     commit(bufi ^ 1);
     if (active) {
       const int cl = sc.col();
-      float ks[4];
-      int keys[4];
-      bool kv[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        keys[b] = kb + b * 16 + cl;
-        ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + cl] : 1.f;
-        kv[b] = keys[b] >= lo && keys[b] < hi;
+      for (int hh = 0; hh < TS; ++hh) {
+        const int kh = kb + kTileKeys * hh;
+        float ks[4];
+        int keys[4];
+        bool kv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          keys[b] = kh + b * 16 + cl;
+          ks[b] = HasKScale<C>::value ? kscale[bufi][kTileKeys * hh + b * 16 + cl] : 1.f;
+          kv[b] = keys[b] >= lo && keys[b] < hi;
+        }
+        // whole step inside the range and visible to every query of the group
+        if (kh >= lo && kh + kTileKeys <= hi && kh + kTileKeys - 1 <= last0)
+          sc.template append4<false>(p, gr, it.region, o[hh], ks, keys, kv, hist[wave]);
+        else
+          sc.template append4<true>(p, gr, it.region, o[hh], ks, keys, kv, hist[wave]);
       }
-      sc.append4(p, gr, it.region, o, ks, keys, kv, hist[wave]);
-      if ((t & 7) == 7) sc.refresh_theta(p.topk);
+      if ((t & (kRefreshTiles / TS - 1)) == kRefreshTiles / TS - 1 && sc.dirty) sc.refresh_theta(p.topk);
     }
     __syncthreads();
   }
@@ -627,8 +699,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
 // ---------------------------------------------------------------------------
 template <int C, int H, int D, int ROLE>
 static hipError_t launch_score_r(const ScoreLaunch& p, hipStream_t s) {
-  if (p.tiled)
-    hipLaunchKernelGGL((score_tiled_kernel<C, H, D, ROLE>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+  if (p.tiled && p.in.page_table != nullptr)
+    hipLaunchKernelGGL((score_tiled_kernel<C, H, D, ROLE, true>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+  else if (p.tiled)
+    hipLaunchKernelGGL((score_tiled_kernel<C, H, D, ROLE, false>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
   else
     hipLaunchKernelGGL((score_list_kernel<C, H, D, ROLE>), dim3(p.n_items), dim3(64), 0, s, p);
   return hipGetLastError();
