@@ -35,6 +35,9 @@ __device__ __forceinline__ uint32_t enc_fp8_p(float x) {
 }
 
 // One 64-lane wavefront per query; lane i owns elements i, i+64 (d <= 128).
+// The query's H x d row and its weights are first staged in LDS with 16-byte
+// loads that are all in flight together, so the per-element sums read LDS
+// instead of waiting on one global load per head.
 template <int C, int H, int D>
 __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   constexpr int QB = (C == C_F32) ? 4 : (C == C_FP8 ? 1 : 2);
@@ -42,10 +45,27 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   constexpr int S = 16 / QW;                     // weighted-query terms per query
   constexpr int NT = (C == C_F32) ? 1 : (C == C_FP8 ? (S < 4 ? S : 4) : (S < 3 ? S : 3));
   constexpr int PER = (D + 63) / 64;
+  constexpr int ROWB = H * D * QB;               // bytes of one query row (a multiple of 16)
+  constexpr int NC = ROWB / 16;                  // 16-byte chunks of the row
+  constexpr int NCH = (NC + 63) / 64;            // per lane
+  __shared__ __attribute__((aligned(16))) uint8_t qrow[ROWB];
+  __shared__ float wrow[H];
   const int q = blockIdx.x;
   const int lane = lane_id();
   if (q >= p.total_q) return;
-  const uint8_t* qraw = static_cast<const uint8_t*>(p.q) + (int64_t)q * H * D * QB;
+  {
+    const v4i* src = reinterpret_cast<const v4i*>(static_cast<const uint8_t*>(p.q) + (int64_t)q * ROWB);
+    v4i c[NCH];
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) c[u] = (lane + 64 * u < NC) ? src[lane + 64 * u] : v4i{0, 0, 0, 0};
+    const float wv = lane < H ? p.w[(int64_t)q * H + lane] : 0.f;
+#pragma unroll
+    for (int u = 0; u < NCH; ++u)
+      if (lane + 64 * u < NC) reinterpret_cast<v4i*>(qrow)[lane + 64 * u] = c[u];
+    if (lane < H) wrow[lane] = wv;
+  }
+  __syncthreads();
+  const uint8_t* qraw = qrow;
   double r[PER];
 #pragma unroll
   for (int v = 0; v < PER; ++v) {
@@ -57,7 +77,7 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
         if constexpr (C == C_F32) x = reinterpret_cast<const float*>(qraw)[h * D + i];
         else if constexpr (C == C_FP8) x = dec_fp8_p(qraw[h * D + i]);
         else x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qraw)[h * D + i] << 16);
-        acc += (double)p.w[(int64_t)q * H + h] * (double)x;
+        acc += (double)wrow[h] * (double)x;
       }
     }
     r[v] = acc;

@@ -313,8 +313,15 @@ struct Scorer {
     asm volatile("" : "+v"(wa));
     typedef __attribute__((address_space(3))) const v4f lds_v4f;
     v4f cur[NB];
+    // Wave priority (s_setprio, inside this wavefront only): 2 while a burst
+    // of MFMAs issues, 1 for the rest of the scoring, 0 outside it.  When the
+    // two wavefronts of a SIMD compete, the one about to feed the matrix pipe
+    // issues first and the one appending candidates fills the gaps (3% faster
+    // on MI355X than equal priorities).
+    __builtin_amdgcn_s_setprio(2);
 #pragma unroll
     for (int b = 0; b < NB; ++b) cur[b] = mma_all(A[0], B[b]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < HG; ++j) {
 #pragma unroll
@@ -323,8 +330,10 @@ struct Scorer {
         for (int s = 0; s < STEPS; ++s) asm volatile("" : "+v"(B[b][s]));
       const v4f w4 = *reinterpret_cast<lds_v4f*>((uintptr_t)(wa + 4u * (uint32_t)(S * j)));
       v4f nxt[NB];
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int b = 0; b < NB; ++b) nxt[b] = (j + 1 < HG) ? mma_all(A[j + 1 < HG ? j + 1 : 0], B[b]) : mma_all(AL, B[b]);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         o[b] = fmaf(w4[0], fabsf(cur[b][0]), o[b]);
@@ -336,6 +345,7 @@ struct Scorer {
       }
     }
     const v4f sl = *reinterpret_cast<lds_v4f*>((uintptr_t)(wa + 4u * (uint32_t)(S * HG)));
+    __builtin_amdgcn_s_setprio(0);   // no MFMA left to issue
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
 #pragma unroll
