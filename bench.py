@@ -52,19 +52,13 @@ def kernel_name(pass_name, wl):
             "prep": "qbar_kernel"}.get(pass_name, pass_name)
 
 
-def bound_bytes(wl, pairs_bounded):
-    """Algorithmic HBM bytes of the bound pass: every bounded key row (plus its
-    scale and norm, 8 B) streamed once per query tile of 32 queries (8 groups
-    of 4 sharing LDS key tiles), or once per group of QW queries when the
-    batch's tiles are too small for the tiled kernel."""
+def bound_bytes(wl, keys_streamed):
+    """Algorithmic HBM bytes of the bound pass: each key row it streams (once
+    per query tile that shares an LDS key tile, or once per query group in the
+    one-wavefront-per-group kernel) plus that key's scale and norm (8 B).
+    Groups the plan marks hopeless stream nothing and count nothing."""
     kb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.k_dtype] * wl.d + 8
-    qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_dtype]
-    per = wl.H * wl.d * qb
-    qw = 4 if (4 * per <= 32768 and wl.H % 4 == 0) else (2 if 2 * per <= 32768 else 1)
-    groups = sum((int(m) + qw - 1) // qw for m in wl.q_lens)
-    tiles = sum((((int(m) + qw - 1) // qw) + 7) // 8 for m in wl.q_lens if m > 0)
-    per_tile_q = 8 * qw if groups >= 4 * tiles else qw
-    return pairs_bounded / per_tile_q * kb
+    return keys_streamed * kb
 
 
 def sources_digest():
@@ -252,7 +246,7 @@ def main():
                 "peak": PEAK_TFLOPS[wl.q_dtype if wl.q_dtype == wl.k_dtype else "bf16"], "unit": "TFLOP/s",
                 "flop_per_launch": per_launch}
     elif dom == "bound":
-        per_launch = bound_bytes(wl, st["pairs_bounded"]) / launches
+        per_launch = bound_bytes(wl, st["keys_streamed"]) / launches
         roof = {"kernel": kname, "bound": "hbm", "achieved": per_launch / (avg_ms / 1e3) / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s", "bytes_per_launch": per_launch}
     else:
@@ -264,17 +258,15 @@ def main():
     roof["traffic"] = measured_traffic(kname, wl.name)
     bound_ms = kern.get("bound", 0.0)
     bound_line = None
-    qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_dtype]
-    qw = 4 if (4 * wl.H * wl.d * qb <= 32768 and wl.H % 4 == 0) else (2 if 2 * wl.H * wl.d * qb <= 32768 else 1)
-    n_groups = sum((int(m) + qw - 1) // qw for m in wl.q_lens) if not wl.chunk else wl.total_q // qw
-    if bound_ms > 0 and st["pairs_bounded"] > 0 and st["groups_skipped"] >= n_groups:
+    if bound_ms > 0 and st["pairs_bounded"] > 0 and st["keys_streamed"] == 0:
         bound_line = {"note": "the plan skipped every group: no keys were streamed"}
-    elif bound_ms > 0 and st["pairs_bounded"] > 0:
-        bb = bound_bytes(wl, st["pairs_bounded"])
+    elif bound_ms > 0 and st["keys_streamed"] > 0:
+        bb = bound_bytes(wl, st["keys_streamed"])
         bound_line = {"kernel": "bound_tiled_kernel or bound_kernel", "bound": "hbm",
                       "achieved": bb / (bound_ms / 1e3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                      "frac": bb / (bound_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
-                      "note": "groups the plan skips stream no keys; their pairs still count"}
+                      "frac": bb / (bound_ms / 1e3) / 1e9 / PEAK_HBM_GBS, "bytes_per_step": bb,
+                      "note": "bytes = key rows streamed (+8 B scale and norm each); the time is the whole pass, "
+                              "including launches whose groups the plan skipped"}
     bounded = max(st["pairs_bounded"], 1)
     extra = {
         "dense_path_scores_per_s": results.get("dsa", {}).get("scores_per_s"),

@@ -51,7 +51,7 @@ class DosaConfig(ctypes.Structure):
 class DosaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "pairs_total", "pairs_seed", "pairs_bounded", "pairs_survived", "pairs_scored",
-        "candidates_written", "reselects", "groups_skipped", "pairs_scored_list")]
+        "candidates_written", "reselects", "groups_skipped", "pairs_scored_list", "keys_streamed")]
 
 
 STAT_FIELDS = [f[0] for f in DosaStats._fields_]

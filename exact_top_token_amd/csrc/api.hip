@@ -571,7 +571,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
                      stream);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(items)");
   if (st) {
-    unsigned long long add[9] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned long long add[10] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     e = launch_stats_add(st, add, stream);
     if (e != hipSuccess) return fail_hip(e, "stats");
   }

@@ -96,7 +96,7 @@ struct ScoreLaunch {
   const int32_t* tile_flags; // per group: 1 if the certificate prunes nothing in its tile (or NULL)
   int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not
   int32_t role;              // Role
-  unsigned long long* stats; // dosa_stats as u64[9] or NULL
+  unsigned long long* stats; // dosa_stats as u64[10] or NULL
 };
 
 struct SelectLaunch {

@@ -765,6 +765,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
   if (!all_hopeless && p.stats != nullptr && lane == 0) {
     atomicAdd(&p.stats[2], nbounded);
     atomicAdd(&p.stats[3], n_surv);
+    atomicAdd(&p.stats[9], (u64)max(hi - lo, 0));
   }
 }
 
@@ -814,6 +815,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   }
   // the whole workgroup leaves if no wavefront has work (and no dump is asked for)
   if (__syncthreads_and(!active || all_hopeless) && p.debug_ub == nullptr) return;
+  if (p.stats != nullptr && threadIdx.x == 0) atomicAdd(&p.stats[9], (u64)max(hi - lo, 0));   // rows this workgroup streams
   typename O::frag A[STEPS];
   {
     const int ra = lane & 15;
@@ -1007,7 +1009,7 @@ __global__ void stats_add_kernel(unsigned long long* st, const dosa_stats add) {
 // ---------------------------------------------------------------------------
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* v, hipStream_t s) {
   dosa_stats a;
-  static_assert(sizeof(dosa_stats) == 9 * sizeof(unsigned long long), "stats layout");
+  static_assert(sizeof(dosa_stats) == 10 * sizeof(unsigned long long), "stats layout");
   memcpy(&a, v, sizeof(a));
   hipLaunchKernelGGL(stats_add_kernel, dim3(1), dim3(64), 0, s, stats, a);
   return hipGetLastError();

@@ -125,6 +125,8 @@ typedef struct {
   uint64_t reselects;          /* in-kernel buffer re-selections */
   uint64_t groups_skipped;     /* query groups whose certificate could prune nothing */
   uint64_t pairs_scored_list;  /* the part of pairs_scored scored from compacted survivor lists */
+  uint64_t keys_streamed;      /* key rows the bound pass read (once per query tile or group that
+                                  streamed them; skipped groups read none) */
 } dosa_stats;
 
 /* Fill *cfg with the defaults for a given topk. */
