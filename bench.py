@@ -41,12 +41,27 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def uses_tiles(wl):
+    """Whether the library scores this batch with the tiled kernel (8 query
+    groups of 4/2/1 queries per workgroup) or, when tiles would hold fewer than
+    4 groups on average (decode-like batches), one wavefront per group."""
+    qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_dtype]
+    per = wl.H * wl.d * qb
+    qw = 4 if (4 * per <= 32768 and wl.H % 4 == 0) else (2 if (2 * per <= 32768 and wl.H % 8 == 0) else 1)
+    lens = [wl.chunk] * (wl.total_q // wl.chunk) if wl.chunk else [int(m) for m in wl.q_lens]
+    groups = sum((m + qw - 1) // qw for m in lens)
+    tiles = sum(((m + qw - 1) // qw + 7) // 8 for m in lens if m > 0)
+    return tiles > 0 and 2 * groups >= 8 * tiles
+
+
 def kernel_name(pass_name, wl):
     """Name of the kernel instantiation a pass launches, as profilers print it."""
     c = COMBO_ID[(wl.q_dtype, wl.k_dtype)]
     if pass_name in ROLE_ID:
-        k = "score_list_kernel" if pass_name == "score_survivor_lists" else "score_tiled_kernel"
-        return f"{k}<{c}, {wl.H}, {wl.d}, {ROLE_ID[pass_name]}>"
+        if pass_name == "score_survivor_lists" or not uses_tiles(wl):
+            return f"score_list_kernel<{c}, {wl.H}, {wl.d}, {ROLE_ID[pass_name]}>"
+        paged = "true" if wl.page_table is not None else "false"
+        return f"score_tiled_kernel<{c}, {wl.H}, {wl.d}, {ROLE_ID[pass_name]}, {paged}>"
     return {"plan": "plan_kernel", "bound": "bound_kernel", "compact": "compact_kernel",
             "key_norms": "key_norm_kernel", "select_seed": "select_kernel", "select_final": "select_kernel",
             "prep": "qbar_kernel"}.get(pass_name, pass_name)

@@ -193,6 +193,11 @@ __device__ __forceinline__ int lane_fresh() {
   return v;
 }
 
+// Lane mask of a per-lane condition.  Takes the condition as a bool, so a
+// comparison result goes straight into the mask (HIP's __ballot takes an int
+// and materialises it in a vector register first).
+__device__ __forceinline__ unsigned long long ballot(bool b) { return __builtin_amdgcn_ballot_w64(b); }
+
 // Wait until every memory operation this wavefront has issued is complete.
 // Placed after the loads that set up a prefetching loop, it keeps the
 // compiler from merging their pending state into the loop, where its wait

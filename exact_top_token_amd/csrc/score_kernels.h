@@ -382,18 +382,18 @@ struct Scorer {
       bool v = own;
       if constexpr (CHECK) {
         v = v && kvalid[b] && key[b] <= pos0 + q_i && q_i < nq;
-        n_scored += __popcll(__ballot(v));
+        n_scored += __popcll(ballot(v));
       }
       take[b] = v && sc[b] >= theta;
       anyt = anyt || take[b];
     }
     if constexpr (!CHECK) n_scored += 64u * (uint32_t)nq;
-    if (__ballot(anyt) == 0ull) return;
+    if (ballot(anyt) == 0ull) return;
     dirty = true;
     uint32_t so[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) so[b] = f2ord(sc[b]);
-    if (__any(hbase == 0)) {
+    if (ballot(hbase == 0) != 0ull) {
       // anchor each query's histogram below the maximum of the first scores
       // it takes (all lanes take part in the exchanges; only unanchored
       // queries update)
@@ -412,7 +412,7 @@ struct Scorer {
     const uint32_t below = (1u << c) - 1u;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const u64 m = __ballot(take[b]);
+      const u64 m = ballot(take[b]);
       if (m == 0ull) continue;
       if (take[b] && hbase != 0 && so[b] >= hbase)
         atomicAdd(&hq[min((so[b] - hbase) >> kHistShift, (uint32_t)(kHistBins - 1))], 1u);
@@ -422,7 +422,7 @@ struct Scorer {
       n_written += __popcll(m);
     }
     const uint32_t hi_water = (uint32_t)(p.cb.cap - 64);
-    if (__any(count > hi_water)) {
+    if (ballot(count > hi_water) != 0ull) {
       refresh_theta(p.topk);
 #pragma unroll 1
       for (int qq = 0; qq < QW; ++qq)
@@ -656,6 +656,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     const int kb = hi - TK * ((ra ? t : t - na) + 1);
     float o[TS][4];
     if (active) {
+      // one fresh lane id for every fragment address of the tile: the blocks'
+      // LDS reads then differ by immediate offsets only
+      const int ln = lane_fresh();
+      const int fcol = ln & 15, fg = ln >> 4;
 #pragma unroll
       for (int hh = 0; hh < TS; ++hh) {
 #pragma unroll
@@ -663,7 +667,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
           typename O::frag B[NBK][SC::STEPS];
 #pragma unroll
           for (int b = 0; b < NBK; ++b)
-            O::load_k(&ktile[bufi][(kTileKeys * hh + (NBK * hb + b) * 16 + sc.col()) * ROW], sc.g(), B[b]);
+            O::load_k(&ktile[bufi][(kTileKeys * hh + (NBK * hb + b) * 16 + fcol) * ROW], fg, B[b]);
           // all blocks' fragments in flight together: one LDS wait, not one per block
 #pragma unroll
           for (int b = 0; b < NBK; ++b)
