@@ -27,6 +27,7 @@ DOSA_NO_PRUNE = 0x1
 DOSA_SORTED = 0x2
 DOSA_SEPARABLE_RHO = 0x4
 DOSA_NO_NEGATIVE = 0x8
+DOSA_NO_PROBE = 0x10
 
 STATUS = {0: "DOSA_OK", -1: "DOSA_ERR_INVALID_ARG", -2: "DOSA_ERR_UNSUPPORTED", -3: "DOSA_ERR_WORKSPACE",
           -4: "DOSA_ERR_HIP"}
@@ -51,7 +52,8 @@ class DosaConfig(ctypes.Structure):
 class DosaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "pairs_total", "pairs_seed", "pairs_bounded", "pairs_survived", "pairs_scored",
-        "candidates_written", "reselects", "groups_skipped", "pairs_scored_list", "keys_streamed")]
+        "candidates_written", "reselects", "groups_skipped", "pairs_scored_list", "keys_streamed",
+        "calls_unpruned")]
 
 
 STAT_FIELDS = [f[0] for f in DosaStats._fields_]

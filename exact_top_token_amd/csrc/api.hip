@@ -22,10 +22,10 @@ thread_local std::string g_err;
 // optional per-pass event timing
 // ---------------------------------------------------------------------------
 enum PassId { P_NORMS = 0, P_SCORE_SEED, P_SELECT_SEED, P_PLAN, P_BOUND, P_COMPACT, P_SURV_TILES, P_SURV_LISTS,
-              P_SCORE_DENSE, P_SELECT_FINAL, P_PREP, P_COUNT };
+              P_SCORE_DENSE, P_SELECT_FINAL, P_PREP, P_PROBE, P_COUNT };
 const char* const kPassNames[P_COUNT] = {"key_norms", "score_seed", "select_seed", "plan", "bound", "compact",
                                          "score_survivor_tiles", "score_survivor_lists", "score_dense",
-                                         "select_final", "prep"};
+                                         "select_final", "prep", "probe"};
 
 struct Profiler {
   bool on = false;
@@ -84,7 +84,9 @@ struct Plan {
   int64_t total_q = 0, total_k = 0;
   std::vector<GroupInfo> groups;
   std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed, tiled-survivor, list-survivor items
-  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items;
+  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items, probe_items;
+  bool probe = false;                // DoSA: plan the last tile first, score densely if it cannot prune
+  int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0, Jp = 0;
   bool tiled = true;
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
@@ -93,7 +95,7 @@ struct Plan {
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0,
-         o_lrows = 0, o_lsig = 0, o_lerr = 0, total = 0;
+         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -205,27 +207,31 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     lo = lo_all + (int)((len * r / J) / align * align);
     hi = (r == J - 1) ? hi_all : lo_all + (int)((len * (r + 1) / J) / align * align);
   };
+  // dense scoring of whole tiles: J key ranges per tile, regions 0..J-1
+  auto dense_tiled_items = [&](std::vector<WorkItem>& out) {
+    const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(NT, avg_keys, tiled_target, 1024);
+    for (const auto& t : tiles)
+      for (int r = 0; r < J; ++r) {
+        int lo, hi;
+        range_split(0, t.n_last, r, J, 64, lo, hi);
+        WorkItem it{};
+        it.group = t.first;
+        it.pad = t.n;
+        it.region = r;
+        if (lo == 0) {
+          it.a0 = 0; it.a1 = std::min(64, hi);   // the attention-sink tile first, then newest to oldest
+          it.b0 = it.a1; it.b1 = hi;
+        } else {
+          it.a0 = it.a1 = lo;
+          it.b0 = lo; it.b1 = hi;
+        }
+        out.push_back(it);
+      }
+    return J;
+  };
   if (dense) {
     if (P.tiled) {
-      int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(NT, avg_keys, tiled_target, 1024);
-      P.J = J;
-      for (const auto& t : tiles)
-        for (int r = 0; r < J; ++r) {
-          int lo, hi;
-          range_split(0, t.n_last, r, J, 64, lo, hi);
-          WorkItem it{};
-          it.group = t.first;
-          it.pad = t.n;
-          it.region = r;
-          if (lo == 0) {
-            it.a0 = 0; it.a1 = std::min(64, hi);   // the attention-sink tile first, then newest to oldest
-            it.b0 = it.a1; it.b1 = hi;
-          } else {
-            it.a0 = it.a1 = lo;
-            it.b0 = lo; it.b1 = hi;
-          }
-          P.items.push_back(it);
-        }
+      P.J = dense_tiled_items(P.items);
     } else {
       int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
       P.J = J;
@@ -351,9 +357,41 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         }
       }
     }
+    // probe: with enough tiles, the last tile (longest contexts) is seeded and
+    // planned first; if its certificate can prune no query, the call scores
+    // every tile densely with the dense path's items (regions 0..Jd-1)
+    if (P.tiled && NT >= 8 && (cfg.flags & DOSA_NO_PROBE) == 0) {
+      P.probe = true;
+      const TileInfo& t = tiles.back();
+      P.probe_group = t.first;
+      P.probe_ngroups = t.n;
+      P.probe_q0 = P.groups[t.first].q_row0;
+      P.probe_nq = 0;
+      for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
+      // the probe tile's seed window in shares of at least 256 keys (up to 16
+      // workgroups): on its own the tile would be scored by one workgroup
+      const int wlo = std::max(0, t.n_last - P.W);
+      const int f = std::min(P.F, wlo);
+      P.Jp = (int)std::max<int64_t>(1, std::min<int64_t>(16, (t.n_last - wlo) / 256));
+      for (int r = 0; r < P.Jp; ++r) {
+        int lo, hi;
+        range_split(wlo, t.n_last, r, P.Jp, 64, lo, hi);
+        WorkItem it{};
+        it.group = t.first;
+        it.pad = t.n;
+        it.region = r;
+        it.a0 = 0; it.a1 = (r == 0) ? f : 0;
+        it.b0 = lo; it.b1 = hi;
+        P.probe_items.push_back(it);
+      }
+      P.Jd = dense_tiled_items(P.dense_items);
+      P.R = std::max(P.R, std::max(P.Jd, P.Jp));
+    }
     P.items.insert(P.items.end(), P.surv_tiled_items.begin(), P.surv_tiled_items.end());
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
     P.items.insert(P.items.end(), P.bound_items.begin(), P.bound_items.end());
+    P.items.insert(P.items.end(), P.dense_items.begin(), P.dense_items.end());
+    P.items.insert(P.items.end(), P.probe_items.begin(), P.probe_items.end());
     P.list_total = loff;
     P.mask_words = (max_bounded + 63) / 64;
     int64_t bsum = 0;
@@ -400,6 +438,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
     P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
+    P.o_mode = take(sizeof(int32_t));
   }
   P.total = o;
 }
@@ -571,7 +610,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
                      stream);
   if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(items)");
   if (st) {
-    unsigned long long add[10] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned long long add[11] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     e = launch_stats_add(st, add, stream);
     if (e != hipSuccess) return fail_hip(e, "stats");
   }
@@ -631,8 +670,60 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_key_norms(P.combo, d, nl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
+    const size_t off_surv = P.seed_items.size(), off_list = off_surv + P.surv_tiled_items.size(),
+                 off_bound = off_list + P.surv_list_items.size(), off_dense = off_bound + P.bound_items.size(),
+                 off_probe = off_dense + P.dense_items.size();
+    int32_t* mode = P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr;
+    // 1b. probe: seed pass, threshold and plan of the last tile only, then the
+    //     decision whether the call runs the certificate pipeline or dense scoring
+    if (P.probe) {
+      PassScope ps(P_PROBE, stream);
+      ScoreLaunch pb{};
+      pb.in = in;
+      pb.lrows = pr.rows;
+      pb.lsig = pr.sig;
+      pb.groups = dg;
+      pb.items = di + off_probe;
+      pb.n_items = P.Jp;
+      pb.cb = cb;
+      pb.topk = topk;
+      pb.scored_slot = 1;
+      pb.tiled = 1;
+      pb.role = ROLE_SEED;
+      e = launch_score(P.combo, H, d, pb, stream);
+      if (e != hipSuccess) return fail_hip(e, "probe seed kernel launch");
+      SelectLaunch pt{};
+      pt.cb = cb;
+      pt.q_first = P.probe_q0;
+      pt.total_q = P.probe_nq;
+      pt.topk = topk;
+      pt.r0 = 0;
+      pt.r1 = P.Jp;
+      pt.tau_out = tau;
+      e = launch_select(pt, stream);
+      if (e != hipSuccess) return fail_hip(e, "probe select kernel launch");
+      PlanLaunch pp{};
+      pp.in = in;
+      pp.groups = dg + P.probe_group;
+      pp.n_groups = P.probe_ngroups;
+      pp.num_proxies = cfg.num_proxies;
+      pp.seed_window = P.W;
+      pp.neg_frac = cfg.neg_support_frac;
+      pp.flags = cfg.flags;
+      pp.tau = tau;
+      pp.lerr = pr.err;
+      pp.norms = norms;
+      pp.rows = ws + P.o_rows;
+      pp.coef = coef;
+      e = launch_plan(P.combo, H, d, pp, stream);
+      if (e != hipSuccess) return fail_hip(e, "probe plan kernel launch");
+      e = launch_probe_decide(coef, P.probe_q0, P.probe_nq, mode, st, stream);
+      if (e != hipSuccess) return fail_hip(e, "probe decision kernel launch");
+    }
     // 2. seed pass: exact scores of the seed keys into regions 0..Js-1
     ScoreLaunch sl{};
+    sl.mode = mode;
+    sl.run_if = MODE_PRUNED;
     sl.in = in;
     sl.lrows = pr.rows;
     sl.lsig = pr.sig;
@@ -652,6 +743,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "seed score kernel launch");
     // 3. tau = K-th largest seed score
     SelectLaunch ts{};
+    ts.mode = mode;
+    ts.run_if = MODE_PRUNED;
     ts.cb = cb;
     ts.total_q = (int32_t)P.total_q;
     ts.topk = topk;
@@ -665,6 +758,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "seed select kernel launch");
     // 4. certificate plan per query
     PlanLaunch pl{};
+    pl.mode = mode;
+    pl.run_if = MODE_PRUNED;
     pl.in = in;
     pl.groups = dg;
     pl.n_groups = G;
@@ -684,6 +779,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "plan kernel launch");
     // 5. bound pass -> survivor bitmasks
     BoundLaunch bl{};
+    bl.mode = mode;
+    bl.run_if = MODE_PRUNED;
     bl.in = in;
     bl.groups = dg;
     bl.n_groups = G;
@@ -696,7 +793,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.debug_ld = max_kv;
     bl.splits = P.bound_splits;
     if (!P.bound_items.empty()) {
-      bl.items = di + P.seed_items.size() + P.surv_tiled_items.size() + P.surv_list_items.size();
+      bl.items = di + off_bound;
       bl.n_items = (int)P.bound_items.size();
     }
     bl.stats = st;
@@ -706,7 +803,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
     // 6. compaction -> survivor key lists
-    CompactLaunch cl{dg, G, coef, masks, std::max(P.mask_words, 1), lists, list_len, gflags};
+    CompactLaunch cl{dg, G, coef, masks, std::max(P.mask_words, 1), lists, list_len, gflags, mode, MODE_PRUNED};
     {
       PassScope ps(P_COMPACT, stream);
       e = launch_compact(cl, stream);
@@ -716,6 +813,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     //    tiles whose certificate prunes nothing take the tiled kernel over the
     //    bounded range, the other groups walk their compacted lists
     ScoreLaunch ml{};
+    ml.mode = mode;
+    ml.run_if = MODE_PRUNED;
     ml.in = in;
     ml.lrows = pr.rows;
     ml.lsig = pr.sig;
@@ -731,7 +830,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ml.role = ROLE_SURVIVORS;
     {
       PassScope ps(P_SURV_TILES, stream);
-      ml.items = di + P.seed_items.size();
+      ml.items = di + off_surv;
       ml.n_items = (int)P.surv_tiled_items.size();
       ml.tiled = P.tiled ? 1 : 0;
       ml.flag_mode = 1;
@@ -739,7 +838,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     if (e == hipSuccess) {
       PassScope ps(P_SURV_LISTS, stream);
-      ml.items = di + P.seed_items.size() + P.surv_tiled_items.size();
+      ml.items = di + off_list;
       ml.n_items = (int)P.surv_list_items.size();
       ml.tiled = 0;
       ml.flag_mode = 2;
@@ -747,16 +846,41 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_score(P.combo, H, d, ml, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
+    // 8. the dense alternative, run only when the probe found nothing to prune
+    if (P.probe) {
+      ScoreLaunch dl{};
+      dl.mode = mode;
+      dl.run_if = MODE_UNPRUNED;
+      dl.in = in;
+      dl.lrows = pr.rows;
+      dl.lsig = pr.sig;
+      dl.groups = dg;
+      dl.items = di + off_dense;
+      dl.n_items = (int)P.dense_items.size();
+      dl.cb = cb;
+      dl.theta_init = nullptr;
+      dl.topk = topk;
+      dl.stats = st;
+      dl.scored_slot = 4;
+      dl.tiled = 1;
+      dl.role = ROLE_DENSE;
+      PassScope ps(P_SCORE_DENSE, stream);
+      e = launch_score(P.combo, H, d, dl, stream);
+      if (e != hipSuccess) return fail_hip(e, "dense score kernel launch");
+    }
   }
   SelectLaunch se{};
   se.cb = cb;
   se.total_q = (int32_t)P.total_q;
   se.topk = topk;
   se.r0 = 0;
-  se.r1 = P.R;
+  se.r1 = dense ? P.R : P.Js + P.J;   // pruned path: seed then survivor regions
   se.out_idx = out_idx;
   se.out_score = out_score;
   se.tau_out = nullptr;
+  se.r1_unpruned = P.probe ? P.Jd : P.R;
+  se.mode = dense ? nullptr : (P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr);
+  se.run_if = -1;
   se.sorted = (cfg.flags & DOSA_SORTED) ? 1 : 0;
   se.stats = st;
   {

@@ -13,6 +13,16 @@ enum Combo : int { C_F32 = 0, C_BF16 = 1, C_FP8 = 2, C_BF16Q_FP8K = 3 };
 // Which pass a scoring launch belongs to (selects a kernel of its own name).
 enum Role : int { ROLE_DENSE = 0, ROLE_SEED = 1, ROLE_SURVIVORS = 2 };
 
+// How a pruned-path call proceeds once its probe tile has been planned: the
+// certificate pipeline, or dense scoring of every key when the certificate
+// cannot prune any query of the probe tile.  Launches carry a mode pointer
+// and the mode they run in; the others return at once.
+enum DosaMode : int { MODE_PRUNED = 0, MODE_UNPRUNED = 1 };
+
+__device__ __forceinline__ bool skip_launch(const int32_t* mode, int32_t run_if) {
+  return mode != nullptr && run_if >= 0 && *mode != run_if;
+}
+
 constexpr int kTileWaves = 8;   // wavefronts (query groups) per tiled scoring workgroup
 
 // A query group: up to 4 consecutive queries of one sequence, scored together
@@ -96,7 +106,9 @@ struct ScoreLaunch {
   const int32_t* tile_flags; // per group: 1 if the certificate prunes nothing in its tile (or NULL)
   int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not
   int32_t role;              // Role
-  unsigned long long* stats; // dosa_stats as u64[10] or NULL
+  unsigned long long* stats; // dosa_stats as u64[11] or NULL
+  const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
+  int32_t run_if;
 };
 
 struct SelectLaunch {
@@ -109,6 +121,10 @@ struct SelectLaunch {
   float* tau_out;            // K-th score per query (-inf if fewer than K), or NULL
   int32_t sorted;
   unsigned long long* stats;
+  int32_t q_first;           // rows q_first .. q_first + total_q - 1
+  int32_t r1_unpruned;       // regions merged instead of [r0, r1) when *mode == MODE_UNPRUNED
+  const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
+  int32_t run_if;
 };
 
 // Certificate plan: per query 4 operand rows of d elements in the query
@@ -133,6 +149,8 @@ struct PlanLaunch {
   const float* norms;        // per logical key (as BoundLaunch::norms)
   void* rows;                // [total_q, 4, d] query storage type
   float* coef;               // [total_q, 8]
+  const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
+  int32_t run_if;
 };
 
 struct BoundLaunch {
@@ -151,6 +169,8 @@ struct BoundLaunch {
                              // pad = groups, [a0, a1) keys, b0 = share index; NULL = per-group kernel
   int32_t n_items;
   unsigned long long* stats;
+  const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
+  int32_t run_if;
 };
 
 struct CompactLaunch {
@@ -162,6 +182,8 @@ struct CompactLaunch {
   int32_t* lists;
   int32_t* list_len;
   int32_t* group_flags;      // out: 1 if the group's tile is scored over its whole bounded range
+  const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
+  int32_t run_if;
 };
 
 struct NormLaunch {
@@ -182,6 +204,8 @@ hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t
 hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* host_vals, hipStream_t s);
+hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
+                               unsigned long long* stats, hipStream_t s);
 
 bool combo_supported(int combo, int H, int d);
 int tile_waves();

@@ -244,6 +244,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   constexpr int NKV = (kSampleKeys * CPK + 255) / 256;
   constexpr int KRS = D * KBY + 16;                 // LDS row stride of staged keys (bytes)
   static_assert(H <= 64 && 256 % H == 0 && D % PARTS == 0, "plan layout");
+  if (skip_launch(p.mode, p.run_if)) return;
   const GroupInfo gr = p.groups[blockIdx.x];
   const int slot = blockIdx.y;
   if (slot >= gr.nq) return;
@@ -672,6 +673,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
   using O = Ops<C, D>;
   constexpr int STEPS = O::STEPS;
   constexpr int KBYTES = D * O::KB;
+  if (skip_launch(p.mode, p.run_if)) return;
   const int lane = lane_id();
   const int gi = blockIdx.x / p.splits, sp = blockIdx.x % p.splits;
   const GroupInfo gr = p.groups[gi];
@@ -788,6 +790,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   constexpr int NCH = (64 * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][64 * ROW];
   __shared__ float kinfo[2][2][64];                  // [buffer][scale, norm][key]
+  if (skip_launch(p.mode, p.run_if)) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;
   const int lane = lane_id();
   const WorkItem it = p.items[blockIdx.x];
@@ -930,6 +933,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
 constexpr float kDenseFrac = 0.4f;
 
 __global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
+  if (skip_launch(p.mode, p.run_if)) return;
   const int gi0 = blockIdx.x;
   const GroupInfo head = p.groups[gi0];
   if (head.tile_first != gi0) return;          // one workgroup per tile
@@ -1007,9 +1011,31 @@ __global__ void stats_add_kernel(unsigned long long* st, const dosa_stats add) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// The pruned path's decision after planning its probe tile (the call's last
+// query tile, its longest contexts): if the certificate cannot prune a single
+// query there, the call scores every key densely instead.  Exactness does not
+// depend on it; only which kernels do the work.
+__global__ void probe_decide_kernel(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
+                                    unsigned long long* stats) {
+  const int lane = lane_id();
+  bool prunes = false;
+  for (int i = lane; i < nq; i += 64) prunes = prunes || coef[(int64_t)(q0 + i) * 8 + 7] == 0.f;
+  const bool any = __ballot(prunes) != 0ull;
+  if (lane == 0) {
+    *mode = any ? MODE_PRUNED : MODE_UNPRUNED;
+    if (!any && stats != nullptr) atomicAdd(&stats[10], 1ull);
+  }
+}
+
+hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
+                               unsigned long long* stats, hipStream_t s) {
+  hipLaunchKernelGGL(probe_decide_kernel, dim3(1), dim3(64), 0, s, coef, q0, nq, mode, stats);
+  return hipGetLastError();
+}
+
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* v, hipStream_t s) {
   dosa_stats a;
-  static_assert(sizeof(dosa_stats) == 10 * sizeof(unsigned long long), "stats layout");
+  static_assert(sizeof(dosa_stats) == 11 * sizeof(unsigned long long), "stats layout");
   memcpy(&a, v, sizeof(a));
   hipLaunchKernelGGL(stats_add_kernel, dim3(1), dim3(64), 0, s, stats, a);
   return hipGetLastError();

@@ -469,6 +469,7 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
   __shared__ uint32_t hist[256];
   __shared__ __attribute__((aligned(16))) float wl[SC::QW * (H + SC::S)];
   __shared__ uint32_t qhist[SC::QW * kHistBins];
+  if (skip_launch(p.mode, p.run_if)) return;
   const WorkItem it = p.items[blockIdx.x];
   const GroupInfo gr = p.groups[it.group];
   if (p.flag_mode != 0) {
@@ -569,6 +570,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   __shared__ uint32_t hist[kTileWaves][256];
   __shared__ uint32_t qhist[kTileWaves][SC::QW * kHistBins];
 
+  if (skip_launch(p.mode, p.run_if)) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;   // wavefront-uniform
   const WorkItem it = p.items[blockIdx.x];
   const int ngroups = it.pad;                        // query groups in this tile

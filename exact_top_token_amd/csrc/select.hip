@@ -9,12 +9,13 @@ namespace dosa {
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
-  const int q = blockIdx.x;
+  if (skip_launch(p.mode, p.run_if)) return;
+  const int q = p.q_first + blockIdx.x;
   const int lane = lane_id();
   const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
   const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
   const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
-  const int nseg = p.r1 - p.r0;
+  const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
   uint32_t total = 0;
   for (int r = 0; r < nseg; ++r) total += cnt[r];
   Segs sg{base, cnt, cap, nseg};
@@ -74,12 +75,13 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
 __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
   __shared__ u64 keys[4096];
-  const int q = blockIdx.x;
+  if (skip_launch(p.mode, p.run_if)) return;
+  const int q = p.q_first + blockIdx.x;
   const int lane = lane_id();
   const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
   const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
   const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
-  const int nseg = p.r1 - p.r0;
+  const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
   uint32_t total = 0;
   for (int r = 0; r < nseg; ++r) total += cnt[r];
   Segs sg{base, cnt, cap, nseg};

@@ -94,6 +94,10 @@ typedef enum {
 #define DOSA_SORTED 0x2u          /* rows of out_idx in (score desc, position asc) order */
 #define DOSA_SEPARABLE_RHO 0x4u   /* residual bound sum_h w_h ||r_h|| instead of the joint bound */
 #define DOSA_NO_NEGATIVE 0x8u     /* drop the negative-head aggregate from the bound */
+#define DOSA_NO_PROBE 0x10u       /* dosa_indexer_topk: no probe tile, always the certificate pipeline
+                                     (by default a call with >= 8 query tiles first seeds and plans
+                                     its last tile and, if the certificate prunes no query there,
+                                     scores every key densely; the result is the same either way) */
 
 /* Knobs of dosa_indexer_topk.  None of them changes the selected set; they
  * only change how much work the certificate saves. */
@@ -127,6 +131,8 @@ typedef struct {
   uint64_t pairs_scored_list;  /* the part of pairs_scored scored from compacted survivor lists */
   uint64_t keys_streamed;      /* key rows the bound pass read (once per query tile or group that
                                   streamed them; skipped groups read none) */
+  uint64_t calls_unpruned;     /* dosa_indexer_topk calls scored densely: the certificate could
+                                  prune no query of the call's probe tile (its last query tile) */
 } dosa_stats;
 
 /* Fill *cfg with the defaults for a given topk. */

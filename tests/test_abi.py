@@ -34,7 +34,7 @@ def test_default_config_values():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(E.DosaStats) == 80
+    assert ctypes.sizeof(E.DosaStats) == 88
     assert ctypes.sizeof(E.DosaConfig) == 40
 
 

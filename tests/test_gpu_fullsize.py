@@ -15,7 +15,7 @@ from parity_helpers import check_vs_oracle
 pytestmark = pytest.mark.gpu
 
 
-def _run_calls(wl, inp, path):
+def _run_calls(wl, inp, path, flags=0):
     import torch
 
     import exact_top_token_amd as E
@@ -25,6 +25,7 @@ def _run_calls(wl, inp, path):
              if wl.chunk else [(0, inp)])
     K = wl.topk
     cfg = E.default_config(K)
+    cfg.flags |= flags
     ws = torch.empty(max(E.workspace_size(c.q_lens, c.kv_lens, c.H, c.d, K, c.q_dtype, c.k_dtype,
                                           c.page_table is not None, path == "dsa", cfg) for _, c in calls),
                      dtype=torch.uint8, device="cuda")
@@ -73,11 +74,20 @@ def _check(wl, n_random):
     print(f"[gpu] full size {wl.name}: q={wl.total_q} H={wl.H} d={wl.d} K={wl.topk} "
           f"{wl.q_dtype}/{wl.k_dtype} pairs={wl.pairs()}", flush=True)
     inp = to_device(wl)
+    import exact_top_token_amd as E
+
     di, ds, dst = _run_calls(wl, inp, "dsa")
-    pi, ps, pst = _run_calls(wl, inp, "dosa")
+    # the certificate pipeline on every call
+    pi, ps, pst = _run_calls(wl, inp, "dosa", E.DOSA_NO_PROBE)
     assert dst["pairs_total"] == wl.pairs() == pst["pairs_total"]
-    assert pst["pairs_seed"] + pst["pairs_bounded"] == wl.pairs()
+    assert pst["pairs_seed"] + pst["pairs_bounded"] == wl.pairs() and pst["calls_unpruned"] == 0
     _same_on_device(pi, ps, di, ds)
+    del pi, ps
+    # the default: calls whose probe tile cannot prune score densely
+    pi, ps, pst2 = _run_calls(wl, inp, "dosa")
+    _same_on_device(pi, ps, di, ds)
+    del pi, ps
+    print(f"[gpu] {wl.name}: calls scored densely after the probe: {pst2['calls_unpruned']}", flush=True)
     rows = _rows(wl, n_random)
     print(f"[gpu] oracle rows {rows.tolist()}", flush=True)
     ri = di[rows].cpu().numpy()

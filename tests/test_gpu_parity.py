@@ -29,15 +29,31 @@ def _both(wl, rows=None, cfg=None, **kw):
 
 
 def test_tiny_prefill_all_rows():
+    import exact_top_token_amd as E
+
     wl = synth.tiny_prefill()
-    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=np.arange(wl.total_q))
+    cfg = E.default_config(wl.topk)
+    cfg.flags |= E.DOSA_NO_PROBE
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=np.arange(wl.total_q), cfg=cfg)
     assert dst["pairs_total"] == wl.pairs() == dst["pairs_scored"]
     assert pst["pairs_seed"] + pst["pairs_bounded"] == wl.pairs()
+    pi2, ps2, _ = _run(wl, "dosa")   # with the probe tile (default)
+    assert_same_selection(pi2, ps2, di, ds)
 
 
 def test_structured_bf16_4k():
+    import exact_top_token_amd as E
+
     wl = synth.dsa_prefill_32k(L=4096)
-    _both(wl, rows=sample_rows(wl, 40))
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 40))
+    # the certificate cannot prune this recipe: the probe tile sends the call to dense scoring
+    assert pst["calls_unpruned"] == 1 and pst["pairs_bounded"] == 0 and pst["pairs_scored"] == wl.pairs()
+    # without the probe the whole certificate pipeline runs, with the same result
+    cfg = E.default_config(wl.topk)
+    cfg.flags |= E.DOSA_NO_PROBE
+    pi2, ps2, pst2 = _run(wl, "dosa", cfg=cfg)
+    assert_same_selection(pi2, ps2, di, ds)
+    assert pst2["calls_unpruned"] == 0 and pst2["pairs_seed"] + pst2["pairs_bounded"] == wl.pairs()
 
 
 def test_fp8_chunked_prefill():
@@ -45,21 +61,27 @@ def test_fp8_chunked_prefill():
 
     from exact_top_token_amd.runner import Runner, slice_chunk, to_device
 
+    import exact_top_token_amd as E
+
     wl = synth.long_prefill_128k(L=8192, chunk=4096)
     inp = to_device(wl)
     outs = {}
-    for path in ("dsa", "dosa"):
+    for path in ("dsa", "dosa", "dosa_no_probe"):
         idx = np.zeros((wl.total_q, wl.topk), np.int32)
         sc = np.zeros((wl.total_q, wl.topk), np.float32)
+        cfg = E.default_config(wl.topk)
+        if path == "dosa_no_probe":
+            cfg.flags |= E.DOSA_NO_PROBE
         for c in wl.chunk_calls():
             print(f"[gpu] fp8 chunk {c} {path}", flush=True)
-            r = Runner(slice_chunk(inp, c["q0"], c["q_len"], c["kv_len"]), path)
+            r = Runner(slice_chunk(inp, c["q0"], c["q_len"], c["kv_len"]), path[:4], cfg)
             a, b = r()
             torch.cuda.synchronize()
             idx[c["q0"]:c["q0"] + c["q_len"]] = a.cpu().numpy()
             sc[c["q0"]:c["q0"] + c["q_len"]] = b.cpu().numpy()
         outs[path] = (idx, sc)
     assert_same_selection(*outs["dosa"], *outs["dsa"])
+    assert_same_selection(*outs["dosa_no_probe"], *outs["dsa"])
     check_vs_oracle(wl, *outs["dsa"], sample_rows(wl, 24))
 
 
@@ -90,13 +112,13 @@ def test_correlated_heads_prunes_and_matches():
     cfg = E.default_config(wl.topk)
     cfg.seed_window = 2048
     (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 24), cfg=cfg)
-    assert pst["pairs_bounded"] > 0
+    assert pst["pairs_bounded"] > 0 and pst["calls_unpruned"] == 0, "the probe tile should keep the pipeline"
     print("correlated stats", pst, flush=True)
     assert pst["pairs_survived"] < pst["pairs_bounded"], "certificate pruned nothing on the correlated recipe"
 
 
 @pytest.mark.parametrize("knob", ["p0", "p1", "p2", "w64", "w512", "cap", "noprune", "separable", "noneg",
-                                  "splits3", "frac0", "frac1"])
+                                  "splits3", "frac0", "frac1", "probe"])
 def test_knob_invariance(knob):
     import exact_top_token_amd as E
     from exact_top_token_amd.runner import run_once
@@ -105,8 +127,11 @@ def test_knob_invariance(knob):
     di, ds, _ = run_once(wl, "dsa")
     cfg = E.default_config(wl.topk)
     cfg.seed_window = 512
+    cfg.flags |= E.DOSA_NO_PROBE     # every knob exercises the certificate pipeline itself
     ks = 0
-    if knob.startswith("p"):
+    if knob == "probe":
+        cfg.flags &= ~E.DOSA_NO_PROBE
+    elif knob.startswith("p"):
         cfg.num_proxies = int(knob[1])
     elif knob == "w64":
         cfg.seed_window = 64
@@ -148,9 +173,13 @@ def test_dense_small_buffer_and_splits():
 
 
 def test_determinism_and_sorted_rows():
+    import exact_top_token_amd as E
+
     wl = synth.dsa_prefill_32k(L=2500, topk=256)
-    a = _run(wl, "dosa")
-    b = _run(wl, "dosa")
+    cfg = E.default_config(wl.topk)
+    cfg.flags |= E.DOSA_NO_PROBE
+    a = _run(wl, "dosa", cfg=cfg)
+    b = _run(wl, "dosa", cfg=cfg)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
     c = _run(wl, "dsa", sorted_rows=True)
     assert_same_selection(c[0], c[1], a[0], a[1])
