@@ -700,7 +700,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       pt.r0 = 0;
       pt.r1 = P.Jp;
       pt.tau_out = tau;
-      e = launch_select(pt, stream);
+      e = launch_select_tau(pt, stream);
       if (e != hipSuccess) return fail_hip(e, "probe select kernel launch");
       PlanLaunch pp{};
       pp.in = in;

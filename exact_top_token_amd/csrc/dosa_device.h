@@ -233,11 +233,15 @@ struct Segs {
 };
 
 // K-th largest of the (distinct) entries of the segments, K >= 1 and
-// K <= total.  Radix select on 11/11/10-bit digits from the top; stops as soon
-// as the digit bin holding the K-th entry is taken whole.  Returns T with
-// exactly K entries >= T.  hist: 2048 u32 of LDS.
-__device__ __noinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) {
+// K <= total, by a workgroup of NT threads.  Radix select on 11/11/10-bit
+// digits from the top; stops as soon as the digit bin holding the K-th entry
+// is taken whole.  Returns T with exactly K entries >= T (the same value in
+// every wavefront: each reads the shared histogram and decides alike).
+// hist: 2048 u32 of LDS.
+template <int NT>
+__device__ __noinline__ u64 select_kth_nt(const Segs sg, int K, uint32_t* hist) {
   const int lane = lane_id();
+  const int tid = (int)threadIdx.x;
   u64 prefix = 0;
   uint32_t rem = (uint32_t)K;
   __syncthreads();
@@ -247,22 +251,22 @@ __device__ __noinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) {
     const int wd = (p == 2 || p == 5) ? 10 : 11;
     const int nb = 1 << wd;
     const int hs = sh + wd;
-    for (int b = lane; b < nb; b += 64) hist[b] = 0;
+    for (int b = tid; b < nb; b += NT) hist[b] = 0;
     __syncthreads();
     const u64 want = (p == 0) ? 0 : (prefix >> hs);
     for (int r = 0; r < sg.nseg; ++r) {
       const u64* ptr = sg.ptr(r);
       const uint32_t n = sg.n(r);
-      for (uint32_t b = 0; b < n; b += 64 * kBatch) {
+      for (uint32_t b = 0; b < n; b += NT * kBatch) {
         u64 e[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {     // all loads of the batch in flight together
-          const uint32_t i = b + 64u * u + lane;
+          const uint32_t i = b + (uint32_t)NT * u + tid;
           e[u] = (i < n) ? ptr[i] : 0ull;
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-          const uint32_t i = b + 64u * u + lane;
+          const uint32_t i = b + (uint32_t)NT * u + tid;
           if (i < n && (p == 0 || (e[u] >> hs) == want))
             atomicAdd(&hist[(uint32_t)(e[u] >> sh) & (uint32_t)(nb - 1)], 1u);
         }
@@ -291,6 +295,8 @@ __device__ __noinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) {
   }
   return prefix;
 }
+
+__device__ __forceinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) { return select_kth_nt<64>(sg, K, hist); }
 
 // Copy the entries >= T of src[0..n) to dst[out..] in order (dst may equal
 // src, with out <= 0 then).  Returns the new end.  Entries are read kBatch

@@ -199,6 +199,7 @@ struct NormLaunch {
 hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s);
 hipError_t launch_prep(int combo, int H, int d, const PrepLaunch& p, hipStream_t s);
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
+hipError_t launch_select_tau(const SelectLaunch& p, hipStream_t s);
 hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s);
 hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t s);
 hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream_t s);

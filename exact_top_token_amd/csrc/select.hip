@@ -70,6 +70,25 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   }
 }
 
+// Threshold only: tau_out = the K-th largest entry's score over regions
+// [r0, r1) (-inf if fewer than K), by 4 wavefronts per query and without
+// touching the regions.  For small launches whose time is one query's latency.
+__global__ __launch_bounds__(256) void select_tau_kernel(const SelectLaunch p) {
+  __shared__ uint32_t hist[2048];
+  if (skip_launch(p.mode, p.run_if)) return;
+  const int q = p.q_first + blockIdx.x;
+  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
+  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
+  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
+  const int nseg = p.r1 - p.r0;
+  uint32_t total = 0;
+  for (int r = 0; r < nseg; ++r) total += cnt[r];
+  Segs sg{base, cnt, cap, nseg};
+  u64 T = 0;
+  if (total >= (uint32_t)K) T = select_kth_nt<256>(sg, K, hist);
+  if (threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
+}
+
 // Same merge, rows ordered by (score desc, position asc): the kept keys are
 // gathered into LDS and bitonic-sorted (K <= 4096 -> 32 KiB).
 __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p) {
@@ -154,6 +173,12 @@ hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream
     case C_BF16Q_FP8K: return launch_score_bf16fp8(H, d, p, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_select_tau(const SelectLaunch& p, hipStream_t s) {
+  if (p.total_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(select_tau_kernel, dim3(p.total_q), dim3(256), 0, s, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {
