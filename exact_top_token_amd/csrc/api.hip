@@ -94,7 +94,7 @@ struct Plan {
   int64_t list_total = 0;
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
-         o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0,
+         o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
          o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, total = 0;
   uint64_t pairs_total = 0;
 };
@@ -433,6 +433,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
     P.o_coef = take((size_t)P.total_q * 8 * sizeof(float));
     P.o_norms = take((size_t)std::max<int64_t>(P.total_k, 1) * sizeof(float));
+    P.o_flag = take(sizeof(int32_t));
     P.o_seqinfo = take((size_t)(batch + 1) * sizeof(int32_t));
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
@@ -616,7 +617,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   }
   Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages};
   PrepLaunch pr{q, w, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
-                reinterpret_cast<float*>(ws + P.o_lerr)};
+                reinterpret_cast<float*>(ws + P.o_lerr), dense ? nullptr : reinterpret_cast<int32_t*>(ws + P.o_flag)};
   {
     PassScope ps(P_PREP, stream);
     e = launch_prep(P.combo, H, d, pr, stream);
@@ -663,13 +664,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* lists = reinterpret_cast<int32_t*>(ws + P.o_lists);
     int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
     int32_t* gflags = reinterpret_cast<int32_t*>(ws + P.o_gflags);
-    // 1. per-key norms
-    NormLaunch nl{in, cu_dev, batch, P.total_k, max_kv, norms};
-    {
-      PassScope ps(P_NORMS, stream);
-      e = launch_key_norms(P.combo, d, nl, stream);
-    }
-    if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
+    int32_t* prunes = reinterpret_cast<int32_t*>(ws + P.o_flag);   // cleared by the prep kernel
     const size_t off_surv = P.seed_items.size(), off_list = off_surv + P.surv_tiled_items.size(),
                  off_bound = off_list + P.surv_list_items.size(), off_dense = off_bound + P.bound_items.size(),
                  off_probe = off_dense + P.dense_items.size();
@@ -712,7 +707,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       pp.flags = cfg.flags;
       pp.tau = tau;
       pp.lerr = pr.err;
-      pp.norms = norms;
+      pp.prunes = prunes;
       pp.rows = ws + P.o_rows;
       pp.coef = coef;
       e = launch_plan(P.combo, H, d, pp, stream);
@@ -769,7 +764,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     pl.flags = cfg.flags;
     pl.tau = tau;
     pl.lerr = pr.err;
-    pl.norms = norms;
+    pl.prunes = prunes;
     pl.rows = ws + P.o_rows;
     pl.coef = coef;
     {
@@ -777,6 +772,14 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_plan(P.combo, H, d, pl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "plan kernel launch");
+    // 4b. per-key norms for the bound pass; the launch returns at once when the
+    //     plan found no query whose certificate can prune
+    NormLaunch nl{in, cu_dev, batch, P.total_k, max_kv, norms, cfg.debug_ub != nullptr ? nullptr : prunes};
+    {
+      PassScope ps(P_NORMS, stream);
+      e = launch_key_norms(P.combo, d, nl, stream);
+    }
+    if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
     // 5. bound pass -> survivor bitmasks
     BoundLaunch bl{};
     bl.mode = mode;

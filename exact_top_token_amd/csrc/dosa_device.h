@@ -219,6 +219,27 @@ __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   return v;
 }
 
+// Squared norm (of the stored values, before any per-key scale) of the key
+// in this lane's column, from the key block's MFMA fragments: B^T B of the 16
+// keys has their squared norms on its diagonal, and column c's entry is
+// element c%4 of lane 16*(c/4) + c.  Products of stored values are exact in
+// fp32 and every term is nonnegative, so the fp32 sum is within d*2^-24 of
+// the exact value.  All 64 lanes must take part (one lane exchange).
+template <class O>
+__device__ __forceinline__ float frag_norm2(const typename O::frag* B) {
+  v4f gm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < O::STEPS; ++s) gm = O::mma(B[s], B[s], gm);
+  const int l = lane_id(), c = l & 15, e = c & 3;
+  float dv = (e == 0) ? gm[0] : (e == 1) ? gm[1] : (e == 2) ? gm[2] : gm[3];
+  dv = ((l >> 4) == (c >> 2)) ? dv : 0.f;
+  return __shfl(dv, 16 * (c >> 2) + c, 64);
+}
+
+// Upper bound on ||k|| (stored values) from frag_norm2: sqrt, then rounded up
+// by 2^-16 relative, which covers the fp32 sum of d <= 128 squares and the sqrt.
+__device__ __forceinline__ float norm_up(float n2) { return sqrtf(n2) * 1.0000153f; }
+
 // Wavefront-rows of 64 candidates loaded together by the streaming loops.
 constexpr int kBatch = 8;
 

@@ -86,6 +86,7 @@ struct PrepLaunch {
   void* rows;
   float* sig;
   float* err;
+  int32_t* flag;        // cleared here (query 0): the plan's "some query can prune" flag, or NULL
 };
 
 struct ScoreLaunch {
@@ -146,9 +147,9 @@ struct PlanLaunch {
   uint32_t flags;
   const float* tau;          // [total_q]
   const float* lerr;         // [total_q, 2] weighted-query representation error and magnitude
-  const float* norms;        // per logical key (as BoundLaunch::norms)
   void* rows;                // [total_q, 4, d] query storage type
   float* coef;               // [total_q, 8]
+  int32_t* prunes;           // set to 1 when some query's certificate can prune (or NULL)
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;
 };
@@ -193,6 +194,7 @@ struct NormLaunch {
   int64_t total_k;
   int32_t max_kv;            // longest sequence
   float* norms;              // [total_k]
+  const int32_t* needed;     // NULL, or the plan's flag: 0 = no query can prune, nothing to do
 };
 
 // Launchers (return hipError_t of the launch).

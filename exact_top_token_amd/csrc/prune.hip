@@ -105,6 +105,7 @@ constexpr int kNormIter = 4;
 
 template <int C, int D>
 __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
+  if (p.needed != nullptr && *p.needed == 0) return;   // the plan marked every query hopeless
   constexpr int KBY = KBytes<C>::value;
   constexpr int CH = D * KBY / 16;            // lanes per key
   constexpr int KPB = 256 / CH;               // keys per block and iteration
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __shared__ __align__(16) uint8_t rowl[4 * D * QB];          // the certificate rows
   __shared__ double wd[H], qn2[H], alpha[H][3], gph[3][H];
   __shared__ double avec[D];
-  __shared__ float ksc[kSampleKeys], knm[kSampleKeys];        // skip-test keys: scale, norm
+  __shared__ float ksc[kSampleKeys];                          // skip-test keys: scale
   __shared__ int prox[3], act[H], inO[H];
   __shared__ double hsum[8];                       // c_0..c_2, rho_sep, rho_lo, sum |w_h| ||q_h||, margin
   __shared__ float cfs[6];                         // row multipliers, rho_lo, rho_sep + margin (scaled)
@@ -307,11 +308,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
       ksv[j] = reinterpret_cast<const uint4*>(kbase + row * D * KBY)[sub];
     }
   }
-  float kscale = 1.f, knorm = 0.f;
+  float kscale = 1.f;
   if (t < nsb) {
     const int key = gr.bound_lo + (int)(((int64_t)t * nb) / nsb);
     if constexpr (HasKScale<C>::value) kscale = p.in.k_scale[key_row(p.in, gr.key_base, gr.seq, key)];
-    knorm = p.norms[(int64_t)gr.norm_base + key];
   }
 
   // ---- 1. query (decoded) and activation keys (stored type) to LDS
@@ -338,10 +338,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     wd[t] = (double)wv;
     act[t] = 0;
   }
-  if (t < kSampleKeys) {
-    ksc[t] = kscale;
-    knm[t] = knorm;
-  }
+  if (t < kSampleKeys) ksc[t] = kscale;
   __syncthreads();
 
   // ---- 2. activation counts of the negative heads on the window keys
@@ -589,9 +586,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
         if (r < np) pz += cfs[r] * fmaxf(c[r], 0.f);
         else nz += cfs[r] * c[r];
       }
+      const float kn2 = frag_norm2<O>(B);   // the sampled key's norm from its fragments
       const bool ok = g == 0 && i < nsb;
       const float base = ok ? ksc[i] * (pz - fmaxf(nz, 0.f)) : 0.f;
-      const float kn = ok ? knm[i] : 0.f;
+      const float kn = ok ? ksc[i] * norm_up(kn2) : 0.f;
       n_surv += (int)__popcll(__ballot(ok && base + cfs[4] * kn >= tau));
       n_sep += (int)__popcll(__ballot(ok && base + cfs[5] * kn >= tau));
     }
@@ -661,6 +659,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     cf[5] = tau;
     cf[6] = (float)np;
     cf[7] = hopeless ? 1.f : 0.f;
+    if (!hopeless && p.prunes != nullptr) atomicOr(p.prunes, 1);   // the bound pass has work: key norms are needed
   }
 }
 
