@@ -35,15 +35,14 @@ __device__ __forceinline__ u64 make_key(float s, int pos) {
 __device__ __forceinline__ int key_pos(u64 e) { return (int)(~(uint32_t)e); }
 __device__ __forceinline__ float key_score(u64 e) { return ord2f((uint32_t)(e >> 32)); }
 
-// fp8 E4M3FN code -> bf16 bits, exact.  Normal codes (exponent field e>0):
-// (1+m/8)*2^(e-7) -> bf16 exponent field e+120, mantissa m<<4.  Subnormal
-// codes m*2^-9 go through an exact float.
-__device__ __forceinline__ uint32_t fp8_to_bf16_bits(uint32_t x) {
-  const uint32_t s = (x & 0x80u) << 8;
-  const uint32_t em = x & 0x7Fu;
-  const uint32_t normal = (em + (120u << 3)) << 4;
-  const uint32_t sub = __float_as_uint((float)(em & 7u) * 0.001953125f) >> 16;
-  return s | ((em >> 3) ? normal : sub);
+// Two fp8 E4M3FN codes (bytes 2*HI, 2*HI+1 of w) -> two bf16 in one word,
+// low half first.  gfx950's converter with scale 1: every finite E4M3 value
+// (subnormals m*2^-9 included) is a bf16 value, so the result is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  typedef __bf16 v2bf_t __attribute__((ext_vector_type(2)));
+  const v2bf_t r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -141,11 +140,9 @@ struct Ops<C_BF16Q_FP8K, D> {
       v4i v;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        uint32_t w = h ? w1 : w0;
-        uint32_t b0 = fp8_to_bf16_bits(w & 0xFFu), b1 = fp8_to_bf16_bits((w >> 8) & 0xFFu);
-        uint32_t b2 = fp8_to_bf16_bits((w >> 16) & 0xFFu), b3 = fp8_to_bf16_bits(w >> 24);
-        v[2 * h] = (int)(b0 | (b1 << 16));
-        v[2 * h + 1] = (int)(b2 | (b3 << 16));
+        const uint32_t w = h ? w1 : w0;
+        v[2 * h] = (int)fp8x2_to_bf16x2<false>(w);
+        v[2 * h + 1] = (int)fp8x2_to_bf16x2<true>(w);
       }
       f[s] = __builtin_bit_cast(v8bf, v);
     }
