@@ -117,6 +117,10 @@ struct Ops<C_FP8, D> {
   }
   __device__ __forceinline__ static void load_k(const void* row, int g, frag* f) { load_q(row, g, f); }
   __device__ __forceinline__ static void zero(frag* f) { f[0] = v8i{0, 0, 0, 0, 0, 0, 0, 0}; }
+  // this lane's d/4 key bytes as loaded (zero-padded to 32), and their fragments
+  typedef v8i raw;
+  __device__ __forceinline__ static void load_raw(const void* row, int g, raw& r) { load_q(row, g, &r); }
+  __device__ __forceinline__ static void from_raw(const raw& r, frag* f) { f[0] = r; }
   __device__ __forceinline__ static v4f mma(frag a, frag b, v4f c) {
     // operand formats 0/0 = fp8 E4M3 for A and B; scales 127 = 2^0
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
@@ -149,7 +153,28 @@ struct Ops<C_BF16Q_FP8K, D> {
   }
   __device__ __forceinline__ static void zero(frag* f) { Ops<C_BF16, D>::zero(f); }
   __device__ __forceinline__ static v4f mma(frag a, frag b, v4f c) { return Ops<C_BF16, D>::mma(a, b, c); }
+  // this lane's d/4 key bytes as loaded (zero-padded to 32), and their fragments
+  typedef v8i raw;
+  __device__ __forceinline__ static void load_raw(const void* row, int g, raw& r) {
+    Ops<C_FP8, D>::load_raw(row, g, r);
+  }
+  __device__ __forceinline__ static void from_raw(const raw& r, frag* f) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      v4i v;
+      v[0] = (int)fp8x2_to_bf16x2<false>((uint32_t)r[2 * s]);
+      v[1] = (int)fp8x2_to_bf16x2<true>((uint32_t)r[2 * s]);
+      v[2] = (int)fp8x2_to_bf16x2<false>((uint32_t)r[2 * s + 1]);
+      v[3] = (int)fp8x2_to_bf16x2<true>((uint32_t)r[2 * s + 1]);
+      f[s] = __builtin_bit_cast(v8bf, v);
+    }
+  }
 };
+
+// Key operands that can be prefetched as raw bytes one step ahead (fp8 keys:
+// 32 bytes per lane and 16-key block).
+template <int C>
+struct KeyRaw { static constexpr bool value = (C == C_FP8 || C == C_BF16Q_FP8K); };
 
 template <int C>
 struct HasQScale { static constexpr bool value = (C == C_FP8); };
@@ -205,6 +230,13 @@ __device__ __forceinline__ void drain_memory() { __builtin_amdgcn_s_waitcnt(0); 
 // and export counters at their maxima).  Unconditional, so the compiler knows
 // afterwards that no load is pending on any path.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Memory fence plus wavefront barrier: this wavefront's LDS and global
+// writes are visible to its own later reads.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
 
 __device__ __forceinline__ uint32_t wave_suffix_sum(uint32_t v) {
   const int lane = lane_id();

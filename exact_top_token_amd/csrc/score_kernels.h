@@ -45,10 +45,6 @@ namespace dosa {
 
 constexpr int kTileKeys = 64;   // keys per LDS tile
 
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-}
 
 // K-th largest of the n distinct entries at ptr, by one wavefront with a
 // private 256-bin LDS histogram (8-bit digits from the top; no workgroup
@@ -505,6 +501,72 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
     if ((++nblk & 7) == 0 && sc.dirty) sc.refresh_theta(p.topk);
   };
 
+  if constexpr (KeyRaw<C>::value) {
+    if (!it.gather) {
+      // The range walk with the next step's key bytes on their way while the
+      // current step is scored: one wavefront works alone on its keys, so
+      // without this every step waits out a full memory latency.
+      const int na = it.a1 > it.a0 ? (it.a1 - it.a0 + 63) / 64 : 0;
+      const int ns = na + (it.b1 > it.b0 ? (it.b1 - it.b0 + 63) / 64 : 0);
+      auto step_kb = [&](int s, int& lo, int& hi) -> int {
+        const bool ra = s < na;
+        lo = ra ? it.a0 : it.b0;
+        hi = ra ? it.a1 : it.b1;
+        return hi - 16 - 64 * (ra ? s : s - na);
+      };
+      typename O::raw rn[4];
+      float ksn[4];
+      auto fetch = [&](int s) {
+        int lo, hi;
+        const int kb = step_kb(s, lo, hi);
+        const int cl = sc.col();
+        // rows first (page-table reads of all four blocks in flight together),
+        // then the key bytes and scales
+        int64_t row[4];
+        bool ok[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int key = kb - 16 * b + cl;
+          ok[b] = key >= lo && key < hi;
+          row[b] = ok[b] ? key_row(p.in, gr.key_base, gr.seq, key) : 0;
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          ksn[b] = 1.f;
+          if (ok[b]) {
+            O::load_raw(kbytes + row[b] * SC::KBYTES, sc.g(), rn[b]);
+            if constexpr (HasKScale<C>::value) ksn[b] = p.in.k_scale[row[b]];
+          } else {
+            rn[b] = typename O::raw{};
+          }
+        }
+      };
+      if (ns > 0) fetch(0);
+#pragma unroll 1
+      for (int s = 0; s < ns; ++s) {
+        int lo, hi;
+        const int kb = step_kb(s, lo, hi);
+        int keys[4];
+        bool v[4];
+        float ks[4], o[4];
+        typename O::frag B[4][SC::STEPS];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          keys[b] = kb - 16 * b + sc.col();
+          v[b] = keys[b] >= lo && keys[b] < hi;
+          O::from_raw(rn[b], B[b]);
+          ks[b] = ksn[b];
+        }
+        if (s + 1 < ns) fetch(s + 1);
+        sc.template scoreN<4>(B, o);
+        sc.template append4<true>(p, gr, it.region, o, ks, keys, v, hist);
+        if ((++nblk & 7) == 0 && sc.dirty) sc.refresh_theta(p.topk);
+      }
+      sc.close(p, gr, it.region, hist);
+      sc.finish(p, it.region);
+      return;
+    }
+  }
   if (!it.gather) {
 #pragma unroll 1
     for (int r = 0; r < 2; ++r) {

@@ -7,7 +7,12 @@ namespace dosa {
 // ---------------------------------------------------------------------------
 // final merge: the exact Top-K of each query over regions [r0, r1)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
+// NT threads per query: the radix passes use them all; the compaction and
+// the output walk stay on wavefront 0 (its order is the regions' order, so
+// rows are the same run to run).  NT = 256 serves launches with few queries,
+// whose time is one query's latency.
+template <int NT>
+__global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
@@ -20,7 +25,8 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
   for (int r = 0; r < nseg; ++r) total += cnt[r];
   Segs sg{base, cnt, cap, nseg};
   u64 T = 0;
-  if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
+  if (total >= (uint32_t)K) T = select_kth_nt<NT>(sg, K, hist);
+  if (threadIdx.x >= 64) return;
   if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
   if (p.out_idx == nullptr) {
     // threshold mode: keep only the K entries >= T in the merged regions, so
@@ -29,7 +35,7 @@ __global__ __launch_bounds__(64) void select_kernel(const SelectLaunch p) {
       for (int r = 0; r < nseg; ++r) {
         u64* ptr = p.cb.cand + ((int64_t)q * R + p.r0 + r) * cap;
         const uint32_t nk = compact_ge(ptr, cnt[r], T, ptr, 0);
-        __syncthreads();
+        wave_sync();   // every lane has read cnt[r] before lane 0 rewrites it
         if (lane == 0) p.cb.counts[(int64_t)q * R + p.r0 + r] = nk;
       }
     }
@@ -185,8 +191,10 @@ hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {
   if (p.total_q == 0) return hipSuccess;
   if (p.sorted && p.out_idx != nullptr)
     hipLaunchKernelGGL(select_sorted_kernel, dim3(p.total_q), dim3(64), 0, s, p);
+  else if (p.total_q <= 2048)
+    hipLaunchKernelGGL((select_kernel<256>), dim3(p.total_q), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(select_kernel, dim3(p.total_q), dim3(64), 0, s, p);
+    hipLaunchKernelGGL((select_kernel<64>), dim3(p.total_q), dim3(64), 0, s, p);
   return hipGetLastError();
 }
 
