@@ -7,6 +7,57 @@ namespace dosa {
 // ---------------------------------------------------------------------------
 // final merge: the exact Top-K of each query over regions [r0, r1)
 // ---------------------------------------------------------------------------
+constexpr int kMaxMergeRegions = 128;   // regions the multi-wavefront output split handles
+
+// Entries >= T among src[0..n), counted by one wavefront.
+__device__ __forceinline__ uint32_t count_ge(const u64* src, uint32_t n, u64 T) {
+  const int lane = lane_id();
+  uint32_t c = 0;
+  for (uint32_t b0 = 0; b0 < n; b0 += 64 * kBatch) {
+    u64 e[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = b0 + 64u * u + lane;
+      e[u] = (i < n) ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = b0 + 64u * u + lane;
+      c += (uint32_t)__popcll(__ballot((i < n) && (e[u] >= T)));
+    }
+  }
+  return c;
+}
+
+// One wavefront writes the entries >= T of src[0..n), in order, to rows
+// out.. of oi / os (positions and scores), none at or past K.  Returns the
+// next free row.
+__device__ __forceinline__ uint32_t emit_ge(const u64* src, uint32_t n, u64 T, int32_t* oi, float* os,
+                                            uint32_t out, int K) {
+  const int lane = lane_id();
+  for (uint32_t b0 = 0; b0 < n; b0 += 64 * kBatch) {
+    u64 e[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = b0 + 64u * u + lane;
+      e[u] = (i < n) ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = b0 + 64u * u + lane;
+      const bool keep = (i < n) && (e[u] >= T);
+      const u64 m = __ballot(keep);
+      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+      if (keep && out + before < (uint32_t)K) {
+        oi[out + before] = key_pos(e[u]);
+        if (os) os[out + before] = key_score(e[u]);
+      }
+      out += __popcll(m);
+    }
+  }
+  return out;
+}
+
 // NT threads per query: the radix passes use them all; the compaction and
 // the output walk stay on wavefront 0 (its order is the regions' order, so
 // rows are the same run to run).  NT = 256 serves launches with few queries,
@@ -26,11 +77,11 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   Segs sg{base, cnt, cap, nseg};
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth_nt<NT>(sg, K, hist);
-  if (threadIdx.x >= 64) return;
-  if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
+  if (p.tau_out != nullptr && threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
   if (p.out_idx == nullptr) {
     // threshold mode: keep only the K entries >= T in the merged regions, so
     // a later merge reads K of them instead of all
+    if (threadIdx.x >= 64) return;
     if (total > (uint32_t)K) {
       for (int r = 0; r < nseg; ++r) {
         u64* ptr = p.cb.cand + ((int64_t)q * R + p.r0 + r) * cap;
@@ -45,30 +96,44 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   int32_t* oi = p.out_idx + (int64_t)q * K;
   float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
   uint32_t out = 0;
-  for (int r = 0; r < nseg; ++r) {
-    const u64* src = sg.ptr(r);
-    const uint32_t n = cnt[r];
-    for (uint32_t b0 = 0; b0 < n; b0 += 64 * kBatch) {
-      u64 e[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t i = b0 + 64u * u + lane;
-        e[u] = (i < n) ? src[i] : 0ull;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const uint32_t i = b0 + 64u * u + lane;
-        const bool keep = (i < n) && (e[u] >= T);
-        const u64 m = __ballot(keep);
-        const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
-        if (keep && out + before < (uint32_t)K) {
-          oi[out + before] = key_pos(e[u]);
-          if (os) os[out + before] = key_score(e[u]);
-        }
-        out += __popcll(m);
+  constexpr int NW = NT / 64;
+  if (NW > 1 && nseg <= kMaxMergeRegions) {
+    // Every wavefront takes a contiguous share of each region: it counts its
+    // entries >= T, the counts are turned into output offsets in region
+    // order, and each share is written at its offset.  Same rows as one
+    // wavefront walking the regions in order.
+    __shared__ uint32_t offs[kMaxMergeRegions * (NW > 1 ? NW : 1)];
+    const int w = (int)(threadIdx.x >> 6);
+    for (int r = 0; r < nseg; ++r) {
+      const uint32_t n = cnt[r];
+      const uint32_t lo = (uint32_t)((uint64_t)n * w / NW), hi = (uint32_t)((uint64_t)n * (w + 1) / NW);
+      const uint32_t c = count_ge(sg.ptr(r) + lo, hi - lo, T);
+      if (lane == 0) offs[r * NW + w] = c;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t acc = 0;
+      for (int i = 0; i < nseg * NW; ++i) {
+        const uint32_t c = offs[i];
+        offs[i] = acc;
+        acc += c;
       }
     }
+    __syncthreads();
+    for (int r = 0; r < nseg; ++r) {
+      const uint32_t n = cnt[r];
+      const uint32_t lo = (uint32_t)((uint64_t)n * w / NW), hi = (uint32_t)((uint64_t)n * (w + 1) / NW);
+      emit_ge(sg.ptr(r) + lo, hi - lo, T, oi, os, offs[r * NW + w], K);
+    }
+    out = min(total, (uint32_t)K);
+    for (uint32_t i = out + threadIdx.x; i < (uint32_t)K; i += NT) {
+      oi[i] = -1;
+      if (os) os[i] = -INFINITY;
+    }
+    return;
   }
+  if (threadIdx.x >= 64) return;
+  for (int r = 0; r < nseg; ++r) out = emit_ge(sg.ptr(r), cnt[r], T, oi, os, out, K);
   out = min(out, (uint32_t)K);
   for (uint32_t i = out + lane; i < (uint32_t)K; i += 64) {
     oi[i] = -1;
@@ -191,6 +256,8 @@ hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {
   if (p.total_q == 0) return hipSuccess;
   if (p.sorted && p.out_idx != nullptr)
     hipLaunchKernelGGL(select_sorted_kernel, dim3(p.total_q), dim3(64), 0, s, p);
+  else if (p.total_q <= 256)
+    hipLaunchKernelGGL((select_kernel<1024>), dim3(p.total_q), dim3(1024), 0, s, p);
   else if (p.total_q <= 2048)
     hipLaunchKernelGGL((select_kernel<256>), dim3(p.total_q), dim3(256), 0, s, p);
   else
