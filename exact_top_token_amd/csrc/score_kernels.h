@@ -458,8 +458,10 @@ struct Scorer {
 // one wavefront per query group: key range (two sub-ranges walked top-down)
 // or survivor list (ascending)
 // ---------------------------------------------------------------------------
+// fp8 keys leave room for two wavefronts per SIMD, which hides the
+// latency of the per-step key gather; the wider f32/bf16 rows would spill.
 template <int C, int H, int D, int ROLE>
-__global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
+__global__ __launch_bounds__(64, KeyRaw<C>::value ? 2 : 1) void score_list_kernel(const ScoreLaunch p) {
   using SC = Scorer<C, H, D>;
   using O = typename SC::O;
   __shared__ uint32_t hist[256];
@@ -492,11 +494,23 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
   };
   // four 16-key blocks per step
   auto step4 = [&](const int* keys, const bool* v) {
-    typename O::frag B[4][SC::STEPS];
     float ks[4], o[4];
+    if constexpr (KeyRaw<C>::value) {
+      // two blocks of fragments at a time (the register budget of the
+      // prefetching range walk above)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) load(keys[b], v[b], B[b], ks[b]);
-    sc.template scoreN<4>(B, o);
+      for (int j = 0; j < 2; ++j) {
+        typename O::frag B[2][SC::STEPS];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) load(keys[2 * j + b], v[2 * j + b], B[b], ks[2 * j + b]);
+        sc.template scoreN<2>(B, o + 2 * j);
+      }
+    } else {
+      typename O::frag B[4][SC::STEPS];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) load(keys[b], v[b], B[b], ks[b]);
+      sc.template scoreN<4>(B, o);
+    }
     sc.template append4<true>(p, gr, it.region, o, ks, keys, v, hist);
     if ((++nblk & 7) == 0 && sc.dirty) sc.refresh_theta(p.topk);
   };
@@ -514,24 +528,28 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
         hi = ra ? it.a1 : it.b1;
         return hi - 16 - 64 * (ra ? s : s - na);
       };
-      typename O::raw rn[4];
-      float ksn[4];
-      auto fetch = [&](int s) {
+      // Half steps of two 16-key blocks: the raw bytes of the next half are
+      // in flight while the current one is scored (two blocks of fragments
+      // at a time keep the kernel within two wavefronts per SIMD); the four
+      // blocks of a step are appended together.
+      typename O::raw rn[2];
+      float ksn[2];
+      auto fetch = [&](int h) {
         int lo, hi;
-        const int kb = step_kb(s, lo, hi);
+        const int kb = step_kb(h >> 1, lo, hi) - 32 * (h & 1);
         const int cl = sc.col();
-        // rows first (page-table reads of all four blocks in flight together),
+        // rows first (page-table reads of both blocks in flight together),
         // then the key bytes and scales
-        int64_t row[4];
-        bool ok[4];
+        int64_t row[2];
+        bool ok[2];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 2; ++b) {
           const int key = kb - 16 * b + cl;
           ok[b] = key >= lo && key < hi;
           row[b] = ok[b] ? key_row(p.in, gr.key_base, gr.seq, key) : 0;
         }
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 2; ++b) {
           ksn[b] = 1.f;
           if (ok[b]) {
             O::load_raw(kbytes + row[b] * SC::KBYTES, sc.g(), rn[b]);
@@ -549,16 +567,22 @@ __global__ __launch_bounds__(64) void score_list_kernel(const ScoreLaunch p) {
         int keys[4];
         bool v[4];
         float ks[4], o[4];
-        typename O::frag B[4][SC::STEPS];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           keys[b] = kb - 16 * b + sc.col();
           v[b] = keys[b] >= lo && keys[b] < hi;
-          O::from_raw(rn[b], B[b]);
-          ks[b] = ksn[b];
         }
-        if (s + 1 < ns) fetch(s + 1);
-        sc.template scoreN<4>(B, o);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          typename O::frag B[2][SC::STEPS];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            O::from_raw(rn[b], B[b]);
+            ks[2 * j + b] = ksn[b];
+          }
+          if (2 * s + j + 1 < 2 * ns) fetch(2 * s + j + 1);
+          sc.template scoreN<2>(B, o + 2 * j);
+        }
         sc.template append4<true>(p, gr, it.region, o, ks, keys, v, hist);
         if ((++nblk & 7) == 0 && sc.dirty) sc.refresh_theta(p.topk);
       }
