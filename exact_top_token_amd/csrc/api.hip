@@ -290,10 +290,19 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       }
     }
     const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
-    P.J = J;
-    P.R = Js + J;
-    // survivors of tiles whose certificate can prune nothing: the tiled kernel
-    // over the bounded range (one wavefront per group when tiles are small)
+    // union lists of tiles (tiled kernel): up to Ju shares per tile, enough
+    // workgroups to fill the GPU when every tile takes this route
+    int Ju = 1;
+    if (P.tiled) {
+      int64_t bsum_t = 0;
+      for (const auto& t : tiles) bsum_t += P.groups[t.first].n_bounded;
+      Ju = cfg.key_splits > 0 ? cfg.key_splits
+                              : choose_splits(NT, NT ? bsum_t / NT : 0, 4 * tiled_target, kUnionMinShare);
+    }
+    P.J = std::max(J, Ju);
+    P.R = Js + P.J;
+    // calls without tiles: groups of tiles whose certificate prunes little
+    // walk the whole bounded range (one wavefront per group)
     if (!P.tiled) {
       for (int gi = 0; gi < G; ++gi) {
         const GroupInfo& g = P.groups[gi];
@@ -309,18 +318,17 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         }
       }
     }
+    // calls with tiles: share r of Ju of the tile's union survivor list
     for (const auto& t : tiles) {
       if (!P.tiled) break;
-      const GroupInfo& g = P.groups[t.first];
-      for (int r = 0; r < J; ++r) {
-        int lo, hi;
-        range_split(g.bound_lo, g.bound_lo + g.n_bounded, r, J, 64, lo, hi);
+      for (int r = 0; r < Ju; ++r) {
         WorkItem it{};
         it.group = t.first;
         it.pad = t.n;
         it.region = Js + r;
-        it.a0 = it.a1 = lo;
-        it.b0 = lo; it.b1 = hi;
+        it.gather = 1;
+        it.a0 = r;
+        it.a1 = Ju;
         P.surv_tiled_items.push_back(it);
       }
     }
@@ -406,7 +414,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     int64_t max_n = 0;
     for (const auto& it : P.items) {
       int64_t n = (int64_t)(it.a1 - it.a0) + (it.b1 - it.b0);
-      if (it.gather) n = (P.groups[it.group].n_bounded + it.a1 - 1) / it.a1 + 16;
+      if (it.gather) {
+        const int64_t nb = P.groups[it.group].n_bounded;
+        n = std::max<int64_t>((nb + it.a1 - 1) / it.a1, std::min<int64_t>(nb, 2 * kUnionMinShare)) + 64;
+      }
       max_n = std::max(max_n, n);
     }
     const double k = (double)topk;
@@ -806,15 +817,32 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
     // 6. compaction -> survivor key lists
-    CompactLaunch cl{dg, G, coef, masks, std::max(P.mask_words, 1), lists, list_len, gflags, mode, MODE_PRUNED};
+    CompactLaunch cl{};
+    cl.groups = dg;
+    cl.tiles = di;                    // the seed items: Js per tile, the first names the tile
+    cl.tile_stride = P.Js;
+    cl.n_tiles = P.Js > 0 ? (int)P.seed_items.size() / P.Js : 0;
+    cl.allow_union = P.tiled ? 1 : 0;
+    cl.coef = coef;
+    cl.masks = masks;
+    cl.mask_words = std::max(P.mask_words, 1);
+    cl.lists = lists;
+    cl.list_len = list_len;
+    cl.group_flags = gflags;
+    cl.counts = cb.counts;
+    cl.R = P.R;
+    cl.r0 = P.Js;
+    cl.r1 = P.Js + P.J;
+    cl.mode = mode;
+    cl.run_if = MODE_PRUNED;
     {
       PassScope ps(P_COMPACT, stream);
       e = launch_compact(cl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
     // 7. survivors scored with all heads into regions Js..Js+J-1, threshold starts at tau:
-    //    tiles whose certificate prunes nothing take the tiled kernel over the
-    //    bounded range, the other groups walk their compacted lists
+    //    flagged tiles take the tiled kernel over their union list (or, in calls
+    //    without tiles, over the bounded range), the other groups walk their own lists
     ScoreLaunch ml{};
     ml.mode = mode;
     ml.run_if = MODE_PRUNED;

@@ -24,6 +24,9 @@ __device__ __forceinline__ bool skip_launch(const int32_t* mode, int32_t run_if)
 }
 
 constexpr int kTileWaves = 8;   // wavefronts (query groups) per tiled scoring workgroup
+// A tile's union survivor list is scored in up to WorkItem::a1 shares of at
+// least this many keys each (shorter lists take fewer workgroups).
+constexpr int kUnionMinShare = 1024;
 
 // A query group: up to 4 consecutive queries of one sequence, scored together
 // by one wavefront (MFMA rows = group queries x head slots).
@@ -176,13 +179,20 @@ struct BoundLaunch {
 
 struct CompactLaunch {
   const GroupInfo* groups;
-  int32_t n_groups;
+  const WorkItem* tiles;     // tile i's first group is tiles[i * tile_stride].group
+  int32_t tile_stride;
+  int32_t n_tiles;           // grid: one workgroup per tile
+  int32_t allow_union;       // 1: tiles may be routed to the tiled kernel's union lists
   const float* coef;         // plan coefficients (coef[7]: hopeless flag per query)
   const unsigned long long* masks;
   int32_t mask_words;
   int32_t* lists;
   int32_t* list_len;
-  int32_t* group_flags;      // out: 1 if the group's tile is scored over its whole bounded range
+  int32_t* group_flags;      // out: 1 if the group's tile is scored whole: over its union list
+                             // (allow_union) or over its bounded range
+  uint32_t* counts;          // candidate counts [total_q, R]: regions [r0, r1) of the tile's
+  int32_t R, r0, r1;         // queries are zeroed here (the survivor pass writes only the regions
+                             // it fills, the final merge reads them all)
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;
 };

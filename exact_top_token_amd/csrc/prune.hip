@@ -920,82 +920,126 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
 }
 
 // ---------------------------------------------------------------------------
-// compaction: one workgroup per tile, one wavefront per query group.  Each
-// wavefront counts its group's union survivors (popcounts of the bitmask; a
-// group whose every query the plan marked hopeless has no bitmask and keeps
-// all its bounded keys); if the tile's survivors are at least kDenseFrac of
-// its bounded keys, the tile is flagged for the tiled kernel, which walks the
-// bounded range directly.  Otherwise each wavefront turns its bitmask into an
-// ascending key list: per-lane popcounts, a wavefront prefix sum for the write
-// offsets, then each lane expands its word.
+// compaction: one workgroup per tile (up to 8 query groups that bound the same
+// key range).  Each group has a survivor bitmask; a group whose every query
+// the plan marked hopeless has none and keeps all its bounded keys.  The masks
+// become ascending key lists, routed one of two ways:
+//   calls with tiles: if scoring the tile's union of survivors U with the
+//     LDS-tiled kernel costs less than walking every group's own list U_g
+//     (groups * |U| <= kTileGain * sum_g |U_g|: the tiled kernel scores a
+//     pair about four times faster than the per-group kernel), the union goes
+//     to the list of the tile's first group and every group of the tile is
+//     flagged; otherwise each group gets its own list.
+//   calls without tiles (one wavefront per group): a tile whose survivors are
+//     at least kDenseFrac of its bounded keys is flagged and scored over its
+//     whole bounded range; otherwise each group gets its own list.
+// Wavefronts expand contiguous runs of mask words, one word per iteration and
+// one key per lane, so the list stores are coalesced.
 // ---------------------------------------------------------------------------
 constexpr float kDenseFrac = 0.4f;
+constexpr int kTileGain = 4;
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += (uint32_t)__shfl_xor((int)v, off, 64);
+  return v;
+}
+
+// keys of mask words [w0, w1) in ascending order at out + base (word wd holds
+// keys key0 + 64 wd + bit); called by a whole wavefront
+template <class Word>
+__device__ __forceinline__ void expand_words(const Word& word, int w0, int w1, int key0, int32_t* out,
+                                             uint32_t base) {
+  const int lane = lane_id();
+  const u64 below = (1ull << lane) - 1ull;
+  for (int wb = w0; wb < w1; wb += 64) {
+    const u64 mine = (wb + lane < w1) ? word(wb + lane) : 0ull;
+    const int n = min(64, w1 - wb);
+    for (int j = 0; j < n; ++j) {
+      const u64 m = __shfl(mine, j, 64);
+      if ((m >> lane) & 1ull) out[base + (uint32_t)__popcll(m & below)] = key0 + 64 * (wb + j) + lane;
+      base += (uint32_t)__popcll(m);
+    }
+  }
+}
 
 __global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
   if (skip_launch(p.mode, p.run_if)) return;
-  const int gi0 = blockIdx.x;
+  const int gi0 = p.tiles[(int64_t)blockIdx.x * p.tile_stride].group;
   const GroupInfo head = p.groups[gi0];
-  if (head.tile_first != gi0) return;          // one workgroup per tile
+  const int tn = head.tile_n;
   const int wave = threadIdx.x >> 6;
   const int lane = lane_id();
-  __shared__ uint32_t surv[8];
-  __shared__ uint32_t bounded[8];
-  const bool active = wave < head.tile_n;
-  const int gi = gi0 + (active ? wave : 0);
-  const GroupInfo gr = p.groups[gi];
-  const int nw = active ? (gr.n_bounded + 63) / 64 : 0;
-  const unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
-  bool all_hopeless = true;
-  for (int i = 0; i < gr.nq; ++i) all_hopeless = all_hopeless && p.coef[(int64_t)(gr.q_row0 + i) * 8 + 7] != 0.f;
-  auto word = [&](int wd) -> u64 {
-    if (!all_hopeless) return mw[wd];
-    const int rem = gr.n_bounded - wd * 64;
-    return rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
-  };
-  uint32_t c = 0;
-  if (all_hopeless) c = (lane == 0) ? (uint32_t)gr.n_bounded : 0u;
-  else
-    for (int wd = lane; wd < nw; wd += 64) c += __popcll(mw[wd]);
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-  if (lane == 0) {
-    surv[wave] = active ? c : 0u;
-    bounded[wave] = active ? (uint32_t)gr.n_bounded : 0u;
+  const int nb = head.n_bounded;                // the same for every group of the tile
+  const int nw = (nb + 63) / 64;
+  __shared__ uint32_t surv[8], part[8];
+  __shared__ int32_t hopeless[8];
+  if (threadIdx.x < 8) {
+    bool h = true;
+    if ((int)threadIdx.x < tn) {
+      const GroupInfo g = p.groups[gi0 + threadIdx.x];
+      for (int i = 0; i < g.nq; ++i) h = h && p.coef[(int64_t)(g.q_row0 + i) * 8 + 7] != 0.f;
+    }
+    hopeless[threadIdx.x] = h ? 1 : 0;
+  }
+  if (wave < tn) {
+    const GroupInfo g = p.groups[gi0 + wave];
+    const int nr = p.r1 - p.r0;
+    for (int e = lane; e < g.nq * nr; e += 64)
+      p.counts[(int64_t)(g.q_row0 + e / nr) * p.R + p.r0 + e % nr] = 0u;
   }
   __syncthreads();
-  uint64_t ts = 0, tb = 0;
+  auto word = [&](int g, int wd) -> u64 {
+    if (hopeless[g]) {
+      const int rem = nb - 64 * wd;
+      return rem >= 64 ? ~0ull : ((1ull << rem) - 1ull);
+    }
+    return p.masks[(int64_t)(gi0 + g) * p.mask_words + wd];
+  };
+  auto uword = [&](int wd) -> u64 {
+    u64 m = 0;
+    for (int g = 0; g < tn; ++g) m |= word(g, wd);
+    return m;
+  };
+  // survivors per group, and of the union over each wavefront's run of words
+  uint32_t c = 0;
+  if (wave < tn) {
+    if (hopeless[wave]) c = (lane == 0) ? (uint32_t)nb : 0u;
+    else
+      for (int wd = lane; wd < nw; wd += 64) c += (uint32_t)__popcll(word(wave, wd));
+  }
+  c = wave_sum_u32(c);
+  const int seg = (nw + 7) / 8;
+  const int s0 = min(nw, wave * seg), s1 = min(nw, s0 + seg);
+  uint32_t u = 0;
+  if (p.allow_union)
+    for (int wd = s0 + lane; wd < s1; wd += 64) u += (uint32_t)__popcll(uword(wd));
+  u = wave_sum_u32(u);
+  if (lane == 0) {
+    surv[wave] = (wave < tn) ? c : 0u;
+    part[wave] = u;
+  }
+  __syncthreads();
+  uint64_t ts = 0, tu = 0;
+  uint32_t ubase = 0;
   for (int i = 0; i < 8; ++i) {
     ts += surv[i];
-    tb += bounded[i];
+    tu += part[i];
+    if (i < wave) ubase += part[i];
   }
-  const bool dense = (float)ts >= kDenseFrac * (float)tb;
-  if (!active) return;
-  if (lane == 0) p.group_flags[gi] = dense ? 1 : 0;
-  if (dense) {
-    if (lane == 0) p.list_len[gi] = 0;
-    return;
+  bool whole;
+  if (p.allow_union) whole = (uint64_t)tn * tu <= (uint64_t)kTileGain * ts;
+  else whole = (float)ts >= kDenseFrac * (float)((uint64_t)nb * (uint64_t)tn);
+  if (wave < tn && lane == 0) {
+    p.group_flags[gi0 + wave] = whole ? 1 : 0;
+    p.list_len[gi0 + wave] = (whole && p.allow_union && wave == 0) ? (int32_t)tu : (whole ? 0 : (int32_t)c);
   }
-  int32_t* out = p.lists + gr.list_off;
-  uint32_t base = 0;
-  for (int w0 = 0; w0 < nw; w0 += 64) {
-    const int wd = w0 + lane;
-    u64 m = (wd < nw) ? word(wd) : 0ull;
-    const uint32_t cnt = __popcll(m);
-    uint32_t incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
-    }
-    uint32_t at = base + incl - cnt;
-    const int k0 = gr.bound_lo + 64 * wd;
-    while (m) {
-      const int b = __ffsll((long long)m) - 1;
-      out[at++] = k0 + b;
-      m &= m - 1ull;
-    }
-    base += __shfl(incl, 63, 64);
+  if (whole) {
+    if (p.allow_union) expand_words(uword, s0, s1, head.bound_lo, p.lists + head.list_off, ubase);
+  } else if (wave < tn) {
+    const GroupInfo gr = p.groups[gi0 + wave];
+    expand_words([&](int wd) { return word(wave, wd); }, 0, nw, gr.bound_lo, p.lists + gr.list_off, 0u);
   }
-  if (lane == 0) p.list_len[gi] = (int32_t)base;
 }
 
 __global__ void stats_add_kernel(unsigned long long* st, const dosa_stats add) {
@@ -1117,8 +1161,8 @@ hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream
 }
 
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s) {
-  if (p.n_groups == 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3(p.n_groups), dim3(512), 0, s, p);
+  if (p.n_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_kernel, dim3(p.n_tiles), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

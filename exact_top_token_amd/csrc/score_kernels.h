@@ -630,10 +630,12 @@ __global__ __launch_bounds__(64, KeyRaw<C>::value ? 2 : 1) void score_list_kerne
 }
 
 // ---------------------------------------------------------------------------
-// 8 wavefronts (consecutive query groups of one sequence) share LDS key tiles
-// (range mode: [a0,a1) then [b0,b1), each from the top tile down).  PAGED:
-// keys go through the page table; otherwise a tile is one contiguous run of
-// rows addressed from a single base.
+// 8 wavefronts (consecutive query groups of one sequence) share LDS key tiles.
+// Range mode: [a0,a1) then [b0,b1), each from the top tile down.  Gather mode
+// (survivor pass only): share a0 of a1 of the tile's union survivor list,
+// from its last entry down; every listed key lies before the tile's first
+// query, so it is visible to all of them.  PAGED: keys go through the page
+// table; otherwise a key row is addressed from a single base.
 // ---------------------------------------------------------------------------
 template <int C, int H, int D, int ROLE, bool PAGED>
 __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const ScoreLaunch p) {
@@ -652,6 +654,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   constexpr int NBK = FB <= 32 ? 4 : (FB <= 64 ? 2 : 1);
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][TK * ROW];
   __shared__ float kscale[2][TK];
+  __shared__ int32_t kid[2][TK];                     // gather mode: the tile's key positions (-1: none)
   __shared__ __attribute__((aligned(16))) float wl[kTileWaves][SC::QW * (H + SC::S)];
   __shared__ uint32_t hist[kTileWaves][256];
   __shared__ uint32_t qhist[kTileWaves][SC::QW * kHistBins];
@@ -668,11 +671,25 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   const bool active = wave < ngroups;
   const GroupInfo gr = p.groups[it.group + (active ? wave : 0)];
   const GroupInfo g0 = p.groups[it.group];
+  // gather mode: entries [e0, e1) of the union list; a short list is cut into
+  // fewer shares of at least kUnionMinShare keys, and the items of the unused
+  // shares leave here
+  constexpr bool kGatherRole = (ROLE == ROLE_SURVIVORS);
+  const bool gather = kGatherRole && it.gather != 0;
+  const int32_t* ulist = p.lists + g0.list_off;
+  int e0 = 0, e1 = 0;
+  if (gather) {
+    const int len = p.list_len[it.group];
+    const int nsh = min(it.a1, max(1, (len + kUnionMinShare - 1) / kUnionMinShare));
+    if (it.a0 >= nsh) return;
+    e0 = (int)((int64_t)len * it.a0 / nsh);
+    e1 = (int)((int64_t)len * (it.a0 + 1) / nsh);
+  }
   SC sc;
   sc.init(p, gr, it.region, wl[wave], qhist[wave], active);
 
-  const int na = (it.a1 > it.a0) ? (it.a1 - it.a0 + TK - 1) / TK : 0;
-  const int nbt = (it.b1 > it.b0) ? (it.b1 - it.b0 + TK - 1) / TK : 0;
+  const int na = gather ? 0 : ((it.a1 > it.a0) ? (it.a1 - it.a0 + TK - 1) / TK : 0);
+  const int nbt = gather ? (e1 - e0 + TK - 1) / TK : ((it.b1 > it.b0) ? (it.b1 - it.b0 + TK - 1) / TK : 0);
   const int ntiles = na + nbt;
   // contiguous storage: row r of the sequence's keys at kseq + r * KB
   const uint8_t* kseq = static_cast<const uint8_t*>(p.in.k) + (PAGED ? 0 : (int64_t)g0.key_base * KB);
@@ -681,7 +698,39 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
 
   v4i stage[NCH];
   float stage_s = 1.f;
+  int stage_id = -1;
+  auto fetch_gather = [&](int t) {
+    const int tid = lane_fresh() + 64 * wave;
+    const int ib = e1 - TK * (t + 1);               // list index of the tile's slot 0
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * 64 * kTileWaves;
+      const int slot = ch / CPK, part = ch % CPK;
+      const int idx = ib + slot;
+      if (slot < TK && idx >= e0) {
+        const int key = ulist[idx];
+        const int64_t row = PAGED ? key_row(p.in, g0.key_base, g0.seq, key) : (int64_t)key;
+        stage[c] = *reinterpret_cast<const v4i*>(kseq + row * KB + part * 16);
+      } else {
+        stage[c] = v4i{0, 0, 0, 0};
+      }
+    }
+    if (tid < TK) {
+      const int idx = ib + tid;
+      stage_id = (idx >= e0) ? ulist[idx] : -1;
+      if constexpr (HasKScale<C>::value) {
+        if (stage_id >= 0)
+          stage_s = PAGED ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, stage_id)] : sseq[(uint32_t)stage_id];
+        else
+          stage_s = 0.f;
+      }
+    }
+  };
   auto fetch = [&](int t) {
+    if (kGatherRole && gather) {
+      fetch_gather(t);
+      return;
+    }
     const int tid = lane_fresh() + 64 * wave;
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
@@ -721,7 +770,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
       const int slot = ch / CPK, part = ch % CPK;
       if (slot < TK) *reinterpret_cast<v4i*>(&ktile[bufi][slot * ROW + part * 16]) = stage[c];
     }
-    if (tid < TK) kscale[bufi][tid] = stage_s;
+    if (tid < TK) {
+      kscale[bufi][tid] = stage_s;
+      if (kGatherRole) kid[bufi][tid] = stage_id;
+    }
   };
 
   drain_memory();   // the query fragments of init, before the prefetching loop
@@ -776,12 +828,21 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
         bool kv[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          keys[b] = kh + b * 16 + cl;
           ks[b] = HasKScale<C>::value ? kscale[bufi][kTileKeys * hh + b * 16 + cl] : 1.f;
-          kv[b] = keys[b] >= lo && keys[b] < hi;
+          if (kGatherRole && gather) {
+            keys[b] = kid[bufi][kTileKeys * hh + b * 16 + cl];
+            kv[b] = keys[b] >= 0;
+          } else {
+            keys[b] = kh + b * 16 + cl;
+            kv[b] = keys[b] >= lo && keys[b] < hi;
+          }
         }
-        // whole step inside the range and visible to every query of the group
-        if (kh >= lo && kh + kTileKeys <= hi && kh + kTileKeys - 1 <= last0)
+        // whole step inside the range (gather: every slot of the tile filled)
+        // and visible to every query of the group
+        const bool full = (kGatherRole && gather)
+                              ? (e1 - TK * (t + 1) >= e0)
+                              : (kh >= lo && kh + kTileKeys <= hi && kh + kTileKeys - 1 <= last0);
+        if (full)
           sc.template append4<false>(p, gr, it.region, o[hh], ks, keys, kv, hist[wave]);
         else
           sc.template append4<true>(p, gr, it.region, o[hh], ks, keys, kv, hist[wave]);
