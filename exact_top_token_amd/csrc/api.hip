@@ -87,6 +87,7 @@ struct Plan {
   std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items, probe_items;
   bool probe = false;                // DoSA: plan the last tile first, score densely if it cannot prune
   int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0, Jp = 0;
+  int bound_gpw = 1;                 // query groups per wavefront of the tiled bound kernel
   bool tiled = true;
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
@@ -346,19 +347,41 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.items = P.seed_items;
     // bound pass over LDS key tiles when tiles hold enough groups: one item per
     // (tile, 64-key-aligned share of its bounded range)
+    // A bound workgroup takes 4/QW consecutive tiles of one sequence with the
+    // same first bounded key, so its wavefronts hold 4 queries each; its key
+    // range runs to the longest of their bounded ranges.
     if (P.tiled) {
-      int64_t bsum_t = 0;
-      for (const auto& t : tiles) bsum_t += P.groups[t.first].n_bounded;
-      const int Jb = choose_splits(NT, NT ? bsum_t / NT : 0, 2 * tiled_target, 2048);
-      for (const auto& t : tiles) {
+      P.bound_gpw = 4 / P.QW;
+      struct BlockInfo { int first, n, lo, hi; };
+      std::vector<BlockInfo> blocks;
+      for (size_t ti = 0; ti < tiles.size(); ++ti) {
+        const TileInfo& t = tiles[ti];
         const GroupInfo& g = P.groups[t.first];
+        const int lo = g.bound_lo, hi = g.bound_lo + g.n_bounded;
+        if (!blocks.empty()) {
+          BlockInfo& bk = blocks.back();
+          const GroupInfo& h = P.groups[bk.first];
+          if (h.seq == g.seq && h.bound_lo == lo && bk.n + t.n <= TW * P.bound_gpw &&
+              bk.first + bk.n == t.first) {
+            bk.n += t.n;
+            bk.hi = std::max(bk.hi, hi);
+            continue;
+          }
+        }
+        blocks.push_back({t.first, t.n, lo, hi});
+      }
+      const int NB = (int)blocks.size();
+      int64_t bsum_t = 0;
+      for (const auto& bk : blocks) bsum_t += bk.hi - bk.lo;
+      const int Jb = choose_splits(NB, NB ? bsum_t / NB : 0, 2 * tiled_target, 2048);
+      for (const auto& bk : blocks) {
         for (int r = 0; r < Jb; ++r) {
           int lo, hi;
-          range_split(g.bound_lo, g.bound_lo + g.n_bounded, r, Jb, 64, lo, hi);
+          range_split(bk.lo, bk.hi, r, Jb, 64, lo, hi);
           if (hi <= lo && r > 0) continue;
           WorkItem it{};
-          it.group = t.first;
-          it.pad = t.n;
+          it.group = bk.first;
+          it.pad = bk.n;
           it.a0 = lo; it.a1 = hi;
           it.b0 = r;
           P.bound_items.push_back(it);
@@ -809,6 +832,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (!P.bound_items.empty()) {
       bl.items = di + off_bound;
       bl.n_items = (int)P.bound_items.size();
+      bl.groups_per_wave = P.bound_gpw;
     }
     bl.stats = st;
     {

@@ -169,9 +169,10 @@ struct BoundLaunch {
   float* debug_ub;           // [total_q, debug_ld] or NULL
   int32_t debug_ld;
   int32_t splits;            // key splits per group (grid = n_groups * splits; per-group kernel)
-  const WorkItem* items;     // tiled kernel: one per (tile, key share): group = first group,
+  const WorkItem* items;     // tiled kernel: one per (query block, key share): group = first group,
                              // pad = groups, [a0, a1) keys, b0 = share index; NULL = per-group kernel
   int32_t n_items;
+  int32_t groups_per_wave;   // tiled kernel: 4 / (queries per group)
   unsigned long long* stats;
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;

@@ -771,13 +771,15 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
-// bound pass over LDS key tiles: a workgroup takes one query tile (up to 8
-// groups, one wavefront each; the groups of a tile share their bounded range)
-// and a 64-key-aligned share of that range.  Keys, their scales and norms are
+// bound pass over LDS key tiles: a workgroup takes up to 32 consecutive
+// queries of one sequence -- groups_per_wave query groups per wavefront, so
+// that each wavefront fills the 4 query slots of its MFMA rows (16 rows = 4
+// certificate rows x 4 queries) -- and a 64-key-aligned share of their
+// bounded keys.  The groups share the first bounded key; each group's range
+// ends where its own seed window starts.  Keys, their scales and norms are
 // staged through LDS (double-buffered, register prefetch), so every key is
-// read once per tile instead of once per group.  Each wavefront evaluates the
-// certificate of its 4 queries on MFMA (16 rows = 4 rows x 4 queries) and
-// writes one 64-bit union-survivor word per 64 keys.
+// read once per workgroup.  Each group gets one 64-bit union-survivor word per
+// 64 keys.
 // ---------------------------------------------------------------------------
 template <int C, int D>
 __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const BoundLaunch p) {
@@ -794,22 +796,32 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   const int lane = lane_id();
   const WorkItem it = p.items[blockIdx.x];
   const GroupInfo g0 = p.groups[it.group];
-  const bool active = wave < it.pad;
-  const int gi = it.group + (active ? wave : 0);
-  const GroupInfo gr = p.groups[gi];
+  const int gpw = p.groups_per_wave, qw = 4 / gpw;   // groups per wavefront, query slots per group
+  const int gbase = it.group + wave * gpw, gend = it.group + it.pad;
+  const bool active = gbase < gend;
   const int col = lane & 15, g = lane >> 4;
   const int lo = it.a0, hi = it.a1;                  // keys [lo, hi), lo - bound_lo a multiple of 64
-  unsigned long long* mw = p.masks + (int64_t)gi * p.mask_words;
-  const bool qok = active && g < gr.nq;
-  const int qrow = gr.q_row0 + g;
+  // this lane's output rows 4g..4g+3 = the 4 certificate rows of query slot g:
+  // query gq of group gj of the wavefront
+  const int gj = g / qw, gq = g % qw;
+  const bool gok = gbase + gj < gend;
+  const GroupInfo gr = p.groups[gok ? gbase + gj : it.group];
+  const int ghi = min(hi, gr.bound_lo + gr.n_bounded);   // the group's bounded keys end here
+  unsigned long long* mw = p.masks + (int64_t)(gok ? gbase + gj : it.group) * p.mask_words;
+  const bool qok = gok && gq < gr.nq;
+  const int qrow = gr.q_row0 + gq;
   float cf[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) cf[i] = qok ? p.coef[(int64_t)qrow * 8 + i] : 0.f;
   const int npx = (int)cf[6];
   const bool hopeless = !qok || cf[7] != 0.f;
-  const bool all_hopeless = __ballot(qok && !hopeless) == 0ull;    // this wavefront's group
-  const u64 nbounded = (u64)max(hi - lo, 0) * (u64)(active ? gr.nq : 0);
-  if (p.stats != nullptr && lane == 0 && active && all_hopeless && it.b0 == 0) {
+  // lanes of this lane's group, and whether every query of it is hopeless
+  const u64 gmask = (qw == 4) ? ~0ull : (((1ull << (16 * qw)) - 1ull) << (16 * qw * gj));
+  const u64 prunable = __ballot(qok && !hopeless);
+  const bool g_hopeless = (prunable & gmask) == 0ull;
+  const bool all_hopeless = prunable == 0ull;        // every group of this wavefront
+  const bool g_lead = gok && gq == 0 && col == 0;    // one lane per group keeps its books
+  if (p.stats != nullptr && g_lead && g_hopeless && it.b0 == 0) {
     const u64 all = (u64)gr.n_bounded * (u64)gr.nq;   // the group's first share counts the whole group
     atomicAdd(&p.stats[2], all);
     atomicAdd(&p.stats[3], all);
@@ -822,8 +834,16 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   {
     const int ra = lane & 15;
     const int qa = ra >> 2, rr = ra & 3;
-    if (active && qa < gr.nq)
-      O::load_q(static_cast<const uint8_t*>(p.rows) + ((int64_t)(gr.q_row0 + qa) * 4 + rr) * D * O::QB, g, A);
+    const int ga = gbase + qa / qw, ia = qa % qw;
+    bool ok = false;
+    int64_t arow = 0;
+    if (ga < gend) {
+      const GroupInfo gg = p.groups[ga];
+      ok = ia < gg.nq;
+      arow = (int64_t)(gg.q_row0 + ia) * 4 + rr;
+    }
+    if (ok)
+      O::load_q(static_cast<const uint8_t*>(p.rows) + arow * D * O::QB, g, A);
     else
       O::zero(A);
   }
@@ -870,7 +890,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   u64 n_surv = 0;
   drain_memory();   // the certificate rows and coefficients, before the prefetching loop
   // Tile t+1 is loaded while tile t is bounded and written to LDS before the
-  // tile's survivor word is stored; the last iteration reloads its own tile
+  // tile's survivor words are stored; the last iteration reloads its own tile
   // into the idle buffer, so no load stays pending across the back edge.
   if (ntiles > 0) {
     fetch(0);
@@ -901,19 +921,30 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
           else neg += cf[i] * c[i];
         }
         const float ub = kinfo[bufi][0][kslot] * (pos - fmaxf(neg, 0.f)) + cf[4] * kinfo[bufi][1][kslot];
-        const bool valid = qok && key < hi;
+        const bool valid = qok && key < ghi;
         if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
         const bool surv = valid && (hopeless || ub >= cf[5]);
         const u64 m = __ballot(surv);
-        n_surv += __popcll(m);
-        word |= (u64)((uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu) << (16 * b);
+        n_surv += __popcll(__ballot(surv && !g_hopeless));
+        // this group's union over its query slots
+        const u64 mg = (m & gmask) >> (16 * qw * gj);
+        const uint32_t u = (uint32_t)(mg | (mg >> 16) | (mg >> 32) | (mg >> 48)) & 0xFFFFu;
+        word |= (u64)u << (16 * b);
       }
     }
     commit(bufi ^ 1);
-    if (work && !all_hopeless && lane == 0) mw[(kb - gr.bound_lo) >> 6] = word;
+    if (work && g_lead && !g_hopeless) mw[(kb - gr.bound_lo) >> 6] = word;
     __syncthreads();
   }
-  if (active && !all_hopeless && p.stats != nullptr && lane == 0) {
+  if (work && lane == 0 && p.stats != nullptr) {
+    // pairs bounded in this share by the wavefront's groups that were not hopeless
+    u64 nbounded = 0;
+    for (int j = 0; j < gpw; ++j) {
+      if (gbase + j >= gend) break;
+      const GroupInfo gg = p.groups[gbase + j];
+      if (((prunable >> (16 * qw * j)) & (qw == 4 ? ~0ull : ((1ull << (16 * qw)) - 1ull))) == 0ull) continue;
+      nbounded += (u64)max(min(hi, gg.bound_lo + gg.n_bounded) - lo, 0) * (u64)gg.nq;
+    }
     atomicAdd(&p.stats[2], nbounded);
     atomicAdd(&p.stats[3], n_surv);
   }
