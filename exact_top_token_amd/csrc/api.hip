@@ -145,6 +145,16 @@ struct TileInfo {
   int first, n, n_last, seq;
 };
 
+// Work items of one launch, longest key range first: the dispatcher hands out
+// workgroups in item order, so the short items fill the tail of the launch
+// (longest-processing-time-first scheduling).  Stable, so the order of equal
+// items stays the plan's.
+void longest_first(std::vector<WorkItem>& v, size_t from) {
+  std::stable_sort(v.begin() + (std::ptrdiff_t)from, v.end(), [](const WorkItem& x, const WorkItem& y) {
+    return (x.a1 - x.a0) + (x.b1 - x.b0) > (y.a1 - y.a0) + (y.b1 - y.b0);
+  });
+}
+
 // Split choice: enough work items to fill the GPU (target items), keeping at
 // least min_keys keys per split.
 int choose_splits(int64_t n_units, int64_t avg_keys, int64_t target, int64_t min_keys) {
@@ -211,6 +221,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   // dense scoring of whole tiles: J key ranges per tile, regions 0..J-1
   auto dense_tiled_items = [&](std::vector<WorkItem>& out) {
     const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(NT, avg_keys, tiled_target, 1024);
+    const size_t first = out.size();
     for (const auto& t : tiles)
       for (int r = 0; r < J; ++r) {
         int lo, hi;
@@ -228,6 +239,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         }
         out.push_back(it);
       }
+    longest_first(out, first);
     return J;
   };
   if (dense) {
@@ -387,6 +399,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
           P.bound_items.push_back(it);
         }
       }
+      longest_first(P.bound_items, 0);
     }
     // probe: with enough tiles, the last tile (longest contexts) is seeded and
     // planned first; if its certificate can prune no query, the call scores
