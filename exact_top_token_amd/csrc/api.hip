@@ -670,7 +670,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     e = launch_prep(P.combo, H, d, pr, stream);
   }
   if (e != hipSuccess) return fail_hip(e, "prep kernel launch");
-  CandBuf cb{reinterpret_cast<u64*>(ws + P.o_cand), reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R, P.cap};
+  CandBuf cb{reinterpret_cast<u64*>(ws + P.o_cand), reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R, P.cap,
+             (int64_t)P.total_q};
   const GroupInfo* dg = reinterpret_cast<const GroupInfo*>(ws + P.o_groups);
   const WorkItem* di = reinterpret_cast<const WorkItem*>(ws + P.o_items);
   if (dense) {
@@ -866,8 +867,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     cl.lists = lists;
     cl.list_len = list_len;
     cl.group_flags = gflags;
-    cl.counts = cb.counts;
-    cl.R = P.R;
+    cl.cb = cb;
     cl.r0 = P.Js;
     cl.r1 = P.Js + P.J;
     cl.mode = mode;

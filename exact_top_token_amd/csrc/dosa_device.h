@@ -273,13 +273,15 @@ __device__ __forceinline__ float norm_up(float n2) { return sqrtf(n2) * 1.000015
 constexpr int kBatch = 8;
 
 // Segmented view of a query's candidate regions.
+// The regions r0.. of one query: entries and counts of region r0 + r.
 struct Segs {
-  const u64* base;   // region 0 of this query
-  const uint32_t* counts;
-  int cap;
+  const u64* base;         // the query's row in region r0
+  const uint32_t* counts;  // the query's count in region r0
+  int64_t rstride;         // entries from one region's row to the next
+  int64_t cstride;         // counts from one region to the next
   int nseg;
-  __device__ __forceinline__ uint32_t n(int r) const { return counts[r]; }
-  __device__ __forceinline__ const u64* ptr(int r) const { return base + (int64_t)r * cap; }
+  __device__ __forceinline__ uint32_t n(int r) const { return counts[(int64_t)r * cstride]; }
+  __device__ __forceinline__ const u64* ptr(int r) const { return base + (int64_t)r * rstride; }
 };
 
 // K-th largest of the (distinct) entries of the segments, K >= 1 and

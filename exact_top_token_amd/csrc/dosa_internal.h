@@ -70,13 +70,20 @@ struct Inputs {
   int32_t max_pages;
 };
 
-// Candidate buffers: entry (q_row, region, i) at cand[(q_row*R + region)*cap + i];
-// counts[q_row*R + region].
+// Candidate buffers, region-major: entry (q_row, region, i) at
+// cand[(region*rows + q_row)*cap + i], count at counts[region*rows + q_row].
+// The rows of one region are contiguous, so a scoring launch that fills a few
+// regions writes a compact span of memory however many regions the call has.
 struct CandBuf {
   unsigned long long* cand;
   uint32_t* counts;
   int32_t R;
   int32_t cap;
+  int64_t rows;              // query rows of the call
+  __host__ __device__ unsigned long long* row(int64_t q, int r) const {
+    return cand + ((int64_t)r * rows + q) * cap;
+  }
+  __host__ __device__ uint32_t* count(int64_t q, int r) const { return counts + (int64_t)r * rows + q; }
 };
 
 // Weighted query sums (see prep.hip): rows [total_q, 16/QW, d] in the query
@@ -191,9 +198,9 @@ struct CompactLaunch {
   int32_t* list_len;
   int32_t* group_flags;      // out: 1 if the group's tile is scored whole: over its union list
                              // (allow_union) or over its bounded range
-  uint32_t* counts;          // candidate counts [total_q, R]: regions [r0, r1) of the tile's
-  int32_t R, r0, r1;         // queries are zeroed here (the survivor pass writes only the regions
-                             // it fills, the final merge reads them all)
+  CandBuf cb;                // candidate counts of regions [r0, r1) of the tile's queries are
+  int32_t r0, r1;            // zeroed here (the survivor pass writes only the regions it fills,
+                             // the final merge reads them all)
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;
 };

@@ -1017,7 +1017,7 @@ __global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
     const GroupInfo g = p.groups[gi0 + wave];
     const int nr = p.r1 - p.r0;
     for (int e = lane; e < g.nq * nr; e += 64)
-      p.counts[(int64_t)(g.q_row0 + e / nr) * p.R + p.r0 + e % nr] = 0u;
+      *p.cb.count(g.q_row0 + e / nr, p.r0 + e % nr) = 0u;
   }
   __syncthreads();
   auto word = [&](int g, int wd) -> u64 {

@@ -198,7 +198,7 @@ struct Scorer {
     // lanes of absent queries get an unreachable threshold, so they never append
     theta = qok() ? (p.theta_init != nullptr ? p.theta_init[qrow()] : -INFINITY) : INFINITY;
     count = 0;
-    buf = qok() ? p.cb.cand + ((int64_t)qrow() * p.cb.R + region) * p.cb.cap : nullptr;
+    buf = qok() ? p.cb.row(qrow(), region) : nullptr;
     qh = hq;
     for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
     hbase = 0;
@@ -266,7 +266,7 @@ struct Scorer {
     const int cap = p.cb.cap;
     const uint32_t cq = __shfl(count, 16 * (qq * (4 / QW)), 64);
     const float tq = __shfl(theta, 16 * (qq * (4 / QW)), 64);
-    u64* bq = p.cb.cand + ((int64_t)(gr.q_row0 + qq) * p.cb.R + region) * cap;
+    u64* bq = p.cb.row(gr.q_row0 + qq, region);
     const u64 r = shrink_region(bq, cq, tq, cap, p.topk, shist);
     const uint32_t nk = (uint32_t)r & 0x7FFFFFFFu;
     if ((uint32_t)r >> 31) ++n_reselect;
@@ -435,7 +435,7 @@ struct Scorer {
       const uint32_t cq = __shfl(count, 16 * (qq * (4 / QW)), 64);
       const float tq = __shfl(theta, 16 * (qq * (4 / QW)), 64);
       if (cq > (uint32_t)p.topk && tq > -INFINITY) {
-        u64* bq = p.cb.cand + ((int64_t)(gr.q_row0 + qq) * p.cb.R + region) * p.cb.cap;
+        u64* bq = p.cb.row(gr.q_row0 + qq, region);
         const uint32_t nk = compact_ge(bq, cq, (u64)f2ord(tq) << 32, bq, 0);
         if (qi() == qq) count = nk;
       }
@@ -444,7 +444,7 @@ struct Scorer {
   }
 
   __device__ __forceinline__ void finish(const ScoreLaunch& p, int region) {
-    if (qok() && lane_id() == owner_lane0()) p.cb.counts[(int64_t)qrow() * p.cb.R + region] = count;
+    if (qok() && lane_id() == owner_lane0()) *p.cb.count(qrow(), region) = count;
     if (p.stats != nullptr && lane_id() == 0) {
       atomicAdd(&p.stats[p.scored_slot], (u64)n_scored);
       if (p.scored_slot2 > 0) atomicAdd(&p.stats[p.scored_slot2], (u64)n_scored);

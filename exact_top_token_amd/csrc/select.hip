@@ -68,13 +68,13 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int lane = lane_id();
-  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
-  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
-  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
+  const int K = p.topk;
+  const u64* base = p.cb.row(q, p.r0);
+  const uint32_t* cnt = p.cb.count(q, p.r0);
   const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
+  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg};
   uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += cnt[r];
-  Segs sg{base, cnt, cap, nseg};
+  for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth_nt<NT>(sg, K, hist);
   if (p.tau_out != nullptr && threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
@@ -84,10 +84,10 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
     if (threadIdx.x >= 64) return;
     if (total > (uint32_t)K) {
       for (int r = 0; r < nseg; ++r) {
-        u64* ptr = p.cb.cand + ((int64_t)q * R + p.r0 + r) * cap;
-        const uint32_t nk = compact_ge(ptr, cnt[r], T, ptr, 0);
-        wave_sync();   // every lane has read cnt[r] before lane 0 rewrites it
-        if (lane == 0) p.cb.counts[(int64_t)q * R + p.r0 + r] = nk;
+        u64* ptr = p.cb.row(q, p.r0 + r);
+        const uint32_t nk = compact_ge(ptr, sg.n(r), T, ptr, 0);
+        wave_sync();   // every lane has read the count before lane 0 rewrites it
+        if (lane == 0) *p.cb.count(q, p.r0 + r) = nk;
       }
     }
     return;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
     __shared__ uint32_t offs[kMaxMergeRegions * (NW > 1 ? NW : 1)];
     const int w = (int)(threadIdx.x >> 6);
     for (int r = 0; r < nseg; ++r) {
-      const uint32_t n = cnt[r];
+      const uint32_t n = sg.n(r);
       const uint32_t lo = (uint32_t)((uint64_t)n * w / NW), hi = (uint32_t)((uint64_t)n * (w + 1) / NW);
       const uint32_t c = count_ge(sg.ptr(r) + lo, hi - lo, T);
       if (lane == 0) offs[r * NW + w] = c;
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
     }
     __syncthreads();
     for (int r = 0; r < nseg; ++r) {
-      const uint32_t n = cnt[r];
+      const uint32_t n = sg.n(r);
       const uint32_t lo = (uint32_t)((uint64_t)n * w / NW), hi = (uint32_t)((uint64_t)n * (w + 1) / NW);
       emit_ge(sg.ptr(r) + lo, hi - lo, T, oi, os, offs[r * NW + w], K);
     }
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
     return;
   }
   if (threadIdx.x >= 64) return;
-  for (int r = 0; r < nseg; ++r) out = emit_ge(sg.ptr(r), cnt[r], T, oi, os, out, K);
+  for (int r = 0; r < nseg; ++r) out = emit_ge(sg.ptr(r), sg.n(r), T, oi, os, out, K);
   out = min(out, (uint32_t)K);
   for (uint32_t i = out + lane; i < (uint32_t)K; i += 64) {
     oi[i] = -1;
@@ -148,13 +148,13 @@ __global__ __launch_bounds__(256) void select_tau_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
-  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
-  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
-  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
+  const int K = p.topk;
+  const u64* base = p.cb.row(q, p.r0);
+  const uint32_t* cnt = p.cb.count(q, p.r0);
   const int nseg = p.r1 - p.r0;
+  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg};
   uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += cnt[r];
-  Segs sg{base, cnt, cap, nseg};
+  for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth_nt<256>(sg, K, hist);
   if (threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
@@ -168,13 +168,13 @@ __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p)
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int lane = lane_id();
-  const int R = p.cb.R, cap = p.cb.cap, K = p.topk;
-  const u64* base = p.cb.cand + ((int64_t)q * R + p.r0) * cap;
-  const uint32_t* cnt = p.cb.counts + (int64_t)q * R + p.r0;
+  const int K = p.topk;
+  const u64* base = p.cb.row(q, p.r0);
+  const uint32_t* cnt = p.cb.count(q, p.r0);
   const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
+  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg};
   uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += cnt[r];
-  Segs sg{base, cnt, cap, nseg};
+  for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth(sg, K, hist);
   if (p.tau_out != nullptr && lane == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p)
   uint32_t out = 0;
   for (int r = 0; r < nseg; ++r) {
     const u64* src = sg.ptr(r);
-    const uint32_t n = cnt[r];
+    const uint32_t n = sg.n(r);
     for (uint32_t b0 = 0; b0 < n; b0 += 64 * kBatch) {
       u64 e[kBatch];
 #pragma unroll
