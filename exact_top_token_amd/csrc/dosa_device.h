@@ -350,6 +350,49 @@ __device__ __noinline__ u64 select_kth_nt(const Segs sg, int K, uint32_t* hist) 
 
 __device__ __forceinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) { return select_kth_nt<64>(sg, K, hist); }
 
+// The same K-th largest for a query whose total entry count fits an LDS
+// stage (total <= stage capacity): the entries of all segments are copied to
+// the stage once, with batches of loads in flight together, and the radix
+// passes then read LDS instead of re-reading every segment from memory.
+// stot: one u32 of LDS.
+template <int NT>
+__device__ __forceinline__ u64 select_kth_staged(const Segs sg, uint32_t total, int K, uint32_t* hist, u64* stage,
+                                                 uint32_t* stot) {
+  const int tid = (int)threadIdx.x;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t a = 0;
+    for (int r = 0; r < sg.nseg; ++r) {
+      hist[r] = a;
+      a += sg.n(r);
+    }
+    hist[sg.nseg] = a;
+    *stot = a;
+  }
+  __syncthreads();
+  constexpr int B = 8;
+  for (uint32_t b = 0; b < total; b += (uint32_t)NT * B) {
+    u64 e[B];
+    int r = 0;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const uint32_t i = b + (uint32_t)NT * u + tid;
+      e[u] = 0ull;
+      if (i < total) {
+        while (hist[r + 1] <= i) ++r;
+        e[u] = sg.ptr(r)[i - hist[r]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const uint32_t i = b + (uint32_t)NT * u + tid;
+      if (i < total) stage[i] = e[u];
+    }
+  }
+  const Segs one{stage, stot, 0, 0, 1};
+  return select_kth_nt<NT>(one, K, hist);   // starts with a barrier
+}
+
 // Copy the entries >= T of src[0..n) to dst[out..] in order (dst may equal
 // src, with out <= 0 then).  Returns the new end.  Entries are read kBatch
 // wavefront-rows at a time before any is written: in place, every write

@@ -144,8 +144,14 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
 // Threshold only: tau_out = the K-th largest entry's score over regions
 // [r0, r1) (-inf if fewer than K), by 4 wavefronts per query and without
 // touching the regions.  For small launches whose time is one query's latency.
-__global__ __launch_bounds__(256) void select_tau_kernel(const SelectLaunch p) {
+constexpr uint32_t kTauStage = 6144;   // entries staged in LDS (48 KiB): the seed window and prefix at defaults
+
+constexpr int kTauThreads = 256;       // per query (1024 measured slower)
+
+__global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
+  __shared__ u64 stage[kTauStage];
+  __shared__ uint32_t stot;
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int K = p.topk;
@@ -156,7 +162,9 @@ __global__ __launch_bounds__(256) void select_tau_kernel(const SelectLaunch p) {
   uint32_t total = 0;
   for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
-  if (total >= (uint32_t)K) T = select_kth_nt<256>(sg, K, hist);
+  if (total >= (uint32_t)K)
+    T = (total <= kTauStage && sg.nseg < 2048) ? select_kth_staged<kTauThreads>(sg, total, K, hist, stage, &stot)
+                                               : select_kth_nt<kTauThreads>(sg, K, hist);
   if (threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
 }
 
@@ -248,7 +256,7 @@ hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream
 
 hipError_t launch_select_tau(const SelectLaunch& p, hipStream_t s) {
   if (p.total_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_tau_kernel, dim3(p.total_q), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(select_tau_kernel, dim3(p.total_q), dim3(kTauThreads), 0, s, p);
   return hipGetLastError();
 }
 
