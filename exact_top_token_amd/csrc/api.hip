@@ -96,7 +96,7 @@ struct Plan {
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
-         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, total = 0;
+         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -154,6 +154,9 @@ void longest_first(std::vector<WorkItem>& v, size_t from) {
     return (x.a1 - x.a0) + (x.b1 - x.b0) > (y.a1 - y.a0) + (y.b1 - y.b0);
   });
 }
+
+// Key splits of one query share their running thresholds (see ScoreLaunch).
+constexpr bool kShareTheta = true;
 
 // Split choice: enough work items to fill the GPU (target items), keeping at
 // least min_keys keys per split.
@@ -475,6 +478,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.o_lrows = take((size_t)P.total_q * LS * d * qbytes(q_dtype));
   P.o_lsig = take((size_t)P.total_q * LS * sizeof(float));
   P.o_lerr = take((size_t)P.total_q * 2 * sizeof(float));
+  P.o_tshare = take((size_t)P.total_q * sizeof(uint32_t));
   if (!dense) {
     P.o_tau = take((size_t)P.total_q * sizeof(float));
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
@@ -664,7 +668,9 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   }
   Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages};
   PrepLaunch pr{q, w, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
-                reinterpret_cast<float*>(ws + P.o_lerr), dense ? nullptr : reinterpret_cast<int32_t*>(ws + P.o_flag)};
+                reinterpret_cast<float*>(ws + P.o_lerr), dense ? nullptr : reinterpret_cast<int32_t*>(ws + P.o_flag),
+                reinterpret_cast<uint32_t*>(ws + P.o_tshare)};
+  uint32_t* tshare = kShareTheta ? reinterpret_cast<uint32_t*>(ws + P.o_tshare) : nullptr;
   {
     PassScope ps(P_PREP, stream);
     e = launch_prep(P.combo, H, d, pr, stream);
@@ -676,6 +682,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   const WorkItem* di = reinterpret_cast<const WorkItem*>(ws + P.o_items);
   if (dense) {
     ScoreLaunch sl{};
+    sl.theta_share = tshare;
     sl.in = in;
     sl.lrows = pr.rows;
     sl.lsig = pr.sig;
@@ -722,6 +729,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (P.probe) {
       PassScope ps(P_PROBE, stream);
       ScoreLaunch pb{};
+      pb.theta_share = tshare;
       pb.in = in;
       pb.lrows = pr.rows;
       pb.lsig = pr.sig;
@@ -765,6 +773,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     // 2. seed pass: exact scores of the seed keys into regions 0..Js-1
     ScoreLaunch sl{};
+    sl.theta_share = tshare;
     sl.mode = mode;
     sl.run_if = MODE_PRUNED;
     sl.in = in;
@@ -881,6 +890,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     //    flagged tiles take the tiled kernel over their union list (or, in calls
     //    without tiles, over the bounded range), the other groups walk their own lists
     ScoreLaunch ml{};
+    ml.theta_share = tshare;
     ml.mode = mode;
     ml.run_if = MODE_PRUNED;
     ml.in = in;
@@ -917,6 +927,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     // 8. the dense alternative, run only when the probe found nothing to prune
     if (P.probe) {
       ScoreLaunch dl{};
+      dl.theta_share = tshare;
       dl.mode = mode;
       dl.run_if = MODE_UNPRUNED;
       dl.in = in;

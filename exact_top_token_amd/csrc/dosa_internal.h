@@ -97,6 +97,7 @@ struct PrepLaunch {
   float* sig;
   float* err;
   int32_t* flag;        // cleared here (query 0): the plan's "some query can prune" flag, or NULL
+  uint32_t* tshare;     // [total_q] cleared here: the shared running thresholds (ScoreLaunch)
 };
 
 struct ScoreLaunch {
@@ -108,6 +109,8 @@ struct ScoreLaunch {
   int32_t n_items;
   CandBuf cb;
   const float* theta_init;   // [total_q] or NULL (-inf)
+  uint32_t* theta_share;     // [total_q] order-preserving images of running thresholds that every
+                             // launch of the call publishes to and adopts from (0 = none yet), or NULL
   const int32_t* lists;      // survivor lists (gather mode)
   const int32_t* list_len;   // survivor list length per group (gather mode)
   int32_t topk;

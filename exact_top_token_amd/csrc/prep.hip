@@ -134,6 +134,7 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   for (int off = 32; off > 0; off >>= 1) e2 += __shfl_xor(e2, off, 64);
   if (lane == 0) {
     if (q == 0 && p.flag != nullptr) *p.flag = 0;
+    if (p.tshare != nullptr) p.tshare[q] = 0u;
     p.err[(int64_t)q * 2] = (float)(sqrt(e2) * 1.0000005);   // ||qbar - sum sigma f|| (rounded up)
     p.err[(int64_t)q * 2 + 1] = (float)(mag * 1.0000005);    // sum_j sigma_j ||f_j||
   }

@@ -157,6 +157,7 @@ struct Scorer {
   uint32_t wq_lds;   // LDS byte address of this lane's query's weights / 2, then its term scales / 2
   uint32_t* qh;      // LDS: this wavefront's query histograms [QW][kHistBins]
   uint32_t hbase;    // ord value of the lower edge of bin 0 (0 = not anchored yet)
+  uint32_t* tshare;  // the call's shared thresholds (indexed by query row), or NULL
   uint32_t n_written, n_reselect, n_scored;
   bool dirty;        // something was appended since the last refresh (wavefront-uniform)
 
@@ -202,6 +203,7 @@ struct Scorer {
     qh = hq;
     for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
     hbase = 0;
+    tshare = p.theta_share;
     n_written = n_reselect = n_scored = 0;
     dirty = false;
   }
@@ -253,6 +255,16 @@ struct Scorer {
     if (segm != 0ull) {
       const float th = ord2f(e);
       if (th > theta) theta = th;
+    }
+    // Share with the call's other sweeps over this query's keys: publish the
+    // threshold and adopt the largest one published.  Any sweep's threshold
+    // is at most the K-th largest score among its own keys, hence at most the
+    // query's K-th largest, so filtering by it never drops a Top-K key.
+    if (tshare != nullptr) {
+      uint32_t gv = 0u;
+      if (j == 0 && q < nq) gv = atomicMax(tshare + q_row0 + q, f2ord(theta));
+      gv = (uint32_t)__shfl((int)gv, q * LPQ, 64);
+      if (gv != 0u && q < nq) theta = fmaxf(theta, ord2f(gv));
     }
     dirty = false;
   }
