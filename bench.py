@@ -142,6 +142,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="long_prefill_128k")
     ap.add_argument("--L", type=int, default=0, help="override the context length (exploration only)")
+    ap.add_argument("--chunk", type=int, default=0, help="query chunk per call, where the recipe takes one")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--paths", default="dosa,dsa")
@@ -164,6 +165,8 @@ def main():
 
     E.lib()
     kw = {"L": a.L} if a.L else {}
+    if a.chunk:
+        kw["chunk"] = a.chunk
     t0 = time.perf_counter()
     wl = synth.make_workload(a.workload, **kw)
     log(f"generated {wl.name}: q {wl.q.shape} {wl.q_dtype}, k {wl.k.shape} {wl.k_dtype}, "
