@@ -711,28 +711,48 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   v4i stage[NCH];
   float stage_s = 1.f;
   int stage_id = -1;
-  auto fetch_gather = [&](int t) {
+  // Gather mode: the list entries (key positions) of a tile are loaded one
+  // tile ahead of its key rows, so a tile's rows wait for one memory latency,
+  // not for the list read and then the rows.  The last iteration's reload
+  // stages an empty tile into the idle buffer; nothing reads it.
+  int idn[NCH];
+  int idn_s = -1;
+  auto load_ids = [&](int tt) {
     const int tid = lane_fresh() + 64 * wave;
-    const int ib = e1 - TK * (t + 1);               // list index of the tile's slot 0
+    const int ib = e1 - TK * (tt + 1);               // list index of tile tt's slot 0
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const int ch = tid + c * 64 * kTileWaves;
-      const int slot = ch / CPK, part = ch % CPK;
+      const int slot = (tid + c * 64 * kTileWaves) / CPK;
       const int idx = ib + slot;
-      if (slot < TK && idx >= e0) {
-        const int key = ulist[idx];
-        const int64_t row = PAGED ? key_row(p.in, g0.key_base, g0.seq, key) : (int64_t)key;
+      idn[c] = (tt < ntiles && slot < TK && idx >= e0) ? ulist[idx] : -1;
+    }
+    if (tid < TK) {
+      const int idx = ib + tid;
+      idn_s = (tt < ntiles && idx >= e0) ? ulist[idx] : -1;
+    }
+  };
+  auto fetch_gather = [&](int t) {
+    const int tid = lane_fresh() + 64 * wave;
+    int idc[NCH];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) idc[c] = idn[c];
+    const int ids = idn_s;
+    load_ids(t + 1);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int part = (tid + c * 64 * kTileWaves) % CPK;
+      if (idc[c] >= 0) {
+        const int64_t row = PAGED ? key_row(p.in, g0.key_base, g0.seq, idc[c]) : (int64_t)idc[c];
         stage[c] = *reinterpret_cast<const v4i*>(kseq + row * KB + part * 16);
       } else {
         stage[c] = v4i{0, 0, 0, 0};
       }
     }
     if (tid < TK) {
-      const int idx = ib + tid;
-      stage_id = (idx >= e0) ? ulist[idx] : -1;
+      stage_id = ids;
       if constexpr (HasKScale<C>::value) {
-        if (stage_id >= 0)
-          stage_s = PAGED ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, stage_id)] : sseq[(uint32_t)stage_id];
+        if (ids >= 0)
+          stage_s = PAGED ? p.in.k_scale[key_row(p.in, g0.key_base, g0.seq, ids)] : sseq[(uint32_t)ids];
         else
           stage_s = 0.f;
       }
@@ -795,6 +815,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   // last iteration reloads its own tile into the idle buffer: an unconditional
   // load and wait leave nothing pending into the next iteration on any path.
   if (ntiles > 0) {
+    if (kGatherRole && gather) load_ids(0);
     fetch(0);
     commit(0);
   }
