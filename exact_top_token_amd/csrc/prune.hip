@@ -1140,7 +1140,7 @@ hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s
 
 template <int C, int H, int D>
 static hipError_t plan_t(const PlanLaunch& p, hipStream_t s) {
-  hipLaunchKernelGGL((plan_kernel<C, H, D>), dim3(p.n_groups, 4), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((plan_kernel<C, H, D>), dim3(p.n_groups, queries_per_wave(C, H, D)), dim3(256), 0, s, p);   // one workgroup per query slot of a group
   return hipGetLastError();
 }
 
