@@ -388,7 +388,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       const int NB = (int)blocks.size();
       int64_t bsum_t = 0;
       for (const auto& bk : blocks) bsum_t += bk.hi - bk.lo;
-      const int Jb = choose_splits(NB, NB ? bsum_t / NB : 0, 2 * tiled_target, 2048);
+      const int Jb = choose_splits(NB, NB ? bsum_t / NB : 0, 4 * tiled_target, 2048);
       for (const auto& bk : blocks) {
         for (int r = 0; r < Jb; ++r) {
           int lo, hi;

@@ -781,7 +781,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
 // read once per workgroup.  Each group gets one 64-bit union-survivor word per
 // 64 keys.
 // ---------------------------------------------------------------------------
-template <int C, int D>
+template <int C, int D, int GPW>
 __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const BoundLaunch p) {
   using O = Ops<C, D>;
   constexpr int STEPS = O::STEPS;
@@ -796,7 +796,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   const int lane = lane_id();
   const WorkItem it = p.items[blockIdx.x];
   const GroupInfo g0 = p.groups[it.group];
-  const int gpw = p.groups_per_wave, qw = 4 / gpw;   // groups per wavefront, query slots per group
+  constexpr int gpw = GPW, qw = 4 / GPW;              // groups per wavefront, query slots per group
   const int gbase = it.group + wave * gpw, gend = it.group + it.pad;
   const bool active = gbase < gend;
   const int col = lane & 15, g = lane >> 4;
@@ -807,7 +807,6 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   const bool gok = gbase + gj < gend;
   const GroupInfo gr = p.groups[gok ? gbase + gj : it.group];
   const int ghi = min(hi, gr.bound_lo + gr.n_bounded);   // the group's bounded keys end here
-  unsigned long long* mw = p.masks + (int64_t)(gok ? gbase + gj : it.group) * p.mask_words;
   const bool qok = gok && gq < gr.nq;
   const int qrow = gr.q_row0 + gq;
   float cf[8];
@@ -887,6 +886,21 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
       kinfo[bufi][1][tid] = st_n;
     }
   };
+  // Row multipliers split by role, zero elsewhere: proxy rows enter as
+  // c_p ReLU(x), aggregate rows as sigma_j x (adding the zero terms leaves
+  // both sums bit for bit what the role test would give).
+  float cpos[4], cneg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    cpos[i] = (i < npx) ? cf[i] : 0.f;
+    cneg[i] = (i < npx) ? 0.f : cf[i];
+  }
+  // groups of this wavefront that keep books (not hopeless), as lane masks
+  u64 keep_lanes = 0;
+  for (int j = 0; j < gpw; ++j) {
+    const u64 mj = (qw == 4) ? ~0ull : (((1ull << (16 * qw)) - 1ull) << (16 * qw * j));
+    if (gbase + j < gend && (prunable & mj) != 0ull) keep_lanes |= mj;
+  }
   u64 n_surv = 0;
   drain_memory();   // the certificate rows and coefficients, before the prefetching loop
   // Tile t+1 is loaded while tile t is bounded and written to LDS before the
@@ -903,7 +917,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
     const int bufi = t & 1;
     fetch(min(t + 1, ntiles - 1));
     const int kb = lo + 64 * t;
-    u64 word = 0;
+    // one survivor word per group of the wavefront (wavefront-uniform)
+    u64 words[gpw];
+#pragma unroll
+    for (int j = 0; j < gpw; ++j) words[j] = 0ull;
     if (work) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
@@ -917,23 +934,35 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
         float pos = 0.f, neg = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (i < npx) pos += cf[i] * fmaxf(c[i], 0.f);
-          else neg += cf[i] * c[i];
+          pos += cpos[i] * fmaxf(c[i], 0.f);
+          neg += cneg[i] * c[i];
         }
         const float ub = kinfo[bufi][0][kslot] * (pos - fmaxf(neg, 0.f)) + cf[4] * kinfo[bufi][1][kslot];
         const bool valid = qok && key < ghi;
         if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
         const bool surv = valid && (hopeless || ub >= cf[5]);
         const u64 m = __ballot(surv);
-        n_surv += __popcll(__ballot(surv && !g_hopeless));
-        // this group's union over its query slots
-        const u64 mg = (m & gmask) >> (16 * qw * gj);
-        const uint32_t u = (uint32_t)(mg | (mg >> 16) | (mg >> 32) | (mg >> 48)) & 0xFFFFu;
-        word |= (u64)u << (16 * b);
+        n_surv += __popcll(m & keep_lanes);
+        // each group's union over its query slots
+#pragma unroll
+        for (int j = 0; j < gpw; ++j) {
+          u64 u = 0;
+#pragma unroll
+          for (int q = 0; q < qw; ++q) u |= (m >> (16 * (qw * j + q))) & 0xFFFFull;
+          words[j] |= u << (16 * b);
+        }
       }
     }
     commit(bufi ^ 1);
-    if (work && g_lead && !g_hopeless) mw[(kb - gr.bound_lo) >> 6] = word;
+    if (work && lane == 0) {
+#pragma unroll
+      for (int j = 0; j < gpw; ++j) {
+        if (gbase + j >= gend) break;
+        const u64 mj = (qw == 4) ? ~0ull : (((1ull << (16 * qw)) - 1ull) << (16 * qw * j));
+        if ((keep_lanes & mj) == 0ull) continue;
+        p.masks[(int64_t)(gbase + j) * p.mask_words + ((kb - g0.bound_lo) >> 6)] = words[j];
+      }
+    }
     __syncthreads();
   }
   if (work && lane == 0 && p.stats != nullptr) {
@@ -1169,9 +1198,14 @@ template <int C>
 static hipError_t bound_c(int d, const BoundLaunch& p, hipStream_t s) {
   if (p.items != nullptr) {
     if (p.n_items == 0) return hipSuccess;
-    if (d == 64) hipLaunchKernelGGL((bound_tiled_kernel<C, 64>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
-    else hipLaunchKernelGGL((bound_tiled_kernel<C, 128>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
-    return hipGetLastError();
+#define DOSA_BT(DD, G)                                                                                      \
+  if (d == DD && p.groups_per_wave == G) {                                                                  \
+    hipLaunchKernelGGL((bound_tiled_kernel<C, DD, G>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p); \
+    return hipGetLastError();                                                                               \
+  }
+    DOSA_BT(64, 1) DOSA_BT(64, 2) DOSA_BT(64, 4) DOSA_BT(128, 1) DOSA_BT(128, 2) DOSA_BT(128, 4)
+#undef DOSA_BT
+    return hipErrorInvalidValue;
   }
   const int nb = p.n_groups * p.splits;
   if (d == 64) hipLaunchKernelGGL((bound_kernel<C, 64>), dim3(nb), dim3(64), 0, s, p);
