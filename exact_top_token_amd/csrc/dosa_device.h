@@ -350,15 +350,18 @@ __device__ __noinline__ u64 select_kth_nt(const Segs sg, int K, uint32_t* hist) 
 
 __device__ __forceinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) { return select_kth_nt<64>(sg, K, hist); }
 
-// The same K-th largest for a query whose total entry count fits an LDS
-// stage (total <= stage capacity): the entries of all segments are copied to
-// the stage once, with batches of loads in flight together, and the radix
-// passes then read LDS instead of re-reading every segment from memory.
-// stot: one u32 of LDS.
+// A score threshold for a query whose total entry count fits an LDS stage
+// (total <= stage capacity, K <= total): the score images (upper 32 bits) of
+// all segments' entries are copied to the stage once, with batches of loads
+// in flight together, then a radix select on 11/11/10-bit digits runs on LDS.
+// Returns an image T with exactly K staged images >= T (the K-th largest
+// image, or the lower edge of the digit bin that holds it whole), so the
+// score ord2f(T) never exceeds the K-th largest score.  stot: one u32 of LDS.
 template <int NT>
-__device__ __forceinline__ u64 select_kth_staged(const Segs sg, uint32_t total, int K, uint32_t* hist, u64* stage,
-                                                 uint32_t* stot) {
+__device__ __forceinline__ uint32_t select_kth_score_staged(const Segs sg, uint32_t total, int K, uint32_t* hist,
+                                                            uint32_t* stage) {
   const int tid = (int)threadIdx.x;
+  const int lane = lane_id();
   __syncthreads();
   if (tid == 0) {
     uint32_t a = 0;
@@ -367,20 +370,19 @@ __device__ __forceinline__ u64 select_kth_staged(const Segs sg, uint32_t total, 
       a += sg.n(r);
     }
     hist[sg.nseg] = a;
-    *stot = a;
   }
   __syncthreads();
   constexpr int B = 8;
   for (uint32_t b = 0; b < total; b += (uint32_t)NT * B) {
-    u64 e[B];
+    uint32_t e[B];
     int r = 0;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const uint32_t i = b + (uint32_t)NT * u + tid;
-      e[u] = 0ull;
+      e[u] = 0u;
       if (i < total) {
         while (hist[r + 1] <= i) ++r;
-        e[u] = sg.ptr(r)[i - hist[r]];
+        e[u] = (uint32_t)(sg.ptr(r)[i - hist[r]] >> 32);
       }
     }
 #pragma unroll
@@ -389,8 +391,41 @@ __device__ __forceinline__ u64 select_kth_staged(const Segs sg, uint32_t total, 
       if (i < total) stage[i] = e[u];
     }
   }
-  const Segs one{stage, stot, 0, 0, 1};
-  return select_kth_nt<NT>(one, K, hist);   // starts with a barrier
+  uint32_t prefix = 0, rem = (uint32_t)K;
+#pragma unroll 1
+  for (int p = 0; p < 3; ++p) {
+    const int sh = (p == 0) ? 21 : (p == 1) ? 10 : 0;
+    const int wd = (p == 2) ? 10 : 11;
+    const int nb = 1 << wd;
+    __syncthreads();   // the stage is written / the previous pass's histogram is read
+    for (int i = tid; i < nb; i += NT) hist[i] = 0;
+    __syncthreads();
+    const uint32_t want = (p == 0) ? 0u : (prefix >> (sh + wd));
+    for (uint32_t i = tid; i < total; i += NT) {
+      const uint32_t v = stage[i];
+      if (p == 0 || (v >> (sh + wd)) == want) atomicAdd(&hist[(v >> sh) & (uint32_t)(nb - 1)], 1u);
+    }
+    __syncthreads();
+    const int per = nb >> 6;
+    uint32_t sum = 0;
+    for (int t = 0; t < per; ++t) sum += hist[lane * per + t];
+    const uint32_t suf = wave_suffix_sum(sum);
+    const bool cross = (suf >= rem) && (suf - sum < rem);
+    const u64 cm = __ballot(cross);
+    const int L = cm ? (__ffsll((long long)cm) - 1) : 0;
+    uint32_t acc = __shfl(suf - sum, L, 64);
+    int bin = L * per;
+    uint32_t cnt_b = 0;
+    for (int t = per - 1; t >= 0; --t) {
+      const uint32_t h = hist[L * per + t];
+      if (acc + h >= rem) { bin = L * per + t; cnt_b = h; break; }
+      acc += h;
+    }
+    rem -= acc;
+    prefix |= (uint32_t)bin << sh;
+    if (cnt_b == rem) break;   // the bin holds exactly the remaining entries
+  }
+  return prefix;
 }
 
 // Copy the entries >= T of src[0..n) to dst[out..] in order (dst may equal

@@ -141,31 +141,29 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   }
 }
 
-// Threshold only: tau_out = the K-th largest entry's score over regions
-// [r0, r1) (-inf if fewer than K), by 4 wavefronts per query and without
-// touching the regions.  For small launches whose time is one query's latency.
-constexpr uint32_t kTauStage = 6144;   // entries staged in LDS (48 KiB): the seed window and prefix at defaults
-
+// Threshold only: tau_out = a score with exactly K of the entries of regions
+// [r0, r1) at or above it -- the K-th largest score, or the lower edge of the
+// radix digit bin that holds it -- (-inf if fewer than K), by 4 wavefronts
+// per query and without touching the regions.  For small launches whose time
+// is one query's latency.
+constexpr uint32_t kTauStage = 12288;  // score images staged in LDS (48 KiB): the seed window and prefix at defaults
 constexpr int kTauThreads = 256;       // per query (1024 measured slower)
 
 __global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
-  __shared__ u64 stage[kTauStage];
-  __shared__ uint32_t stot;
+  __shared__ uint32_t stage[kTauStage];
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int K = p.topk;
-  const u64* base = p.cb.row(q, p.r0);
-  const uint32_t* cnt = p.cb.count(q, p.r0);
-  const int nseg = p.r1 - p.r0;
-  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg};
+  const Segs sg{p.cb.row(q, p.r0), p.cb.count(q, p.r0), p.cb.rows * p.cb.cap, p.cb.rows, p.r1 - p.r0};
   uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += sg.n(r);
-  u64 T = 0;
-  if (total >= (uint32_t)K)
-    T = (total <= kTauStage && sg.nseg < 2048) ? select_kth_staged<kTauThreads>(sg, total, K, hist, stage, &stot)
-                                               : select_kth_nt<kTauThreads>(sg, K, hist);
-  if (threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
+  for (int r = 0; r < sg.nseg; ++r) total += sg.n(r);
+  float tau = -INFINITY;
+  if (total >= (uint32_t)K) {
+    if (total <= kTauStage && sg.nseg < 2048) tau = ord2f(select_kth_score_staged<kTauThreads>(sg, total, K, hist, stage));
+    else tau = key_score(select_kth_nt<kTauThreads>(sg, K, hist));
+  }
+  if (threadIdx.x == 0) p.tau_out[q] = tau;
 }
 
 // Same merge, rows ordered by (score desc, position asc): the kept keys are

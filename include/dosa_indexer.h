@@ -103,7 +103,7 @@ typedef enum {
  * only change how much work the certificate saves. */
 typedef struct {
   int32_t num_proxies;      /* positive heads evaluated exactly in the bound: 0..3 (default 3) */
-  int32_t seed_window;      /* seed = the last seed_window visible keys ... (default 4096) */
+  int32_t seed_window;      /* seed = the last seed_window visible keys ... (default 4*topk, >= 64) */
   int32_t seed_prefix;      /* ... plus the first seed_prefix keys (default 64) */
   int32_t buffer_cap;       /* entries per candidate region (each query has one region per key
                                range scored in parallel); 0 = automatic (default): about

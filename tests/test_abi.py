@@ -29,7 +29,8 @@ def test_library_loads_and_exports_all_declared_symbols():
 
 def test_default_config_values():
     c = E.default_config(2048)
-    assert (c.num_proxies, c.seed_window, c.seed_prefix, c.buffer_cap) == (3, 4096, 64, 0)
+    assert (c.num_proxies, c.seed_window, c.seed_prefix, c.buffer_cap) == (3, 8192, 64, 0)
+    assert E.default_config(8).seed_window == 64
     assert abs(c.neg_support_frac - 0.5) < 1e-7 and c.flags == 0
 
 
