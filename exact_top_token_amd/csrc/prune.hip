@@ -19,6 +19,7 @@
 // UB >= S for the fp32 values both kernels compute.  A key is pruned iff
 // UB < tau, tau being the K-th largest seed score.
 #include <cstring>
+#include <type_traits>
 #include <vector>
 
 #include "dosa_device.h"
@@ -255,8 +256,17 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   const int hh = t / PARTS, part = t % PARTS;
   const int g = lane >> 4, col = lane & 15;
 
-  constexpr int QS = D + 4;                        // LDS row stride of the decoded query (floats)
-  __shared__ float qf[H * QS];                     // decoded, unscaled (exact in fp32)
+  constexpr int QS = D + 4;                        // LDS row stride of the query (elements)
+  // the query in its stored type (decoded on read: fp8 and bf16 values are
+  // exact in fp32), rows of QS elements; a decoded fp32 copy would double or
+  // quadruple the kernel's LDS and cost a resident workgroup per CU
+  typedef typename std::conditional<QB == 4, float, typename std::conditional<QB == 2, uint16_t, uint8_t>::type>::type qraw_t;
+  __shared__ __align__(16) qraw_t qf[H * QS];
+  auto qval = [&](int idx) -> float {
+    if constexpr (QB == 4) return qf[idx];
+    else if constexpr (QB == 2) return dec_bf16((uint32_t)qf[idx]);
+    else return dec_fp8((uint32_t)qf[idx]);
+  };
   __shared__ __align__(16) uint8_t kraw[kSampleKeys * KRS];   // staged keys, stored type
   __shared__ __align__(16) uint8_t rowl[4 * D * QB];          // the certificate rows
   __shared__ double wd[H], qn2[H], alpha[H][3], gph[3][H];
@@ -314,18 +324,14 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     if constexpr (HasKScale<C>::value) kscale = p.in.k_scale[key_row(p.in, gr.key_base, gr.seq, key)];
   }
 
-  // ---- 1. query (decoded) and activation keys (stored type) to LDS
+  // ---- 1. query and activation keys (stored type) to LDS
 #pragma unroll
   for (int j = 0; j < NQV; ++j) {
     const int c = t + 256 * j;
     if (c < QCH) {
-      float f[16 / QB];
-      dec16<QB>(qv[j], f);
-#pragma unroll
-      for (int m = 0; m < 16 / QB; ++m) {
-        const int e = c * (16 / QB) + m;
-        qf[(e / D) * QS + e % D] = f[m];
-      }
+      const int e = c * (16 / QB);                   // first element of the chunk (one row holds it whole)
+      uint32_t* dst = reinterpret_cast<uint32_t*>(&qf[(e / D) * QS + e % D]);
+      dst[0] = qv[j].x; dst[1] = qv[j].y; dst[2] = qv[j].z; dst[3] = qv[j].w;
     }
   }
 #pragma unroll
@@ -366,7 +372,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   // ---- 3. squared norms, proxies, proxy inner products (fp64 of exact values)
   float qr[EL];
 #pragma unroll
-  for (int e = 0; e < EL; ++e) qr[e] = qf[hh * QS + part + PARTS * e];
+  for (int e = 0; e < EL; ++e) qr[e] = qval(hh * QS + part + PARTS * e);
   {
     double s2 = 0.0;
 #pragma unroll
@@ -398,10 +404,10 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __syncthreads();
   const int np = np_s;
   for (int r = 0; r < np; ++r) {
-    const float* pr = qf + prox[r] * QS + part;
+    const int pr = prox[r] * QS + part;
     double dsum = 0.0;
 #pragma unroll
-    for (int e = 0; e < EL; ++e) dsum = fma((double)qr[e], (double)pr[PARTS * e], dsum);
+    for (int e = 0; e < EL; ++e) dsum = fma((double)qr[e], (double)qval(pr + PARTS * e), dsum);
     dsum = part_sum<PARTS>(dsum);
     if (part == 0) gph[r][hh] = dsum;
   }
@@ -460,7 +466,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
 #pragma unroll 8
         for (int h = 0; h < H; ++h) {
           const bool in_a = wd[h] < 0.0 && (ns > 0 ? (double)act[h] >= need : p.neg_frac <= 0.f);
-          if (in_a) sacc = fma(-wd[h], (double)qf[h * QS + i], sacc);
+          if (in_a) sacc = fma(-wd[h], (double)qval(h * QS + i), sacc);
         }
       }
       avec[i] = sacc;
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   if (wave == 0) {
     for (int e = lane; e < np * D; e += 64) {
       const int r = e / D, i = e % D;
-      const float v = qf[prox[r] * QS + i];
+      const float v = qval(prox[r] * QS + i);
       if constexpr (QB == 1) rowl[r * D + i] = (uint8_t)enc_fp8(v);
       else if constexpr (QB == 4) reinterpret_cast<float*>(rowl)[r * D + i] = v;
       else reinterpret_cast<uint16_t*>(rowl)[r * D + i] = (uint16_t)enc_bf16(v);
@@ -620,14 +626,14 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
       while (rem >= NBLK - bi) { rem -= NBLK - bi; ++bi; }
       const int bj = bi + rem;
       const int ha = 16 * bi + lr, hb = 16 * bj + lr;       // operand rows of this lane
-      const float* pa = qf + (ha < H ? ha : 0) * QS + lk;
-      const float* pb = qf + (hb < H ? hb : 0) * QS + lk;
+      const int pa = (ha < H ? ha : 0) * QS + lk;
+      const int pb = (hb < H ? hb : 0) * QS + lk;
       typedef double v4d __attribute__((ext_vector_type(4)));
       v4d gacc = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll 8
       for (int k = 0; k < D / 4; ++k) {
-        const double a = (ha < H) ? (double)pa[4 * k] : 0.0;
-        const double b = (hb < H) ? (double)pb[4 * k] : 0.0;
+        const double a = (ha < H) ? (double)qval(pa + 4 * k) : 0.0;
+        const double b = (hb < H) ? (double)qval(pb + 4 * k) : 0.0;
         gacc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, gacc, 0, 0, 0);
       }
       const int j = 16 * bj + lr;                          // column of this lane's results
