@@ -96,7 +96,7 @@ struct Plan {
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
-         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, total = 0;
+         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -491,6 +491,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
     P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
     P.o_mode = take(sizeof(int32_t));
+    P.o_order = take(sizeof(int32_t) * std::max<size_t>(P.surv_tiled_items.size(), 1));
   }
   P.total = o;
 }
@@ -915,7 +916,14 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       ml.n_items = (int)P.surv_tiled_items.size();
       ml.tiled = P.tiled ? 1 : 0;
       ml.flag_mode = 1;
-      e = launch_score(P.combo, H, d, ml, stream);
+      // union shares are cut on the device: launch them longest first
+      if (P.tiled && ml.n_items > 0 && ml.n_items <= kMaxOrderItems) {
+        OrderLaunch ol{ml.items, ml.n_items, list_len, gflags, reinterpret_cast<int32_t*>(ws + P.o_order), mode,
+                       MODE_PRUNED};
+        e = launch_order(ol, stream);
+        ml.order = ol.order;
+      }
+      if (e == hipSuccess) e = launch_score(P.combo, H, d, ml, stream);
     }
     if (e == hipSuccess) {
       PassScope ps(P_SURV_LISTS, stream);

@@ -118,6 +118,7 @@ struct ScoreLaunch {
   int32_t scored_slot2;      // a second field that counts them too (0 = none)
   int32_t tiled;             // 1: score_tiled_kernel, 0: score_list_kernel
   const int32_t* tile_flags; // per group: 1 if the certificate prunes nothing in its tile (or NULL)
+  const int32_t* order;      // [n_items]: workgroup b takes item order[b] (longest first), or NULL
   int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not
   int32_t role;              // Role
   unsigned long long* stats; // dosa_stats as u64[11] or NULL
@@ -208,6 +209,20 @@ struct CompactLaunch {
   int32_t run_if;
 };
 
+// Launch order of the tiled survivor pass: its items (share r of a tile's
+// union list) sorted by share length, longest first, so that the launch's
+// tail holds the short shares.  One workgroup; at most kMaxOrderItems items.
+constexpr int kMaxOrderItems = 4096;
+struct OrderLaunch {
+  const WorkItem* items;
+  int32_t n_items;
+  const int32_t* list_len;
+  const int32_t* tile_flags;
+  int32_t* order;            // out: [n_items]
+  const int32_t* mode;
+  int32_t run_if;
+};
+
 struct NormLaunch {
   Inputs in;
   const int32_t* cu_kv;      // [batch+1] logical key offsets
@@ -227,6 +242,7 @@ hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s
 hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t s);
 hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
+hipError_t launch_order(const OrderLaunch& p, hipStream_t s);
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* host_vals, hipStream_t s);
 hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
                                unsigned long long* stats, hipStream_t s);

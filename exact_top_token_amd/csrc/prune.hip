@@ -1231,6 +1231,53 @@ hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream
   return hipErrorInvalidValue;
 }
 
+// Share lengths of the tiled survivor items as the survivor kernel will cut
+// them (0 for shares it skips and for tiles routed to per-group lists), then a
+// bitonic sort on (length, ~item) descending: the longest shares first, equal
+// lengths in item order.
+__global__ __launch_bounds__(1024) void order_kernel(const OrderLaunch p) {
+  __shared__ u64 key[kMaxOrderItems];
+  if (skip_launch(p.mode, p.run_if)) return;
+  const int n = p.n_items;
+  int N = 1;
+  while (N < n) N <<= 1;
+  for (int i = threadIdx.x; i < N; i += blockDim.x) {
+    uint32_t len = 0;
+    if (i < n) {
+      const WorkItem it = p.items[i];
+      bool all = true;
+      for (int g = 0; g < it.pad; ++g) all = all && (p.tile_flags[it.group + g] != 0);
+      if (all) {
+        const int L = p.list_len[it.group];
+        const int nsh = min(it.a1, max(1, (L + kUnionMinShare - 1) / kUnionMinShare));
+        if (it.a0 < nsh)
+          len = (uint32_t)((int64_t)L * (it.a0 + 1) / nsh - (int64_t)L * it.a0 / nsh);
+      }
+    }
+    key[i] = (i < n) ? (((u64)len << 32) | (u64)(0xFFFFFFFFu - (uint32_t)i)) : 0ull;
+  }
+  __syncthreads();
+  for (int size = 2; size <= N; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < (N >> 1); i += blockDim.x) {
+        const int lo = 2 * stride * (i / stride) + (i % stride);
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const u64 a = key[lo], b = key[hi];
+        if (desc ? (a < b) : (a > b)) { key[lo] = b; key[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = threadIdx.x; i < n; i += blockDim.x) p.order[i] = (int32_t)(0xFFFFFFFFu - (uint32_t)key[i]);
+}
+
+hipError_t launch_order(const OrderLaunch& p, hipStream_t s) {
+  if (p.n_items <= 0 || p.n_items > kMaxOrderItems) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(order_kernel, dim3(1), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s) {
   if (p.n_tiles == 0) return hipSuccess;
   hipLaunchKernelGGL(compact_kernel, dim3(p.n_tiles), dim3(512), 0, s, p);

@@ -673,7 +673,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
 
   if (skip_launch(p.mode, p.run_if)) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;   // wavefront-uniform
-  const WorkItem it = p.items[blockIdx.x];
+  const WorkItem it = p.items[p.order != nullptr ? p.order[blockIdx.x] : (int)blockIdx.x];
   const int ngroups = it.pad;                        // query groups in this tile
   if (p.flag_mode == 1) {
     bool all = true;
