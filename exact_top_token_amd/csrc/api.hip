@@ -472,6 +472,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   P.o_groups = take(sizeof(GroupInfo) * std::max(G, 1));
   P.o_items = take(sizeof(WorkItem) * std::max<size_t>(P.items.size(), 1));
+  if (!dense) P.o_seqinfo = take((size_t)(batch + 1) * sizeof(int32_t));   // copied with groups and items
   P.o_cand = take((size_t)P.total_q * P.R * P.cap * sizeof(u64));
   P.o_counts = take((size_t)P.total_q * P.R * sizeof(uint32_t));
   const int LS = 16 / P.QW;   // weighted-query terms per query
@@ -485,7 +486,6 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_coef = take((size_t)P.total_q * 8 * sizeof(float));
     P.o_norms = take((size_t)std::max<int64_t>(P.total_k, 1) * sizeof(float));
     P.o_flag = take(sizeof(int32_t));
-    P.o_seqinfo = take((size_t)(batch + 1) * sizeof(int32_t));
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
@@ -659,12 +659,24 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   char* ws = static_cast<char*>(workspace);
   unsigned long long* st = reinterpret_cast<unsigned long long*>(stats);
   hipError_t e;
-  e = hipMemcpyAsync(ws + P.o_groups, P.groups.data(), sizeof(GroupInfo) * P.groups.size(),
-                     hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(groups)");
-  e = hipMemcpyAsync(ws + P.o_items, P.items.data(), sizeof(WorkItem) * P.items.size(), hipMemcpyHostToDevice,
-                     stream);
-  if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(items)");
+  // The call's plan -- groups, work items and (pruned path) the sequences'
+  // key offsets, adjacent in the workspace -- goes over in one copy: a copy
+  // from pageable host memory can hold the host until the stream reaches it,
+  // so one copy at the start costs one such wait instead of one per array.
+  {
+    const size_t n_items = sizeof(WorkItem) * P.items.size();
+    const size_t end = dense ? P.o_items + n_items : P.o_seqinfo + (size_t)(batch + 1) * sizeof(int32_t);
+    std::vector<char> stage(end - P.o_groups, 0);
+    std::memcpy(stage.data(), P.groups.data(), sizeof(GroupInfo) * P.groups.size());
+    std::memcpy(stage.data() + (P.o_items - P.o_groups), P.items.data(), n_items);
+    if (!dense) {
+      int32_t* cu = reinterpret_cast<int32_t*>(stage.data() + (P.o_seqinfo - P.o_groups));
+      cu[0] = 0;
+      for (int b = 0; b < batch; ++b) cu[b + 1] = cu[b] + kv_lens[b];
+    }
+    e = hipMemcpyAsync(ws + P.o_groups, stage.data(), stage.size(), hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(plan)");
+  }
   if (st) {
     unsigned long long add[11] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     e = launch_stats_add(st, add, stream);
@@ -707,15 +719,9 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "score kernel launch");
   } else {
     const int G = (int)P.groups.size();
-    std::vector<int32_t> cu(batch + 1, 0);
     int32_t max_kv = 0;
-    for (int b = 0; b < batch; ++b) {
-      cu[b + 1] = cu[b] + kv_lens[b];
-      max_kv = std::max(max_kv, kv_lens[b]);
-    }
+    for (int b = 0; b < batch; ++b) max_kv = std::max(max_kv, kv_lens[b]);
     int32_t* cu_dev = reinterpret_cast<int32_t*>(ws + P.o_seqinfo);
-    e = hipMemcpyAsync(cu_dev, cu.data(), sizeof(int32_t) * cu.size(), hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(cu_kv)");
     float* tau = reinterpret_cast<float*>(ws + P.o_tau);
     float* norms = reinterpret_cast<float*>(ws + P.o_norms);
     float* coef = reinterpret_cast<float*>(ws + P.o_coef);
