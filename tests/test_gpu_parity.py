@@ -117,6 +117,21 @@ def test_correlated_heads_prunes_and_matches():
     assert pst["pairs_survived"] < pst["pairs_bounded"], "certificate pruned nothing on the correlated recipe"
 
 
+def test_survivor_shares_ragged_launch_order():
+    """Union shares launched in the device-side order (longest first, a tile's shares on one XCD):
+    a ragged tile count gives a share count that is not a multiple of the 32-item permutation
+    runs, so the tail of the order is exercised too."""
+    import exact_top_token_amd as E
+
+    wl = synth.correlated_heads(L=5000, topk=256)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 512
+    cfg.flags |= E.DOSA_NO_PROBE
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 16), cfg=cfg)
+    print("ragged shares stats", pst, flush=True)
+    assert pst["pairs_bounded"] > 0 and pst["pairs_survived"] < pst["pairs_bounded"]
+
+
 @pytest.mark.parametrize("knob", ["p0", "p1", "p2", "w64", "w512", "cap", "noprune", "separable", "noneg",
                                   "splits3", "frac0", "frac1", "probe"])
 def test_knob_invariance(knob):
