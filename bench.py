@@ -13,7 +13,7 @@ per-pass kernel times from HIP events recorded around every launch, the
 roofline fraction of the dominant kernel, and the CPU oracle timed on a
 bounded sample on the host cores.
 
-    python bench.py [--gpus 1] [--steps 3] [--warmup 1] [--workload long_prefill_128k]
+    python bench.py [--gpus 1] [--steps 5] [--warmup 2] [--workload long_prefill_128k]
 """
 from __future__ import annotations
 
@@ -138,8 +138,8 @@ def cpu_baseline(wl, budget_s: float = 20.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="long_prefill_128k")
     ap.add_argument("--L", type=int, default=0, help="override the context length (exploration only)")
     ap.add_argument("--chunk", type=int, default=0, help="query chunk per call, where the recipe takes one")
