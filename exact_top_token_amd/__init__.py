@@ -46,6 +46,8 @@ class DosaConfig(ctypes.Structure):
         ("neg_support_frac", ctypes.c_float),
         ("flags", ctypes.c_uint32),
         ("debug_ub", ctypes.c_void_p),
+        ("debug_tau", ctypes.c_void_p),
+        ("debug_mask", ctypes.c_void_p),
     ]
 
 
@@ -72,13 +74,39 @@ class DosaError(RuntimeError):
 _lib = None
 
 
+def hip_runtimes_mapped() -> list:
+    """Paths of the HIP runtime libraries mapped into this process (Linux)."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                parts = line.split()
+                if len(parts) >= 6 and os.path.basename(parts[5]).startswith("libamdhip64.so"):
+                    paths.add(os.path.realpath(parts[5]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
 def lib():
-    """The loaded shared library (raises if it has not been built)."""
+    """The loaded shared library (raises if it has not been built).
+
+    PyTorch ships its own HIP runtime under the same soname as the system one
+    the library is linked against.  torch is imported first, so the dynamic
+    loader binds the library to the runtime torch already mapped: one HIP (and
+    HSA) runtime per process, and torch's streams and device pointers are
+    valid in the library's calls.  Loading fails if two runtimes are mapped.
+    """
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} not found: build it with `python -m exact_top_token_amd.build`")
+        import torch  # noqa: F401  (maps torch's HIP runtime before the library's dependency is resolved)
+
         L = ctypes.CDLL(LIB_PATH)
+        rt = hip_runtimes_mapped()
+        if len(rt) > 1:
+            raise RuntimeError(f"two HIP runtimes are mapped into this process: {rt}")
         vp, i32, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
         L.dosa_default_config.argtypes = [i32, ctypes.POINTER(DosaConfig)]
         L.dosa_default_config.restype = ctypes.c_int

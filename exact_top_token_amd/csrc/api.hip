@@ -121,6 +121,20 @@ int check_shapes(int32_t batch, const int32_t* q_lens, const int32_t* kv_lens, i
     g_err = "unsupported dtype combination, H, d or topk";
     return DOSA_ERR_UNSUPPORTED;
   }
+  // Index arithmetic limits: query rows, key rows and per-key norm slots are
+  // int32; a contiguous sequence's key rows are addressed by 32-bit byte
+  // offsets from its first row.
+  int64_t tq = 0, tk = 0, kmax = 0;
+  for (int b = 0; b < batch; ++b) {
+    tq += q_lens[b];
+    tk += kv_lens[b];
+    kmax = std::max<int64_t>(kmax, kv_lens[b]);
+  }
+  const int64_t kbytes = (k_dtype == DOSA_F32) ? 4 : (k_dtype == DOSA_BF16 ? 2 : 1);
+  if (tq >= (int64_t(1) << 31) || tk >= (int64_t(1) << 31) || kmax * d * kbytes >= (int64_t(1) << 32)) {
+    g_err = "too many queries or keys for 32-bit row indices";
+    return DOSA_ERR_UNSUPPORTED;
+  }
   return DOSA_OK;
 }
 
@@ -170,7 +184,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
                 int32_t topk, int32_t q_dtype, int32_t k_dtype, bool paged, bool dense,
                 const dosa_config& cfg) {
   P.combo = combo_of(q_dtype, k_dtype);
-  P.QW = queries_per_wave(P.combo, H, d);
+  P.QW = queries_per_wave(P.combo, padded_heads(H), d);
   P.dense = dense;
   P.F = cfg.seed_prefix;
   P.W = std::max(cfg.seed_window, 64);
@@ -299,7 +313,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         GroupInfo& g = P.groups[t.first + i];
         g.bound_lo = f;
         g.n_bounded = wlo - f;
-        g.list_off = (int32_t)loff;
+        g.list_off = loff;
         g.list_cap = (g.n_bounded + 15) / 16 * 16;
         loff += g.list_cap;
         max_bounded = std::max(max_bounded, g.n_bounded);
@@ -682,8 +696,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     e = launch_stats_add(st, add, stream);
     if (e != hipSuccess) return fail_hip(e, "stats");
   }
-  Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages};
-  PrepLaunch pr{q, w, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
+  Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages, H};
+  PrepLaunch pr{q, w, H, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
                 reinterpret_cast<float*>(ws + P.o_lerr), dense ? nullptr : reinterpret_cast<int32_t*>(ws + P.o_flag),
                 reinterpret_cast<uint32_t*>(ws + P.o_tshare)};
   uint32_t* tshare = kShareTheta ? reinterpret_cast<uint32_t*>(ws + P.o_tshare) : nullptr;
@@ -813,6 +827,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ts.r0 = 0;
     ts.r1 = P.Js;
     ts.tau_out = tau;
+    ts.tau_copy = cfg.debug_tau;
     {
       PassScope ps(P_SELECT_SEED, stream);
       e = launch_select(ts, stream);
@@ -861,6 +876,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.mask_words = std::max(P.mask_words, 1);
     bl.debug_ub = cfg.debug_ub;
     bl.debug_ld = max_kv;
+    bl.debug_mask = reinterpret_cast<unsigned long long*>(cfg.debug_mask);
+    bl.debug_mask_ld = (max_kv + 63) / 64;
     bl.splits = P.bound_splits;
     if (!P.bound_items.empty()) {
       bl.items = di + off_bound;

@@ -454,4 +454,39 @@ __device__ __forceinline__ uint32_t compact_ge(const u64* src, uint32_t n, u64 T
   return out;
 }
 
+// compact_ge, also lowering mn (wavefront-uniform on return) to the smallest
+// entry kept.  When exactly K entries are >= T, that is the K-th largest.
+__device__ __forceinline__ uint32_t compact_ge_min(const u64* src, uint32_t n, u64 T, u64* dst, uint32_t out,
+                                                   u64& mn) {
+  const int lane = lane_id();
+  u64 m_lane = mn;
+  for (uint32_t base = 0; base < n; base += 64 * kBatch) {
+    u64 e[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = base + 64u * u + lane;
+      e[u] = (i < n) ? src[i] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const uint32_t i = base + 64u * u + lane;
+      const bool keep = (i < n) && (e[u] >= T);
+      const u64 m = __ballot(keep);
+      const uint32_t before = __popcll(m & ((1ull << lane) - 1ull));
+      if (keep) {
+        dst[out + before] = e[u];
+        m_lane = e[u] < m_lane ? e[u] : m_lane;
+      }
+      out += __popcll(m);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const u64 o = __shfl_xor(m_lane, off, 64);
+    m_lane = o < m_lane ? o : m_lane;
+  }
+  mn = m_lane;
+  return out;
+}
+
 }  // namespace dosa

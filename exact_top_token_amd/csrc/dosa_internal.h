@@ -31,12 +31,13 @@ constexpr int kUnionMinShare = 1024;
 // A query group: up to 4 consecutive queries of one sequence, scored together
 // by one wavefront (MFMA rows = group queries x head slots).
 struct GroupInfo {
+  int64_t list_off;  // start of the group's survivor list (DoSA); the lists of a call can
+                     // hold more than 2^31 entries (long contexts x many query groups)
   int32_t seq;       // sequence index
   int32_t q_row0;    // global row of the first query
   int32_t nq;        // queries in the group
   int32_t pos0;      // position of the first query (queries are consecutive)
   int32_t key_base;  // contiguous storage: row of the sequence's key 0
-  int32_t list_off;  // start of the group's survivor list (DoSA)
   int32_t list_cap;  // capacity of that list
   int32_t n_bounded; // keys the bound pass covers: [bound_lo, bound_lo + n_bounded)
   int32_t bound_lo;  // first bounded key (end of the seed prefix)
@@ -58,6 +59,13 @@ struct WorkItem {
   int32_t pad;
 };
 
+// Head slots the kernels are built for: the head count rounded up to 8, 16,
+// 32 or 64.  Slots past the real count hold zero queries with zero weight, so
+// they add nothing to a score and are neither positive nor negative heads.
+__host__ __device__ constexpr int padded_heads(int H) {
+  return H <= 8 ? 8 : (H <= 16 ? 16 : (H <= 32 ? 32 : 64));
+}
+
 // Where the inputs live, as the kernels see them.
 struct Inputs {
   const void* q;
@@ -68,6 +76,7 @@ struct Inputs {
   const int32_t* page_table;  // NULL = contiguous
   int32_t page_size;
   int32_t max_pages;
+  int32_t H;                  // heads per query: the row stride of q and w (<= the kernel's head slots)
 };
 
 // Candidate buffers, region-major: entry (q_row, region, i) at
@@ -92,6 +101,7 @@ struct CandBuf {
 struct PrepLaunch {
   const void* q;
   const float* w;
+  int32_t H;            // heads per query (row stride of q and w)
   int64_t total_q;
   void* rows;
   float* sig;
@@ -134,6 +144,7 @@ struct SelectLaunch {
   int32_t* out_idx;          // NULL: threshold-only mode
   float* out_score;
   float* tau_out;            // K-th score per query (-inf if fewer than K), or NULL
+  float* tau_copy;           // a second copy of tau_out (the caller's debug array), or NULL
   int32_t sorted;
   unsigned long long* stats;
   int32_t q_first;           // rows q_first .. q_first + total_q - 1
@@ -179,6 +190,8 @@ struct BoundLaunch {
   int32_t mask_words;
   float* debug_ub;           // [total_q, debug_ld] or NULL
   int32_t debug_ld;
+  unsigned long long* debug_mask;  // [total_q, debug_mask_ld] survivor bits per (query, key) or NULL
+  int32_t debug_mask_ld;
   int32_t splits;            // key splits per group (grid = n_groups * splits; per-group kernel)
   const WorkItem* items;     // tiled kernel: one per (query block, key share): group = first group,
                              // pad = groups, [a0, a1) keys, b0 = share index; NULL = per-group kernel

@@ -45,20 +45,21 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   constexpr int S = 16 / QW;                     // weighted-query terms per query
   constexpr int NT = (C == C_F32) ? 1 : (C == C_FP8 ? (S < 4 ? S : 4) : (S < 3 ? S : 3));
   constexpr int PER = (D + 63) / 64;
-  constexpr int ROWB = H * D * QB;               // bytes of one query row (a multiple of 16)
-  constexpr int NC = ROWB / 16;                  // 16-byte chunks of the row
-  constexpr int NCH = (NC + 63) / 64;            // per lane
+  constexpr int ROWB = H * D * QB;               // bytes of H head rows (a multiple of 16)
+  constexpr int NCH = (ROWB / 16 + 63) / 64;     // 16-byte chunks per lane
   __shared__ __attribute__((aligned(16))) uint8_t qrow[ROWB];
   __shared__ float wrow[H];
   const int q = blockIdx.x;
   const int lane = lane_id();
   if (q >= p.total_q) return;
+  const int Hr = p.H;                            // heads stored per query (<= H)
+  const int NC = Hr * D * QB / 16;               // 16-byte chunks of the stored row
   {
-    const v4i* src = reinterpret_cast<const v4i*>(static_cast<const uint8_t*>(p.q) + (int64_t)q * ROWB);
+    const v4i* src = reinterpret_cast<const v4i*>(static_cast<const uint8_t*>(p.q) + (int64_t)q * NC * 16);
     v4i c[NCH];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) c[u] = (lane + 64 * u < NC) ? src[lane + 64 * u] : v4i{0, 0, 0, 0};
-    const float wv = lane < H ? p.w[(int64_t)q * H + lane] : 0.f;
+    const float wv = lane < Hr ? p.w[(int64_t)q * Hr + lane] : 0.f;
 #pragma unroll
     for (int u = 0; u < NCH; ++u)
       if (lane + 64 * u < NC) reinterpret_cast<v4i*>(qrow)[lane + 64 * u] = c[u];
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
     const int i = lane + 64 * v;
     double acc = 0.0;
     if (i < D) {
-      for (int h = 0; h < H; ++h) {
+      for (int h = 0; h < Hr; ++h) {
         float x;
         if constexpr (C == C_F32) x = reinterpret_cast<const float*>(qraw)[h * D + i];
         else if constexpr (C == C_FP8) x = dec_fp8_p(qraw[h * D + i]);
@@ -149,7 +150,8 @@ static hipError_t prep_t(const PrepLaunch& p, hipStream_t s) {
 template <int C>
 static hipError_t prep_c(int H, int d, const PrepLaunch& p, hipStream_t s) {
 #define DOSA_HD(HH, DD) \
-  if (H == HH && d == DD) return prep_t<C, HH, DD>(p, s);
+  if (HP == HH && d == DD) return prep_t<C, HH, DD>(p, s);
+  const int HP = padded_heads(H);
   DOSA_HD(8, 64) DOSA_HD(16, 64) DOSA_HD(32, 64) DOSA_HD(64, 64)
   DOSA_HD(8, 128) DOSA_HD(16, 128) DOSA_HD(32, 128) DOSA_HD(64, 128)
 #undef DOSA_HD

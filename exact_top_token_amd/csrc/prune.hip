@@ -279,17 +279,22 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __shared__ int np_s, nsurv_s, nsep_s;
 
   // ---- 0. issue the loads
-  const uint8_t* qrow_raw = static_cast<const uint8_t*>(p.in.q) + (int64_t)qrow * H * D * QB;
+  // Heads stored per query (a multiple of 8, at most H): the head slots past
+  // Hr get zero rows and zero weight, so they are neither positive nor
+  // negative heads and every sum below skips them.
+  const int Hr = p.in.H;
+  const int qch = Hr * D * QB / 16;                // 16-byte chunks of the stored query row
+  const uint8_t* qrow_raw = static_cast<const uint8_t*>(p.in.q) + (int64_t)qrow * Hr * D * QB;
   uint4 qv[NQV];
 #pragma unroll
   for (int j = 0; j < NQV; ++j) {
     const int c = t + 256 * j;
-    qv[j] = (c < QCH) ? reinterpret_cast<const uint4*>(qrow_raw)[c] : make_uint4(0u, 0u, 0u, 0u);
+    qv[j] = (c < qch) ? reinterpret_cast<const uint4*>(qrow_raw)[c] : make_uint4(0u, 0u, 0u, 0u);
   }
   typename O::frag qa[O::STEPS];                   // MFMA rows: heads 16*wave + col
-  if (wave * 16 + col < H) O::load_q(qrow_raw + (wave * 16 + col) * D * QB, g, qa);
+  if (wave * 16 + col < Hr) O::load_q(qrow_raw + (wave * 16 + col) * D * QB, g, qa);
   else O::zero(qa);
-  const float wv = (t < H) ? p.in.w[(int64_t)qrow * H + t] : 0.f;
+  const float wv = (t < Hr) ? p.in.w[(int64_t)qrow * Hr + t] : 0.f;
   const float tau = p.tau[qrow];
   const float qscale = HasQScale<C>::value ? p.in.q_scale[qrow] : 1.f;
   const float l_err_f = p.lerr[(int64_t)qrow * 2], l_mag_f = p.lerr[(int64_t)qrow * 2 + 1];
@@ -328,12 +333,13 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
 #pragma unroll
   for (int j = 0; j < NQV; ++j) {
     const int c = t + 256 * j;
-    if (c < QCH) {
+    if (c < qch) {
       const int e = c * (16 / QB);                   // first element of the chunk (one row holds it whole)
       uint32_t* dst = reinterpret_cast<uint32_t*>(&qf[(e / D) * QS + e % D]);
       dst[0] = qv[j].x; dst[1] = qv[j].y; dst[2] = qv[j].z; dst[3] = qv[j].w;
     }
   }
+  for (int i = t; i < (H - Hr) * D; i += 256) qf[(Hr + i / D) * QS + i % D] = (qraw_t)0;
 #pragma unroll
   for (int j = 0; j < NKV; ++j) {
     const int c = t + 256 * j;
@@ -709,7 +715,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
       atomicAdd(&p.stats[3], all);
       atomicAdd(&p.stats[7], 1ull);
     }
-    if (p.debug_ub == nullptr) return;
+    if (p.debug_ub == nullptr && p.debug_mask == nullptr) return;
   }
   typename O::frag A[STEPS];
   {
@@ -749,6 +755,8 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
     const bool valid = qok && key < hi;
     const bool surv = valid && (hopeless || ub >= cf[5]);
     if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
+    if (p.debug_mask != nullptr && surv)
+      atomicOr(&p.debug_mask[(int64_t)qrow * p.debug_mask_ld + (key >> 6)], 1ull << (key & 63));
     if (all_hopeless) return;
     const u64 m = __ballot(surv);
     const uint32_t u = (uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu;
@@ -833,7 +841,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
     atomicAdd(&p.stats[7], 1ull);
   }
   // the whole workgroup leaves if no wavefront has work (and no dump is asked for)
-  if (__syncthreads_and(!active || all_hopeless) && p.debug_ub == nullptr) return;
+  const bool dump = p.debug_ub != nullptr || p.debug_mask != nullptr;
+  if (__syncthreads_and(!active || all_hopeless) && !dump) return;
   if (p.stats != nullptr && threadIdx.x == 0) atomicAdd(&p.stats[9], (u64)max(hi - lo, 0));   // rows this workgroup streams
   typename O::frag A[STEPS];
   {
@@ -917,7 +926,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
     commit(0);
   }
   __syncthreads();
-  const bool work = active && !(all_hopeless && p.debug_ub == nullptr);
+  const bool work = active && !(all_hopeless && !dump);
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
     const int bufi = t & 1;
@@ -947,6 +956,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
         const bool valid = qok && key < ghi;
         if (p.debug_ub != nullptr && valid) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = ub;
         const bool surv = valid && (hopeless || ub >= cf[5]);
+        if (p.debug_mask != nullptr && surv)
+          atomicOr(&p.debug_mask[(int64_t)qrow * p.debug_mask_ld + (key >> 6)], 1ull << (key & 63));
         const u64 m = __ballot(surv);
         n_surv += __popcll(m & keep_lanes);
         // each group's union over its query slots
@@ -1184,7 +1195,8 @@ static hipError_t plan_t(const PlanLaunch& p, hipStream_t s) {
 template <int C>
 static hipError_t plan_c(int H, int d, const PlanLaunch& p, hipStream_t s) {
 #define DOSA_HD(HH, DD) \
-  if (H == HH && d == DD) return plan_t<C, HH, DD>(p, s);
+  if (HP == HH && d == DD) return plan_t<C, HH, DD>(p, s);
+  const int HP = padded_heads(H);
   DOSA_HD(8, 64) DOSA_HD(16, 64) DOSA_HD(32, 64) DOSA_HD(64, 64)
   DOSA_HD(8, 128) DOSA_HD(16, 128) DOSA_HD(32, 128) DOSA_HD(64, 128)
 #undef DOSA_HD

@@ -175,11 +175,12 @@ struct Scorer {
       const int qa = ra / S, hs = ra % S;
       const bool ok = qa < nq;
       const uint8_t* qb = static_cast<const uint8_t*>(p.in.q);
+      const int Hr = p.in.H;   // heads stored per query row (head slots past it stay zero)
 #pragma unroll
       for (int j = 0; j < HG; ++j) {
         const int head = S * j + hs;
-        if (ok)
-          O::load_q(qb + ((int64_t)(gr.q_row0 + qa) * H + head) * D * O::QB, g, A[j]);
+        if (ok && (H == Hr || head < Hr))
+          O::load_q(qb + ((int64_t)(gr.q_row0 + qa) * Hr + head) * D * O::QB, g, A[j]);
         else
           O::zero(A[j]);
       }
@@ -191,7 +192,10 @@ struct Scorer {
     for (int e = lane; e < QW * (H + S); e += 64) {
       const int q = e / (H + S), h = e % (H + S);
       float v = 0.f;
-      if (q < nq) v = 0.5f * (h < H ? p.in.w[(int64_t)(gr.q_row0 + q) * H + h] : p.lsig[(int64_t)(gr.q_row0 + q) * S + (h - H)]);
+      if (q < nq) {
+        if (h >= H) v = 0.5f * p.lsig[(int64_t)(gr.q_row0 + q) * S + (h - H)];
+        else if (h < p.in.H) v = 0.5f * p.in.w[(int64_t)(gr.q_row0 + q) * p.in.H + h];
+      }
       wl[e] = v;
     }
     wq_lds = (uint32_t)(uintptr_t)(wl + qi() * (H + S));   // low 32 bits of a generic LDS address = the LDS offset
@@ -917,7 +921,8 @@ static hipError_t launch_score_t(const ScoreLaunch& p, hipStream_t s) {
 template <int C>
 static hipError_t launch_score_c(int H, int d, const ScoreLaunch& p, hipStream_t s) {
 #define DOSA_HD(HH, DD) \
-  if (H == HH && d == DD) return launch_score_t<C, HH, DD>(p, s);
+  if (HP == HH && d == DD) return launch_score_t<C, HH, DD>(p, s);
+  const int HP = padded_heads(H);
   DOSA_HD(8, 64) DOSA_HD(16, 64) DOSA_HD(32, 64) DOSA_HD(64, 64)
   DOSA_HD(8, 128) DOSA_HD(16, 128) DOSA_HD(32, 128) DOSA_HD(64, 128)
 #undef DOSA_HD

@@ -77,18 +77,25 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth_nt<NT>(sg, K, hist);
-  if (p.tau_out != nullptr && threadIdx.x == 0) p.tau_out[q] = (total >= (uint32_t)K) ? key_score(T) : -INFINITY;
   if (p.out_idx == nullptr) {
     // threshold mode: keep only the K entries >= T in the merged regions, so
-    // a later merge reads K of them instead of all
+    // a later merge reads K of them instead of all.  T is the lower edge of
+    // the radix bin that holds the K-th entry; the smallest kept entry is the
+    // K-th largest itself, and its score is the threshold tau.
     if (threadIdx.x >= 64) return;
-    if (total > (uint32_t)K) {
+    u64 mn = ~0ull;
+    if (total >= (uint32_t)K) {
       for (int r = 0; r < nseg; ++r) {
         u64* ptr = p.cb.row(q, p.r0 + r);
-        const uint32_t nk = compact_ge(ptr, sg.n(r), T, ptr, 0);
+        const uint32_t nk = compact_ge_min(ptr, sg.n(r), T, ptr, 0, mn);
         wave_sync();   // every lane has read the count before lane 0 rewrites it
         if (lane == 0) *p.cb.count(q, p.r0 + r) = nk;
       }
+    }
+    const float tau = (total >= (uint32_t)K) ? key_score(mn) : -INFINITY;
+    if (lane == 0) {
+      if (p.tau_out != nullptr) p.tau_out[q] = tau;
+      if (p.tau_copy != nullptr) p.tau_copy[q] = tau;
     }
     return;
   }
@@ -141,10 +148,9 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   }
 }
 
-// Threshold only: tau_out = a score with exactly K of the entries of regions
-// [r0, r1) at or above it -- the K-th largest score, or the lower edge of the
-// radix digit bin that holds it -- (-inf if fewer than K), by 4 wavefronts
-// per query and without touching the regions.  For small launches whose time
+// Threshold only: tau_out = the K-th largest score of the entries of regions
+// [r0, r1) (-inf if fewer than K), by 4 wavefronts per query and without
+// touching the regions.  For small launches whose time
 // is one query's latency.
 constexpr uint32_t kTauStage = 12288;  // score images staged in LDS (48 KiB): the seed window and prefix at defaults
 constexpr int kTauThreads = 256;       // per query (1024 measured slower)
@@ -156,12 +162,40 @@ __global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLau
   const int q = p.q_first + blockIdx.x;
   const int K = p.topk;
   const Segs sg{p.cb.row(q, p.r0), p.cb.count(q, p.r0), p.cb.rows * p.cb.cap, p.cb.rows, p.r1 - p.r0};
+  __shared__ u64 kth;
   uint32_t total = 0;
   for (int r = 0; r < sg.nseg; ++r) total += sg.n(r);
   float tau = -INFINITY;
   if (total >= (uint32_t)K) {
-    if (total <= kTauStage && sg.nseg < 2048) tau = ord2f(select_kth_score_staged<kTauThreads>(sg, total, K, hist, stage));
-    else tau = key_score(select_kth_nt<kTauThreads>(sg, K, hist));
+    // T: the lower edge of the radix bin that holds the K-th entry (exactly K
+    // entries at or above it); the smallest of those is the K-th largest.
+    if (threadIdx.x == 0) kth = ~0ull;
+    const int tid = (int)threadIdx.x;
+    if (total <= kTauStage && sg.nseg < 2048) {
+      const uint32_t T = select_kth_score_staged<kTauThreads>(sg, total, K, hist, stage);
+      uint32_t m = 0xFFFFFFFFu;
+      for (uint32_t i = tid; i < total; i += kTauThreads) {
+        const uint32_t v = stage[i];
+        if (v >= T && v < m) m = v;
+      }
+      atomicMin(&kth, (u64)m);
+      __syncthreads();
+      tau = ord2f((uint32_t)kth);
+    } else {
+      const u64 T = select_kth_nt<kTauThreads>(sg, K, hist);
+      u64 m = ~0ull;
+      for (int r = 0; r < sg.nseg; ++r) {
+        const u64* ptr = sg.ptr(r);
+        const uint32_t n = sg.n(r);
+        for (uint32_t i = tid; i < n; i += kTauThreads) {
+          const u64 e = ptr[i];
+          if (e >= T && e < m) m = e;
+        }
+      }
+      atomicMin(&kth, m);
+      __syncthreads();
+      tau = key_score(kth);
+    }
   }
   if (threadIdx.x == 0) p.tau_out[q] = tau;
 }
@@ -276,7 +310,7 @@ int tile_waves() { return kTileWaves; }
 bool combo_supported(int combo, int H, int d) {
   if (combo < 0 || combo > 3) return false;
   if (!(d == 64 || d == 128)) return false;
-  if (!(H == 8 || H == 16 || H == 32 || H == 64)) return false;
+  if (H < 8 || H > 64 || H % 8 != 0) return false;   // kernels built for 8/16/32/64 head slots
   return true;
 }
 

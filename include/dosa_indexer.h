@@ -51,8 +51,10 @@
  *   Row order inside out_idx is unspecified unless DOSA_SORTED is set (then
  *   score descending, position ascending); it is deterministic run to run.
  *
- * Supported: d in {64, 128}; H in {8, 16, 32, 64}; 1 <= topk <= 4096;
- * (q_dtype, k_dtype) in {(F32,F32), (BF16,BF16), (FP8,FP8), (BF16,FP8)}.
+ * Supported: d in {64, 128}; H a multiple of 8 in [8, 64]; 1 <= topk <= 4096;
+ * (q_dtype, k_dtype) in {(F32,F32), (BF16,BF16), (FP8,FP8), (BF16,FP8)};
+ * contiguous keys: sum(kv_lens) < 2^31 and kv_lens[b] * d * sizeof(k) < 2^32;
+ * sum(q_lens) < 2^31.  Other shapes return DOSA_ERR_UNSUPPORTED.
  * Inputs must be finite.
  *
  * Ownership and synchronisation: the caller owns every buffer, including the
@@ -102,7 +104,9 @@ typedef enum {
 /* Knobs of dosa_indexer_topk.  None of them changes the selected set; they
  * only change how much work the certificate saves. */
 typedef struct {
-  int32_t num_proxies;      /* positive heads evaluated exactly in the bound: 0..3 (default 3) */
+  int32_t num_proxies;      /* positive heads evaluated exactly in the bound: 0..3 (default 3;
+                               the bound kernels give each query 4 MFMA rows: p proxy rows and
+                               4 - p rows for the negative-head aggregate) */
   int32_t seed_window;      /* seed = the last seed_window visible keys ... (default 4*topk, >= 64) */
   int32_t seed_prefix;      /* ... plus the first seed_prefix keys (default 64) */
   int32_t buffer_cap;       /* entries per candidate region (each query has one region per key
@@ -114,7 +118,16 @@ typedef struct {
                                fraction of the sampled seed keys (default 0.5) */
   uint32_t flags;           /* DOSA_* flags */
   float* debug_ub;          /* optional DEVICE [total_q, max_kv] fp32: certificate value per
-                               bounded key (NaN elsewhere); for testing only */
+                               bounded key (untouched elsewhere); for testing only */
+  float* debug_tau;         /* optional DEVICE [total_q] fp32: each query's seed threshold tau
+                               (the K-th largest exactly scored seed score, -inf with fewer than
+                               K seeds); written only when the call runs the certificate
+                               pipeline (always with DOSA_NO_PROBE); for testing only */
+  uint64_t* debug_mask;     /* optional DEVICE [total_q, ceil(max_kv/64)] u64, zeroed by the
+                               caller: bit s%64 of word s/64 is OR-ed in for every bounded key s
+                               whose certificate reached tau for that query (every bounded key
+                               of a query whose plan found nothing to prune); seed keys are not
+                               marked; for testing only */
 } dosa_config;
 
 /* Device-resident counters, accumulated (not reset) by each call that gets a

@@ -15,6 +15,7 @@ from .workloads import (  # noqa: F401
     decode_mtp,
     million_chunk,
     correlated_heads,
+    correlated_decode,
     custom,
     quantize_fp8_per_token,
     to_bf16_bits,

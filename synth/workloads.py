@@ -359,10 +359,8 @@ def decode_mtp(seed: int = 0, batch: int = 64, q_per_seq: int = 2, kv_min: int =
                     recipe="per-sequence structured keys, permuted page pool, queries at the last positions")
 
 
-def correlated_heads(seed: int = 0, L: int = 32768, H: int = 64, d: int = 128, topk: int = 2048,
-                     dtype: str = "bf16", corr: float = 0.9995, head_noise: float = 0.05,
-                     topic_window: int = 64, q_len: Optional[int] = None, chunk: int = 0):
-    """Supplementary recipe with cross-head structure (not one of the headline workloads).
+def _correlated_tokens(rngs, L, H, d, pos, corr, head_noise, topic_window):
+    """Keys of L tokens and queries at positions ``pos`` with cross-head structure.
 
     Keys drift slowly through topics: k_s = mu + U c_s + eps_s, where the
     rank-16 coordinates follow c_s = corr c_{s-1} + sqrt(1-corr^2) xi_s
@@ -373,43 +371,103 @@ def correlated_heads(seed: int = 0, L: int = 32768, H: int = 64, d: int = 128, t
     plus ``head_noise`` sqrt(d) of its own random direction, times a per-head
     gain in [0.5, inf); a negative-weight head instead points mostly along mu
     (0.8 sqrt(d)) with 0.3 of the topic, so it fires on nearly every key.
-    Heads are then close to one another and the negative heads are active on
-    broad support: the indexer shape the certificate is designed for, and one
-    where the recent-window seed holds most of the true Top-K.
+    ``rngs``: seven generators.  Returns (k32 [L, d], q32 [m, H, d], w [m, H]).
     """
     from scipy.signal import lfilter
 
-    m = L if q_len is None else q_len
-    r = _streams(seed, 7, 8)
-    U = _low_rank_basis(r[0], d)
-    mu = r[1].standard_normal(d).astype(np.float32)
+    m = len(pos)
+    U = _low_rank_basis(rngs[0], d)
+    mu = rngs[1].standard_normal(d).astype(np.float32)
     mu *= np.float32(0.6 * math.sqrt(d)) / np.linalg.norm(mu)
-    xi = r[2].standard_normal((L, RANK)).astype(np.float64)
+    xi = rngs[2].standard_normal((L, RANK)).astype(np.float64)
     xi[1:] *= math.sqrt(1.0 - corr * corr)
     c = lfilter([1.0], [1.0, -corr], xi, axis=0).astype(np.float32)
     z = c @ U.T                                                 # [L, d] topic part
-    k32 = mu + z + r[3].standard_normal((L, d)).astype(np.float32) * np.float32(0.3)
+    k32 = mu + z + rngs[3].standard_normal((L, d)).astype(np.float32) * np.float32(0.3)
     k32[:SINKS] *= np.float32(4.0)
-    pos = np.arange(L - m, L, dtype=np.int64)
-    w = _mixed_sign_weights(m, H, r[4])
+    w = _mixed_sign_weights(m, H, rngs[4])
     cs = np.concatenate([np.zeros((1, d), np.float64), np.cumsum(z, axis=0, dtype=np.float64)])
     lo = np.maximum(pos - topic_window, 0)
     hi = np.maximum(pos, 1)
     topic = ((cs[hi] - cs[lo]) / (hi - lo)[:, None]).astype(np.float32)
     topic *= np.float32(math.sqrt(d)) / np.maximum(np.linalg.norm(topic, axis=1, keepdims=True), 1e-6)
-    n = _iid((m, H, d), r[5], 1024)
+    n = _iid((m, H, d), rngs[5], 1024)
     n *= np.float32(head_noise * math.sqrt(d)) / np.maximum(np.linalg.norm(n, axis=-1, keepdims=True), 1e-6)
-    gain = np.abs(r[6].standard_normal((m, H))).astype(np.float32) * np.float32(0.5) + np.float32(0.5)
+    gain = np.abs(rngs[6].standard_normal((m, H))).astype(np.float32) * np.float32(0.5) + np.float32(0.5)
     mu_hat = mu / np.linalg.norm(mu)
     neg = (w < 0)[..., None]
     q32 = np.where(neg, np.float32(0.8 * math.sqrt(d)) * mu_hat + np.float32(0.3) * topic[:, None, :],
                    topic[:, None, :]) + n
     q32 *= gain[..., None]
-    return _contig("correlated_heads", H, d, topk, dtype, dtype, q32.astype(np.float32), w, k32, [m], [L],
+    return k32, q32.astype(np.float32), w
+
+
+def correlated_heads(seed: int = 0, L: int = 32768, H: int = 64, d: int = 128, topk: int = 2048,
+                     dtype: str = "bf16", corr: float = 0.9995, head_noise: float = 0.05,
+                     topic_window: int = 64, q_len: Optional[int] = None, chunk: int = 0):
+    """Supplementary recipe with cross-head structure (not one of the headline workloads).
+
+    One sequence of L tokens, the last q_len (default all) as queries, q and k
+    in ``dtype`` (fp8: per-token scales), generated by _correlated_tokens.
+    Heads are close to one another and the negative heads are active on broad
+    support: the indexer shape the certificate is designed for, and one where
+    the recent-window seed holds most of the true Top-K.
+    """
+    m = L if q_len is None else q_len
+    r = _streams(seed, 7, 8)
+    pos = np.arange(L - m, L, dtype=np.int64)
+    k32, q32, w = _correlated_tokens(r, L, H, d, pos, corr, head_noise, topic_window)
+    return _contig("correlated_heads", H, d, topk, dtype, dtype, q32, w, k32, [m], [L],
                    chunk=chunk,
                    recipe=f"supplementary: AR({corr}) topic-drift keys + common offset; heads along the "
                           f"topic of the last {topic_window} keys + {head_noise} noise; negative heads "
                           f"along the offset")
+
+
+def correlated_decode(seed: int = 0, batch: int = 8, q_per_seq: int = 2, kv_min: int = 4096,
+                      kv_max: int = 20000, page_size: int = 64, H: int = 64, d: int = 128, topk: int = 2048,
+                      q_dtype: str = "bf16", k_dtype: str = "fp8", corr: float = 0.9995,
+                      head_noise: float = 0.05, topic_window: int = 64):
+    """Supplementary decode batch with the cross-head structure of correlated_heads.
+
+    Like decode_mtp (paged key cache, one randomly permuted page pool, junk
+    past each sequence's end, the q_per_seq queries at the last positions),
+    but every sequence's keys and queries come from _correlated_tokens with
+    streams of its own, so the certificate can prune.
+    """
+    r = _streams(seed, 9, 4)
+    kv = r[0].integers(kv_min, kv_max + 1, size=batch).astype(np.int32)
+    npg = (kv + page_size - 1) // page_size
+    total_pages = int(npg.sum())
+    max_pages = int((int(kv.max()) + page_size - 1) // page_size)
+    perm = r[1].permutation(total_pages).astype(np.int32)
+    table = np.full((batch, max_pages), -1, dtype=np.int32)
+    seq_roots = _child_streams(r[2], batch)
+    k_pool32 = np.full((total_pages, page_size, d), 300.0, dtype=np.float32)
+    q32 = np.empty((batch * q_per_seq, H, d), dtype=np.float32)
+    w = np.empty((batch * q_per_seq, H), dtype=np.float32)
+    off = 0
+    for b in range(batch):
+        n = int(kv[b])
+        pos = np.arange(n - q_per_seq, n, dtype=np.int64)
+        kb, qb, wb = _correlated_tokens(_child_streams(seq_roots[b], 7), n, H, d, pos, corr, head_noise,
+                                        topic_window)
+        pages = perm[off: off + npg[b]]
+        table[b, : npg[b]] = pages
+        padded = np.full((npg[b] * page_size, d), 300.0, dtype=np.float32)
+        padded[:n] = kb
+        k_pool32[pages] = padded.reshape(npg[b], page_size, d)
+        q32[b * q_per_seq:(b + 1) * q_per_seq] = qb
+        w[b * q_per_seq:(b + 1) * q_per_seq] = wb
+        off += npg[b]
+    q, qs = _encode(q32, q_dtype, 1)
+    k, ks = _encode(k_pool32, k_dtype, 2)
+    return Workload(name="correlated_decode", H=H, d=d, topk=topk, q_dtype=q_dtype, k_dtype=k_dtype, q=q,
+                    q_scale=qs, w=w, k=k, k_scale=ks,
+                    q_lens=np.full(batch, q_per_seq, np.int32), kv_lens=kv,
+                    page_table=table, page_size=page_size,
+                    recipe="supplementary: correlated-heads sequences in a permuted page pool, queries at "
+                           "the last positions")
 
 
 def custom(seed: int, lens, H: int, d: int, topk: int, q_dtype: str = "f32", k_dtype: str = "f32",
@@ -478,6 +536,7 @@ WORKLOADS = {
     "million_chunk": million_chunk,
     "million_chunk_iid": lambda seed=1, **kw: million_chunk(seed=seed, iid=True, **kw),
     "correlated_heads": correlated_heads,
+    "correlated_decode": correlated_decode,
 }
 
 

@@ -1,51 +1,127 @@
 """Comparison of GPU results with the oracle, and of the two GPU paths with each other.
 
-Readings applied (the pages give the exact-selection claim and a 1e-3
-relative score tolerance with fp32 accumulation; ties go to the lower index):
-* a returned score passes if |S_gpu - S_ref| <= 1e-3 * max(|S_ref|, A), where
-  A = sum_h |w_h| |q_h . k| is the scale of the terms that cancel in S;
-* the GPU's set may differ from the oracle's only by keys whose oracle score
-  lies within that tolerance of the oracle's K-th score (boundary ties);
+Readings applied (the pages claim an exact selection; the benchmark spec asks for
+scores within 1e-3 relative with fp32 accumulation and ties to the lower index):
+* a returned score passes if |S_gpu - S_ref| <= 1e-3 * |S_ref|, unless the pair
+  cancels, i.e. |S_ref| < CANCEL * A with A = sum_h |w_h| |q_h . k| (more than
+  90% of the heads' absolute contribution cancels); a cancelling pair is held to
+  1e-3 * A instead, since no fp32 evaluation of a sum of terms of size A can
+  promise a relative accuracy on a result far smaller than A;
+* the GPU's set may differ from the oracle's only by keys whose oracle score lies
+  within that tolerance of the oracle's K-th score theta (boundary ties), with
+  |theta| in place of |S_ref|;
 * the pruned path must return exactly the dense path's keys with bit-identical scores.
+
+The oracle runs on a thread pool over blocks of query rows (NumPy releases the
+GIL inside its kernels); each worker computes the oracle's Top-K of its rows and
+the oracle's scores of the keys the GPU returned.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from oracle import indexer
 
 REL = 1e-3
+CANCEL = 0.1
 
 
-def check_vs_oracle(wl, gidx, gsc, rows, rel=REL):
-    """Returns (max relative score error vs A, number of boundary swaps)."""
-    rows = np.asarray(rows, dtype=np.int64)
+def score_tol(ref, A, rel=REL):
+    """Tolerance on |S_gpu - ref| for scores ref with absolute head mass A."""
+    ref = np.abs(np.asarray(ref, dtype=np.float64))
+    A = np.asarray(A, dtype=np.float64)
+    return rel * np.where(ref >= CANCEL * A, ref, A)
+
+
+def _workers():
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _check_block(wl, rows, gidx, gsc, rel):
+    """Oracle checks of a block of rows; returns per-block statistics."""
     o_idx, o_sc, theta = indexer.topk_rows(wl, rows)
-    _, pos = indexer.query_positions(wl)
+    seq, pos = indexer.query_positions(wl)
     K = wl.topk
-    worst = 0.0
-    swaps = 0
-    for j, r in enumerate(rows):
-        g = gidx[r]
-        keep = g >= 0
-        gv = g[keep]
-        nvis = min(K, int(pos[r]) + 1)
-        assert gv.size == nvis, (r, gv.size, nvis)
-        assert np.all(g[:nvis] >= 0) and np.all(g[nvis:] == -1), f"row {r}: padding layout"
-        assert np.unique(gv).size == gv.size, f"row {r}: duplicate keys"
-        assert gv.min(initial=0) >= 0 and gv.max(initial=0) <= pos[r], f"row {r}: key out of range"
-        S, A = indexer.score_pairs(wl, np.full(gv.size, r), gv)
-        err = np.abs(gsc[r][keep].astype(np.float64) - S)
-        tol = rel * np.maximum(np.abs(S), A) + 1e-30
-        assert np.all(err <= tol), f"row {r}: score error {np.max(err / tol) * rel}"
-        worst = max(worst, float(np.max(err / np.maximum(A, 1e-30))) if err.size else 0.0)
-        ov = o_idx[j][o_idx[j] >= 0]
-        diff = np.array(sorted(set(gv.tolist()) ^ set(ov.tolist())), dtype=np.int64)
-        if diff.size:
-            Sd, Ad = indexer.score_pairs(wl, np.full(diff.size, r), diff)
-            th = theta[j]
-            ok = np.abs(Sd - th) <= rel * np.maximum(np.abs(th), Ad)
-            assert np.all(ok), f"row {r}: set differs beyond boundary ties: {diff[~ok][:5]}"
-            swaps += diff.size // 2
-    return worst, swaps
+    st = {"rows": 0, "max_rel_S": 0.0, "max_rel_A_cancel": 0.0, "max_rel_A": 0.0, "n_cancel": 0, "swaps": 0,
+          "pairs": 0}
+    for b in np.unique(seq[rows]):
+        sel = np.nonzero(seq[rows] == b)[0]
+        kb = indexer.seq_keys(wl, int(b), int(pos[rows[sel]].max()) + 1)
+        qb = indexer.query_rows(wl, rows[sel])
+        wb = indexer.weights(wl, rows[sel])
+        for jj, j in enumerate(sel):
+            r = int(rows[j])
+            g = np.asarray(gidx[r])
+            keep = g >= 0
+            gv = g[keep].astype(np.int64)
+            nvis = min(K, int(pos[r]) + 1)
+            assert gv.size == nvis, (r, gv.size, nvis)
+            assert np.all(g[:nvis] >= 0) and np.all(g[nvis:] == -1), f"row {r}: padding layout"
+            assert np.unique(gv).size == gv.size, f"row {r}: duplicate keys"
+            assert gv.min(initial=0) >= 0 and gv.max(initial=0) <= pos[r], f"row {r}: key out of range"
+            q1, w1 = qb[jj][None], wb[jj][None]
+            S = indexer.scores(q1, w1, kb[gv])[0]
+            A = indexer.abs_mass(q1, w1, kb[gv])[0]
+            err = np.abs(np.asarray(gsc[r])[keep].astype(np.float64) - S)
+            tol = score_tol(S, A, rel)
+            bad = err > tol
+            assert not np.any(bad), (f"row {r}: score error {err[bad][:3]} > tol {tol[bad][:3]} "
+                                     f"(S {S[bad][:3]}, A {A[bad][:3]})")
+            canc = np.abs(S) < CANCEL * A
+            st["n_cancel"] += int(canc.sum())
+            st["pairs"] += int(gv.size)
+            if np.any(~canc):
+                st["max_rel_S"] = max(st["max_rel_S"], float(np.max(err[~canc] / np.abs(S[~canc]))))
+            if np.any(canc):
+                st["max_rel_A_cancel"] = max(st["max_rel_A_cancel"],
+                                             float(np.max(err[canc] / np.maximum(A[canc], 1e-300))))
+            if gv.size:
+                st["max_rel_A"] = max(st["max_rel_A"], float(np.max(err / np.maximum(A, 1e-300))))
+            ov = o_idx[j][o_idx[j] >= 0]
+            diff = np.array(sorted(set(gv.tolist()) ^ set(ov.tolist())), dtype=np.int64)
+            if diff.size:
+                Sd = indexer.scores(q1, w1, kb[diff])[0]
+                Ad = indexer.abs_mass(q1, w1, kb[diff])[0]
+                th = theta[j]
+                ok = np.abs(Sd - th) <= score_tol(np.full(diff.size, th), Ad, rel)
+                assert np.all(ok), f"row {r}: set differs beyond boundary ties: {diff[~ok][:5]}"
+                st["swaps"] += diff.size // 2
+            st["rows"] += 1
+    return st
+
+
+def check_vs_oracle(wl, gidx, gsc, rows, rel=REL, block=None, verbose=False):
+    """Check the GPU rows gidx[r], gsc[r] (r in rows; arrays or dicts) against the oracle.
+
+    Returns a dict with the largest error relative to |S| over non-cancelling pairs
+    ('max_rel_S'), relative to A over cancelling pairs ('max_rel_A_cancel') and over
+    all pairs ('max_rel_A'), the number of cancelling pairs and of boundary swaps.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    if block is None:
+        block = max(1, min(256, (rows.size + 4 * _workers() - 1) // (4 * _workers())))
+    blocks = [rows[i:i + block] for i in range(0, rows.size, block)]
+    from threadpoolctl import threadpool_limits
+
+    tot = {"rows": 0, "max_rel_S": 0.0, "max_rel_A_cancel": 0.0, "max_rel_A": 0.0, "n_cancel": 0, "swaps": 0,
+           "pairs": 0}
+    with threadpool_limits(1):   # one BLAS thread per worker
+        with ThreadPoolExecutor(_workers()) as ex:
+            futs = [ex.submit(_check_block, wl, b, gidx, gsc, rel) for b in blocks]
+            for i, f in enumerate(futs):
+                st = f.result()
+                for k in ("rows", "n_cancel", "swaps", "pairs"):
+                    tot[k] += st[k]
+                for k in ("max_rel_S", "max_rel_A_cancel", "max_rel_A"):
+                    tot[k] = max(tot[k], st[k])
+                if verbose and (i % 16 == 15 or i == len(futs) - 1):
+                    print(f"[oracle] {wl.name}: {tot['rows']}/{rows.size} rows checked", flush=True)
+    if verbose:
+        print(f"[oracle] {wl.name}: max |err|/|S| {tot['max_rel_S']:.3g} over {tot['pairs'] - tot['n_cancel']} "
+              f"pairs, max |err|/A {tot['max_rel_A_cancel']:.3g} over {tot['n_cancel']} cancelling pairs, "
+              f"boundary swaps {tot['swaps']}", flush=True)
+    return tot
 
 
 def assert_same_selection(idx_a, sc_a, idx_b, sc_b):

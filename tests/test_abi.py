@@ -36,7 +36,46 @@ def test_default_config_values():
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(E.DosaStats) == 88
-    assert ctypes.sizeof(E.DosaConfig) == 40
+    assert ctypes.sizeof(E.DosaConfig) == 56
+    assert E.DosaConfig.debug_mask.offset == 48
+
+
+def test_one_hip_runtime_when_the_library_loads_first():
+    """A fresh process that loads the library before anything else maps exactly one HIP runtime
+    (the one torch brings), so torch's streams and pointers are valid in library calls."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import exact_top_token_amd as E; E.lib(); import torch; "
+            "rt = E.hip_runtimes_mapped(); print(len(rt)); assert len(rt) == 1, rt")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+@pytest.mark.parametrize("q_len,kv_len", [(16384, 1048576), (8192, 1100000)])
+def test_workspace_beyond_int32_list_offsets(q_len, kv_len):
+    """Shapes whose survivor lists hold more than 2^31 entries (one per bounded key and query
+    group) are planned with 64-bit list offsets: the workspace covers all of them."""
+    n = E.workspace_size([q_len], [kv_len], 64, 128, 2048, "fp8", "fp8", False, False)
+    groups = q_len // 4
+    bounded = kv_len - q_len - 4 * 2048           # keys before the seed window of a group, at least
+    assert groups * bounded > 2 ** 31
+    assert n >= 4 * groups * bounded
+
+
+@pytest.mark.parametrize("H", [8, 24, 40, 48, 56, 64])
+def test_head_counts_multiple_of_eight(H):
+    assert E.workspace_size([5], [9], H, 128, 16, "bf16", "bf16", False, False) > 0
+    assert E.workspace_size([5], [9], H, 64, 16, "f32", "f32", False, True) > 0
+
+
+def test_32bit_index_limits():
+    # a contiguous f32 sequence of 2^23 keys of 128 floats spans 2^32 bytes
+    assert E.workspace_size([1], [1 << 23], 8, 128, 16, "f32", "f32", False, True) == 0
+    assert E.workspace_size([1], [(1 << 23) - 1], 8, 128, 16, "f32", "f32", False, True) > 0
+    assert E.workspace_size([1, 1], [1 << 30, 1 << 30], 8, 64, 16, "fp8", "fp8", False, True) == 0
 
 
 @pytest.mark.parametrize("dense", [True, False])
@@ -45,7 +84,8 @@ def test_workspace_size(dense):
     b = E.workspace_size([4096], [8192], 64, 128, 2048, "fp8", "fp8", False, dense)
     assert a > 0 and b > 0 and a >= b
     assert E.workspace_size([5], [3], 64, 128, 2048, "fp8", "fp8", False, dense) == 0      # q_len > kv_len
-    assert E.workspace_size([5], [9], 48, 128, 2048, "fp8", "fp8", False, dense) == 0      # H unsupported
+    assert E.workspace_size([5], [9], 44, 128, 2048, "fp8", "fp8", False, dense) == 0      # H not a multiple of 8
+    assert E.workspace_size([5], [9], 72, 128, 2048, "fp8", "fp8", False, dense) == 0      # H above 64
     assert E.workspace_size([5], [9], 64, 96, 2048, "fp8", "fp8", False, dense) == 0       # d unsupported
     assert E.workspace_size([5], [9], 64, 128, 5000, "fp8", "fp8", False, dense) == 0      # topk too large
     assert E.workspace_size([5], [9], 64, 128, 64, "fp8", "bf16", False, dense) == 0       # dtype combo
@@ -82,7 +122,8 @@ def _call(path, **over):
     (dict(q_lens=[5], kv_lens=[3]), -1),
     (dict(topk=0), -1),
     (dict(H=0), -1),
-    (dict(H=48), -2),
+    (dict(H=44), -2),
+    (dict(H=72), -2),
     (dict(d=96), -2),
     (dict(topk=4097), -2),
     (dict(q_dtype="fp8", k_dtype="bf16"), -2),

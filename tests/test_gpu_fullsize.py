@@ -2,9 +2,11 @@
 times (chunked prefill as one call per chunk on shared device inputs).
 
 Every row: the pruned path returns exactly the dense path's keys with
-bit-identical scores (compared on the device).  Sampled rows (first and last
-query of several chunks plus random ones): both paths against the oracle,
-which scores those rows one by one over all their visible keys.
+bit-identical scores (compared on the device).  Against the oracle, which
+scores each checked row over all its visible keys: every row of the 32K
+prefill and of the decode batch; 1024 rows of the 128K chunked prefill (the
+first and last query of every chunk, the rest at random); 128 rows of each 1M
+chunk (its first and last query, the rest at random).
 """
 import numpy as np
 import pytest
@@ -52,23 +54,28 @@ def _same_on_device(ia, sa, ib, sb, block=8192):
         assert torch.equal(va, vb), f"scores of the same keys differ in rows {r0}..{r0 + block}"
 
 
-def _rows(wl, n_random, seed=0):
+def _rows(wl, n_target, seed=0):
+    """Stratified rows: the first and last query of every chunk call (or sequence), then random
+    rows up to n_target (all rows if n_target >= total_q)."""
+    if n_target >= wl.total_q:
+        return np.arange(wl.total_q, dtype=np.int64)
     picks = set()
     if wl.chunk:
-        calls = list(wl.chunk_calls())
-        for c in (calls[0], calls[len(calls) // 2], calls[-1]):
+        for c in wl.chunk_calls():
             picks.update([c["q0"], c["q0"] + c["q_len"] - 1])
     else:
         cu = wl.cu_q()
-        for b in (0, wl.batch // 2, wl.batch - 1):
+        for b in range(wl.batch):
             if cu[b + 1] > cu[b]:
                 picks.update([int(cu[b]), int(cu[b + 1] - 1)])
     rng = np.random.default_rng(seed)
-    picks.update(rng.choice(wl.total_q, size=n_random, replace=False).tolist())
+    rest = np.setdiff1d(np.arange(wl.total_q), np.array(sorted(picks), dtype=np.int64))
+    need = max(0, n_target - len(picks))
+    picks.update(rng.choice(rest, size=min(need, rest.size), replace=False).tolist())
     return np.array(sorted(picks), dtype=np.int64)
 
 
-def _check(wl, n_random):
+def _check(wl, n_rows):
     from exact_top_token_amd.runner import to_device
 
     print(f"[gpu] full size {wl.name}: q={wl.total_q} H={wl.H} d={wl.d} K={wl.topk} "
@@ -88,28 +95,29 @@ def _check(wl, n_random):
     _same_on_device(pi, ps, di, ds)
     del pi, ps
     print(f"[gpu] {wl.name}: calls scored densely after the probe: {pst2['calls_unpruned']}", flush=True)
-    rows = _rows(wl, n_random)
-    print(f"[gpu] oracle rows {rows.tolist()}", flush=True)
+    rows = _rows(wl, n_rows)
+    print(f"[gpu] oracle on {rows.size} rows of {wl.total_q}", flush=True)
     ri = di[rows].cpu().numpy()
     rs = ds[rows].cpu().numpy()
-    worst, swaps = check_vs_oracle(wl, {int(r): ri[j] for j, r in enumerate(rows)},
-                                   {int(r): rs[j] for j, r in enumerate(rows)}, rows)
-    print(f"[gpu] {wl.name}: max |S_gpu - S_ref| / A = {worst:.3g}, boundary swaps {swaps}, "
-          f"filtered {1 - pst['pairs_survived'] / max(pst['pairs_bounded'], 1):.3f}", flush=True)
+    del di, ds, inp
+    st = check_vs_oracle(wl, {int(r): ri[j] for j, r in enumerate(rows)},
+                         {int(r): rs[j] for j, r in enumerate(rows)}, rows, verbose=True)
+    assert st["rows"] == rows.size
+    print(f"[gpu] {wl.name}: filtered {1 - pst['pairs_survived'] / max(pst['pairs_bounded'], 1):.3f}", flush=True)
 
 
 def test_full_long_prefill_128k_fp8_chunked():
-    _check(synth.long_prefill_128k(), 4)
+    _check(synth.long_prefill_128k(), 1024)
 
 
 def test_full_dsa_prefill_32k_bf16():
-    _check(synth.dsa_prefill_32k(), 6)
+    _check(synth.dsa_prefill_32k(), 1 << 30)       # every row
 
 
 def test_full_decode_mtp_paged():
-    _check(synth.decode_mtp(), 8)
+    _check(synth.decode_mtp(), 1 << 30)            # every row
 
 
 @pytest.mark.parametrize("iid", [False, True])
 def test_full_million_chunk(iid):
-    _check(synth.make_workload("million_chunk_iid") if iid else synth.million_chunk(), 3)
+    _check(synth.make_workload("million_chunk_iid") if iid else synth.million_chunk(), 128)

@@ -204,32 +204,186 @@ def test_determinism_and_sorted_rows():
         assert np.all((s[:-1] > s[1:]) | ((s[:-1] == s[1:]) & (i[:-1] < i[1:]))), r
 
 
-def test_bound_dump_dominates_oracle_scores():
+def _debug_run(wl, cfg):
+    """One pruned-path call with every debug dump attached; returns (idx, scores, stats, ub, tau, mask)."""
+    import torch
+
+    from exact_top_token_amd.runner import Runner, to_device
+
+    inp = to_device(wl)
+    maxkv = int(max(wl.kv_lens))
+    dbg = torch.full((wl.total_q, maxkv), float("nan"), dtype=torch.float32, device="cuda")
+    tau = torch.full((wl.total_q,), float("nan"), dtype=torch.float32, device="cuda")
+    mask = torch.zeros((wl.total_q, (maxkv + 63) // 64), dtype=torch.int64, device="cuda")
+    cfg.debug_ub = dbg.data_ptr()
+    cfg.debug_tau = tau.data_ptr()
+    cfg.debug_mask = mask.data_ptr()
+    print(f"[gpu] debug dumps {wl.name} q={wl.total_q} {wl.q_dtype}/{wl.k_dtype}", flush=True)
+    r = Runner(inp, "dosa", cfg)
+    idx, sc = r()
+    torch.cuda.synchronize()
+    cfg.debug_ub = cfg.debug_tau = cfg.debug_mask = None
+    return (idx.cpu().numpy(), sc.cpu().numpy(), r.stats_dict(), dbg.cpu().numpy(), tau.cpu().numpy(),
+            mask.cpu().numpy().view(np.uint64))
+
+
+def check_debug_dumps(wl, ub, tau, mask, rows):
+    """The certificate as the GPU evaluated it, against the oracle, on the given rows:
+    * every bound the GPU dumped dominates the oracle's exact score of that pair;
+    * tau is the K-th largest oracle score over the query's seed keys (the visible keys
+      that got no bound), within the score tolerance, hence a lower bound on the K-th score;
+    * the survivor bits are exactly the bounded keys whose bound reached tau, or every
+      bounded key (a query whose plan found nothing to prune);
+    * no key of the oracle's Top-K (clear of boundary ties) was pruned.
+    Returns the number of (query, key) bounds checked."""
+    from oracle import certificate as cert
+    from oracle import indexer
+    from parity_helpers import score_tol
+
+    seq, pos = indexer.query_positions(wl)
+    o_idx, _, theta = indexer.topk_rows(wl, rows)
+    n_checked = 0
+    for j, r in enumerate(rows):
+        n = int(pos[r]) + 1
+        kv = indexer.seq_keys(wl, int(seq[r]), n)
+        q = indexer.query_rows(wl, [r])
+        w = indexer.weights(wl, [r])
+        S = indexer.scores(q, w, kv)[0]
+        A = indexer.abs_mass(q, w, kv)[0]
+        bounded = ~np.isnan(ub[r, :n])
+        keys = np.nonzero(bounded)[0]
+        n_checked += keys.size
+        assert np.all(ub[r, keys] >= S[keys] - 1e-6 * A[keys]), f"row {r}: bound below the exact score"
+        seeds = np.nonzero(~bounded)[0]
+        t_or = cert.seed_threshold(S[seeds], wl.topk)
+        if np.isinf(t_or):
+            assert np.isneginf(tau[r]), (r, tau[r])
+        else:
+            kth = seeds[np.argsort(-S[seeds], kind="stable")[wl.topk - 1]]
+            assert abs(float(tau[r]) - t_or) <= score_tol(t_or, A[kth]), (r, tau[r], t_or)
+            assert float(tau[r]) <= theta[j] + score_tol(theta[j], A[kth]), (r, tau[r], theta[j])
+        bits = np.unpackbits(mask[r].view(np.uint8), bitorder="little")[:n].astype(bool)
+        assert not np.any(bits & ~bounded), f"row {r}: survivor bit on a key without a bound"
+        reach = bounded & (ub[r, :n] >= tau[r])
+        assert np.array_equal(bits, reach) or np.array_equal(bits, bounded), f"row {r}: survivor bits"
+        top = o_idx[j][o_idx[j] >= 0]
+        if np.isneginf(theta[j]):
+            clear = top                   # fewer than K visible keys: every one is selected
+        else:
+            clear = top[S[top] > theta[j] + score_tol(np.full(top.size, theta[j]), A[top])]
+        assert np.all(~bounded[clear] | bits[clear]), f"row {r}: a Top-K key was pruned"
+    return n_checked
+
+
+@pytest.mark.parametrize("name", ["tiny", "correlated_bf16"])
+def test_bound_dump_dominates_oracle_scores(name):
+    import exact_top_token_amd as E
+
+    wl = synth.tiny_prefill(L=1024, topk=64) if name == "tiny" else synth.correlated_heads(L=3000, topk=128)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 256
+    cfg.flags |= E.DOSA_NO_PROBE
+    idx, sc, st, ub, tau, mask = _debug_run(wl, cfg)
+    di, ds, _ = _run(wl, "dsa")
+    assert_same_selection(idx, sc, di, ds)
+    n = check_debug_dumps(wl, ub, tau, mask, sample_rows(wl, 16))
+    assert n > 0, "no bound was dumped"
+
+
+def test_correlated_fp8_chunked_prunes():
+    """fp8 q and k with per-token scales (the headline operand type) on the correlated recipe:
+    the certificate prunes, every chunk call matches the dense path bit for bit, and the
+    fp8 certificate rows, aggregate terms and margin keep every bound above the exact score."""
     import torch
 
     import exact_top_token_amd as E
-    from exact_top_token_amd.runner import Runner, to_device
-    from oracle import indexer
+    from exact_top_token_amd.runner import Runner, slice_chunk, to_device
 
-    for wl in (synth.tiny_prefill(L=1024, topk=64), synth.correlated_heads(L=3000, topk=128)):
-        inp = to_device(wl)
-        maxkv = int(max(wl.kv_lens))
-        dbg = torch.full((wl.total_q, maxkv), float("nan"), dtype=torch.float32, device="cuda")
+    wl = synth.correlated_heads(L=16384, dtype="fp8", chunk=4096)
+    inp = to_device(wl)
+    outs = {}
+    stats = {}
+    for path in ("dsa", "dosa"):
+        idx = np.zeros((wl.total_q, wl.topk), np.int32)
+        sc = np.zeros((wl.total_q, wl.topk), np.float32)
         cfg = E.default_config(wl.topk)
-        cfg.seed_window = 256
-        cfg.debug_ub = dbg.data_ptr()
-        r = Runner(inp, "dosa", cfg)
-        r()
-        torch.cuda.synchronize()
-        ub = dbg.cpu().numpy()
-        rows = sample_rows(wl, 16)
-        _, sc, theta = indexer.topk_rows(wl, rows)
-        for j, q in enumerate(rows):
-            keys = np.nonzero(~np.isnan(ub[q]))[0]
-            if keys.size == 0:
-                continue
-            S, A = indexer.score_pairs(wl, np.full(keys.size, q), keys)
-            assert np.all(ub[q, keys] >= S - 1e-6 * A), f"{wl.name} row {q}: bound below score"
+        cfg.flags |= E.DOSA_NO_PROBE
+        cfg.seed_window = 2048
+        tot = {}
+        for c in wl.chunk_calls():
+            print(f"[gpu] correlated fp8 chunk {c} {path}", flush=True)
+            r = Runner(slice_chunk(inp, c["q0"], c["q_len"], c["kv_len"]), path, cfg)
+            a, b = r()
+            torch.cuda.synchronize()
+            idx[c["q0"]:c["q0"] + c["q_len"]] = a.cpu().numpy()
+            sc[c["q0"]:c["q0"] + c["q_len"]] = b.cpu().numpy()
+            for k, v in r.stats_dict().items():
+                tot[k] = tot.get(k, 0) + v
+        outs[path] = (idx, sc)
+        stats[path] = tot
+    pst = stats["dosa"]
+    print("correlated fp8 stats", pst, flush=True)
+    assert pst["pairs_bounded"] > 0 and pst["pairs_survived"] < pst["pairs_bounded"]
+    assert pst["groups_skipped"] < wl.total_q // 4, "every fp8 group was skipped"
+    assert_same_selection(*outs["dosa"], *outs["dsa"])
+    check_vs_oracle(wl, *outs["dsa"], sample_rows(wl, 192), verbose=True)
+    # the last chunk again with the debug dumps: bounds, tau and survivor bits against the oracle
+    c = list(wl.chunk_calls())[-1]
+    sub = synth.Workload(name="correlated_fp8_last_chunk", H=wl.H, d=wl.d, topk=wl.topk, q_dtype="fp8",
+                         k_dtype="fp8", q=wl.q[c["q0"]:], q_scale=wl.q_scale[c["q0"]:], w=wl.w[c["q0"]:],
+                         k=wl.k[:c["kv_len"]], k_scale=wl.k_scale[:c["kv_len"]],
+                         q_lens=np.array([c["q_len"]], np.int32), kv_lens=np.array([c["kv_len"]], np.int32))
+    cfg = E.default_config(wl.topk)
+    cfg.flags |= E.DOSA_NO_PROBE
+    cfg.seed_window = 2048
+    idx, sc, st, ub, tau, mask = _debug_run(sub, cfg)
+    assert_same_selection(idx, sc, outs["dsa"][0][c["q0"]:], outs["dsa"][1][c["q0"]:])
+    assert check_debug_dumps(sub, ub, tau, mask, sample_rows(sub, 12)) > 0
+
+
+def test_correlated_decode_bf16q_fp8k_prunes():
+    """bf16 queries against a paged fp8 key cache (the decode operand types), correlated keys:
+    groups are planned, bounded and pruned; the pruned path equals the dense path and the
+    oracle on every row; the debug dumps check out against the oracle."""
+    import exact_top_token_amd as E
+
+    wl = synth.correlated_decode(batch=6, kv_min=3000, kv_max=20000, topk=256)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 256
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=np.arange(wl.total_q), cfg=cfg)
+    print("correlated decode stats", pst, flush=True)
+    assert pst["pairs_bounded"] > 0 and pst["pairs_survived"] < pst["pairs_bounded"]
+    assert pst["groups_skipped"] < wl.total_q // 2, "every decode group was skipped"
+    idx, sc, st, ub, tau, mask = _debug_run(wl, cfg)
+    assert_same_selection(idx, sc, di, ds)
+    assert check_debug_dumps(wl, ub, tau, mask, np.arange(wl.total_q)) > 0
+
+
+@pytest.mark.parametrize("H", [24, 40, 48, 56])
+@pytest.mark.parametrize("qd,kd", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
+def test_head_counts_padded(H, qd, kd):
+    """Head counts between the kernels' 8/16/32/64 head slots: the stored rows are read with
+    their own stride and the extra slots stay zero."""
+    import exact_top_token_amd as E
+
+    wl = synth.custom(6, [(37, 900), (3, 3), (9, 80)], H=H, d=128 if H != 24 else 64, topk=96, q_dtype=qd,
+                      k_dtype=kd, page_size=16 if kd == "fp8" else 0)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 128
+    cfg.flags |= E.DOSA_NO_PROBE
+    _both(wl, rows=np.arange(wl.total_q), cfg=cfg)
+
+
+def test_correlated_heads_h32_prunes():
+    """The GLM-5.2 head count (32 indexer heads) on the correlated recipe."""
+    import exact_top_token_amd as E
+
+    wl = synth.correlated_heads(L=6000, H=32, topk=512)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 1024
+    cfg.flags |= E.DOSA_NO_PROBE
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 64), cfg=cfg)
+    assert pst["pairs_survived"] < pst["pairs_bounded"]
 
 
 @pytest.mark.parametrize("case", ["all_negative_w", "zero_queries", "huge_scale"])

@@ -362,3 +362,132 @@ def test_seed_threshold_is_lower_bound():
         tau = cert.seed_threshold(S[seeds], K)
         kth = np.sort(S)[::-1][K - 1] if S.size >= K else -np.inf
         assert tau <= kth
+
+
+# ----------------------------------------------------------------------------
+# helpers the parity checks lean on: score_pairs, abs_mass, seed_keys, filter_rate
+# ----------------------------------------------------------------------------
+def _dyadic_paged_workload(seed):
+    """Small paged multi-sequence f32 workload with dyadic values (every float64 product and
+    sum of the definition is exact)."""
+    rng = np.random.default_rng(seed)
+    lens = [(3, 40), (2, 17), (4, 33)]
+    wl = synth.custom(seed, lens, H=3, d=5, topk=6, page_size=16)
+    wl.q = (rng.integers(-8, 9, size=wl.q.shape) / 4.0).astype(np.float32)
+    wl.w = (rng.integers(-8, 9, size=wl.w.shape) / 8.0).astype(np.float32)
+    kvals = (rng.integers(-8, 9, size=wl.k.shape) / 2.0).astype(np.float32)
+    wl.k = np.where(wl.k == 300.0, wl.k, kvals).astype(np.float32)   # keep the junk past each end
+    return wl
+
+
+def _logical_key(wl, b, s):
+    pg = wl.page_table[b, s // wl.page_size]
+    return wl.k[pg, s % wl.page_size].astype(np.float64)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_score_pairs_and_abs_mass_exact_fractions(seed):
+    """S and A of explicit (row, key) pairs across sequences of a paged cache, against exact
+    rational arithmetic over the logical keys read through the page table by hand."""
+    wl = _dyadic_paged_workload(seed)
+    seq, pos = indexer.query_positions(wl)
+    rng = np.random.default_rng(seed)
+    rows = rng.integers(0, wl.total_q, size=60)
+    keys = np.array([int(rng.integers(0, pos[r] + 1)) for r in rows])
+    S, A = indexer.score_pairs(wl, rows, keys)
+    for i, (r, s) in enumerate(zip(rows, keys)):
+        k = _logical_key(wl, int(seq[r]), int(s))
+        tot_s, tot_a = Fraction(0), Fraction(0)
+        for h in range(wl.H):
+            x = sum(Fraction(float(wl.q[r, h, j])) * Fraction(float(k[j])) for j in range(wl.d))
+            wf = Fraction(float(wl.w[r, h]))
+            tot_s += wf * (x if x > 0 else Fraction(0))
+            tot_a += abs(wf) * abs(x)
+        assert S[i] == float(tot_s) and A[i] == float(tot_a), (r, s)
+    # the same pairs through the dense scorer of whole rows
+    for r in np.unique(rows):
+        kv = indexer.seq_keys(wl, int(seq[r]), int(pos[r]) + 1)
+        full = indexer.scores(indexer.query_rows(wl, [r]), indexer.weights(wl, [r]), kv)[0]
+        sel = rows == r
+        assert np.array_equal(full[keys[sel]], S[sel])
+
+
+def test_abs_mass_hand_values():
+    q = np.array([[[1.0, -2.0], [0.5, 0.5]]])          # 2 heads, d = 2
+    w = np.array([[-3.0, 2.0]])
+    k = np.array([[1.0, 1.0], [2.0, -1.0]])
+    # key 0: x = (-1, 1) -> A = 3*1 + 2*1 = 5 ; key 1: x = (4, 0.5) -> A = 12 + 1 = 13
+    assert indexer.abs_mass(q, w, k)[0].tolist() == [5.0, 13.0]
+    # and S: key 0 -> 0 + 2*1 = 2 ; key 1 -> -12 + 1 = -11
+    assert indexer.scores(q, w, k)[0].tolist() == [2.0, -11.0]
+
+
+def test_seed_keys_hand_values():
+    assert cert.seed_keys(10, 3, prefix=2, window=4).tolist() == [0, 1, 7, 8, 9, 10]
+    assert cert.seed_keys(3, 3, prefix=8, window=4).tolist() == [0, 1, 2, 3]        # everything visible
+    assert cert.seed_keys(5, 3, prefix=2, window=5).tolist() == [0, 1, 2, 3, 4, 5]  # prefix meets window
+    assert cert.seed_keys(100, 4, prefix=0).tolist() == [97, 98, 99, 100]          # window defaults to K
+    assert cert.seed_keys(0, 4, prefix=64, window=16).tolist() == [0]
+
+
+def test_filter_rate_equality_case_counts_from_the_definition():
+    """With every positive head a proxy and one negative head in the support the bound equals
+    the score, so the pruned pairs are exactly the non-seed keys scoring below the K-th seed
+    score: counted here from the scores and a sort."""
+    rng = np.random.default_rng(61)
+    H, d, L, K = 5, 8, 300, 7
+    q = rng.standard_normal((L, H, d)).astype(np.float32)
+    w = np.abs(rng.standard_normal((L, H))).astype(np.float32)
+    w[:, 1] = -w[:, 1]
+    k = rng.standard_normal((L, d)).astype(np.float32)
+    wl = synth.Workload(name="eq", H=H, d=d, topk=K, q_dtype="f32", k_dtype="f32", q=q, q_scale=None, w=w, k=k,
+                        k_scale=None, q_lens=np.array([L], np.int32), kv_lens=np.array([L], np.int32))
+    rows = [40, 151, 299]
+    rate, bounded, pruned = cert.filter_rate(wl, rows, num_proxies=H, support_frac=0.0, prefix=3, window=12)
+    want_b = want_p = 0
+    for r in rows:
+        S = indexer.scores(q[r][None].astype(np.float64), w[r][None].astype(np.float64),
+                           k[: r + 1].astype(np.float64))[0]
+        seeds = np.union1d(np.arange(3), np.arange(r + 1 - 12, r + 1))
+        tau = np.sort(S[seeds])[::-1][K - 1]
+        rest = np.setdiff1d(np.arange(r + 1), seeds)
+        want_b += rest.size
+        # equality up to the float64 rounding of UB: exclude keys within 1e-9 of tau
+        want_p += int(np.sum(S[rest] < tau - 1e-9))
+        assert not np.any(np.abs(S[rest] - tau) <= 1e-9)
+    assert bounded == want_b and pruned == want_p
+    assert rate == pruned / bounded
+
+
+def _ub_dominates(wl, rows, **kw):
+    seq, pos = indexer.query_positions(wl)
+    worst = np.inf
+    for r in rows:
+        kv = indexer.seq_keys(wl, int(seq[r]), int(pos[r]) + 1)
+        q = indexer.query_rows(wl, [r])[0]
+        w = indexer.weights(wl, [r])[0]
+        c = cert.query_certificate(q, w, kv, int(pos[r]), wl.topk, **kw)
+        A = indexer.abs_mass(q[None], w[None], kv)[0]
+        worst = min(worst, float(np.min((c["UB"] - c["S"]) / (A + 1.0))))
+    return worst
+
+
+def test_bound_dominates_every_pair_of_the_tiny_prefill():
+    """UB >= S for all 2,098,176 causal pairs of the tiny prefill (L = 2048, H = 8, d = 64,
+    K = 256), with the seed prefix and window the library uses by default (64 and 4K)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    wl = synth.tiny_prefill()
+    blocks = np.array_split(np.arange(wl.total_q), 16)
+    with ThreadPoolExecutor(8) as ex:
+        worst = min(ex.map(lambda b: _ub_dominates(wl, b, num_proxies=3, prefix=64, window=1024), blocks))
+    assert worst >= -1e-12
+
+
+def test_bound_dominates_sampled_queries_of_the_32k_prefill():
+    """UB >= S over all visible keys of sampled queries of the 32K bf16 prefill (H = 64,
+    d = 128), for the joint and the separable residual constant."""
+    wl = synth.dsa_prefill_32k()
+    rows = [100, 5000, 20000, 32767]
+    assert _ub_dominates(wl, rows, num_proxies=3, prefix=64, window=8192) >= -1e-12
+    assert _ub_dominates(wl, rows[-1:], num_proxies=3, prefix=64, window=8192, rho_kind="separable") >= -1e-12
