@@ -33,7 +33,10 @@ STATUS = {0: "DOSA_OK", -1: "DOSA_ERR_INVALID_ARG", -2: "DOSA_ERR_UNSUPPORTED", 
           -4: "DOSA_ERR_HIP"}
 
 EXPORTS = ("dosa_default_config", "dosa_workspace_size", "dosa_indexer_topk", "dsa_indexer_topk",
-           "dosa_status_string", "dosa_version", "dosa_profile_begin", "dosa_profile_end")
+           "dosa_indexer_topk_noalloc", "dosa_status_string", "dosa_version", "dosa_profile_begin",
+           "dosa_profile_end")
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # DOSA_NOALLOC_SCRATCH_BYTES
 
 
 class DosaConfig(ctypes.Structure):
@@ -118,6 +121,8 @@ def lib():
         L.dosa_indexer_topk.restype = ctypes.c_int
         L.dsa_indexer_topk.argtypes = common + [ctypes.POINTER(DosaConfig), vp, vp]
         L.dsa_indexer_topk.restype = ctypes.c_int
+        L.dosa_indexer_topk_noalloc.argtypes = common[:-2] + [ctypes.POINTER(DosaConfig), vp, vp]
+        L.dosa_indexer_topk_noalloc.restype = ctypes.c_int
         L.dosa_status_string.argtypes = [ctypes.c_int]
         L.dosa_status_string.restype = ctypes.c_char_p
         L.dosa_version.argtypes = []
@@ -217,3 +222,19 @@ def dsa_indexer_topk(q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_len
     tail = [ctypes.byref(cfg) if cfg is not None else None, _ptr(stats), _stream(stream)]
     return _call(lib().dsa_indexer_topk, tail, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens,
                  page_table, page_size, H, d, topk, out_idx, out_score, workspace)
+
+
+def dosa_indexer_topk_noalloc(q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, page_table,
+                              page_size, H, d, topk, out_idx, out_score, cfg: Optional[DosaConfig] = None,
+                              stats=None, stream=None):
+    """dosa_indexer_topk in the library's own scratch memory (no workspace argument, nothing
+    allocated; calls that need more than NOALLOC_SCRATCH_BYTES are rejected)."""
+    ql, kl = _i32_array(q_lens), _i32_array(kv_lens)
+    max_pages = int(page_table.shape[1]) if page_table is not None else 0
+    st = lib().dosa_indexer_topk_noalloc(
+        _ptr(q), DTYPES[q_dtype], _ptr(q_scale), _ptr(w), _ptr(k), DTYPES[k_dtype], _ptr(k_scale), ql, kl,
+        len(q_lens), _ptr(page_table), int(page_size), max_pages, int(H), int(d), int(topk), _ptr(out_idx),
+        _ptr(out_score), ctypes.byref(cfg) if cfg is not None else None, _ptr(stats), _stream(stream))
+    if st != 0:
+        raise DosaError(st, status_string(st))
+    return st

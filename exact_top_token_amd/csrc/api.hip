@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -526,6 +527,47 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
         int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes, const dosa_config& cfg,
         dosa_stats* stats, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// scratch memory of dosa_indexer_topk_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel or a copy (on the host it only stands in for the
+// symbol); it uses the device address hipGetSymbolAddress returns, looked up
+// once per device with that device current.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchBytes = (size_t)DOSA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    g_err = "device index " + std::to_string(dev) + " out of range for the scratch table";
+    return DOSA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) {
+      g_err = "hipGetSymbolAddress(scratch) returned NULL";
+      return DOSA_ERR_HIP;
+    }
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return DOSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -592,6 +634,38 @@ int dosa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, cons
     if (st != DOSA_OK) return st;
     return run(false, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, batch, page_table, page_size,
                max_pages, H, d, topk, out_idx, out_score, workspace, workspace_bytes, c, stats,
+               static_cast<hipStream_t>(stream));
+  } catch (...) {
+    g_err = "internal error";
+    return DOSA_ERR_HIP;
+  }
+}
+
+int dosa_indexer_topk_noalloc(const void* q, int32_t q_dtype, const float* q_scale, const float* w, const void* k,
+                              int32_t k_dtype, const float* k_scale, const int32_t* q_lens, const int32_t* kv_lens,
+                              int32_t batch, const int32_t* page_table, int32_t page_size, int32_t max_pages,
+                              int32_t H, int32_t d, int32_t topk, int32_t* out_idx, float* out_score,
+                              const dosa_config* cfg, dosa_stats* stats, void* stream) {
+  try {
+    int st = check_shapes(batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype);
+    if (st != DOSA_OK) return st;
+    dosa_config c;
+    st = resolve_cfg(cfg, topk, &c);
+    if (st != DOSA_OK) return st;
+    {
+      Plan P;
+      build_plan(P, batch, q_lens, kv_lens, H, d, topk, q_dtype, k_dtype, page_table != nullptr, false, c);
+      if (P.total > kScratchBytes) {
+        g_err = "the call needs " + std::to_string(P.total) + " bytes of workspace; the no-allocation entry "
+                "point has " + std::to_string(kScratchBytes) + " (use dosa_indexer_topk with a workspace)";
+        return DOSA_ERR_UNSUPPORTED;
+      }
+    }
+    void* ws = nullptr;
+    st = scratch_for_current_device(&ws);
+    if (st != DOSA_OK) return st;
+    return run(false, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, batch, page_table, page_size,
+               max_pages, H, d, topk, out_idx, out_score, ws, kScratchBytes, c, stats,
                static_cast<hipStream_t>(stream));
   } catch (...) {
     g_err = "internal error";

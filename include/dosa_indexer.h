@@ -180,6 +180,28 @@ int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const
                      void* workspace, size_t workspace_bytes,
                      const dosa_config* cfg, dosa_stats* stats, void* stream);
 
+/* dosa_indexer_topk without a workspace argument, for callers that cannot
+ * allocate device memory (serving loops or harnesses that forbid allocation):
+ * the call allocates nothing and runs in a scratch array the library holds
+ * in device memory, DOSA_NOALLOC_SCRATCH_BYTES per GPU, reserved when the
+ * library's code is loaded on that GPU and kept until the process ends.  The
+ * GPU is the device current on the calling thread (the one `stream` belongs
+ * to).  A call whose workspace would exceed the scratch size
+ * (dosa_workspace_size with dense = 0) returns DOSA_ERR_UNSUPPORTED and
+ * enqueues nothing.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on the device (concurrent streams, or other threads) race and
+ * must be serialised by the caller; consecutive calls on one stream are safe,
+ * and no state carries over from one call to the next.  Arguments, results and
+ * errors otherwise as dosa_indexer_topk. */
+#define DOSA_NOALLOC_SCRATCH_BYTES (128u << 20)
+int dosa_indexer_topk_noalloc(const void* q, int32_t q_dtype, const float* q_scale, const float* w,
+                              const void* k, int32_t k_dtype, const float* k_scale,
+                              const int32_t* q_lens, const int32_t* kv_lens, int32_t batch,
+                              const int32_t* page_table, int32_t page_size, int32_t max_pages,
+                              int32_t H, int32_t d, int32_t topk,
+                              int32_t* out_idx, float* out_score,
+                              const dosa_config* cfg, dosa_stats* stats, void* stream);
+
 /* Per-pass timing (tracing for benchmarks).  Between dosa_profile_begin()
  * and dosa_profile_end(), every kernel the calling thread enqueues through
  * this library is bracketed by two HIP events recorded on the kernel's own
