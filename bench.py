@@ -41,12 +41,18 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def padded_heads(H):
+    """Head slots of the kernel instantiation that serves H heads."""
+    return 8 if H <= 8 else (16 if H <= 16 else (32 if H <= 32 else 64))
+
+
 def uses_tiles(wl):
     """Whether the library scores this batch with the tiled kernel (8 query
     groups of 4/2/1 queries per workgroup) or, when tiles would hold fewer than
-    4 groups on average (decode-like batches), one wavefront per group."""
+    4 groups on average (decode-like batches), the split kernel (a workgroup's
+    8 wavefronts on one group's keys)."""
     qb = {"fp8": 1, "bf16": 2, "f32": 4}[wl.q_dtype]
-    per = wl.H * wl.d * qb
+    per = padded_heads(wl.H) * wl.d * qb
     qw = 4 if (4 * per <= 32768 and wl.H % 4 == 0) else (2 if (2 * per <= 32768 and wl.H % 8 == 0) else 1)
     lens = [wl.chunk] * (wl.total_q // wl.chunk) if wl.chunk else [int(m) for m in wl.q_lens]
     groups = sum((m + qw - 1) // qw for m in lens)
@@ -57,11 +63,14 @@ def uses_tiles(wl):
 def kernel_name(pass_name, wl):
     """Name of the kernel instantiation a pass launches, as profilers print it."""
     c = COMBO_ID[(wl.q_dtype, wl.k_dtype)]
+    H = padded_heads(wl.H)
     if pass_name in ROLE_ID:
-        if pass_name == "score_survivor_lists" or not uses_tiles(wl):
-            return f"score_list_kernel<{c}, {wl.H}, {wl.d}, {ROLE_ID[pass_name]}>"
+        if not uses_tiles(wl):
+            return f"score_split_kernel<{c}, {H}, {wl.d}, {ROLE_ID[pass_name]}>"
+        if pass_name == "score_survivor_lists":
+            return f"score_list_kernel<{c}, {H}, {wl.d}, {ROLE_ID[pass_name]}>"
         paged = "true" if wl.page_table is not None else "false"
-        return f"score_tiled_kernel<{c}, {wl.H}, {wl.d}, {ROLE_ID[pass_name]}, {paged}>"
+        return f"score_tiled_kernel<{c}, {H}, {wl.d}, {ROLE_ID[pass_name]}, {paged}>"
     return {"plan": "plan_kernel", "bound": "bound_kernel", "compact": "compact_kernel",
             "key_norms": "key_norm_kernel", "select_seed": "select_kernel", "select_final": "select_kernel",
             "prep": "qbar_kernel"}.get(pass_name, pass_name)

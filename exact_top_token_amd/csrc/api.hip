@@ -90,8 +90,11 @@ struct Plan {
   int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0, Jp = 0;
   int bound_gpw = 1;                 // query groups per wavefront of the tiled bound kernel
   bool tiled = true;
+  int RW = 1;                        // candidate regions per item region: 1, or kTileWaves for the split
+                                     // kernel (decode-like batches: one region per wavefront)
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
+  int n_tiles = 0;                   // query tiles (seed items 0 .. n_tiles*Js-1 are Js per tile, tile order)
   int mask_words = 0;
   int64_t list_total = 0;
   // workspace offsets
@@ -173,6 +176,10 @@ void longest_first(std::vector<WorkItem>& v, size_t from) {
 // Key splits of one query share their running thresholds (see ScoreLaunch).
 constexpr bool kShareTheta = true;
 
+// Items per call of the split kernel (decode-like batches): one 8-wavefront
+// workgroup per CU.
+constexpr int64_t kSplitItems = 256;
+
 // Split choice: enough work items to fill the GPU (target items), keeping at
 // least min_keys keys per split.
 int choose_splits(int64_t n_units, int64_t avg_keys, int64_t target, int64_t min_keys) {
@@ -220,15 +227,59 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     }
   P.total_q = cq;
   P.total_k = ck;
+  P.n_tiles = (int)tiles.size();
   P.pairs_total = pairs;
   const int G = (int)P.groups.size();
   const int NT = (int)tiles.size();
   int64_t key_sum = 0;
   for (auto& t : tiles) key_sum += t.n_last;
   const int64_t avg_keys = NT ? key_sum / NT : 0;
-  // Tiles that hold few groups waste the tiled kernel's wavefronts: use one
-  // wavefront per group there (decode-like batches).
+  // Tiles that hold few groups waste the tiled kernel's wavefronts: decode-
+  // like batches are scored by the split kernel instead (a workgroup's 8
+  // wavefronts on one group's keys), in items of balanced key counts.
   P.tiled = (NT > 0) && (2 * G >= TW * NT);
+  P.RW = P.tiled ? 1 : TW;
+  // balanced items of the split kernel: key ranges of at most `chunk` keys,
+  // the smallest chunk (a multiple of 64, at least 1024) for which the ranges
+  // of all groups make at most kSplitItems items -- one 8-wavefront workgroup
+  // per CU, all in one round, so no CU runs a second item while the others idle
+  auto split_chunk = [&](const std::vector<int64_t>& lens) -> int64_t {
+    int64_t lo = 1024, hi = 1024;
+    for (int64_t n : lens) hi = std::max(hi, (n + 63) / 64 * 64);
+    auto items = [&](int64_t c) {
+      int64_t k = 0;
+      for (int64_t n : lens) k += (n + c - 1) / c;
+      return k;
+    };
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2 / 64 * 64;
+      if (mid <= lo) break;
+      if (items(mid) <= kSplitItems) hi = mid;
+      else lo = mid + 64;
+    }
+    return items(lo) <= kSplitItems ? lo : hi;
+  };
+  auto split_range = [&](int gi, int lo_all, int hi_all, int region0, int64_t chunk, std::vector<WorkItem>& out) {
+    const int n = hi_all - lo_all;
+    const int J = cfg.key_splits > 0 ? cfg.key_splits : (int)std::max<int64_t>(1, (n + chunk - 1) / chunk);
+    for (int r = 0; r < J; ++r) {
+      const int64_t len = n;
+      const int lo = lo_all + (int)((len * r / J) / 64 * 64);
+      const int hi = (r == J - 1) ? hi_all : lo_all + (int)((len * (r + 1) / J) / 64 * 64);
+      WorkItem it{};
+      it.group = gi;
+      it.region = region0 + r;
+      if (lo == 0) {
+        it.a0 = 0; it.a1 = std::min(64, hi);   // the attention-sink keys first, then newest to oldest
+        it.b0 = it.a1; it.b1 = hi;
+      } else {
+        it.a0 = it.a1 = lo;
+        it.b0 = lo; it.b1 = hi;
+      }
+      out.push_back(it);
+    }
+    return J;
+  };
   // work items that give every SIMD two wavefronts of tiled scoring
   const int64_t tiled_target = 2048 / TW;
   auto range_split = [](int lo_all, int hi_all, int r, int J, int align, int& lo, int& hi) {
@@ -264,37 +315,30 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     if (P.tiled) {
       P.J = dense_tiled_items(P.items);
     } else {
-      int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
-      P.J = J;
+      std::vector<int64_t> lens;
+      for (const auto& g : P.groups) lens.push_back(g.pos0 + g.nq);
+      const int64_t chunk = split_chunk(lens);
+      int J = 1;
       for (int gi = 0; gi < G; ++gi) {
         const GroupInfo& g = P.groups[gi];
-        const int n = g.pos0 + g.nq;
-        for (int r = 0; r < J; ++r) {
-          int lo, hi;
-          range_split(0, n, r, J, 16, lo, hi);
-          WorkItem it{};
-          it.group = gi;
-          it.region = r;
-          if (lo == 0) {
-            it.a0 = 0; it.a1 = std::min(16, hi);
-            it.b0 = it.a1; it.b1 = hi;
-          } else {
-            it.a0 = it.a1 = lo;
-            it.b0 = lo; it.b1 = hi;
-          }
-          P.items.push_back(it);
-        }
+        J = std::max(J, split_range(gi, 0, g.pos0 + g.nq, 0, chunk, P.items));
       }
+      longest_first(P.items, 0);
+      P.J = J;
     }
-    P.R = P.J;
+    P.R = P.J * P.RW;
   } else {
     // seed pass per tile: the first F keys and the last W keys of the tile's
     // last query, the window split Js ways (regions 0..Js-1) so that the
     // launch fills the GPU; the keys in between get a certificate
     int64_t loff = 0;
     int max_bounded = 0;
-    const int Js = choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), tiled_target, 1024);
+    // split kernel (decode-like): about half as many seed items as CUs, each a
+    // window share of at least 2048 keys for its 8 wavefronts
+    const int Js = P.tiled ? choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), tiled_target, 1024)
+                           : choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), kSplitItems / 2, 2048);
     P.Js = Js;
+    std::vector<WorkItem> seed_extra;   // split kernel: the seed window of a tile's other groups
     for (const auto& t : tiles) {
       const int wlo = std::max(0, t.n_last - P.W);
       const int f = std::min(P.F, wlo);
@@ -309,6 +353,11 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         it.b0 = lo; it.b1 = hi;
         it.gather = 0;
         P.seed_items.push_back(it);
+        for (int i = 1; !P.tiled && i < t.n; ++i) {
+          it.group = t.first + i;
+          it.pad = 1;
+          seed_extra.push_back(it);
+        }
       }
       for (int i = 0; i < t.n; ++i) {
         GroupInfo& g = P.groups[t.first + i];
@@ -320,7 +369,12 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         max_bounded = std::max(max_bounded, g.n_bounded);
       }
     }
-    const int J = cfg.key_splits > 0 ? cfg.key_splits : choose_splits(G, avg_keys, 2048, 1024);
+    // survivor lists: J shares per group (one wavefront each with the list
+    // kernel; with the split kernel, 8 wavefronts each, so fewer shares)
+    const int J = cfg.key_splits > 0 ? cfg.key_splits
+                  : (P.tiled ? choose_splits(G, avg_keys, 2048, 1024)
+                             : (int)std::max<int64_t>(1, std::min<int64_t>(16, (kSplitItems + G - 1) / std::max(G, 1))));
+    P.seed_items.insert(P.seed_items.end(), seed_extra.begin(), seed_extra.end());
     // union lists of tiles (tiled kernel): up to Ju shares per tile, enough
     // workgroups to fill the GPU when every tile takes this route
     int Ju = 1;
@@ -331,24 +385,20 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
                               : choose_splits(NT, NT ? bsum_t / NT : 0, 4 * tiled_target, kUnionMinShare);
     }
     P.J = std::max(J, Ju);
-    P.R = Js + P.J;
     // calls without tiles: groups of tiles whose certificate prunes little
-    // walk the whole bounded range (one wavefront per group)
+    // walk the whole bounded range (split kernel, balanced key ranges)
     if (!P.tiled) {
+      std::vector<int64_t> lens;
+      for (const auto& g : P.groups) lens.push_back(std::max(g.n_bounded, 0));
+      const int64_t chunk = split_chunk(lens);
       for (int gi = 0; gi < G; ++gi) {
         const GroupInfo& g = P.groups[gi];
-        for (int r = 0; r < J; ++r) {
-          int lo, hi;
-          range_split(g.bound_lo, g.bound_lo + g.n_bounded, r, J, 16, lo, hi);
-          WorkItem it{};
-          it.group = gi;
-          it.region = Js + r;
-          it.a0 = it.a1 = lo;
-          it.b0 = lo; it.b1 = hi;
-          P.surv_tiled_items.push_back(it);
-        }
+        if (g.n_bounded <= 0) continue;
+        P.J = std::max(P.J, split_range(gi, g.bound_lo, g.bound_lo + g.n_bounded, Js, chunk, P.surv_tiled_items));
       }
+      longest_first(P.surv_tiled_items, 0);
     }
+    P.R = (Js + P.J) * P.RW;
     // calls with tiles: share r of Ju of the tile's union survivor list
     for (const auto& t : tiles) {
       if (!P.tiled) break;
@@ -472,6 +522,8 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         const int64_t nb = P.groups[it.group].n_bounded;
         n = std::max<int64_t>((nb + it.a1 - 1) / it.a1, std::min<int64_t>(nb, 2 * kUnionMinShare)) + 64;
       }
+      // split kernel: each wavefront's region takes every 8th 64-key step
+      if (P.RW > 1) n = ((n + 63) / 64 + P.RW - 1) / P.RW * 64;
       max_n = std::max(max_n, n);
     }
     const double k = (double)topk;
@@ -770,10 +822,13 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     e = launch_stats_add(st, add, stream);
     if (e != hipSuccess) return fail_hip(e, "stats");
   }
-  Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages, H};
+  int page_shift = -1;
+  if (page_table != nullptr && (page_size & (page_size - 1)) == 0)
+    for (page_shift = 0; (1 << page_shift) < page_size; ++page_shift) {}
+  Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages, H, page_shift};
   PrepLaunch pr{q, w, H, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
                 reinterpret_cast<float*>(ws + P.o_lerr), dense ? nullptr : reinterpret_cast<int32_t*>(ws + P.o_flag),
-                reinterpret_cast<uint32_t*>(ws + P.o_tshare)};
+                reinterpret_cast<uint32_t*>(ws + P.o_tshare), reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R};
   uint32_t* tshare = kShareTheta ? reinterpret_cast<uint32_t*>(ws + P.o_tshare) : nullptr;
   {
     PassScope ps(P_PREP, stream);
@@ -798,7 +853,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.topk = topk;
     sl.stats = st;
     sl.scored_slot = 4;
-    sl.tiled = P.tiled ? 1 : 0;
+    sl.tiled = P.tiled ? 1 : 2;
     sl.role = ROLE_DENSE;
     {
       PassScope ps(P_SCORE_DENSE, stream);
@@ -884,7 +939,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.topk = topk;
     sl.stats = st;
     sl.scored_slot = 1;
-    sl.tiled = 1;
+    sl.tiled = P.tiled ? 1 : 2;
     sl.role = ROLE_SEED;
     {
       PassScope ps(P_SCORE_SEED, stream);
@@ -899,7 +954,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ts.total_q = (int32_t)P.total_q;
     ts.topk = topk;
     ts.r0 = 0;
-    ts.r1 = P.Js;
+    ts.r1 = P.Js * P.RW;
     ts.tau_out = tau;
     ts.tau_copy = cfg.debug_tau;
     {
@@ -969,7 +1024,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     cl.groups = dg;
     cl.tiles = di;                    // the seed items: Js per tile, the first names the tile
     cl.tile_stride = P.Js;
-    cl.n_tiles = P.Js > 0 ? (int)P.seed_items.size() / P.Js : 0;
+    cl.n_tiles = P.n_tiles;
     cl.allow_union = P.tiled ? 1 : 0;
     cl.coef = coef;
     cl.masks = masks;
@@ -978,8 +1033,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     cl.list_len = list_len;
     cl.group_flags = gflags;
     cl.cb = cb;
-    cl.r0 = P.Js;
-    cl.r1 = P.Js + P.J;
+    cl.r0 = P.Js * P.RW;
+    cl.r1 = (P.Js + P.J) * P.RW;
     cl.mode = mode;
     cl.run_if = MODE_PRUNED;
     {
@@ -1011,7 +1066,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       PassScope ps(P_SURV_TILES, stream);
       ml.items = di + off_surv;
       ml.n_items = (int)P.surv_tiled_items.size();
-      ml.tiled = P.tiled ? 1 : 0;
+      ml.tiled = P.tiled ? 1 : 2;
       ml.flag_mode = 1;
       // union shares are cut on the device: launch them longest first
       if (P.tiled && ml.n_items > 0 && ml.n_items <= kMaxOrderItems) {
@@ -1026,7 +1081,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       PassScope ps(P_SURV_LISTS, stream);
       ml.items = di + off_list;
       ml.n_items = (int)P.surv_list_items.size();
-      ml.tiled = 0;
+      ml.tiled = P.tiled ? 0 : 2;
       ml.flag_mode = 2;
       ml.scored_slot2 = 8;
       e = launch_score(P.combo, H, d, ml, stream);
@@ -1061,7 +1116,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   se.total_q = (int32_t)P.total_q;
   se.topk = topk;
   se.r0 = 0;
-  se.r1 = dense ? P.R : P.Js + P.J;   // pruned path: seed then survivor regions
+  se.r1 = dense ? P.R : (P.Js + P.J) * P.RW;   // pruned path: seed then survivor regions
   se.out_idx = out_idx;
   se.out_score = out_score;
   se.tau_out = nullptr;

@@ -197,6 +197,10 @@ __host__ __device__ constexpr int queries_per_wave(int C, int H, int D) {
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int64_t key_row(const Inputs& in, int key_base, int seq, int key) {
   if (in.page_table == nullptr) return (int64_t)key_base + key;
+  if (in.page_shift >= 0) {   // power-of-two pages: shift and mask instead of an integer division
+    const int pg = in.page_table[(int64_t)seq * in.max_pages + (key >> in.page_shift)];
+    return ((int64_t)pg << in.page_shift) + (key & (in.page_size - 1));
+  }
   const int pg = in.page_table[(int64_t)seq * in.max_pages + key / in.page_size];
   return (int64_t)pg * in.page_size + key % in.page_size;
 }
@@ -280,9 +284,31 @@ struct Segs {
   int64_t rstride;         // entries from one region's row to the next
   int64_t cstride;         // counts from one region to the next
   int nseg;
-  __device__ __forceinline__ uint32_t n(int r) const { return counts[(int64_t)r * cstride]; }
+  uint32_t cap;            // entries a region holds: a count is never read as more
+  const uint32_t* off;     // LDS [nseg + 1]: prefix sums of the (clamped) counts, or NULL
+  __device__ __forceinline__ uint32_t n(int r) const { return min(counts[(int64_t)r * cstride], cap); }
   __device__ __forceinline__ const u64* ptr(int r) const { return base + (int64_t)r * rstride; }
 };
+
+// Queries with more segments than this are read as one flattened index range
+// (many short regions: one segment's loads at a time would serialise their
+// latencies); with fewer, segment by segment (cheaper per entry).
+constexpr int kFlatSegments = 8;
+
+// The prefix sums of a query's segment counts into LDS off[0..nseg] (thread 0;
+// the caller synchronises before use).  With them, a pass over the query's
+// entries runs over one flattened index range with the loads of all segments
+// in flight together, instead of one segment after the other.
+__device__ __forceinline__ void segment_offsets(const Segs& sg, uint32_t* off) {
+  if (threadIdx.x == 0) {
+    uint32_t a = 0;
+    for (int r = 0; r < sg.nseg; ++r) {
+      off[r] = a;
+      a += sg.n(r);
+    }
+    off[sg.nseg] = a;
+  }
+}
 
 // K-th largest of the (distinct) entries of the segments, K >= 1 and
 // K <= total, by a workgroup of NT threads.  Radix select on 11/11/10-bit
@@ -306,21 +332,46 @@ __device__ __noinline__ u64 select_kth_nt(const Segs sg, int K, uint32_t* hist) 
     for (int b = tid; b < nb; b += NT) hist[b] = 0;
     __syncthreads();
     const u64 want = (p == 0) ? 0 : (prefix >> hs);
-    for (int r = 0; r < sg.nseg; ++r) {
-      const u64* ptr = sg.ptr(r);
-      const uint32_t n = sg.n(r);
-      for (uint32_t b = 0; b < n; b += NT * kBatch) {
+    if (sg.off != nullptr && sg.nseg > kFlatSegments) {
+      // one flattened index range over all segments (a thread's indices only
+      // grow, so its segment cursor only moves forward)
+      const uint32_t total = sg.off[sg.nseg];
+      int r = 0;
+      for (uint32_t b = 0; b < total; b += NT * kBatch) {
         u64 e[kBatch];
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {     // all loads of the batch in flight together
           const uint32_t i = b + (uint32_t)NT * u + tid;
-          e[u] = (i < n) ? ptr[i] : 0ull;
+          e[u] = 0ull;
+          if (i < total) {
+            while (sg.off[r + 1] <= i) ++r;
+            e[u] = sg.ptr(r)[i - sg.off[r]];
+          }
         }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
           const uint32_t i = b + (uint32_t)NT * u + tid;
-          if (i < n && (p == 0 || (e[u] >> hs) == want))
+          if (i < total && (p == 0 || (e[u] >> hs) == want))
             atomicAdd(&hist[(uint32_t)(e[u] >> sh) & (uint32_t)(nb - 1)], 1u);
+        }
+      }
+    } else {
+      for (int r = 0; r < sg.nseg; ++r) {
+        const u64* ptr = sg.ptr(r);
+        const uint32_t n = sg.n(r);
+        for (uint32_t b = 0; b < n; b += NT * kBatch) {
+          u64 e[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {     // all loads of the batch in flight together
+            const uint32_t i = b + (uint32_t)NT * u + tid;
+            e[u] = (i < n) ? ptr[i] : 0ull;
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const uint32_t i = b + (uint32_t)NT * u + tid;
+            if (i < n && (p == 0 || (e[u] >> hs) == want))
+              atomicAdd(&hist[(uint32_t)(e[u] >> sh) & (uint32_t)(nb - 1)], 1u);
+          }
         }
       }
     }

@@ -77,6 +77,7 @@ struct Inputs {
   int32_t page_size;
   int32_t max_pages;
   int32_t H;                  // heads per query: the row stride of q and w (<= the kernel's head slots)
+  int32_t page_shift;         // log2(page_size) when it is a power of two, else -1
 };
 
 // Candidate buffers, region-major: entry (q_row, region, i) at
@@ -108,6 +109,8 @@ struct PrepLaunch {
   float* err;
   int32_t* flag;        // cleared here (query 0): the plan's "some query can prune" flag, or NULL
   uint32_t* tshare;     // [total_q] cleared here: the shared running thresholds (ScoreLaunch)
+  uint32_t* counts;     // candidate counts [n_regions, total_q], cleared here: a region no item
+  int32_t n_regions;    // of the call fills reads as empty in the final merge
 };
 
 struct ScoreLaunch {
@@ -126,7 +129,8 @@ struct ScoreLaunch {
   int32_t topk;
   int32_t scored_slot;       // dosa_stats field (u64 index) that counts scored pairs
   int32_t scored_slot2;      // a second field that counts them too (0 = none)
-  int32_t tiled;             // 1: score_tiled_kernel, 0: score_list_kernel
+  int32_t tiled;             // 1: score_tiled_kernel, 0: score_list_kernel, 2: score_split_kernel
+                             // (regions r * kTileWaves + wavefront of the items' regions r)
   const int32_t* tile_flags; // per group: 1 if the certificate prunes nothing in its tile (or NULL)
   const int32_t* order;      // [n_items]: workgroup b takes item order[b] (longest first), or NULL
   int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not

@@ -158,6 +158,7 @@ struct Scorer {
   uint32_t* qh;      // LDS: this wavefront's query histograms [QW][kHistBins]
   uint32_t hbase;    // ord value of the lower edge of bin 0 (0 = not anchored yet)
   uint32_t* tshare;  // the call's shared thresholds (indexed by query row), or NULL
+  uint32_t* anchor;  // LDS [QW]: histogram anchors shared with the workgroup's other wavefronts, or NULL
   uint32_t n_written, n_reselect, n_scored;
   bool dirty;        // something was appended since the last refresh (wavefront-uniform)
 
@@ -165,7 +166,7 @@ struct Scorer {
   // of its weighted-query terms (filled here);
   // hq: LDS [QW][kHistBins] running-threshold histograms (zeroed here).
   __device__ __forceinline__ void init(const ScoreLaunch& p, const GroupInfo& gr, int region, float* wl,
-                                       uint32_t* hq, bool active) {
+                                       uint32_t* hq, bool active, bool write_lds = true) {
     const int lane = lane_id(), g = lane >> 4;
     nq = active ? gr.nq : 0;
     q_row0 = gr.q_row0;
@@ -189,7 +190,7 @@ struct Scorer {
       else
         O::zero(AL);
     }
-    for (int e = lane; e < QW * (H + S); e += 64) {
+    for (int e = lane; write_lds && e < QW * (H + S); e += 64) {
       const int q = e / (H + S), h = e % (H + S);
       float v = 0.f;
       if (q < nq) {
@@ -205,8 +206,10 @@ struct Scorer {
     count = 0;
     buf = qok() ? p.cb.row(qrow(), region) : nullptr;
     qh = hq;
-    for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
+    if (write_lds)
+      for (int e = lane; e < QW * kHistBins; e += 64) hq[e] = 0;
     hbase = 0;
+    anchor = nullptr;
     tshare = p.theta_share;
     n_written = n_reselect = n_scored = 0;
     dirty = false;
@@ -223,6 +226,7 @@ struct Scorer {
     wave_sync();
     const int ln = lane_fresh();
     const int j = ln % LPQ, q = ln / LPQ;        // q == qi()
+    if (anchor != nullptr && hbase == 0u) hbase = anchor[q];   // anchored by another wavefront
     const uint32_t* h = qh + q * kHistBins + j * BPL;
     uint32_t hv[BPL];
 #pragma unroll
@@ -417,7 +421,13 @@ struct Scorer {
       mx = __shfl(mx, ol0 + c, 64);
       if (hbase == 0 && mx != 0u) {
         const uint32_t lo = (uint32_t)kHistAnchor << kHistShift;
-        hbase = (mx > 0x00800000u + lo) ? mx - lo : 0x00800000u;
+        uint32_t a = (mx > 0x00800000u + lo) ? mx - lo : 0x00800000u;
+        if (anchor != nullptr) {
+          // one anchor per query for the workgroup: the first wavefront to take sets it
+          const uint32_t prev = atomicCAS(&anchor[q_i], 0u, a);
+          a = prev != 0u ? prev : a;
+        }
+        hbase = a;
       }
     }
     uint32_t* hq = qh + q_i * kHistBins;
@@ -643,6 +653,185 @@ __global__ __launch_bounds__(64, KeyRaw<C>::value ? 2 : 1) void score_list_kerne
   }
   sc.close(p, gr, it.region, hist);
   sc.finish(p, it.region);
+}
+
+// ---------------------------------------------------------------------------
+// Decode-like batches (query tiles of fewer than 4 groups): the 8 wavefronts
+// of a workgroup score ONE query group over the item's key range (or its
+// share of the group's survivor list), taking the 64-key steps round robin:
+// wavefront w scores steps w, w + 8, w + 16, ...  Each wavefront appends to a
+// region of its own (region r * 8 + w), but the running threshold of each
+// query comes from one LDS histogram that all 8 wavefronts count into (one
+// anchor per query, set by the first wavefront that takes a score), so it
+// rises with every key the workgroup has scored instead of one wavefront's
+// eighth of them; a workgroup also keeps 8 wavefronts' key loads in flight
+// for one group, where one wavefront per group kept a single step's.
+// ---------------------------------------------------------------------------
+template <int C, int H, int D, int ROLE>
+__global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const ScoreLaunch p) {
+  using SC = Scorer<C, H, D>;
+  using O = typename SC::O;
+  __shared__ uint32_t hist[kTileWaves][256];
+  __shared__ __attribute__((aligned(16))) float wl[SC::QW * (H + SC::S)];
+  __shared__ uint32_t qhist[SC::QW * kHistBins];
+  __shared__ uint32_t anchor[SC::QW];
+  if (skip_launch(p.mode, p.run_if)) return;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;   // wavefront-uniform
+  const WorkItem it = p.items[blockIdx.x];
+  const GroupInfo gr = p.groups[it.group];
+  if (p.flag_mode != 0) {
+    bool all = true;
+    for (int i = 0; i < gr.tile_n; ++i) all = all && (p.tile_flags[gr.tile_first + i] != 0);
+    if (p.flag_mode == 2 && all) return;    // this tile's bounded range is scored whole
+    if (p.flag_mode == 1 && !all) return;   // this group's survivor list is scored instead
+  }
+  SC sc;
+  sc.init(p, gr, it.region * kTileWaves + wave, wl, qhist, true, wave == 0);
+  if (threadIdx.x < (unsigned)SC::QW) anchor[threadIdx.x] = 0u;
+  sc.anchor = anchor;
+  __syncthreads();
+  int nstep = 0;
+  uint32_t* shist = hist[wave];
+  const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
+  auto after_step = [&]() {
+    // every 4 steps of this wavefront: the histogram also holds the others' counts
+    if ((++nstep & 3) == 0) sc.refresh_theta(p.topk);
+  };
+  auto load = [&](int key, bool kvalid, typename O::frag* B, float& ks) {
+    ks = 1.f;
+    if (kvalid) {
+      const int64_t row = key_row(p.in, gr.key_base, gr.seq, key);
+      O::load_k(kbytes + row * SC::KBYTES, sc.g(), B);
+      if constexpr (HasKScale<C>::value) ks = p.in.k_scale[row];
+    } else {
+      O::zero(B);
+    }
+  };
+  // blocks of key fragments held at once: within the two-wavefronts-per-SIMD
+  // register budget next to the query fragments
+  constexpr int NBS = (int)sizeof(typename O::frag) * SC::STEPS <= 64 ? 2 : 1;
+  auto step4 = [&](const int* keys, const bool* v) {
+    float ks[4], o[4];
+#pragma unroll
+    for (int j = 0; j < 4 / NBS; ++j) {
+      typename O::frag B[NBS][SC::STEPS];
+#pragma unroll
+      for (int b = 0; b < NBS; ++b) load(keys[NBS * j + b], v[NBS * j + b], B[b], ks[NBS * j + b]);
+      sc.template scoreN<NBS>(B, o + NBS * j);
+    }
+    sc.template append4<true>(p, gr, it.region * kTileWaves + wave, o, ks, keys, v, shist);
+    after_step();
+  };
+  const int region = it.region * kTileWaves + wave;
+
+  if constexpr (KeyRaw<C>::value) {
+    if (!it.gather) {
+      // range walk with the next step's key bytes in flight while the current
+      // step is scored (half steps of two 16-key blocks, as the list kernel)
+      const int na = it.a1 > it.a0 ? (it.a1 - it.a0 + 63) / 64 : 0;
+      const int ns = na + (it.b1 > it.b0 ? (it.b1 - it.b0 + 63) / 64 : 0);
+      auto step_kb = [&](int s, int& lo, int& hi) -> int {
+        const bool ra = s < na;
+        lo = ra ? it.a0 : it.b0;
+        hi = ra ? it.a1 : it.b1;
+        return hi - 16 - 64 * (ra ? s : s - na);
+      };
+      typename O::raw rn[2];
+      float ksn[2];
+      auto fetch = [&](int h) {
+        int lo, hi;
+        const int kb = step_kb(h >> 1, lo, hi) - 32 * (h & 1);
+        const int cl = sc.col();
+        int64_t row[2];
+        bool ok[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int key = kb - 16 * b + cl;
+          ok[b] = key >= lo && key < hi;
+          row[b] = ok[b] ? key_row(p.in, gr.key_base, gr.seq, key) : 0;
+        }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          ksn[b] = 1.f;
+          if (ok[b]) {
+            O::load_raw(kbytes + row[b] * SC::KBYTES, sc.g(), rn[b]);
+            if constexpr (HasKScale<C>::value) ksn[b] = p.in.k_scale[row[b]];
+          } else {
+            rn[b] = typename O::raw{};
+          }
+        }
+      };
+      if (wave < ns) fetch(2 * wave);
+#pragma unroll 1
+      for (int s = wave; s < ns; s += kTileWaves) {
+        int lo, hi;
+        const int kb = step_kb(s, lo, hi);
+        int keys[4];
+        bool v[4];
+        float ks[4], o[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          keys[b] = kb - 16 * b + sc.col();
+          v[b] = keys[b] >= lo && keys[b] < hi;
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          typename O::frag B[2][SC::STEPS];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            O::from_raw(rn[b], B[b]);
+            ks[2 * j + b] = ksn[b];
+          }
+          if (j == 0) fetch(2 * s + 1);
+          else if (s + kTileWaves < ns) fetch(2 * (s + kTileWaves));
+          sc.template scoreN<2>(B, o + 2 * j);
+        }
+        sc.template append4<true>(p, gr, region, o, ks, keys, v, shist);
+        after_step();
+      }
+      sc.close(p, gr, region, shist);
+      sc.finish(p, region);
+      return;
+    }
+  }
+  if (!it.gather) {
+    const int na = it.a1 > it.a0 ? (it.a1 - it.a0 + 63) / 64 : 0;
+    const int ns = na + (it.b1 > it.b0 ? (it.b1 - it.b0 + 63) / 64 : 0);
+#pragma unroll 1
+    for (int s = wave; s < ns; s += kTileWaves) {
+      const bool ra = s < na;
+      const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
+      const int kb = hi - 16 - 64 * (ra ? s : s - na);
+      int keys[4];
+      bool v[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        keys[b] = kb - 16 * b + sc.col();
+        v[b] = keys[b] >= lo && keys[b] < hi;
+      }
+      step4(keys, v);
+    }
+  } else {
+    // share a0 of a1 of the group's survivor list, 64 entries per step
+    const int32_t* lst = p.lists + gr.list_off;
+    const int len = p.list_len[it.group];
+    const int e0 = (int)(((int64_t)len * it.a0 / it.a1) & ~15LL);
+    const int e1 = (it.a0 == it.a1 - 1) ? len : (int)(((int64_t)len * (it.a0 + 1) / it.a1) & ~15LL);
+#pragma unroll 1
+    for (int e = e0 + 64 * wave; e < e1; e += 64 * kTileWaves) {
+      int keys[4];
+      bool v[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int i0 = e + 16 * b + sc.col();
+        v[b] = i0 < e1;
+        keys[b] = v[b] ? lst[i0] : 0;
+      }
+      step4(keys, v);
+    }
+  }
+  sc.close(p, gr, region, shist);
+  sc.finish(p, region);
 }
 
 // ---------------------------------------------------------------------------
@@ -899,7 +1088,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
 // ---------------------------------------------------------------------------
 template <int C, int H, int D, int ROLE>
 static hipError_t launch_score_r(const ScoreLaunch& p, hipStream_t s) {
-  if (p.tiled && p.in.page_table != nullptr)
+  if (p.tiled == 2)
+    hipLaunchKernelGGL((score_split_kernel<C, H, D, ROLE>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
+  else if (p.tiled && p.in.page_table != nullptr)
     hipLaunchKernelGGL((score_tiled_kernel<C, H, D, ROLE, true>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);
   else if (p.tiled)
     hipLaunchKernelGGL((score_tiled_kernel<C, H, D, ROLE, false>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);

@@ -7,7 +7,7 @@ namespace dosa {
 // ---------------------------------------------------------------------------
 // final merge: the exact Top-K of each query over regions [r0, r1)
 // ---------------------------------------------------------------------------
-constexpr int kMaxMergeRegions = 128;   // regions the multi-wavefront output split handles
+constexpr int kMaxMergeRegions = 256;   // regions whose offsets the merge keeps in LDS
 
 // Entries >= T among src[0..n), counted by one wavefront.
 __device__ __forceinline__ uint32_t count_ge(const u64* src, uint32_t n, u64 T) {
@@ -65,6 +65,9 @@ __device__ __forceinline__ uint32_t emit_ge(const u64* src, uint32_t n, u64 T, i
 template <int NT>
 __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
+  __shared__ uint32_t segoff[kMaxMergeRegions + 1];
+  constexpr int NW = NT / 64;
+  __shared__ uint32_t woff[NW];
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int lane = lane_id();
@@ -72,9 +75,16 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   const u64* base = p.cb.row(q, p.r0);
   const uint32_t* cnt = p.cb.count(q, p.r0);
   const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
-  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg};
+  Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg, (uint32_t)p.cb.cap, nullptr};
+  if (nseg <= kMaxMergeRegions) {
+    segment_offsets(sg, segoff);
+    __syncthreads();
+    sg.off = segoff;
+  }
   uint32_t total = 0;
-  for (int r = 0; r < nseg; ++r) total += sg.n(r);
+  if (sg.off != nullptr) total = sg.off[nseg];
+  else
+    for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
   if (total >= (uint32_t)K) T = select_kth_nt<NT>(sg, K, hist);
   if (p.out_idx == nullptr) {
@@ -99,38 +109,39 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
     }
     return;
   }
-  // exactly min(K, total) entries are >= T; write them in region order
+  // exactly min(K, total) entries are >= T; write them in flattened order
+  // (region by region), which is the same run to run
   int32_t* oi = p.out_idx + (int64_t)q * K;
   float* os = p.out_score ? p.out_score + (int64_t)q * K : nullptr;
   uint32_t out = 0;
-  constexpr int NW = NT / 64;
-  if (NW > 1 && nseg <= kMaxMergeRegions) {
-    // Every wavefront takes a contiguous share of each region: it counts its
-    // entries >= T, the counts are turned into output offsets in region
-    // order, and each share is written at its offset.  Same rows as one
-    // wavefront walking the regions in order.
-    __shared__ uint32_t offs[kMaxMergeRegions * (NW > 1 ? NW : 1)];
+  if (NW > 1 && sg.off != nullptr) {
+    // Each wavefront takes one contiguous share of the flattened entries: it
+    // counts its entries >= T, the counts become output offsets in order, and
+    // each share is written at its offset.
     const int w = (int)(threadIdx.x >> 6);
-    for (int r = 0; r < nseg; ++r) {
-      const uint32_t n = sg.n(r);
-      const uint32_t lo = (uint32_t)((uint64_t)n * w / NW), hi = (uint32_t)((uint64_t)n * (w + 1) / NW);
-      const uint32_t c = count_ge(sg.ptr(r) + lo, hi - lo, T);
-      if (lane == 0) offs[r * NW + w] = c;
+    const uint32_t lo = (uint32_t)((uint64_t)total * w / NW), hi = (uint32_t)((uint64_t)total * (w + 1) / NW);
+    int r0 = 0;
+    while (r0 < nseg && sg.off[r0 + 1] <= lo) ++r0;
+    uint32_t c = 0;
+    for (int r = r0; r < nseg && sg.off[r] < hi; ++r) {
+      const uint32_t s0 = max(lo, sg.off[r]) - sg.off[r], s1 = min(hi, sg.off[r + 1]) - sg.off[r];
+      c += count_ge(sg.ptr(r) + s0, s1 - s0, T);
     }
+    if (lane == 0) woff[w] = c;
     __syncthreads();
     if (threadIdx.x == 0) {
       uint32_t acc = 0;
-      for (int i = 0; i < nseg * NW; ++i) {
-        const uint32_t c = offs[i];
-        offs[i] = acc;
-        acc += c;
+      for (int i = 0; i < NW; ++i) {
+        const uint32_t v = woff[i];
+        woff[i] = acc;
+        acc += v;
       }
     }
     __syncthreads();
-    for (int r = 0; r < nseg; ++r) {
-      const uint32_t n = sg.n(r);
-      const uint32_t lo = (uint32_t)((uint64_t)n * w / NW), hi = (uint32_t)((uint64_t)n * (w + 1) / NW);
-      emit_ge(sg.ptr(r) + lo, hi - lo, T, oi, os, offs[r * NW + w], K);
+    uint32_t o = woff[w];
+    for (int r = r0; r < nseg && sg.off[r] < hi; ++r) {
+      const uint32_t s0 = max(lo, sg.off[r]) - sg.off[r], s1 = min(hi, sg.off[r + 1]) - sg.off[r];
+      o = emit_ge(sg.ptr(r) + s0, s1 - s0, T, oi, os, o, K);
     }
     out = min(total, (uint32_t)K);
     for (uint32_t i = out + threadIdx.x; i < (uint32_t)K; i += NT) {
@@ -161,7 +172,8 @@ __global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLau
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int K = p.topk;
-  const Segs sg{p.cb.row(q, p.r0), p.cb.count(q, p.r0), p.cb.rows * p.cb.cap, p.cb.rows, p.r1 - p.r0};
+  const Segs sg{p.cb.row(q, p.r0), p.cb.count(q, p.r0), p.cb.rows * p.cb.cap, p.cb.rows, p.r1 - p.r0,
+                (uint32_t)p.cb.cap, nullptr};
   __shared__ u64 kth;
   uint32_t total = 0;
   for (int r = 0; r < sg.nseg; ++r) total += sg.n(r);
@@ -212,7 +224,7 @@ __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p)
   const u64* base = p.cb.row(q, p.r0);
   const uint32_t* cnt = p.cb.count(q, p.r0);
   const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
-  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg};
+  const Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg, (uint32_t)p.cb.cap, nullptr};
   uint32_t total = 0;
   for (int r = 0; r < nseg; ++r) total += sg.n(r);
   u64 T = 0;
