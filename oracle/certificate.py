@@ -24,6 +24,8 @@ Method section; the zicq.com summary, "Technical Mechanism Analysis" items
 5. Certificate: UB(t,s) = sum_p c_p ReLU(q_p.k_s) + rho ||k_s|| - ReLU(a.k_s)
    >= S(t,s).  A key with UB < tau cannot enter the Top-K (K seed keys score
    at least tau > S), whatever the tie rule, so it is pruned.
+6. Key blocks: a block's centre, radius and largest norm give one bound that
+   dominates UB for every key of the block (block_upper_bound).
 
 None of the choices (seed set, proxy count, rho variant, support) affects the
 selected set as long as each bound is valid; they only change how much is
@@ -129,6 +131,48 @@ def upper_bound(pl, k: np.ndarray) -> np.ndarray:
     if pl["P"].size:
         ub = ub + np.maximum(pl["qP"] @ k.T, 0.0).T @ pl["c"]
     ub = ub - np.maximum(k @ pl["a"], 0.0)
+    return ub
+
+
+def block_summaries(k: np.ndarray, block: int = 64):
+    """Summaries of the blocks of ``block`` consecutive keys (the last one may be short).
+
+    Any centre works for the block bound; this one is the mean of the block's keys.
+    Returns (centre [n_blocks, d], radius [n_blocks] = max_s ||k_s - centre||,
+    maxnorm [n_blocks] = max_s ||k_s||), float64.
+    """
+    n = k.shape[0]
+    nb = (n + block - 1) // block
+    centre = np.zeros((nb, k.shape[1]))
+    radius = np.zeros(nb)
+    maxnorm = np.zeros(nb)
+    for b in range(nb):
+        kb = k[b * block:(b + 1) * block]
+        centre[b] = kb.mean(axis=0)
+        radius[b] = np.linalg.norm(kb - centre[b], axis=1).max()
+        maxnorm[b] = np.linalg.norm(kb, axis=1).max()
+    return centre, radius, maxnorm
+
+
+def block_upper_bound(pl, centre, radius, maxnorm):
+    """One bound for every key of a block (DoSA pages: the transcript's Conclusion
+    names certificates over key blocks instead of individual keys).
+
+    For a key s of a block with centre c and radius r (||k_s - c|| <= r) and
+    N >= ||k_s||:  q_p.k_s <= q_p.c + ||q_p|| r, and ReLU and c_p >= 0 keep the
+    order, so the proxy term is at most sum_p c_p ReLU(q_p.c + ||q_p|| r); the
+    residual term rho ||k_s|| is at most rho N; a.k_s >= a.c - ||a|| r, so the
+    negative aggregate subtracts at least ReLU(a.c - ||a|| r).  Hence
+        BUB = sum_p c_p ReLU(q_p.c + ||q_p|| r) + rho N - ReLU(a.c - ||a|| r)
+    is at least UB(t, s) for every key of the block, and a block with BUB < tau
+    holds no key the per-key certificate would keep.
+    """
+    centre = np.atleast_2d(centre)
+    ub = pl["rho"] * np.asarray(maxnorm, dtype=np.float64)
+    if pl["P"].size:
+        qn = np.linalg.norm(pl["qP"], axis=1)
+        ub = ub + np.maximum(centre @ pl["qP"].T + np.outer(radius, qn), 0.0) @ pl["c"]
+    ub = ub - np.maximum(centre @ pl["a"] - np.linalg.norm(pl["a"]) * np.asarray(radius), 0.0)
     return ub
 
 

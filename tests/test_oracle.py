@@ -491,3 +491,72 @@ def test_bound_dominates_sampled_queries_of_the_32k_prefill():
     rows = [100, 5000, 20000, 32767]
     assert _ub_dominates(wl, rows, num_proxies=3, prefix=64, window=8192) >= -1e-12
     assert _ub_dominates(wl, rows[-1:], num_proxies=3, prefix=64, window=8192, rho_kind="separable") >= -1e-12
+
+
+# ----------------------------------------------------------------------------
+# key-block certificate
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("p,frac,block", [(3, 0.5, 64), (1, 0.0, 16), (0, 0.5, 7), (3, 1.0, 1)])
+def test_block_bound_dominates_every_key_bound(p, frac, block):
+    """BUB >= UB(t, s) for every key of every block (i.i.d. and drifting keys)."""
+    rng = np.random.default_rng(71 + p + block)
+    H, d, n = 8, 16, 400
+    for t in range(4):
+        q = rng.standard_normal((H, d))
+        w = rng.standard_normal(H)
+        if t % 2:
+            k = rng.standard_normal((n, d)) * rng.uniform(0.2, 3.0, size=(n, 1))
+        else:   # slowly drifting keys: tight blocks
+            k = np.cumsum(rng.standard_normal((n, d)) * 0.1, axis=0) + rng.standard_normal((n, d)) * 0.05
+        pl = cert.plan(q, w, q @ k[:40].T, num_proxies=p, support_frac=frac)
+        UB = cert.upper_bound(pl, k)
+        cen, rad, mx = cert.block_summaries(k, block)
+        BUB = cert.block_upper_bound(pl, cen, rad, mx)
+        scale = indexer.abs_mass(q[None], w[None], k)[0] + 1.0
+        for b in range(BUB.size):
+            sl = slice(b * block, (b + 1) * block)
+            assert np.all(BUB[b] - UB[sl] >= -1e-12 * scale[sl].max()), (t, b)
+
+
+def test_block_bound_of_one_key_is_the_key_bound():
+    """A one-key block has centre k, radius 0 and largest norm ||k||: BUB = UB exactly."""
+    rng = np.random.default_rng(72)
+    q = rng.standard_normal((6, 12))
+    w = rng.standard_normal(6)
+    k = rng.standard_normal((50, 12))
+    pl = cert.plan(q, w, q @ k.T, num_proxies=2, support_frac=0.3)
+    cen, rad, mx = cert.block_summaries(k, 1)
+    assert np.all(rad == 0) and np.allclose(mx, np.linalg.norm(k, axis=1))
+    assert np.allclose(cert.block_upper_bound(pl, cen, rad, mx), cert.upper_bound(pl, k), rtol=1e-13, atol=1e-12)
+
+
+def test_block_bound_without_radius_is_caught():
+    """A plausible mistake -- the centre used as if it were every key (radius dropped) --
+    breaks BUB >= UB on some block."""
+    rng = np.random.default_rng(73)
+    q = rng.standard_normal((8, 16))
+    w = np.abs(rng.standard_normal(8))
+    k = rng.standard_normal((512, 16))
+    pl = cert.plan(q, w, None, 3)
+    cen, rad, mx = cert.block_summaries(k, 64)
+    UB = cert.upper_bound(pl, k).reshape(8, 64).max(axis=1)
+    assert np.all(cert.block_upper_bound(pl, cen, rad, mx) >= UB - 1e-9)
+    assert np.any(cert.block_upper_bound(pl, cen, np.zeros_like(rad), mx) < UB - 1e-6)
+
+
+def test_block_pruning_is_within_key_pruning_on_the_correlated_recipe():
+    """Blocks the block bound prunes hold only keys the per-key certificate prunes, and the
+    block bound does prune on the correlated recipe (a late query of a 12K context)."""
+    wl = synth.correlated_heads(L=12288, topk=512)
+    r = wl.total_q - 1
+    kv = indexer.seq_keys(wl, 0, r + 1)
+    c = cert.query_certificate(indexer.query_rows(wl, [r])[0], indexer.weights(wl, [r])[0], kv, r, wl.topk,
+                               prefix=64, window=2048)
+    cen, rad, mx = cert.block_summaries(kv, 64)
+    BUB = cert.block_upper_bound(c["plan"], cen, rad, mx)
+    seeds = np.zeros(r + 1, bool)
+    seeds[c["seeds"]] = True
+    pruned_blocks = [b for b in range(BUB.size) if BUB[b] < c["tau"] and not seeds[b * 64:(b + 1) * 64].any()]
+    assert len(pruned_blocks) > 0
+    for b in pruned_blocks:
+        assert np.all(c["pruned"][b * 64:(b + 1) * 64])
