@@ -157,6 +157,7 @@ def main():
     ap.add_argument("--paths", default="dosa,dsa")
     ap.add_argument("--buffer-cap", type=int, default=0, help="candidate buffer entries per query (0 = default)")
     ap.add_argument("--key-splits", type=int, default=0)
+    ap.add_argument("--flags", type=lambda x: int(x, 0), default=0, help="DOSA_* flags OR-ed into the config")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this size first (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -201,6 +202,7 @@ def main():
             cfg.buffer_cap = a.buffer_cap
         if a.key_splits:
             cfg.key_splits = a.key_splits
+        cfg.flags |= a.flags
         ws_bytes = max(E.workspace_size(c.q_lens, c.kv_lens, c.H, c.d, K, c.q_dtype, c.k_dtype,
                                         c.page_table is not None, path == "dsa", cfg) for _, c in calls)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)

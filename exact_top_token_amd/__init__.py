@@ -28,6 +28,7 @@ DOSA_SORTED = 0x2
 DOSA_SEPARABLE_RHO = 0x4
 DOSA_NO_NEGATIVE = 0x8
 DOSA_NO_PROBE = 0x10
+DOSA_KEY_BLOCKS = 0x20
 
 STATUS = {0: "DOSA_OK", -1: "DOSA_ERR_INVALID_ARG", -2: "DOSA_ERR_UNSUPPORTED", -3: "DOSA_ERR_WORKSPACE",
           -4: "DOSA_ERR_HIP"}
@@ -58,7 +59,7 @@ class DosaStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "pairs_total", "pairs_seed", "pairs_bounded", "pairs_survived", "pairs_scored",
         "candidates_written", "reselects", "groups_skipped", "pairs_scored_list", "keys_streamed",
-        "calls_unpruned")]
+        "calls_unpruned", "key_blocks_skipped")]
 
 
 STAT_FIELDS = [f[0] for f in DosaStats._fields_]

@@ -97,10 +97,12 @@ struct Plan {
   int n_tiles = 0;                   // query tiles (seed items 0 .. n_tiles*Js-1 are Js per tile, tile order)
   int mask_words = 0;
   int64_t list_total = 0;
+  int64_t n_blocks = 0;              // 64-key blocks of all sequences (key-block summaries)
   // workspace offsets
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
-         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, total = 0;
+         o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, o_blk_code = 0, o_blk_info = 0,
+         total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -197,7 +199,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.F = cfg.seed_prefix;
   P.W = std::max(cfg.seed_window, 64);
   const int TW = tile_waves();
-  int64_t cq = 0, ck = 0;
+  int64_t cq = 0, ck = 0, cb = 0;
   uint64_t pairs = 0;
   std::vector<TileInfo> tiles;
   for (int b = 0; b < batch; ++b) {
@@ -210,6 +212,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       g.pos0 = n - m + i;
       g.key_base = paged ? 0 : (int32_t)ck;
       g.norm_base = (int32_t)ck;
+      g.blk_base = (int32_t)cb;
       const int gi = (int)P.groups.size();
       if (tiles.empty() || tiles.back().seq != b || tiles.back().n == TW) tiles.push_back({gi, 0, 0, b});
       tiles.back().n += 1;
@@ -219,7 +222,9 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     pairs += (uint64_t)m * (uint64_t)(n - m + 1) + (uint64_t)m * (uint64_t)(m - 1) / 2;
     cq += m;
     ck += n;
+    cb += (n + kKeyBlock - 1) / kKeyBlock;
   }
+  P.n_blocks = cb;
   for (auto& t : tiles)
     for (int i = 0; i < t.n; ++i) {
       P.groups[t.first + i].tile_first = t.first;
@@ -539,7 +544,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes); return at; };
   P.o_groups = take(sizeof(GroupInfo) * std::max(G, 1));
   P.o_items = take(sizeof(WorkItem) * std::max<size_t>(P.items.size(), 1));
-  if (!dense) P.o_seqinfo = take((size_t)(batch + 1) * sizeof(int32_t));   // copied with groups and items
+  if (!dense) P.o_seqinfo = take((size_t)2 * (batch + 1) * sizeof(int32_t));   // cu_kv, cu_blk: copied with the plan
   P.o_cand = take((size_t)P.total_q * P.R * P.cap * sizeof(u64));
   P.o_counts = take((size_t)P.total_q * P.R * sizeof(uint32_t));
   const int LS = 16 / P.QW;   // weighted-query terms per query
@@ -550,7 +555,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   if (!dense) {
     P.o_tau = take((size_t)P.total_q * sizeof(float));
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
-    P.o_coef = take((size_t)P.total_q * 8 * sizeof(float));
+    P.o_coef = take((size_t)P.total_q * kCoefStride * sizeof(float));
     P.o_norms = take((size_t)std::max<int64_t>(P.total_k, 1) * sizeof(float));
     P.o_flag = take(sizeof(int32_t));
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
@@ -559,6 +564,9 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
     P.o_mode = take(sizeof(int32_t));
     P.o_order = take(sizeof(int32_t) * std::max<size_t>(P.surv_tiled_items.size(), 1));
+    const int kbytes = (k_dtype == DOSA_F32) ? 4 : (k_dtype == DOSA_BF16 ? 2 : 1);
+    P.o_blk_code = take((size_t)std::max<int64_t>(P.n_blocks, 1) * d * kbytes);
+    P.o_blk_info = take((size_t)std::max<int64_t>(P.n_blocks, 1) * 4 * sizeof(float));
   }
   P.total = o;
 }
@@ -805,20 +813,25 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   // so one copy at the start costs one such wait instead of one per array.
   {
     const size_t n_items = sizeof(WorkItem) * P.items.size();
-    const size_t end = dense ? P.o_items + n_items : P.o_seqinfo + (size_t)(batch + 1) * sizeof(int32_t);
+    const size_t end = dense ? P.o_items + n_items : P.o_seqinfo + (size_t)2 * (batch + 1) * sizeof(int32_t);
     std::vector<char> stage(end - P.o_groups, 0);
     std::memcpy(stage.data(), P.groups.data(), sizeof(GroupInfo) * P.groups.size());
     std::memcpy(stage.data() + (P.o_items - P.o_groups), P.items.data(), n_items);
     if (!dense) {
       int32_t* cu = reinterpret_cast<int32_t*>(stage.data() + (P.o_seqinfo - P.o_groups));
+      int32_t* cub = cu + (batch + 1);
       cu[0] = 0;
-      for (int b = 0; b < batch; ++b) cu[b + 1] = cu[b] + kv_lens[b];
+      cub[0] = 0;
+      for (int b = 0; b < batch; ++b) {
+        cu[b + 1] = cu[b] + kv_lens[b];
+        cub[b + 1] = cub[b] + (kv_lens[b] + kKeyBlock - 1) / kKeyBlock;
+      }
     }
     e = hipMemcpyAsync(ws + P.o_groups, stage.data(), stage.size(), hipMemcpyHostToDevice, stream);
     if (e != hipSuccess) return fail_hip(e, "hipMemcpyAsync(plan)");
   }
   if (st) {
-    unsigned long long add[11] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
+    unsigned long long add[12] = {P.pairs_total, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0};
     e = launch_stats_add(st, add, stream);
     if (e != hipSuccess) return fail_hip(e, "stats");
   }
@@ -985,10 +998,14 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     if (e != hipSuccess) return fail_hip(e, "plan kernel launch");
     // 4b. per-key norms for the bound pass; the launch returns at once when the
     //     plan found no query whose certificate can prune
-    NormLaunch nl{in, cu_dev, batch, P.total_k, max_kv, norms, cfg.debug_ub != nullptr ? nullptr : prunes};
+    const bool key_blocks = P.tiled && (cfg.flags & DOSA_KEY_BLOCKS) != 0;
+    NormLaunch nl{in, cu_dev, batch, P.total_k, max_kv, norms, cfg.debug_ub != nullptr ? nullptr : prunes,
+                  cu_dev + (batch + 1), key_blocks ? reinterpret_cast<uint8_t*>(ws + P.o_blk_code) : nullptr,
+                  reinterpret_cast<float*>(ws + P.o_blk_info)};
     {
       PassScope ps(P_NORMS, stream);
       e = launch_key_norms(P.combo, d, nl, stream);
+      if (e == hipSuccess) e = launch_key_blocks(P.combo, d, nl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
     // 5. bound pass -> survivor bitmasks
@@ -1007,6 +1024,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     bl.debug_ld = max_kv;
     bl.debug_mask = reinterpret_cast<unsigned long long*>(cfg.debug_mask);
     bl.debug_mask_ld = (max_kv + 63) / 64;
+    if (key_blocks) {
+      bl.blk_code = reinterpret_cast<const uint8_t*>(ws + P.o_blk_code);
+      bl.blk_info = reinterpret_cast<const float*>(ws + P.o_blk_info);
+    }
     bl.splits = P.bound_splits;
     if (!P.bound_items.empty()) {
       bl.items = di + off_bound;

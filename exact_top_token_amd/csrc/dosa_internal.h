@@ -44,6 +44,7 @@ struct GroupInfo {
   int32_t norm_base; // index of the sequence's key 0 in the per-key norm array
   int32_t tile_first;// first group of the tile (<= 8 consecutive groups) this group belongs to
   int32_t tile_n;    // groups in that tile
+  int32_t blk_base;  // index of the sequence's first 64-key block in the key-block summaries
 };
 
 // A share of scoring: a group (list kernel) or a tile of up to 8 groups
@@ -135,7 +136,7 @@ struct ScoreLaunch {
   const int32_t* order;      // [n_items]: workgroup b takes item order[b] (longest first), or NULL
   int32_t flag_mode;         // 0: run every item; 1: only tiles flagged; 2: only groups whose tile is not
   int32_t role;              // Role
-  unsigned long long* stats; // dosa_stats as u64[11] or NULL
+  unsigned long long* stats; // dosa_stats as u64[12] or NULL
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;
 };
@@ -158,14 +159,17 @@ struct SelectLaunch {
 };
 
 // Certificate plan: per query 4 operand rows of d elements in the query
-// storage type (proxy rows first, then terms of the negative aggregate) and 8
-// fp32 coefficients:
+// storage type (proxy rows first, then terms of the negative aggregate) and
+// kCoefStride fp32 coefficients:
 //   coef[0..3] : per-row multiplier (proxy rows: c_p * q_scale; aggregate
 //                rows: sigma_j * q_scale)
 //   coef[4]    : rho' * q_scale (joint residual constant plus rounding margin)
 //   coef[5]    : tau (seed threshold)
 //   coef[6]    : number of proxy rows p (rows p..3 are aggregate terms)
 //   coef[7]    : 1 if the certificate cannot prune any key of this query
+//   coef[8..11]: Euclidean norm of each row's stored values (rounded up), for
+//                the key-block bound
+constexpr int kCoefStride = 16;
 struct PlanLaunch {
   Inputs in;
   const GroupInfo* groups;
@@ -196,6 +200,8 @@ struct BoundLaunch {
   int32_t debug_ld;
   unsigned long long* debug_mask;  // [total_q, debug_mask_ld] survivor bits per (query, key) or NULL
   int32_t debug_mask_ld;
+  const uint8_t* blk_code;   // key-block centres [blocks, d] in the key storage type, or NULL (no block test)
+  const float* blk_info;     // [blocks, 4]: centre scale, radius, largest key norm, centre norm
   int32_t splits;            // key splits per group (grid = n_groups * splits; per-group kernel)
   const WorkItem* items;     // tiled kernel: one per (query block, key share): group = first group,
                              // pad = groups, [a0, a1) keys, b0 = share index; NULL = per-group kernel
@@ -248,7 +254,13 @@ struct NormLaunch {
   int32_t max_kv;            // longest sequence
   float* norms;              // [total_k]
   const int32_t* needed;     // NULL, or the plan's flag: 0 = no query can prune, nothing to do
+  const int32_t* cu_blk;     // [batch+1] offsets of the sequences' 64-key blocks (key-block kernel)
+  uint8_t* blk_code;         // [blocks, d] centres in the key storage type (key-block kernel)
+  float* blk_info;           // [blocks, 4] (key-block kernel)
 };
+
+constexpr int kKeyBlock = 64;       // keys per key block (= the bound pass's key tile)
+constexpr int kMaxBoundTiles = 4096;// key tiles of a bound item that the block test covers
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s);
@@ -256,6 +268,7 @@ hipError_t launch_prep(int combo, int H, int d, const PrepLaunch& p, hipStream_t
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
 hipError_t launch_select_tau(const SelectLaunch& p, hipStream_t s);
 hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s);
+hipError_t launch_key_blocks(int combo, int d, const NormLaunch& p, hipStream_t s);
 hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t s);
 hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);

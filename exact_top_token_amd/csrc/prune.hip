@@ -150,6 +150,123 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
 }
 
 // ---------------------------------------------------------------------------
+// key-block summaries for the block certificate: per block of 64 consecutive
+// keys of a sequence (the last one may be short), a centre stored in the key
+// storage type (fp8: codes times a per-block scale), the radius of the block
+// around that centre, its largest key norm and the centre's norm.  Any centre
+// gives a valid bound; this one is the block mean, rounded to the storage
+// type, and the radius is measured against the rounded centre itself.
+// One wavefront per block: the rows are staged in LDS, lane i averages
+// elements i (and i + 64), then lane s measures key s.  Sums are fp32 of
+// exactly decoded values; radius and norms are rounded up (2^-16 relative for
+// the sums of at most 128 squares and the square root, plus 2^-21 of the
+// magnitudes for the fp32 rounding of the dequantised values and differences).
+// ---------------------------------------------------------------------------
+template <int C, int D>
+__global__ __launch_bounds__(64) void key_block_kernel(const NormLaunch p) {
+  if (p.needed != nullptr && *p.needed == 0) return;   // the plan marked every query hopeless
+  constexpr int KBY = KBytes<C>::value;
+  constexpr int ROWB = D * KBY;
+  constexpr int RS = ROWB + 16;                        // padded LDS row (bytes)
+  constexpr int CPR = ROWB / 16;                       // 16-byte chunks per row
+  constexpr int PER = (D + 63) / 64;                   // elements per lane
+  __shared__ __attribute__((aligned(16))) uint8_t rows[kKeyBlock * RS];
+  __shared__ float ksc[kKeyBlock];
+  __shared__ float cen[D];
+  const int lane = lane_id();
+  auto elem = [&](int s, int i) -> float {             // stored value i of staged key s (undecoded scale)
+    const uint8_t* r = rows + s * RS;
+    if constexpr (KBY == 4) return reinterpret_cast<const float*>(r)[i];
+    else if constexpr (KBY == 2) return dec_bf16((uint32_t)reinterpret_cast<const uint16_t*>(r)[i]);
+    else return dec_fp8((uint32_t)r[i]);
+  };
+#pragma unroll 1
+  for (int b = blockIdx.y; b < p.batch; b += gridDim.y) {
+    const int n = p.cu_kv[b + 1] - p.cu_kv[b];
+    const int k0 = blockIdx.x * kKeyBlock;
+    if (k0 >= n) continue;
+    const int ns = min(kKeyBlock, n - k0);
+    const int64_t blk = (int64_t)p.cu_blk[b] + blockIdx.x;
+    // stage the block's rows and scales
+    for (int c = lane; c < ns * CPR; c += 64) {
+      const int s = c / CPR, part = c % CPR;
+      const int64_t row = key_row(p.in, p.cu_kv[b], b, k0 + s);
+      *reinterpret_cast<uint4*>(rows + s * RS + 16 * part) =
+          reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(p.in.k) + row * ROWB)[part];
+    }
+    if (lane < ns) ksc[lane] = HasKScale<C>::value ? p.in.k_scale[key_row(p.in, p.cu_kv[b], b, k0 + lane)] : 1.f;
+    __syncthreads();
+    // mean, rounded to the storage type (fp8: per-block scale = max |mean| / 448)
+    float mean[PER];
+    float amax = 0.f;
+#pragma unroll
+    for (int v = 0; v < PER; ++v) {
+      const int i = lane + 64 * v;
+      float acc = 0.f;
+      if (i < D)
+        for (int s = 0; s < ns; ++s) acc = fmaf(ksc[s], elem(s, i), acc);
+      mean[v] = acc / (float)ns;
+      amax = fmaxf(amax, fabsf(mean[v]));
+    }
+    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    float sc = 1.f;
+    if constexpr (KBY == 1) {
+      sc = amax > 0.f ? amax / 448.f : 1.f;
+      if (!(sc > 0.f)) sc = 1.f;
+    }
+    uint8_t* code = p.blk_code + blk * ROWB;
+#pragma unroll
+    for (int v = 0; v < PER; ++v) {
+      const int i = lane + 64 * v;
+      if (i >= D) continue;
+      float cv;
+      if constexpr (KBY == 4) {
+        reinterpret_cast<float*>(code)[i] = mean[v];
+        cv = mean[v];
+      } else if constexpr (KBY == 2) {
+        const uint32_t bits = enc_bf16(mean[v]);
+        reinterpret_cast<uint16_t*>(code)[i] = (uint16_t)bits;
+        cv = dec_bf16(bits);
+      } else {
+        const uint32_t c8 = enc_fp8(mean[v] / sc);
+        code[i] = (uint8_t)c8;
+        cv = sc * dec_fp8(c8);
+      }
+      cen[i] = cv;
+    }
+    __syncthreads();
+    // lane s: distance of key s from the centre, and its norm
+    float d2 = 0.f, n2 = 0.f, c2 = 0.f;
+    if (lane < ns) {
+      const float ks = ksc[lane];
+      for (int i = 0; i < D; ++i) {
+        const float e = elem(lane, i);
+        const float df = ks * e - cen[i];
+        d2 = fmaf(df, df, d2);
+        n2 = fmaf(e, e, n2);
+      }
+    }
+    for (int i = lane; i < D; i += 64) c2 = fmaf(cen[i], cen[i], c2);
+    for (int off = 32; off > 0; off >>= 1) c2 += __shfl_xor(c2, off, 64);
+    float dmax = sqrtf(d2), nmax = (lane < ns) ? sqrtf(n2) * ksc[lane] : 0.f;
+    for (int off = 32; off > 0; off >>= 1) {
+      dmax = fmaxf(dmax, __shfl_xor(dmax, off, 64));
+      nmax = fmaxf(nmax, __shfl_xor(nmax, off, 64));
+    }
+    if (lane == 0) {
+      const float cn = sqrtf(c2) * 1.0000153f;
+      const float nb = nmax * 1.0000153f;
+      float* info = p.blk_info + blk * 4;
+      info[0] = sc;
+      info[1] = dmax * 1.0000153f + 4.7683716e-7f * (nb + cn);   // + 2^-21 (N + ||c||)
+      info[2] = nb;
+      info[3] = cn;
+    }
+    __syncthreads();   // the staged rows are rewritten by the next sequence's block
+  }
+}
+
+// ---------------------------------------------------------------------------
 // per-query plan, one workgroup of 256 threads per query
 // ---------------------------------------------------------------------------
 // Nonnegative least squares of a head on <= 3 proxies, exhaustive over
@@ -276,6 +393,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __shared__ double hsum[8];                       // c_0..c_2, rho_sep, rho_lo, sum |w_h| ||q_h||, margin
   __shared__ float cfs[6];                         // row multipliers, rho_lo, rho_sep + margin (scaled)
   __shared__ double red4[4];
+  __shared__ float rnorm[4];                       // norms of the 4 stored certificate rows (rounded up)
   __shared__ int np_s, nsurv_s, nsep_s;
 
   // ---- 0. issue the loads
@@ -580,6 +698,23 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   // clearly larger part of the sample than the separable one.  Skipping
   // either is always correct, so these are cost decisions only.
   if (t == 0) nsep_s = 0;
+  if (wave == 1) {
+    // Euclidean norm of each stored row (the values the bound pass multiplies),
+    // for the key-block bound: fp32 sums of squares of exactly decoded values,
+    // rounded up by 2^-16 relative
+    for (int r = 0; r < 4; ++r) {
+      float acc = 0.f;
+      for (int i = lane; i < D; i += 64) {
+        float v;
+        if constexpr (QB == 1) v = dec_fp8((uint32_t)rowl[r * D + i]);
+        else if constexpr (QB == 4) v = reinterpret_cast<const float*>(rowl)[r * D + i];
+        else v = dec_bf16((uint32_t)reinterpret_cast<const uint16_t*>(rowl)[r * D + i]);
+        acc = fmaf(v, v, acc);
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) rnorm[r] = sqrtf(acc) * 1.0000153f;
+    }
+  }
   if (wave == 0 && nsb > 0) {
     typename O::frag A[O::STEPS];
     if (col < 4) O::load_q(rowl + col * D * QB, g, A);
@@ -665,12 +800,13 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   if (t == 0) {
     const double qs = (double)qscale;
     const double rho_p = (rho + hsum[6]) * qs;
-    float* cf = p.coef + (int64_t)qrow * 8;
+    float* cf = p.coef + (int64_t)qrow * kCoefStride;
     for (int r = 0; r < 4; ++r) cf[r] = (r < np) ? (float)(hsum[r] * qs) : (float)(sig[r] * qs);
     cf[4] = (float)rho_p * 1.0000005f;
     cf[5] = tau;
     cf[6] = (float)np;
     cf[7] = hopeless ? 1.f : 0.f;
+    for (int r = 0; r < 4; ++r) cf[8 + r] = rnorm[r];
     if (!hopeless && p.prunes != nullptr) atomicOr(p.prunes, 1);   // the bound pass has work: key norms are needed
   }
 }
@@ -699,7 +835,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
   const int qrow = gr.q_row0 + g;
   float cf[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cf[i] = qok ? p.coef[(int64_t)qrow * 8 + i] : 0.f;
+  for (int i = 0; i < 8; ++i) cf[i] = qok ? p.coef[(int64_t)qrow * kCoefStride + i] : 0.f;
   const int npx = (int)cf[6];
   const bool hopeless = !qok || cf[7] != 0.f;
   const u64 hm = __ballot(qok && hopeless);
@@ -795,7 +931,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
 // read once per workgroup.  Each group gets one 64-bit union-survivor word per
 // 64 keys.
 // ---------------------------------------------------------------------------
-template <int C, int D, int GPW>
+template <int C, int D, int GPW, bool BLOCKS>
 __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const BoundLaunch p) {
   using O = Ops<C, D>;
   constexpr int STEPS = O::STEPS;
@@ -805,6 +941,9 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   constexpr int NCH = (64 * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][64 * ROW];
   __shared__ float kinfo[2][2][64];                  // [buffer][scale, norm][key]
+  // key-block test (BLOCKS): bit t set if tile t is loaded / if this wavefront bounds it
+  __shared__ uint32_t keep[BLOCKS ? kMaxBoundTiles / 32 : 1];
+  __shared__ uint32_t keep_w[kTileWaves][BLOCKS ? kMaxBoundTiles / 32 : 1];
   if (skip_launch(p.mode, p.run_if)) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;
   const int lane = lane_id();
@@ -825,7 +964,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   const int qrow = gr.q_row0 + gq;
   float cf[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) cf[i] = qok ? p.coef[(int64_t)qrow * 8 + i] : 0.f;
+  for (int i = 0; i < 8; ++i) cf[i] = qok ? p.coef[(int64_t)qrow * kCoefStride + i] : 0.f;
   const int npx = (int)cf[6];
   const bool hopeless = !qok || cf[7] != 0.f;
   // lanes of this lane's group, and whether every query of it is hopeless
@@ -843,7 +982,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
   // the whole workgroup leaves if no wavefront has work (and no dump is asked for)
   const bool dump = p.debug_ub != nullptr || p.debug_mask != nullptr;
   if (__syncthreads_and(!active || all_hopeless) && !dump) return;
-  if (p.stats != nullptr && threadIdx.x == 0) atomicAdd(&p.stats[9], (u64)max(hi - lo, 0));   // rows this workgroup streams
+  if (!BLOCKS && p.stats != nullptr && threadIdx.x == 0)
+    atomicAdd(&p.stats[9], (u64)max(hi - lo, 0));   // rows this workgroup streams
   typename O::frag A[STEPS];
   {
     const int ra = lane & 15;
@@ -917,26 +1057,165 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
     if (gbase + j < gend && (prunable & mj) != 0ull) keep_lanes |= mj;
   }
   u64 n_surv = 0;
+  const bool work = active && !(all_hopeless && !dump);
+  // Key-block test (DoSA pages: the transcript's Conclusion, certificates over
+  // key blocks).  Tiles are 64-key blocks when the item starts on a block
+  // boundary.  A lane of a query that keeps survivor books vetoes skipping a
+  // tile unless the block bound
+  //   BUB = sum_p c_p ReLU(s x_p + |r_p| rad) + rho' N - ReLU(s x_a - |a| rad) + margin
+  // (x = row . centre on MFMA, s the centre's scale) is below its tau; tiles no
+  // lane vetoes are never loaded, and their survivor words are zero.
+  const bool blocks_on = BLOCKS && (lo & (kKeyBlock - 1)) == 0 && ntiles <= kMaxBoundTiles;
+  float nr[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) nr[i] = (BLOCKS && qok) ? p.coef[(int64_t)qrow * kCoefStride + 8 + i] : 0.f;
+  // the centre fragment and summary of block column col of chunk c0
+  struct BlockFrag {
+    typename O::frag B[STEPS];
+    v4f inf;
+  };
+  auto block_load = [&](int c0, BlockFrag& f) {
+    const int bt = c0 + col;
+    const int64_t blk = (int64_t)g0.blk_base + (lo >> 6) + bt;
+    if (bt < ntiles) {
+      O::load_k(p.blk_code + blk * KBYTES, g, f.B);
+      f.inf = *reinterpret_cast<const v4f*>(p.blk_info + blk * 4);
+    } else {
+      O::zero(f.B);
+      f.inf = v4f{1.f, 0.f, 0.f, 0.f};
+    }
+  };
+  // block bound of this lane's query for block column col of chunk c0 (all lanes take part)
+  auto block_bound_of = [&](int c0, const BlockFrag& f, bool& bv) -> float {
+    bv = c0 + col < ntiles;
+    const v4f inf = f.inf;
+    const typename O::frag* B = f.B;
+    v4f c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) c = O::mma(A[s], B[s], c);
+    const float sc = inf[0], rad = inf[1], nb = inf[2], cn = inf[3];
+    float pos = 0.f, neg = 0.f, wsum = 0.f, nrad = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pos += cpos[i] * fmaxf(fmaf(sc, c[i], nr[i] * rad), 0.f);
+      neg += cneg[i] * (sc * c[i]);
+      nrad += cneg[i] * nr[i];
+      wsum += (cpos[i] + cneg[i]) * nr[i];
+    }
+    neg -= nrad * rad;
+    // rounding margin: 2 gamma_n (sum_r cf_r |r| (|c| + rad) + rho' N), n = d + 16, u = 2^-22
+    constexpr float gam = (float)((D + 16) * 2.384185791015625e-7 / (1.0 - (D + 16) * 2.384185791015625e-7));
+    const float base = pos - fmaxf(neg, 0.f) + cf[4] * nb;
+    const float mg = 2.f * gam * (wsum * (cn + rad) + cf[4] * nb);
+    return base + mg + 1e-6f * fabsf(base);
+  };
+  auto block_bound = [&](int c0, bool& bv) -> float {
+    BlockFrag f;
+    block_load(c0, f);
+    return block_bound_of(c0, f, bv);
+  };
+  if (BLOCKS && blocks_on) {
+    const int tid = (int)threadIdx.x;
+    for (int i = tid; i < (ntiles + 31) / 32; i += 64 * kTileWaves) keep[i] = 0u;
+    for (int i = lane; i < (ntiles + 31) / 32; i += 64) keep_w[wave][i] = 0u;
+    __syncthreads();
+    if (work) {
+      const bool books = ((keep_lanes >> lane) & 1ull) != 0ull;
+      // the next chunk's centres load while this chunk's bounds are evaluated
+      BlockFrag fcur, fnext;
+      block_load(0, fcur);
+      for (int c0 = 0; c0 < ntiles; c0 += 16) {
+        if (c0 + 16 < ntiles) block_load(c0 + 16, fnext);
+        bool bv;
+        const float bub = block_bound_of(c0, fcur, bv);
+        const bool veto = bv && books && qok && (hopeless || !(bub < cf[5]));
+        const u64 m = __ballot(veto);
+        const uint32_t u = (uint32_t)(m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFu;
+        if (lane == 0 && u != 0u) {
+          atomicOr(&keep[c0 >> 5], u << (c0 & 31));
+          keep_w[wave][c0 >> 5] |= u << (c0 & 31);   // only this wavefront writes its row
+        }
+        if (c0 + 16 < ntiles) fcur = fnext;
+      }
+    }
+    __syncthreads();
+    // skipped tiles: zero survivor words for the groups that keep books; with a
+    // dump, the block bound as every key's bound (and hopeless queries' bits)
+    if (work) {
+      for (int c0 = 0; c0 < ntiles; c0 += 16) {
+        const uint32_t kw = (keep[c0 >> 5] >> (c0 & 31)) & 0xFFFFu;
+        const uint32_t live = (ntiles - c0 >= 16) ? 0xFFFFu : ((1u << (ntiles - c0)) - 1u);
+        if ((~kw & live) == 0u) continue;            // every tile of the chunk is loaded
+        if (lane == 0) {
+          for (int b = 0; b < 16; ++b) {
+            if (!((live >> b) & 1u) || ((kw >> b) & 1u)) continue;
+            const int kb = lo + 64 * (c0 + b);
+            for (int j = 0; j < gpw; ++j) {
+              if (gbase + j >= gend) break;
+              const u64 mj = (qw == 4) ? ~0ull : (((1ull << (16 * qw)) - 1ull) << (16 * qw * j));
+              if ((keep_lanes & mj) == 0ull) continue;
+              p.masks[(int64_t)(gbase + j) * p.mask_words + ((kb - g0.bound_lo) >> 6)] = 0ull;
+            }
+          }
+          if (p.stats != nullptr && wave == 0) atomicAdd(&p.stats[11], (u64)__popc(~kw & live));
+        }
+        if (dump) {
+          bool bv;
+          const float bub = block_bound(c0, bv);
+          const int bt = c0 + col;
+          if (bv && qok && !((kw >> col) & 1u)) {
+            const int kb = lo + 64 * bt;
+            for (int s2 = 0; s2 < 64; ++s2) {
+              const int key = kb + s2;
+              if (key >= ghi) break;
+              if (p.debug_ub != nullptr) p.debug_ub[(int64_t)qrow * p.debug_ld + key] = bub;
+              if (p.debug_mask != nullptr && hopeless)
+                atomicOr(&p.debug_mask[(int64_t)qrow * p.debug_mask_ld + (key >> 6)], 1ull << (key & 63));
+            }
+          }
+        }
+      }
+    }
+  }
+  auto kept = [&](int t) -> bool { return !blocks_on || ((keep[t >> 5] >> (t & 31)) & 1u) != 0u; };
+  auto next_kept = [&](int t) -> int {   // first loaded tile at or after t (ntiles if none)
+    if constexpr (!BLOCKS) return min(t, ntiles);
+    while (t < ntiles && !kept(t)) {
+      if (blocks_on && (t & 31) == 0 && keep[t >> 5] == 0u) t += 32;
+      else ++t;
+    }
+    return min(t, ntiles);
+  };
+  if (BLOCKS && p.stats != nullptr && threadIdx.x == 0) {
+    u64 rows = 0;   // key rows this workgroup streams
+    for (int t = next_kept(0); t < ntiles; t = next_kept(t + 1)) rows += (u64)min(64, hi - (lo + 64 * t));
+    atomicAdd(&p.stats[9], rows);
+  }
   drain_memory();   // the certificate rows and coefficients, before the prefetching loop
-  // Tile t+1 is loaded while tile t is bounded and written to LDS before the
-  // tile's survivor words are stored; the last iteration reloads its own tile
-  // into the idle buffer, so no load stays pending across the back edge.
-  if (ntiles > 0) {
-    fetch(0);
+  // Tile t+1 (the next loaded tile) is loaded while tile t is bounded and
+  // written to LDS before the tile's survivor words are stored; the last
+  // iteration reloads its own tile into the idle buffer, so no load stays
+  // pending across the back edge.
+  int t = next_kept(0);
+  if (t < ntiles) {
+    fetch(t);
     commit(0);
   }
   __syncthreads();
-  const bool work = active && !(all_hopeless && !dump);
+  int bufi = 0;
 #pragma unroll 1
-  for (int t = 0; t < ntiles; ++t) {
-    const int bufi = t & 1;
-    fetch(min(t + 1, ntiles - 1));
+  while (t < ntiles) {
+    const int tn = next_kept(t + 1);
+    fetch(tn < ntiles ? tn : t);
     const int kb = lo + 64 * t;
     // one survivor word per group of the wavefront (wavefront-uniform)
     u64 words[gpw];
 #pragma unroll
     for (int j = 0; j < gpw; ++j) words[j] = 0ull;
-    if (work) {
+    // a tile this wavefront's queries all prune by the block bound keeps zero
+    // survivor words without per-key bounds (with a dump, every key is bounded)
+    const bool mine = !BLOCKS || !blocks_on || dump || ((keep_w[wave][t >> 5] >> (t & 31)) & 1u) != 0u;
+    if (work && mine) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         const int kslot = b * 16 + col;
@@ -981,6 +1260,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
       }
     }
     __syncthreads();
+    bufi ^= 1;
+    t = tn;
   }
   if (work && lane == 0 && p.stats != nullptr) {
     // pairs bounded in this share by the wavefront's groups that were not hopeless
@@ -1057,7 +1338,7 @@ __global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
     bool h = true;
     if ((int)threadIdx.x < tn) {
       const GroupInfo g = p.groups[gi0 + threadIdx.x];
-      for (int i = 0; i < g.nq; ++i) h = h && p.coef[(int64_t)(g.q_row0 + i) * 8 + 7] != 0.f;
+      for (int i = 0; i < g.nq; ++i) h = h && p.coef[(int64_t)(g.q_row0 + i) * kCoefStride + 7] != 0.f;
     }
     hopeless[threadIdx.x] = h ? 1 : 0;
   }
@@ -1141,7 +1422,7 @@ __global__ void probe_decide_kernel(const float* coef, int32_t q0, int32_t nq, i
                                     unsigned long long* stats) {
   const int lane = lane_id();
   bool prunes = false;
-  for (int i = lane; i < nq; i += 64) prunes = prunes || coef[(int64_t)(q0 + i) * 8 + 7] == 0.f;
+  for (int i = lane; i < nq; i += 64) prunes = prunes || coef[(int64_t)(q0 + i) * kCoefStride + 7] == 0.f;
   const bool any = __ballot(prunes) != 0ull;
   if (lane == 0) {
     *mode = any ? MODE_PRUNED : MODE_UNPRUNED;
@@ -1157,7 +1438,7 @@ hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_
 
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* v, hipStream_t s) {
   dosa_stats a;
-  static_assert(sizeof(dosa_stats) == 11 * sizeof(unsigned long long), "stats layout");
+  static_assert(sizeof(dosa_stats) == 12 * sizeof(unsigned long long), "stats layout");
   memcpy(&a, v, sizeof(a));
   hipLaunchKernelGGL(stats_add_kernel, dim3(1), dim3(64), 0, s, stats, a);
   return hipGetLastError();
@@ -1175,6 +1456,23 @@ static hipError_t norms_t(const NormLaunch& p, hipStream_t s) {
 template <int C>
 static hipError_t norms_c(int d, const NormLaunch& p, hipStream_t s) {
   return d == 64 ? norms_t<C, 64>(p, s) : norms_t<C, 128>(p, s);
+}
+
+template <int C, int D>
+static hipError_t blocks_t(const NormLaunch& p, hipStream_t s) {
+  const int nb = (int)((p.max_kv + kKeyBlock - 1) / kKeyBlock);
+  if (nb == 0 || p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL((key_block_kernel<C, D>), dim3(nb, p.batch < 65535 ? p.batch : 65535), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_blocks(int combo, int d, const NormLaunch& p, hipStream_t s) {
+  if (p.total_k == 0 || p.blk_code == nullptr) return hipSuccess;
+  switch (combo) {
+    case C_F32: return d == 64 ? blocks_t<C_F32, 64>(p, s) : blocks_t<C_F32, 128>(p, s);
+    case C_BF16: return d == 64 ? blocks_t<C_BF16, 64>(p, s) : blocks_t<C_BF16, 128>(p, s);
+    default: return d == 64 ? blocks_t<C_FP8, 64>(p, s) : blocks_t<C_FP8, 128>(p, s);   // fp8 keys
+  }
 }
 
 hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s) {
@@ -1218,10 +1516,13 @@ template <int C>
 static hipError_t bound_c(int d, const BoundLaunch& p, hipStream_t s) {
   if (p.items != nullptr) {
     if (p.n_items == 0) return hipSuccess;
-#define DOSA_BT(DD, G)                                                                                      \
-  if (d == DD && p.groups_per_wave == G) {                                                                  \
-    hipLaunchKernelGGL((bound_tiled_kernel<C, DD, G>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p); \
-    return hipGetLastError();                                                                               \
+#define DOSA_BT(DD, G)                                                                                            \
+  if (d == DD && p.groups_per_wave == G) {                                                                        \
+    if (p.blk_code != nullptr)                                                                                    \
+      hipLaunchKernelGGL((bound_tiled_kernel<C, DD, G, true>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p);  \
+    else                                                                                                          \
+      hipLaunchKernelGGL((bound_tiled_kernel<C, DD, G, false>), dim3(p.n_items), dim3(64 * kTileWaves), 0, s, p); \
+    return hipGetLastError();                                                                                     \
   }
     DOSA_BT(64, 1) DOSA_BT(64, 2) DOSA_BT(64, 4) DOSA_BT(128, 1) DOSA_BT(128, 2) DOSA_BT(128, 4)
 #undef DOSA_BT

@@ -96,6 +96,13 @@ typedef enum {
 #define DOSA_SORTED 0x2u          /* rows of out_idx in (score desc, position asc) order */
 #define DOSA_SEPARABLE_RHO 0x4u   /* residual bound sum_h w_h ||r_h|| instead of the joint bound */
 #define DOSA_NO_NEGATIVE 0x8u     /* drop the negative-head aggregate from the bound */
+#define DOSA_KEY_BLOCKS 0x20u     /* dosa_indexer_topk: key-block test in the bound pass (calls with query
+                                     tiles): per 64-key block a centre, radius and largest norm give one
+                                     bound for all its keys (certificates over key blocks, the DoSA
+                                     transcript's Conclusion); a block below tau for every query of a
+                                     32-query bound tile is never loaded.  Off by default: on the
+                                     correlated 128K recipe it skips 5.6% of the tiles and the test
+                                     costs more than that saves */
 #define DOSA_NO_PROBE 0x10u       /* dosa_indexer_topk: no probe tile, always the certificate pipeline
                                      (by default a call with >= 8 query tiles first seeds and plans
                                      its last tile and, if the certificate prunes no query there,
@@ -146,6 +153,9 @@ typedef struct {
                                   streamed them; skipped groups read none) */
   uint64_t calls_unpruned;     /* dosa_indexer_topk calls scored densely: the certificate could
                                   prune no query of the call's probe tile (its last query tile) */
+  uint64_t key_blocks_skipped; /* 64-key tiles the bound pass never loaded: the key-block bound
+                                  (centre, radius and largest norm of the block's keys) was below
+                                  tau for every query of the query tile that needed them */
 } dosa_stats;
 
 /* Fill *cfg with the defaults for a given topk. */

@@ -35,7 +35,7 @@ def test_default_config_values():
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(E.DosaStats) == 88
+    assert ctypes.sizeof(E.DosaStats) == 96
     assert ctypes.sizeof(E.DosaConfig) == 56
     assert E.DosaConfig.debug_mask.offset == 48
 

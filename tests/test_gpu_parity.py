@@ -133,7 +133,7 @@ def test_survivor_shares_ragged_launch_order():
 
 
 @pytest.mark.parametrize("knob", ["p0", "p1", "p2", "w64", "w512", "cap", "noprune", "separable", "noneg",
-                                  "splits3", "frac0", "frac1", "probe"])
+                                  "splits3", "frac0", "frac1", "probe", "blocks"])
 def test_knob_invariance(knob):
     import exact_top_token_amd as E
     from exact_top_token_amd.runner import run_once
@@ -166,6 +166,8 @@ def test_knob_invariance(knob):
         cfg.neg_support_frac = 0.0
     elif knob == "frac1":
         cfg.neg_support_frac = 1.0
+    elif knob == "blocks":
+        cfg.flags |= E.DOSA_KEY_BLOCKS
     print(f"[gpu] knob {knob}", flush=True)
     pi, ps, _ = run_once(wl, "dosa", cfg=cfg, key_splits=ks)
     assert_same_selection(pi, ps, di, ds)
@@ -323,6 +325,7 @@ def test_correlated_fp8_chunked_prunes():
         stats[path] = tot
     pst = stats["dosa"]
     print("correlated fp8 stats", pst, flush=True)
+    print(f"[gpu] key blocks skipped by the bound pass: {pst['key_blocks_skipped']}", flush=True)
     assert pst["pairs_bounded"] > 0 and pst["pairs_survived"] < pst["pairs_bounded"]
     assert pst["groups_skipped"] < wl.total_q // 4, "every fp8 group was skipped"
     assert_same_selection(*outs["dosa"], *outs["dsa"])
@@ -401,3 +404,21 @@ def test_degenerate_score_distributions(case):
         for r in range(wl.total_q):
             v = np.sort(di[r][di[r] >= 0])
             assert np.array_equal(v, np.arange(v.size)), r
+
+
+def test_key_block_test_skips_blocks_and_matches():
+    """The key-block test of the bound pass (DOSA_KEY_BLOCKS): on the last queries of a long
+    correlated context whole 64-key blocks fall below tau and are never loaded; the selection
+    still equals the dense path's, and the dumped bounds -- the block bound for every key of a
+    skipped block -- dominate the oracle's scores."""
+    import exact_top_token_amd as E
+
+    wl = synth.correlated_heads(L=32768, q_len=128)
+    cfg = E.default_config(wl.topk)
+    cfg.flags |= E.DOSA_NO_PROBE | E.DOSA_KEY_BLOCKS
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 8), cfg=cfg)
+    print("key-block stats", pst, flush=True)
+    assert pst["key_blocks_skipped"] > 0, "no key block was skipped"
+    idx, sc, st, ub, tau, mask = _debug_run(wl, cfg)
+    assert_same_selection(idx, sc, di, ds)
+    assert check_debug_dumps(wl, ub, tau, mask, sample_rows(wl, 6)) > 0
