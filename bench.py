@@ -152,6 +152,8 @@ def main():
     ap.add_argument("--workload", default="long_prefill_128k")
     ap.add_argument("--L", type=int, default=0, help="override the context length (exploration only)")
     ap.add_argument("--chunk", type=int, default=0, help="query chunk per call, where the recipe takes one")
+    ap.add_argument("--q-len", type=int, default=0, help="new queries of a chunk recipe (million_chunk)")
+    ap.add_argument("--H", type=int, default=0, help="indexer heads (default: the recipe's)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--paths", default="dosa,dsa")
@@ -177,6 +179,10 @@ def main():
     kw = {"L": a.L} if a.L else {}
     if a.chunk:
         kw["chunk"] = a.chunk
+    if a.q_len:
+        kw["q_len"] = a.q_len
+    if a.H:
+        kw["H"] = a.H
     t0 = time.perf_counter()
     wl = synth.make_workload(a.workload, **kw)
     log(f"generated {wl.name}: q {wl.q.shape} {wl.q_dtype}, k {wl.k.shape} {wl.k_dtype}, "

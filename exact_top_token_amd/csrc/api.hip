@@ -95,6 +95,7 @@ struct Plan {
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
   int n_tiles = 0;                   // query tiles (seed items 0 .. n_tiles*Js-1 are Js per tile, tile order)
+  int pcap = 0;                      // probe: entries per region of its own candidate buffer
   int mask_words = 0;
   int64_t list_total = 0;
   int64_t n_blocks = 0;              // 64-key blocks of all sequences (key-block summaries)
@@ -102,7 +103,7 @@ struct Plan {
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
          o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, o_blk_code = 0, o_blk_info = 0,
-         total = 0;
+         o_liststart = 0, o_pcand = 0, o_pcounts = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -370,9 +371,13 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         g.n_bounded = wlo - f;
         g.list_off = loff;
         g.list_cap = (g.n_bounded + 15) / 16 * 16;
-        loff += g.list_cap;
+        if (!P.tiled) loff += g.list_cap;   // a list of its own per group
         max_bounded = std::max(max_bounded, g.n_bounded);
       }
+      // calls with query tiles: one list area per tile, for its union list or
+      // its groups' lists one after the other (compaction takes that route only
+      // when they total fewer entries than the union)
+      if (P.tiled) loff += (wlo - f + 15) / 16 * 16 + 16 * t.n;
     }
     // survivor lists: J shares per group (one wavefront each with the list
     // kernel; with the split kernel, 8 wavefronts each, so fewer shares)
@@ -502,7 +507,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         P.probe_items.push_back(it);
       }
       P.Jd = dense_tiled_items(P.dense_items);
-      P.R = std::max(P.R, std::max(P.Jd, P.Jp));
+      P.R = std::max(P.R, P.Jd);   // the probe's regions live in a buffer of their own
     }
     P.items.insert(P.items.end(), P.surv_tiled_items.begin(), P.surv_tiled_items.end());
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
@@ -519,9 +524,23 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   // threshold receives about K (1 + ln(n / K)) entries (the expected number of
   // records among n draws); automatic sizing takes 1.3x that plus slack, so a
   // region rarely has to be compacted mid-sweep, and never more than n + 64.
+  const size_t n_main_items = P.items.size() - P.probe_items.size();   // probe items come last
+  auto est_cap = [&](int64_t max_n) {
+    const double k = (double)topk;
+    const double est = 1.3 * k * (1.0 + std::log(std::max((double)max_n, k) / k)) + 256.0;
+    int64_t cap = std::min<int64_t>((int64_t)est, max_n + 64);
+    cap = std::max<int64_t>(cap, topk + 64);
+    return (int)((cap + 63) / 64 * 64);
+  };
+  if (P.probe) {
+    int64_t pn = 0;
+    for (const auto& it : P.probe_items) pn = std::max<int64_t>(pn, (int64_t)(it.a1 - it.a0) + (it.b1 - it.b0));
+    P.pcap = cfg.buffer_cap == 0 ? est_cap(pn) : (cfg.buffer_cap + 63) / 64 * 64;
+  }
   if (cfg.buffer_cap == 0) {
     int64_t max_n = 0;
-    for (const auto& it : P.items) {
+    for (size_t ii = 0; ii < n_main_items; ++ii) {
+      const WorkItem& it = P.items[ii];
       int64_t n = (int64_t)(it.a1 - it.a0) + (it.b1 - it.b0);
       if (it.gather) {
         const int64_t nb = P.groups[it.group].n_bounded;
@@ -531,11 +550,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       if (P.RW > 1) n = ((n + 63) / 64 + P.RW - 1) / P.RW * 64;
       max_n = std::max(max_n, n);
     }
-    const double k = (double)topk;
-    const double est = 1.3 * k * (1.0 + std::log(std::max((double)max_n, k) / k)) + 256.0;
-    int64_t cap = std::min<int64_t>((int64_t)est, max_n + 64);
-    cap = std::max<int64_t>(cap, topk + 64);
-    P.cap = (int)((cap + 63) / 64 * 64);
+    P.cap = est_cap(max_n);
   } else {
     P.cap = (cfg.buffer_cap + 63) / 64 * 64;
   }
@@ -561,6 +576,11 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
+    P.o_liststart = take((size_t)std::max(G, 1) * sizeof(int32_t));
+    if (P.probe) {
+      P.o_pcand = take((size_t)P.probe_nq * P.Jp * P.pcap * sizeof(u64));
+      P.o_pcounts = take((size_t)P.probe_nq * P.Jp * sizeof(uint32_t));
+    }
     P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
     P.o_mode = take(sizeof(int32_t));
     P.o_order = take(sizeof(int32_t) * std::max<size_t>(P.surv_tiled_items.size(), 1));
@@ -892,8 +912,12 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* mode = P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr;
     // 1b. probe: seed pass, threshold and plan of the last tile only, then the
     //     decision whether the call runs the certificate pipeline or dense scoring
+    int32_t* list_start = reinterpret_cast<int32_t*>(ws + P.o_liststart);
     if (P.probe) {
       PassScope ps(P_PROBE, stream);
+      // the probe tile's seed candidates: a buffer of its own (its queries only)
+      const CandBuf pcb{reinterpret_cast<u64*>(ws + P.o_pcand), reinterpret_cast<uint32_t*>(ws + P.o_pcounts), P.Jp,
+                        P.pcap, (int64_t)P.probe_nq, (int64_t)P.probe_q0};
       ScoreLaunch pb{};
       pb.theta_share = tshare;
       pb.in = in;
@@ -902,7 +926,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       pb.groups = dg;
       pb.items = di + off_probe;
       pb.n_items = P.Jp;
-      pb.cb = cb;
+      pb.cb = pcb;
       pb.topk = topk;
       pb.scored_slot = 1;
       pb.tiled = 1;
@@ -910,7 +934,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_score(P.combo, H, d, pb, stream);
       if (e != hipSuccess) return fail_hip(e, "probe seed kernel launch");
       SelectLaunch pt{};
-      pt.cb = cb;
+      pt.cb = pcb;
       pt.q_first = P.probe_q0;
       pt.total_q = P.probe_nq;
       pt.topk = topk;
@@ -1052,6 +1076,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     cl.mask_words = std::max(P.mask_words, 1);
     cl.lists = lists;
     cl.list_len = list_len;
+    cl.list_start = list_start;
     cl.group_flags = gflags;
     cl.cb = cb;
     cl.r0 = P.Js * P.RW;
@@ -1078,6 +1103,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ml.theta_init = tau;
     ml.lists = lists;
     ml.list_len = list_len;
+    ml.list_start = list_start;
     ml.topk = topk;
     ml.stats = st;
     ml.scored_slot = 4;

@@ -90,11 +90,12 @@ struct CandBuf {
   uint32_t* counts;
   int32_t R;
   int32_t cap;
-  int64_t rows;              // query rows of the call
+  int64_t rows;              // query rows the buffer holds
+  int64_t q_base;            // global row of its first query (0: the whole call)
   __host__ __device__ unsigned long long* row(int64_t q, int r) const {
-    return cand + ((int64_t)r * rows + q) * cap;
+    return cand + ((int64_t)r * rows + (q - q_base)) * cap;
   }
-  __host__ __device__ uint32_t* count(int64_t q, int r) const { return counts + (int64_t)r * rows + q; }
+  __host__ __device__ uint32_t* count(int64_t q, int r) const { return counts + (int64_t)r * rows + (q - q_base); }
 };
 
 // Weighted query sums (see prep.hip): rows [total_q, 16/QW, d] in the query
@@ -127,6 +128,7 @@ struct ScoreLaunch {
                              // launch of the call publishes to and adopts from (0 = none yet), or NULL
   const int32_t* lists;      // survivor lists (gather mode)
   const int32_t* list_len;   // survivor list length per group (gather mode)
+  const int32_t* list_start; // per group: start of its list after GroupInfo::list_off (or NULL: 0)
   int32_t topk;
   int32_t scored_slot;       // dosa_stats field (u64 index) that counts scored pairs
   int32_t scored_slot2;      // a second field that counts them too (0 = none)
@@ -223,6 +225,9 @@ struct CompactLaunch {
   int32_t mask_words;
   int32_t* lists;
   int32_t* list_len;
+  int32_t* list_start;       // out: per group, start of its list after list_off (the groups of a tile
+                             // with query tiles share one list area: a union list, or their own
+                             // lists packed one after the other)
   int32_t* group_flags;      // out: 1 if the group's tile is scored whole: over its union list
                              // (allow_union) or over its bounded range
   CandBuf cb;                // candidate counts of regions [r0, r1) of the tile's queries are

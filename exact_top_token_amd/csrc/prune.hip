@@ -1390,15 +1390,22 @@ __global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
   bool whole;
   if (p.allow_union) whole = (uint64_t)tn * tu <= (uint64_t)kTileGain * ts;
   else whole = (float)ts >= kDenseFrac * (float)((uint64_t)nb * (uint64_t)tn);
+  // With query tiles the tile's groups share one list area of n_bounded + 16 per
+  // group entries: the union list, or the groups' own lists one after the
+  // other (that route is taken only when they total less than the union).
+  uint32_t start = 0;
+  if (!whole && p.allow_union)
+    for (int i = 0; i < wave && i < tn; ++i) start += (surv[i] + 15u) & ~15u;
   if (wave < tn && lane == 0) {
     p.group_flags[gi0 + wave] = whole ? 1 : 0;
     p.list_len[gi0 + wave] = (whole && p.allow_union && wave == 0) ? (int32_t)tu : (whole ? 0 : (int32_t)c);
+    p.list_start[gi0 + wave] = (int32_t)start;
   }
   if (whole) {
     if (p.allow_union) expand_words(uword, s0, s1, head.bound_lo, p.lists + head.list_off, ubase);
   } else if (wave < tn) {
     const GroupInfo gr = p.groups[gi0 + wave];
-    expand_words([&](int wd) { return word(wave, wd); }, 0, nw, gr.bound_lo, p.lists + gr.list_off, 0u);
+    expand_words([&](int wd) { return word(wave, wd); }, 0, nw, gr.bound_lo, p.lists + gr.list_off + start, 0u);
   }
 }
 

@@ -54,15 +54,23 @@ def test_one_hip_runtime_when_the_library_loads_first():
     assert r.stdout.strip().splitlines()[-1] == "1"
 
 
-@pytest.mark.parametrize("q_len,kv_len", [(16384, 1048576), (8192, 1100000)])
+@pytest.mark.parametrize("q_len,kv_len", [(65536, 1200000), (32768, 2200000)])
 def test_workspace_beyond_int32_list_offsets(q_len, kv_len):
-    """Shapes whose survivor lists hold more than 2^31 entries (one per bounded key and query
-    group) are planned with 64-bit list offsets: the workspace covers all of them."""
+    """Shapes whose survivor lists hold more than 2^31 entries (one list area of a tile's bounded
+    keys per 32-query tile) are planned with 64-bit list offsets: the workspace covers them."""
     n = E.workspace_size([q_len], [kv_len], 64, 128, 2048, "fp8", "fp8", False, False)
-    groups = q_len // 4
-    bounded = kv_len - q_len - 4 * 2048           # keys before the seed window of a group, at least
-    assert groups * bounded > 2 ** 31
-    assert n >= 4 * groups * bounded
+    tiles = q_len // 32
+    bounded = kv_len - q_len - 4 * 2048           # keys before the seed window of a tile, at least
+    assert tiles * bounded > 2 ** 31
+    assert n >= 4 * tiles * bounded
+
+
+def test_workspace_of_long_chunks_fits_hbm():
+    """The 1M-key context with 32K-query chunks: the pruned path's workspace stays a small part of
+    the 288 GB of one MI355X (one list area per query tile; the probe tile's seed regions in a
+    buffer of their own)."""
+    n = E.workspace_size([32768], [1048576], 64, 128, 2048, "fp8", "fp8", False, False)
+    assert 0 < n < 20 * 2 ** 30
 
 
 @pytest.mark.parametrize("H", [8, 24, 40, 48, 56, 64])

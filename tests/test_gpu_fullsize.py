@@ -121,3 +121,14 @@ def test_full_decode_mtp_paged():
 @pytest.mark.parametrize("iid", [False, True])
 def test_full_million_chunk(iid):
     _check(synth.make_workload("million_chunk_iid") if iid else synth.million_chunk(), 128)
+
+
+@pytest.mark.parametrize("q_len", [16384, 32768])
+def test_full_million_chunk_long_chunks(q_len):
+    """The 1M-key context with 16K- and 32K-query chunks (the pages' larger prefill chunk sizes)."""
+    _check(synth.million_chunk(q_len=q_len), 128)
+
+
+def test_full_long_prefill_128k_h32():
+    """The 128K fp8 chunked prefill with 32 indexer heads (the GLM-5.2 indexer's head count)."""
+    _check(synth.long_prefill_128k(H=32), 512)
