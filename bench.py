@@ -122,12 +122,22 @@ def cpu_baseline(wl, budget_s: float = 20.0):
 
     from oracle import indexer
 
+    blas = []
     try:
         from threadpoolctl import threadpool_info
 
-        cores = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [os.cpu_count() or 1])
+        pools = threadpool_info()
+        cores = max([int(i.get("num_threads", 1)) for i in pools] or [os.cpu_count() or 1])
+        blas = [f"{i.get('internal_api')} {i.get('version')} ({i.get('user_api')}, {i.get('num_threads')} threads)"
+                for i in pools]
     except Exception:  # noqa: BLE001
         cores = os.cpu_count() or 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:
+        pass
     _, pos = indexer.query_positions(wl)
     order = np.argsort(-pos, kind="stable")        # the longest queries: the last chunk
     done, pairs, t0 = 0, 0, time.perf_counter()
@@ -140,6 +150,7 @@ def cpu_baseline(wl, budget_s: float = 20.0):
         done += 1
     dt = time.perf_counter() - t0
     return {"value": pairs / dt, "unit": "scores/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model, "cpus_visible": os.cpu_count(), "blas": blas,
             "sample": f"{done} queries of the last chunk (positions {int(pos[rows[-1]])}..{int(pos[rows[0]])}), "
                       f"{pairs} causal pairs, float64 dense scores + full sort, {dt:.1f} s"}
 
