@@ -73,7 +73,7 @@ def kernel_name(pass_name, wl):
         return f"score_tiled_kernel<{c}, {H}, {wl.d}, {ROLE_ID[pass_name]}, {paged}>"
     return {"plan": "plan_kernel", "bound": "bound_kernel", "compact": "compact_kernel",
             "key_norms": "key_norm_kernel", "select_seed": "select_kernel", "select_final": "select_kernel",
-            "prep": "qbar_kernel"}.get(pass_name, pass_name)
+            "prep": "qbar_kernel", "seed_extra": "seed_union_kernel"}.get(pass_name, pass_name)
 
 
 def bound_bytes(wl, keys_streamed):
@@ -171,6 +171,12 @@ def main():
     ap.add_argument("--buffer-cap", type=int, default=0, help="candidate buffer entries per query (0 = default)")
     ap.add_argument("--key-splits", type=int, default=0)
     ap.add_argument("--flags", type=lambda x: int(x, 0), default=0, help="DOSA_* flags OR-ed into the config")
+    ap.add_argument("--batch", type=int, default=0, help="sequences of a decode recipe (default: the recipe's)")
+    ap.add_argument("--kv-min", type=int, default=0, help="shortest cache of a decode recipe")
+    ap.add_argument("--kv-max", type=int, default=0, help="longest cache of a decode recipe")
+    ap.add_argument("--seeds", choices=["none", "prev"], default="none",
+                    help="decode recipes: 'prev' passes each query the previous decode step's Top-K (the dense "
+                         "path's, for the queries q_per_seq positions earlier) as extra seed keys")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="run one plain copy of this size first (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -194,8 +200,19 @@ def main():
         kw["q_len"] = a.q_len
     if a.H:
         kw["H"] = a.H
+    for k_, v_ in (("batch", a.batch), ("kv_min", a.kv_min), ("kv_max", a.kv_max)):
+        if v_:
+            kw[k_] = v_
     t0 = time.perf_counter()
-    wl = synth.make_workload(a.workload, **kw)
+    prev = None
+    if a.seeds == "prev":
+        # two consecutive decode steps: the batch's sequences with twice the queries, split
+        if a.workload not in ("decode_mtp", "correlated_decode"):
+            sys.exit("--seeds prev needs a decode recipe (decode_mtp or correlated_decode)")
+        kw["q_per_seq"] = 4
+        prev, wl = synth.split_decode_steps(synth.make_workload(a.workload, **kw), 2)
+    else:
+        wl = synth.make_workload(a.workload, **kw)
     log(f"generated {wl.name}: q {wl.q.shape} {wl.q_dtype}, k {wl.k.shape} {wl.k_dtype}, "
         f"{wl.pairs()} pairs in {time.perf_counter() - t0:.1f}s")
     dev = torch.device("cuda:0")
@@ -213,6 +230,15 @@ def main():
     pairs = wl.pairs()
     results = {}
     outs = {}
+    seed_t = None
+    if prev is not None:
+        from exact_top_token_amd.runner import Runner
+
+        rp = Runner(to_device(prev, dev), "dsa", want_scores=False, device=dev)
+        seed_t = rp()[0].clone()
+        torch.cuda.synchronize()
+        del rp
+        log(f"previous decode step's Top-K as extra seeds: {tuple(seed_t.shape)}")
     for path in a.paths.split(","):
         cfg = E.default_config(K)
         if a.buffer_cap:
@@ -220,6 +246,8 @@ def main():
         if a.key_splits:
             cfg.key_splits = a.key_splits
         cfg.flags |= a.flags
+        if seed_t is not None and path == "dosa":
+            cfg.seed_idx, cfg.seed_count = seed_t.data_ptr(), int(seed_t.shape[1])
         ws_bytes = max(E.workspace_size(c.q_lens, c.kv_lens, c.H, c.d, K, c.q_dtype, c.k_dtype,
                                         c.page_table is not None, path == "dsa", cfg) for _, c in calls)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -356,7 +384,7 @@ def main():
         "config": {"workload": wl.name, "seq_len": int(max(wl.kv_lens)), "queries": wl.total_q,
                    "chunk": wl.chunk, "heads": wl.H, "head_dim": wl.d, "topk": K,
                    "pairs_per_step": pairs, "path": f"{main_path}_indexer_topk",
-                   "recipe": wl.recipe},
+                   "recipe": wl.recipe, "extra_seeds": a.seeds},
         "roofline": roof,
         "cpu_baseline": None if a.no_cpu else cpu_baseline(wl, a.cpu_budget),
         **extra,

@@ -52,6 +52,9 @@ class DosaConfig(ctypes.Structure):
         ("debug_ub", ctypes.c_void_p),
         ("debug_tau", ctypes.c_void_p),
         ("debug_mask", ctypes.c_void_p),
+        ("seed_idx", ctypes.c_void_p),
+        ("seed_count", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -23,10 +23,10 @@ thread_local std::string g_err;
 // optional per-pass event timing
 // ---------------------------------------------------------------------------
 enum PassId { P_NORMS = 0, P_SCORE_SEED, P_SELECT_SEED, P_PLAN, P_BOUND, P_COMPACT, P_SURV_TILES, P_SURV_LISTS,
-              P_SCORE_DENSE, P_SELECT_FINAL, P_PREP, P_PROBE, P_COUNT };
+              P_SCORE_DENSE, P_SELECT_FINAL, P_PREP, P_PROBE, P_SEED_EXTRA, P_COUNT };
 const char* const kPassNames[P_COUNT] = {"key_norms", "score_seed", "select_seed", "plan", "bound", "compact",
                                          "score_survivor_tiles", "score_survivor_lists", "score_dense",
-                                         "select_final", "prep", "probe"};
+                                         "select_final", "prep", "probe", "seed_extra"};
 
 struct Profiler {
   bool on = false;
@@ -85,7 +85,8 @@ struct Plan {
   int64_t total_q = 0, total_k = 0;
   std::vector<GroupInfo> groups;
   std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed, tiled-survivor, list-survivor items
-  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items, probe_items;
+  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items, probe_items,
+      x_items;                       // DoSA with extra seed keys: their scoring items (regions Js..Js+X-1)
   bool probe = false;                // DoSA: plan the last tile first, score densely if it cannot prune
   int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0, Jp = 0;
   int bound_gpw = 1;                 // query groups per wavefront of the tiled bound kernel
@@ -94,6 +95,8 @@ struct Plan {
                                      // kernel (decode-like batches: one region per wavefront)
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
+  int X = 0;                         // DoSA: regions of the extra seed keys (after the seed regions)
+  int64_t x_stride = 0;              // entries per group of the extra seed lists
   int n_tiles = 0;                   // query tiles (seed items 0 .. n_tiles*Js-1 are Js per tile, tile order)
   int pcap = 0;                      // probe: entries per region of its own candidate buffer
   int mask_words = 0;
@@ -103,7 +106,7 @@ struct Plan {
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
          o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, o_blk_code = 0, o_blk_info = 0,
-         o_liststart = 0, o_pcand = 0, o_pcounts = 0, total = 0;
+         o_liststart = 0, o_pcand = 0, o_pcounts = 0, o_xlists = 0, o_xlen = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -158,6 +161,11 @@ int resolve_cfg(const dosa_config* in, int32_t topk, dosa_config* out) {
       g_err = "buffer_cap must be >= topk + 64";
       return DOSA_ERR_INVALID_ARG;
     }
+    if (out->seed_count < 0 || out->seed_count > kMaxSeedCount || (out->seed_count > 0 && out->seed_idx == nullptr)) {
+      g_err = "seed_count must be in 0.." + std::to_string(kMaxSeedCount) + ", with seed_idx when positive";
+      return DOSA_ERR_INVALID_ARG;
+    }
+    if (out->seed_idx == nullptr) out->seed_count = 0;
   }
   return DOSA_OK;
 }
@@ -344,6 +352,13 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     const int Js = P.tiled ? choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), tiled_target, 1024)
                            : choose_splits(NT, std::min<int64_t>(avg_keys, P.W + P.F), kSplitItems / 2, 2048);
     P.Js = Js;
+    // extra seed keys: one share per 2048 listed keys of a group (list kernel,
+    // one wavefront each), or one 8-wavefront item per group (split kernel)
+    const int X = cfg.seed_count <= 0 ? 0
+                  : (P.tiled ? (int)std::min<int64_t>(8, std::max<int64_t>(1, ((int64_t)P.QW * cfg.seed_count + 2047) / 2048))
+                             : 1);
+    P.X = X;
+    P.x_stride = ((int64_t)P.QW * cfg.seed_count + 15) / 16 * 16;
     std::vector<WorkItem> seed_extra;   // split kernel: the seed window of a tile's other groups
     for (const auto& t : tiles) {
       const int wlo = std::max(0, t.n_last - P.W);
@@ -404,11 +419,11 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       for (int gi = 0; gi < G; ++gi) {
         const GroupInfo& g = P.groups[gi];
         if (g.n_bounded <= 0) continue;
-        P.J = std::max(P.J, split_range(gi, g.bound_lo, g.bound_lo + g.n_bounded, Js, chunk, P.surv_tiled_items));
+        P.J = std::max(P.J, split_range(gi, g.bound_lo, g.bound_lo + g.n_bounded, Js + X, chunk, P.surv_tiled_items));
       }
       longest_first(P.surv_tiled_items, 0);
     }
-    P.R = (Js + P.J) * P.RW;
+    P.R = (Js + X + P.J) * P.RW;
     // calls with tiles: share r of Ju of the tile's union survivor list
     for (const auto& t : tiles) {
       if (!P.tiled) break;
@@ -416,7 +431,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         WorkItem it{};
         it.group = t.first;
         it.pad = t.n;
-        it.region = Js + r;
+        it.region = Js + X + r;
         it.gather = 1;
         it.a0 = r;
         it.a1 = Ju;
@@ -428,12 +443,25 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       for (int r = 0; r < J; ++r) {
         WorkItem it{};
         it.group = gi;
-        it.region = Js + r;
+        it.region = Js + X + r;
         it.gather = 1;
         it.a0 = r;
         it.a1 = J;
         P.surv_list_items.push_back(it);
       }
+    // extra seed keys: share r of X of each group's list
+    for (int gi = 0; X > 0 && gi < G; ++gi) {
+      if (P.groups[gi].n_bounded <= 0) continue;
+      for (int r = 0; r < X; ++r) {
+        WorkItem it{};
+        it.group = gi;
+        it.region = Js + r;
+        it.gather = 1;
+        it.a0 = r;
+        it.a1 = X;
+        P.x_items.push_back(it);
+      }
+    }
     P.items = P.seed_items;
     // bound pass over LDS key tiles when tiles hold enough groups: one item per
     // (tile, 64-key-aligned share of its bounded range)
@@ -513,6 +541,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
     P.items.insert(P.items.end(), P.bound_items.begin(), P.bound_items.end());
     P.items.insert(P.items.end(), P.dense_items.begin(), P.dense_items.end());
+    P.items.insert(P.items.end(), P.x_items.begin(), P.x_items.end());
     P.items.insert(P.items.end(), P.probe_items.begin(), P.probe_items.end());
     P.list_total = loff;
     P.mask_words = (max_bounded + 63) / 64;
@@ -525,6 +554,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   // records among n draws); automatic sizing takes 1.3x that plus slack, so a
   // region rarely has to be compacted mid-sweep, and never more than n + 64.
   const size_t n_main_items = P.items.size() - P.probe_items.size();   // probe items come last
+  const size_t x_end = n_main_items, x_begin = x_end - P.x_items.size();   // extra seed items before them
   auto est_cap = [&](int64_t max_n) {
     const double k = (double)topk;
     const double est = 1.3 * k * (1.0 + std::log(std::max((double)max_n, k) / k)) + 256.0;
@@ -545,6 +575,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       if (it.gather) {
         const int64_t nb = P.groups[it.group].n_bounded;
         n = std::max<int64_t>((nb + it.a1 - 1) / it.a1, std::min<int64_t>(nb, 2 * kUnionMinShare)) + 64;
+        if (ii >= x_begin && ii < x_end) n = std::min<int64_t>(nb, (P.x_stride + it.a1 - 1) / it.a1) + 64;
       }
       // split kernel: each wavefront's region takes every 8th 64-key step
       if (P.RW > 1) n = ((n + 63) / 64 + P.RW - 1) / P.RW * 64;
@@ -582,6 +613,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       P.o_pcounts = take((size_t)P.probe_nq * P.Jp * sizeof(uint32_t));
     }
     P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
+    if (P.X > 0) {
+      P.o_xlists = take((size_t)std::max(G, 1) * P.x_stride * sizeof(int32_t));
+      P.o_xlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
+    }
     P.o_mode = take(sizeof(int32_t));
     P.o_order = take(sizeof(int32_t) * std::max<size_t>(P.surv_tiled_items.size(), 1));
     const int kbytes = (k_dtype == DOSA_F32) ? 4 : (k_dtype == DOSA_BF16 ? 2 : 1);
@@ -692,6 +727,7 @@ int dsa_indexer_topk(const void* q, int32_t q_dtype, const float* q_scale, const
     st = resolve_cfg(cfg, topk, &c);
     if (st != DOSA_OK) return st;
     c.flags &= DOSA_SORTED;
+    c.seed_count = 0;
     return run(true, q, q_dtype, q_scale, w, k, k_dtype, k_scale, q_lens, kv_lens, batch, page_table, page_size,
                max_pages, H, d, topk, out_idx, out_score, workspace, workspace_bytes, c, stats,
                static_cast<hipStream_t>(stream));
@@ -908,7 +944,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* prunes = reinterpret_cast<int32_t*>(ws + P.o_flag);   // cleared by the prep kernel
     const size_t off_surv = P.seed_items.size(), off_list = off_surv + P.surv_tiled_items.size(),
                  off_bound = off_list + P.surv_list_items.size(), off_dense = off_bound + P.bound_items.size(),
-                 off_probe = off_dense + P.dense_items.size();
+                 off_x = off_dense + P.dense_items.size(), off_probe = off_x + P.x_items.size();
     int32_t* mode = P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr;
     // 1b. probe: seed pass, threshold and plan of the last tile only, then the
     //     decision whether the call runs the certificate pipeline or dense scoring
@@ -983,6 +1019,38 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_score(P.combo, H, d, sl, stream);
     }
     if (e != hipSuccess) return fail_hip(e, "seed score kernel launch");
+    // 2b. extra seed keys: the union list of each group, scored into regions
+    //     Js..Js+X-1 (read by the threshold select only; compaction clears them)
+    if (P.X > 0) {
+      PassScope ps(P_SEED_EXTRA, stream);
+      int32_t* xlists = reinterpret_cast<int32_t*>(ws + P.o_xlists);
+      int32_t* xlen = reinterpret_cast<int32_t*>(ws + P.o_xlen);
+      SeedUnionLaunch su{dg, G, cfg.seed_idx, cfg.seed_count, xlists, P.x_stride, xlen, mode, MODE_PRUNED};
+      e = launch_seed_union(su, stream);
+      if (e == hipSuccess && !P.x_items.empty()) {
+        ScoreLaunch xl{};
+        xl.theta_share = tshare;
+        xl.mode = mode;
+        xl.run_if = MODE_PRUNED;
+        xl.in = in;
+        xl.lrows = pr.rows;
+        xl.lsig = pr.sig;
+        xl.groups = dg;
+        xl.items = di + off_x;
+        xl.n_items = (int)P.x_items.size();
+        xl.cb = cb;
+        xl.lists = xlists;
+        xl.list_len = xlen;
+        xl.list_stride = P.x_stride;
+        xl.topk = topk;
+        xl.stats = st;
+        xl.scored_slot = 1;
+        xl.tiled = P.tiled ? 0 : 2;
+        xl.role = ROLE_SURVIVORS;
+        e = launch_score(P.combo, H, d, xl, stream);
+      }
+    }
+    if (e != hipSuccess) return fail_hip(e, "extra seed kernel launch");
     // 3. tau = K-th largest seed score
     SelectLaunch ts{};
     ts.mode = mode;
@@ -991,7 +1059,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ts.total_q = (int32_t)P.total_q;
     ts.topk = topk;
     ts.r0 = 0;
-    ts.r1 = P.Js * P.RW;
+    ts.r1 = (P.Js + P.X) * P.RW;
     ts.tau_out = tau;
     ts.tau_copy = cfg.debug_tau;
     {
@@ -1079,8 +1147,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     cl.list_start = list_start;
     cl.group_flags = gflags;
     cl.cb = cb;
-    cl.r0 = P.Js * P.RW;
-    cl.r1 = (P.Js + P.J) * P.RW;
+    cl.r0 = P.Js * P.RW;                       // the extra seed regions too
+    cl.r1 = (P.Js + P.X + P.J) * P.RW;
     cl.mode = mode;
     cl.run_if = MODE_PRUNED;
     {
@@ -1163,7 +1231,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   se.total_q = (int32_t)P.total_q;
   se.topk = topk;
   se.r0 = 0;
-  se.r1 = dense ? P.R : (P.Js + P.J) * P.RW;   // pruned path: seed then survivor regions
+  se.r1 = dense ? P.R : (P.Js + P.X + P.J) * P.RW;   // pruned path: seed, (cleared) extra seed, survivor regions
   se.out_idx = out_idx;
   se.out_score = out_score;
   se.tau_out = nullptr;

@@ -129,6 +129,7 @@ struct ScoreLaunch {
   const int32_t* lists;      // survivor lists (gather mode)
   const int32_t* list_len;   // survivor list length per group (gather mode)
   const int32_t* list_start; // per group: start of its list after GroupInfo::list_off (or NULL: 0)
+  int64_t list_stride;       // > 0: group g's list starts at lists + g * list_stride instead
   int32_t topk;
   int32_t scored_slot;       // dosa_stats field (u64 index) that counts scored pairs
   int32_t scored_slot2;      // a second field that counts them too (0 = none)
@@ -264,6 +265,23 @@ struct NormLaunch {
   float* blk_info;           // [blocks, 4] (key-block kernel)
 };
 
+// Extra seed keys (dosa_config::seed_idx): per query group, the union of its
+// queries' rows restricted to the group's bounded keys, sorted and without
+// repeats, at lists + group * stride; its length in list_len[group].
+constexpr int kMaxSeedCount = 4096;          // entries per query row
+constexpr int kSeedUnionMax = 4 * kMaxSeedCount;   // entries of a group's rows (<= 4 queries)
+struct SeedUnionLaunch {
+  const GroupInfo* groups;
+  int32_t n_groups;
+  const int32_t* seed_idx;   // [total_q, seed_count]
+  int32_t seed_count;
+  int32_t* lists;            // out: [n_groups, stride]
+  int64_t stride;
+  int32_t* list_len;         // out: [n_groups]
+  const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
+  int32_t run_if;
+};
+
 constexpr int kKeyBlock = 64;       // keys per key block (= the bound pass's key tile)
 constexpr int kMaxBoundTiles = 4096;// key tiles of a bound item that the block test covers
 
@@ -278,6 +296,7 @@ hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t
 hipError_t launch_bound(int combo, int H, int d, const BoundLaunch& p, hipStream_t s);
 hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_order(const OrderLaunch& p, hipStream_t s);
+hipError_t launch_seed_union(const SeedUnionLaunch& p, hipStream_t s);
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* host_vals, hipStream_t s);
 hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
                                unsigned long long* stats, hipStream_t s);

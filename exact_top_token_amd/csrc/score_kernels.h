@@ -634,7 +634,8 @@ __global__ __launch_bounds__(64, KeyRaw<C>::value ? 2 : 1) void score_list_kerne
       }
     }
   } else {
-    const int32_t* lst = p.lists + gr.list_off + (p.list_start != nullptr ? p.list_start[it.group] : 0);
+    const int32_t* lst = p.list_stride > 0 ? p.lists + (int64_t)it.group * p.list_stride
+                                           : p.lists + gr.list_off + (p.list_start != nullptr ? p.list_start[it.group] : 0);
     const int len = p.list_len[it.group];
     const int e0 = (int)(((int64_t)len * it.a0 / it.a1) & ~15LL);
     const int e1 = (it.a0 == it.a1 - 1) ? len : (int)(((int64_t)len * (it.a0 + 1) / it.a1) & ~15LL);
@@ -813,7 +814,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
     }
   } else {
     // share a0 of a1 of the group's survivor list, 64 entries per step
-    const int32_t* lst = p.lists + gr.list_off + (p.list_start != nullptr ? p.list_start[it.group] : 0);
+    const int32_t* lst = p.list_stride > 0 ? p.lists + (int64_t)it.group * p.list_stride
+                                           : p.lists + gr.list_off + (p.list_start != nullptr ? p.list_start[it.group] : 0);
     const int len = p.list_len[it.group];
     const int e0 = (int)(((int64_t)len * it.a0 / it.a1) & ~15LL);
     const int e1 = (it.a0 == it.a1 - 1) ? len : (int)(((int64_t)len * (it.a0 + 1) / it.a1) & ~15LL);

@@ -60,12 +60,19 @@ class Runner:
 
     def __init__(self, inp: DeviceInputs, path: str = "dosa", cfg: Optional[DosaConfig] = None,
                  sorted_rows: bool = False, key_splits: int = 0, want_scores: bool = True,
-                 device="cuda"):
+                 device="cuda", seeds=None):
         import torch
 
         self.inp = inp
         self.path = path
         self.cfg = cfg if cfg is not None else default_config(inp.topk)
+        self.seeds = None
+        if seeds is not None:   # extra seed keys per query row: [total_q, S] int32, -1 padding
+            self.seeds = (seeds if isinstance(seeds, torch.Tensor) else _t(np.asarray(seeds, np.int32), device))
+            self.seeds = self.seeds.to(device=device, dtype=torch.int32).contiguous()
+            assert self.seeds.dim() == 2 and self.seeds.shape[0] == inp.total_q
+            self.cfg.seed_idx = self.seeds.data_ptr()
+            self.cfg.seed_count = int(self.seeds.shape[1])
         if key_splits:
             self.cfg.key_splits = key_splits
         if sorted_rows:
@@ -113,12 +120,12 @@ def slice_chunk(inp: DeviceInputs, q0: int, q_len: int, kv_len: int) -> DeviceIn
                         q_dtype=inp.q_dtype, k_dtype=inp.k_dtype)
 
 
-def run_once(wl, path="dosa", cfg=None, sorted_rows=False, key_splits=0, device="cuda"):
+def run_once(wl, path="dosa", cfg=None, sorted_rows=False, key_splits=0, device="cuda", seeds=None):
     """Convenience: inputs to device, one call, results to host numpy."""
     import torch
 
     inp = to_device(wl, device)
-    r = Runner(inp, path, cfg, sorted_rows, key_splits, device=device)
+    r = Runner(inp, path, cfg, sorted_rows, key_splits, device=device, seeds=seeds)
     idx, sc = r()
     torch.cuda.synchronize()
     return idx.cpu().numpy(), sc.cpu().numpy(), r.stats_dict()

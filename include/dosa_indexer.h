@@ -135,6 +135,20 @@ typedef struct {
                                whose certificate reached tau for that query (every bounded key
                                of a query whose plan found nothing to prune); seed keys are not
                                marked; for testing only */
+  const int32_t* seed_idx;  /* optional DEVICE [total_q, seed_count] int32: extra seed keys per query,
+                               scored exactly and used for tau only -- e.g. the previous decode
+                               step's Top-K (the DoSA transcript, Experiments: decode reuses the
+                               scores of recently selected keys) or a candidate set shared by a
+                               group of nearby queries (the PIVOT record: one scan per query
+                               group).  Logical key positions; entries outside the keys that get
+                               a certificate (negative, past the query, or inside the seed prefix
+                               or window) and repeats are ignored, -1 may pad a row.  Queries
+                               scored together (up to 4 consecutive queries of a sequence) share
+                               the union of their rows, which keeps every seed visible to each of
+                               them.  Any content leaves the selected set unchanged; keys that
+                               score high raise tau and so the pruning */
+  int32_t seed_count;       /* entries per row of seed_idx, 0..4096 (0 = none, the default) */
+  int32_t reserved;         /* set to 0 */
 } dosa_config;
 
 /* Device-resident counters, accumulated (not reset) by each call that gets a

@@ -16,6 +16,7 @@ from .workloads import (  # noqa: F401
     million_chunk,
     correlated_heads,
     correlated_decode,
+    split_decode_steps,
     custom,
     quantize_fp8_per_token,
     to_bf16_bits,

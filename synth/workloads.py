@@ -470,6 +470,30 @@ def correlated_decode(seed: int = 0, batch: int = 8, q_per_seq: int = 2, kv_min:
                            "the last positions")
 
 
+def split_decode_steps(wl: Workload, q_per_step: int):
+    """Two consecutive decode steps of a paged decode batch.
+
+    ``wl`` holds 2 * q_per_step queries at the last positions of each
+    sequence.  Returns (prev, cur): prev has each sequence's first q_per_step
+    queries and a KV cache q_per_step keys shorter (the step before), cur the
+    last q_per_step queries over the whole cache.  Pure slicing: the same keys,
+    page table and query rows.
+    """
+    m = 2 * q_per_step
+    assert wl.page_table is not None and np.all(wl.q_lens == m)
+    rows = np.arange(wl.total_q).reshape(wl.batch, m)
+    first, last = rows[:, :q_per_step].ravel(), rows[:, q_per_step:].ravel()
+
+    def take(r, kv, tag):
+        return Workload(name=f"{wl.name}_{tag}", H=wl.H, d=wl.d, topk=wl.topk, q_dtype=wl.q_dtype,
+                        k_dtype=wl.k_dtype, q=wl.q[r], q_scale=None if wl.q_scale is None else wl.q_scale[r],
+                        w=wl.w[r], k=wl.k, k_scale=wl.k_scale, q_lens=np.full(wl.batch, q_per_step, np.int32),
+                        kv_lens=kv.astype(np.int32), page_table=wl.page_table, page_size=wl.page_size,
+                        recipe=wl.recipe + f" ({tag} decode step)")
+
+    return take(first, wl.kv_lens - q_per_step, "prev"), take(last, wl.kv_lens, "cur")
+
+
 def custom(seed: int, lens, H: int, d: int, topk: int, q_dtype: str = "f32", k_dtype: str = "f32",
            structured: bool = False, page_size: int = 0, name: str = "custom"):
     """Small batched inputs for edge-case tests.

@@ -36,8 +36,35 @@ def test_default_config_values():
 
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(E.DosaStats) == 96
-    assert ctypes.sizeof(E.DosaConfig) == 56
+    assert ctypes.sizeof(E.DosaConfig) == 72
     assert E.DosaConfig.debug_mask.offset == 48
+    assert E.DosaConfig.seed_idx.offset == 56 and E.DosaConfig.seed_count.offset == 64
+
+
+def test_seed_config_checks():
+    """Extra seed keys: seed_count in 0..4096 with a pointer when positive; a call with seeds
+    needs a little more workspace (the groups' union lists and their regions); the dense path
+    ignores them."""
+    c = E.default_config(2048)
+    args = ([2] * 64, [200000] * 64, 64, 128, 2048, "bf16", "fp8", True)
+    base = E.workspace_size(*args, False, c)
+    c.seed_idx, c.seed_count = 0x1000, 2048
+    with_seeds = E.workspace_size(*args, False, c)
+    assert with_seeds > base
+    assert E.workspace_size(*args, True, c) == E.workspace_size(*args, True, E.default_config(2048))
+    c.seed_count = 4097
+    assert E.workspace_size(*args, False, c) == 0
+    c.seed_count, c.seed_idx = 16, None
+    assert E.workspace_size(*args, False, c) == 0
+    c.seed_count = -1
+    assert E.workspace_size(*args, False, c) == 0
+    for cnt, ptr in ((4097, 0x1000), (8, None), (-2, 0x1000)):
+        c = E.default_config(16)
+        c.seed_idx, c.seed_count = ptr, cnt
+        with pytest.raises(E.DosaError) as ei:
+            E.dosa_indexer_topk(_Fake(), "fp8", _Fake(), _Fake(), _Fake(), "fp8", _Fake(), [4], [64], None, 0, 64,
+                                128, 16, _Fake(), None, _Fake(), cfg=c, stream=0)
+        assert ei.value.status == -1
 
 
 def test_one_hip_runtime_when_the_library_loads_first():
