@@ -518,11 +518,13 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       P.probe_q0 = P.groups[t.first].q_row0;
       P.probe_nq = 0;
       for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
-      // the probe tile's seed window in shares of at least 256 keys (up to 16
-      // workgroups): on its own the tile would be scored by one workgroup
+      // the probe tile's seed window in shares of at least 256 keys (up to 32
+      // workgroups): the probe's time is its latency, with most of the GPU
+      // idle; more shares score faster but give the threshold select more
+      // regions to read
       const int wlo = std::max(0, t.n_last - P.W);
       const int f = std::min(P.F, wlo);
-      P.Jp = (int)std::max<int64_t>(1, std::min<int64_t>(16, (t.n_last - wlo) / 256));
+      P.Jp = (int)std::max<int64_t>(1, std::min<int64_t>(32, (t.n_last - wlo) / 256));
       for (int r = 0; r < P.Jp; ++r) {
         int lo, hi;
         range_split(wlo, t.n_last, r, P.Jp, 64, lo, hi);
@@ -603,7 +605,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
     P.o_coef = take((size_t)P.total_q * kCoefStride * sizeof(float));
     P.o_norms = take((size_t)std::max<int64_t>(P.total_k, 1) * sizeof(float));
-    P.o_flag = take(sizeof(int32_t));
+    P.o_flag = take(2 * sizeof(int32_t));   // prunes flag, probe ticket
     P.o_masks = take((size_t)std::max(G, 1) * std::max(P.mask_words, 1) * sizeof(u64));
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
@@ -992,10 +994,13 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       pp.prunes = prunes;
       pp.rows = ws + P.o_rows;
       pp.coef = coef;
+      pp.ticket = prunes + 1;
+      pp.decide_q0 = P.probe_q0;
+      pp.decide_nq = P.probe_nq;
+      pp.decide_mode = mode;
+      pp.stats = st;
       e = launch_plan(P.combo, H, d, pp, stream);
       if (e != hipSuccess) return fail_hip(e, "probe plan kernel launch");
-      e = launch_probe_decide(coef, P.probe_q0, P.probe_nq, mode, st, stream);
-      if (e != hipSuccess) return fail_hip(e, "probe decision kernel launch");
     }
     // 2. seed pass: exact scores of the seed keys into regions 0..Js-1
     ScoreLaunch sl{};

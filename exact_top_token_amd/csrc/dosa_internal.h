@@ -109,7 +109,8 @@ struct PrepLaunch {
   void* rows;
   float* sig;
   float* err;
-  int32_t* flag;        // cleared here (query 0): the plan's "some query can prune" flag, or NULL
+  int32_t* flag;        // [2] cleared here (query 0): the plan's "some query can prune" flag and the
+                        // probe plan's ticket counter, or NULL
   uint32_t* tshare;     // [total_q] cleared here: the shared running thresholds (ScoreLaunch)
   uint32_t* counts;     // candidate counts [n_regions, total_q], cleared here: a region no item
   int32_t n_regions;    // of the call fills reads as empty in the final merge
@@ -188,6 +189,13 @@ struct PlanLaunch {
   int32_t* prunes;           // set to 1 when some query's certificate can prune (or NULL)
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;
+  // probe decision (or NULL): the last of the decide_nq planned queries (a
+  // ticket counter, zeroed by the prep kernel) sets *decide_mode from their
+  // plans, queries decide_q0 .. decide_q0 + decide_nq - 1
+  int32_t* ticket;
+  int32_t decide_q0, decide_nq;
+  int32_t* decide_mode;
+  unsigned long long* stats;
 };
 
 struct BoundLaunch {
@@ -298,8 +306,6 @@ hipError_t launch_compact(const CompactLaunch& p, hipStream_t s);
 hipError_t launch_order(const OrderLaunch& p, hipStream_t s);
 hipError_t launch_seed_union(const SeedUnionLaunch& p, hipStream_t s);
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* host_vals, hipStream_t s);
-hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
-                               unsigned long long* stats, hipStream_t s);
 
 bool combo_supported(int combo, int H, int d);
 int tile_waves();

@@ -136,7 +136,10 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   if (p.counts != nullptr)
     for (int r = lane; r < p.n_regions; r += 64) p.counts[(int64_t)r * p.total_q + q] = 0u;
   if (lane == 0) {
-    if (q == 0 && p.flag != nullptr) *p.flag = 0;
+    if (q == 0 && p.flag != nullptr) {
+      p.flag[0] = 0;
+      p.flag[1] = 0;
+    }
     if (p.tshare != nullptr) p.tshare[q] = 0u;
     p.err[(int64_t)q * 2] = (float)(sqrt(e2) * 1.0000005);   // ||qbar - sum sigma f|| (rounded up)
     p.err[(int64_t)q * 2 + 1] = (float)(mag * 1.0000005);    // sum_j sigma_j ||f_j||

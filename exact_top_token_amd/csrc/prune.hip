@@ -808,6 +808,21 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     cf[7] = hopeless ? 1.f : 0.f;
     for (int r = 0; r < 4; ++r) cf[8 + r] = rnorm[r];
     if (!hopeless && p.prunes != nullptr) atomicOr(p.prunes, 1);   // the bound pass has work: key norms are needed
+    if (p.ticket != nullptr) {
+      // probe: the last planned query decides whether the call runs the
+      // certificate pipeline (some probe query can prune) or dense scoring
+      __threadfence();
+      if (atomicAdd(p.ticket, 1) == p.decide_nq - 1) {
+        __threadfence();
+        bool any = false;
+        for (int i = 0; i < p.decide_nq && !any; ++i) {
+          const uint32_t* f = reinterpret_cast<const uint32_t*>(p.coef + (int64_t)(p.decide_q0 + i) * kCoefStride + 7);
+          any = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;   // coef[7] == 0.f
+        }
+        *p.decide_mode = any ? MODE_PRUNED : MODE_UNPRUNED;
+        if (!any && p.stats != nullptr) atomicAdd(&p.stats[10], 1ull);
+      }
+    }
   }
 }
 
@@ -1425,24 +1440,6 @@ __global__ void stats_add_kernel(unsigned long long* st, const dosa_stats add) {
 // query tile, its longest contexts): if the certificate cannot prune a single
 // query there, the call scores every key densely instead.  Exactness does not
 // depend on it; only which kernels do the work.
-__global__ void probe_decide_kernel(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
-                                    unsigned long long* stats) {
-  const int lane = lane_id();
-  bool prunes = false;
-  for (int i = lane; i < nq; i += 64) prunes = prunes || coef[(int64_t)(q0 + i) * kCoefStride + 7] == 0.f;
-  const bool any = __ballot(prunes) != 0ull;
-  if (lane == 0) {
-    *mode = any ? MODE_PRUNED : MODE_UNPRUNED;
-    if (!any && stats != nullptr) atomicAdd(&stats[10], 1ull);
-  }
-}
-
-hipError_t launch_probe_decide(const float* coef, int32_t q0, int32_t nq, int32_t* mode,
-                               unsigned long long* stats, hipStream_t s) {
-  hipLaunchKernelGGL(probe_decide_kernel, dim3(1), dim3(64), 0, s, coef, q0, nq, mode, stats);
-  return hipGetLastError();
-}
-
 hipError_t launch_stats_add(unsigned long long* stats, const unsigned long long* v, hipStream_t s) {
   dosa_stats a;
   static_assert(sizeof(dosa_stats) == 12 * sizeof(unsigned long long), "stats layout");

@@ -77,8 +77,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   const int nseg = ((p.mode != nullptr && *p.mode == MODE_UNPRUNED) ? p.r1_unpruned : p.r1) - p.r0;
   Segs sg{base, cnt, p.cb.rows * p.cb.cap, p.cb.rows, nseg, (uint32_t)p.cb.cap, nullptr};
   if (nseg <= kMaxMergeRegions) {
-    segment_offsets(sg, segoff);
-    __syncthreads();
+    segment_offsets_wg<NT>(sg, segoff);
     sg.off = segoff;
   }
   uint32_t total = 0;
@@ -169,6 +168,7 @@ constexpr int kTauThreads = 256;       // per query (1024 measured slower)
 __global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLaunch p) {
   __shared__ uint32_t hist[2048];
   __shared__ uint32_t stage[kTauStage];
+  __shared__ uint32_t segoff[kMaxMergeRegions + 1];
   if (skip_launch(p.mode, p.run_if)) return;
   const int q = p.q_first + blockIdx.x;
   const int K = p.topk;
@@ -176,15 +176,21 @@ __global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLau
                 (uint32_t)p.cb.cap, nullptr};
   __shared__ u64 kth;
   uint32_t total = 0;
-  for (int r = 0; r < sg.nseg; ++r) total += sg.n(r);
+  const bool offs = sg.nseg <= kMaxMergeRegions;
+  if (offs) {
+    segment_offsets_wg<kTauThreads>(sg, segoff);
+    total = segoff[sg.nseg];
+  } else {
+    for (int r = 0; r < sg.nseg; ++r) total += sg.n(r);
+  }
   float tau = -INFINITY;
   if (total >= (uint32_t)K) {
     // T: the lower edge of the radix bin that holds the K-th entry (exactly K
     // entries at or above it); the smallest of those is the K-th largest.
     if (threadIdx.x == 0) kth = ~0ull;
     const int tid = (int)threadIdx.x;
-    if (total <= kTauStage && sg.nseg < 2048) {
-      const uint32_t T = select_kth_score_staged<kTauThreads>(sg, total, K, hist, stage);
+    if (total <= kTauStage && offs) {
+      const uint32_t T = select_kth_score_staged<kTauThreads>(sg, segoff, total, K, hist, stage);
       uint32_t m = 0xFFFFFFFFu;
       for (uint32_t i = tid; i < total; i += kTauThreads) {
         const uint32_t v = stage[i];
