@@ -96,6 +96,7 @@ struct Plan {
   int bound_splits = 1;
   int Js = 1;                        // DoSA: regions of the seed pass
   int X = 0;                         // DoSA: regions of the extra seed keys (after the seed regions)
+  int n_parts = 0;                   // split-threshold slots per query (tiled dense / seed launches)
   int64_t x_stride = 0;              // entries per group of the extra seed lists
   int n_tiles = 0;                   // query tiles (seed items 0 .. n_tiles*Js-1 are Js per tile, tile order)
   int pcap = 0;                      // probe: entries per region of its own candidate buffer
@@ -106,7 +107,7 @@ struct Plan {
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
          o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, o_blk_code = 0, o_blk_info = 0,
-         o_liststart = 0, o_pcand = 0, o_pcounts = 0, o_xlists = 0, o_xlen = 0, total = 0;
+         o_liststart = 0, o_pcand = 0, o_pcounts = 0, o_xlists = 0, o_xlen = 0, o_tpart = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -600,6 +601,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.o_lsig = take((size_t)P.total_q * LS * sizeof(float));
   P.o_lerr = take((size_t)P.total_q * 2 * sizeof(float));
   P.o_tshare = take((size_t)P.total_q * sizeof(uint32_t));
+  // split thresholds of the tiled sweeps: the dense launch's J parts; in the
+  // pruned path the seed launch's Js parts, then the dense launch's Jd
+  P.n_parts = !P.tiled ? 0 : (dense ? P.J : P.Js + (P.probe ? P.Jd : 0));
+  if (P.n_parts > 0) P.o_tpart = take((size_t)P.total_q * P.n_parts * sizeof(uint32_t));
   if (!dense) {
     P.o_tau = take((size_t)P.total_q * sizeof(float));
     P.o_rows = take((size_t)P.total_q * 4 * d * qbytes(q_dtype));
@@ -899,8 +904,11 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   Inputs in{q, q_scale, w, k, k_scale, page_table, page_size, max_pages, H, page_shift};
   PrepLaunch pr{q, w, H, P.total_q, ws + P.o_lrows, reinterpret_cast<float*>(ws + P.o_lsig),
                 reinterpret_cast<float*>(ws + P.o_lerr), dense ? nullptr : reinterpret_cast<int32_t*>(ws + P.o_flag),
-                reinterpret_cast<uint32_t*>(ws + P.o_tshare), reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R};
+                reinterpret_cast<uint32_t*>(ws + P.o_tshare),
+                P.n_parts > 0 ? reinterpret_cast<uint32_t*>(ws + P.o_tpart) : nullptr, P.n_parts,
+                reinterpret_cast<uint32_t*>(ws + P.o_counts), P.R};
   uint32_t* tshare = kShareTheta ? reinterpret_cast<uint32_t*>(ws + P.o_tshare) : nullptr;
+  uint32_t* tpart = P.n_parts > 0 ? reinterpret_cast<uint32_t*>(ws + P.o_tpart) : nullptr;
   {
     PassScope ps(P_PREP, stream);
     e = launch_prep(P.combo, H, d, pr, stream);
@@ -926,6 +934,12 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.scored_slot = 4;
     sl.tiled = P.tiled ? 1 : 2;
     sl.role = ROLE_DENSE;
+    if (P.tiled) {
+      sl.theta_part = tpart;
+      sl.part_stride = P.n_parts;
+      sl.part_base = 0;
+      sl.part_n = P.J;
+    }
     {
       PassScope ps(P_SCORE_DENSE, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -1019,6 +1033,12 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.scored_slot = 1;
     sl.tiled = P.tiled ? 1 : 2;
     sl.role = ROLE_SEED;
+    if (P.tiled) {
+      sl.theta_part = tpart;
+      sl.part_stride = P.n_parts;
+      sl.part_base = 0;
+      sl.part_n = P.Js;
+    }
     {
       PassScope ps(P_SCORE_SEED, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -1226,6 +1246,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       dl.scored_slot = 4;
       dl.tiled = 1;
       dl.role = ROLE_DENSE;
+      dl.theta_part = tpart;
+      dl.part_stride = P.n_parts;
+      dl.part_base = P.Js;
+      dl.part_n = P.Jd;
       PassScope ps(P_SCORE_DENSE, stream);
       e = launch_score(P.combo, H, d, dl, stream);
       if (e != hipSuccess) return fail_hip(e, "dense score kernel launch");

@@ -112,6 +112,8 @@ struct PrepLaunch {
   int32_t* flag;        // [2] cleared here (query 0): the plan's "some query can prune" flag and the
                         // probe plan's ticket counter, or NULL
   uint32_t* tshare;     // [total_q] cleared here: the shared running thresholds (ScoreLaunch)
+  uint32_t* tpart;      // [total_q, n_parts] cleared here: the split thresholds (ScoreLaunch), or NULL
+  int32_t n_parts;
   uint32_t* counts;     // candidate counts [n_regions, total_q], cleared here: a region no item
   int32_t n_regions;    // of the call fills reads as empty in the final merge
 };
@@ -127,6 +129,14 @@ struct ScoreLaunch {
   const float* theta_init;   // [total_q] or NULL (-inf)
   uint32_t* theta_share;     // [total_q] order-preserving images of running thresholds that every
                              // launch of the call publishes to and adopts from (0 = none yet), or NULL
+  // Split thresholds: the launch scores each query's keys in part_n disjoint
+  // sweeps (item region r = sweep r, every one present).  Sweep r publishes
+  // the image of its ceil(K / part_n)-th largest score so far in
+  // theta_part[q * part_stride + part_base + r]; once all part_n are
+  // published, their minimum has at least K scores at or above it over the
+  // sweeps together, a valid threshold for each of them.  NULL: off.
+  uint32_t* theta_part;
+  int32_t part_stride, part_base, part_n;
   const int32_t* lists;      // survivor lists (gather mode)
   const int32_t* list_len;   // survivor list length per group (gather mode)
   const int32_t* list_start; // per group: start of its list after GroupInfo::list_off (or NULL: 0)

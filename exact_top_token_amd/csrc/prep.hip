@@ -135,6 +135,8 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   for (int off = 32; off > 0; off >>= 1) e2 += __shfl_xor(e2, off, 64);
   if (p.counts != nullptr)
     for (int r = lane; r < p.n_regions; r += 64) p.counts[(int64_t)r * p.total_q + q] = 0u;
+  if (p.tpart != nullptr)
+    for (int r = lane; r < p.n_parts; r += 64) p.tpart[(int64_t)q * p.n_parts + r] = 0u;
   if (lane == 0) {
     if (q == 0 && p.flag != nullptr) {
       p.flag[0] = 0;

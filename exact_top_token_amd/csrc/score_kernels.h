@@ -159,6 +159,8 @@ struct Scorer {
   uint32_t hbase;    // ord value of the lower edge of bin 0 (0 = not anchored yet)
   uint32_t* tshare;  // the call's shared thresholds (indexed by query row), or NULL
   uint32_t* anchor;  // LDS [QW]: histogram anchors shared with the workgroup's other wavefronts, or NULL
+  uint32_t* tpart;   // the call's split thresholds (ScoreLaunch::theta_part) at this sweep's query rows, or NULL
+  int part_stride, part_n, part_idx;
   uint32_t n_written, n_reselect, n_scored;
   bool dirty;        // something was appended since the last refresh (wavefront-uniform)
 
@@ -211,6 +213,10 @@ struct Scorer {
     hbase = 0;
     anchor = nullptr;
     tshare = p.theta_share;
+    tpart = (p.theta_part != nullptr && p.part_n > 1) ? p.theta_part + p.part_base : nullptr;
+    part_stride = p.part_stride;
+    part_n = p.part_n;
+    part_idx = region;
     n_written = n_reselect = n_scored = 0;
     dirty = false;
   }
@@ -263,6 +269,41 @@ struct Scorer {
     if (segm != 0ull) {
       const float th = ord2f(e);
       if (th > theta) theta = th;
+    }
+    if (tpart != nullptr) {
+      // This sweep's ceil(K / part_n)-th largest score so far (the lower
+      // edge of its bin), published for the launch's part_n disjoint sweeps
+      // over the query's keys.  Each published value has that many of its
+      // sweep's scores at or above it, so the smallest of all part_n values
+      // has at least K scores at or above it among the query's keys: a valid
+      // threshold, near the K-th largest of all the sweeps' scores together,
+      // where each sweep's own histogram reaches only its own K-th.
+      const uint32_t K2 = ((uint32_t)K + (uint32_t)part_n - 1u) / (uint32_t)part_n;
+      const bool cross2 = hbase != 0u && suf >= K2 && suf - s < K2;
+      uint32_t a2 = suf - s;
+      int bt2 = 0;
+      bool found2 = false;
+#pragma unroll
+      for (int t = BPL - 1; t >= 0; --t) {
+        const bool hit = !found2 && a2 + hv[t] >= K2;
+        bt2 = hit ? t : bt2;
+        found2 = found2 || hit;
+        a2 += hv[t];
+      }
+      uint32_t edge2 = hbase + ((uint32_t)(j * BPL + bt2) << kHistShift);
+      if (edge2 < hbase || edge2 > 0xFF7FFFFFu) edge2 = 0xFF7FFFFFu;
+      const u64 cm2 = __ballot(cross2);
+      const u64 segm2 = (cm2 >> (q * LPQ)) & (LPQ == 64 ? ~0ull : ((1ull << (LPQ & 63)) - 1ull));
+      const int L2 = segm2 ? q * LPQ + (__ffsll((long long)segm2) - 1) : ln;
+      const uint32_t e2 = (uint32_t)__shfl((int)edge2, L2, 64);
+      uint32_t* row = tpart + (int64_t)(q_row0 + q) * part_stride;
+      if (segm2 != 0ull && j == 0 && q < nq) atomicMax(row + part_idx, e2);
+      uint32_t mn = 0xFFFFFFFFu;
+      for (int r = j; r < part_n; r += LPQ)
+        mn = min(mn, q < nq ? __hip_atomic_load(row + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u);
+#pragma unroll
+      for (int off = 1; off < LPQ; off <<= 1) mn = min(mn, (uint32_t)__shfl_xor((int)mn, off, LPQ));
+      if (q < nq && mn != 0u && mn != 0xFFFFFFFFu) theta = fmaxf(theta, ord2f(mn));
     }
     // Share with the call's other sweeps over this query's keys: publish the
     // threshold and adopt the largest one published.  Any sweep's threshold
