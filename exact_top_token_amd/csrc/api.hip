@@ -284,6 +284,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       WorkItem it{};
       it.group = gi;
       it.region = region0 + r;
+      it.nparts = J;
       if (lo == 0) {
         it.a0 = 0; it.a1 = std::min(64, hi);   // the attention-sink keys first, then newest to oldest
         it.b0 = it.a1; it.b1 = hi;
@@ -314,6 +315,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         it.group = t.first;
         it.pad = t.n;
         it.region = r;
+        it.nparts = J;
         if (lo == 0) {
           it.a0 = 0; it.a1 = std::min(64, hi);   // the attention-sink tile first, then newest to oldest
           it.b0 = it.a1; it.b1 = hi;
@@ -371,6 +373,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         it.group = t.first;
         it.pad = t.n;
         it.region = r;
+        it.nparts = Js;
         it.a0 = 0; it.a1 = (r == 0) ? f : 0;
         it.b0 = lo; it.b1 = hi;
         it.gather = 0;
@@ -601,9 +604,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.o_lsig = take((size_t)P.total_q * LS * sizeof(float));
   P.o_lerr = take((size_t)P.total_q * 2 * sizeof(float));
   P.o_tshare = take((size_t)P.total_q * sizeof(uint32_t));
-  // split thresholds of the tiled sweeps: the dense launch's J parts; in the
-  // pruned path the seed launch's Js parts, then the dense launch's Jd
-  P.n_parts = !P.tiled ? 0 : (dense ? P.J : P.Js + (P.probe ? P.Jd : 0));
+  // split thresholds: the dense launch's J parts; in the pruned path the seed
+  // launch's Js parts, then the dense launch's Jd (calls with a probe) or the
+  // survivor range items' J (calls without tiles)
+  P.n_parts = dense ? P.J : P.Js + (P.probe ? P.Jd : 0) + (P.tiled ? 0 : P.J);
   if (P.n_parts > 0) P.o_tpart = take((size_t)P.total_q * P.n_parts * sizeof(uint32_t));
   if (!dense) {
     P.o_tau = take((size_t)P.total_q * sizeof(float));
@@ -934,12 +938,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.scored_slot = 4;
     sl.tiled = P.tiled ? 1 : 2;
     sl.role = ROLE_DENSE;
-    if (P.tiled) {
-      sl.theta_part = tpart;
-      sl.part_stride = P.n_parts;
-      sl.part_base = 0;
-      sl.part_n = P.J;
-    }
+    sl.theta_part = tpart;
+    sl.part_stride = P.n_parts;
     {
       PassScope ps(P_SCORE_DENSE, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -1033,12 +1033,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.scored_slot = 1;
     sl.tiled = P.tiled ? 1 : 2;
     sl.role = ROLE_SEED;
-    if (P.tiled) {
-      sl.theta_part = tpart;
-      sl.part_stride = P.n_parts;
-      sl.part_base = 0;
-      sl.part_n = P.Js;
-    }
+    sl.theta_part = tpart;
+    sl.part_stride = P.n_parts;
     {
       PassScope ps(P_SCORE_SEED, stream);
       e = launch_score(P.combo, H, d, sl, stream);
@@ -1208,6 +1204,12 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       ml.n_items = (int)P.surv_tiled_items.size();
       ml.tiled = P.tiled ? 1 : 2;
       ml.flag_mode = 1;
+      if (!P.tiled) {   // survivor range items of groups scored whole: disjoint sweeps
+        ml.theta_part = tpart;
+        ml.part_stride = P.n_parts;
+        ml.part_base = P.Js;
+        ml.part_rbase = P.Js + P.X;
+      }
       // union shares are cut on the device: launch them longest first
       if (P.tiled && ml.n_items > 0 && ml.n_items <= kMaxOrderItems) {
         OrderLaunch ol{ml.items, ml.n_items, list_len, gflags, reinterpret_cast<int32_t*>(ws + P.o_order), mode,
@@ -1219,6 +1221,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     if (e == hipSuccess) {
       PassScope ps(P_SURV_LISTS, stream);
+      ml.theta_part = nullptr;
       ml.items = di + off_list;
       ml.n_items = (int)P.surv_list_items.size();
       ml.tiled = P.tiled ? 0 : 2;
@@ -1249,7 +1252,6 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       dl.theta_part = tpart;
       dl.part_stride = P.n_parts;
       dl.part_base = P.Js;
-      dl.part_n = P.Jd;
       PassScope ps(P_SCORE_DENSE, stream);
       e = launch_score(P.combo, H, d, dl, stream);
       if (e != hipSuccess) return fail_hip(e, "dense score kernel launch");

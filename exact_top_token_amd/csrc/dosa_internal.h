@@ -58,6 +58,8 @@ struct WorkItem {
   int32_t b0, b1;
   int32_t gather;
   int32_t pad;
+  int32_t nparts;   // split thresholds: the launch's disjoint sweeps over this item's queries' keys
+                    // (the items of its tile or group in the launch), 0 = not counted
 };
 
 // Head slots the kernels are built for: the head count rounded up to 8, 16,
@@ -129,14 +131,16 @@ struct ScoreLaunch {
   const float* theta_init;   // [total_q] or NULL (-inf)
   uint32_t* theta_share;     // [total_q] order-preserving images of running thresholds that every
                              // launch of the call publishes to and adopts from (0 = none yet), or NULL
-  // Split thresholds: the launch scores each query's keys in part_n disjoint
-  // sweeps (item region r = sweep r, every one present).  Sweep r publishes
-  // the image of its ceil(K / part_n)-th largest score so far in
-  // theta_part[q * part_stride + part_base + r]; once all part_n are
-  // published, their minimum has at least K scores at or above it over the
-  // sweeps together, a valid threshold for each of them.  NULL: off.
+  // Split thresholds: the launch scores each query's keys in P = nparts
+  // disjoint sweeps (its items; every one present).  Sweep r publishes the
+  // image of its ceil(K / P)-th largest score so far in
+  // theta_part[q * part_stride + part_base + r]; once all P are published,
+  // their minimum has at least K scores at or above it over the sweeps
+  // together, a valid threshold for each of them.  NULL: off.
   uint32_t* theta_part;
-  int32_t part_stride, part_base, part_n;
+  int32_t part_stride, part_base;
+  int32_t part_rbase;        // region of sweep 0: sweep index = item region - part_rbase; the sweep
+                             // count is the item's nparts
   const int32_t* lists;      // survivor lists (gather mode)
   const int32_t* list_len;   // survivor list length per group (gather mode)
   const int32_t* list_start; // per group: start of its list after GroupInfo::list_off (or NULL: 0)

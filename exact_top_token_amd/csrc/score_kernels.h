@@ -213,12 +213,22 @@ struct Scorer {
     hbase = 0;
     anchor = nullptr;
     tshare = p.theta_share;
-    tpart = (p.theta_part != nullptr && p.part_n > 1) ? p.theta_part + p.part_base : nullptr;
+    tpart = nullptr;
     part_stride = p.part_stride;
-    part_n = p.part_n;
-    part_idx = region;
+    part_n = 0;
+    part_idx = 0;
     n_written = n_reselect = n_scored = 0;
     dirty = false;
+  }
+
+  // The item's place among the launch's sweeps over its queries' keys (split
+  // thresholds, ScoreLaunch::theta_part); off with one sweep.
+  __device__ __forceinline__ void set_part(const ScoreLaunch& p, const WorkItem& it) {
+    if (p.theta_part != nullptr && it.nparts > 1) {
+      tpart = p.theta_part + p.part_base;
+      part_n = it.nparts;
+      part_idx = it.region - p.part_rbase;
+    }
   }
 
   // Raise theta of every query of the wavefront to the lower edge of the
@@ -729,6 +739,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
   }
   SC sc;
   sc.init(p, gr, it.region * kTileWaves + wave, wl, qhist, true, wave == 0);
+  sc.set_part(p, it);
   if (threadIdx.x < (unsigned)SC::QW) anchor[threadIdx.x] = 0u;
   sc.anchor = anchor;
   __syncthreads();
@@ -935,6 +946,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   }
   SC sc;
   sc.init(p, gr, it.region, wl[wave], qhist[wave], active);
+  sc.set_part(p, it);
 
   const int na = gather ? 0 : ((it.a1 > it.a0) ? (it.a1 - it.a0 + TK - 1) / TK : 0);
   const int nbt = gather ? (e1 - e0 + TK - 1) / TK : ((it.b1 > it.b0) ? (it.b1 - it.b0 + TK - 1) / TK : 0);
