@@ -66,6 +66,68 @@ int fail_hip(hipError_t e, const char* what) {
   return DOSA_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// The certificate stages of a call with a probe run on a side stream of the
+// library's own, next to the dense alternative on the caller's stream: the
+// probe's decision lets exactly one of the two do work, and the other's
+// launches return at once without delaying it.  One side stream per device,
+// created on first use (default priority) and kept until the process ends.
+// Each call forks it from the caller's stream after the probe and joins it
+// back before the final selection, with events of its own, so the caller's
+// stream order covers all of the call's work (graph capture included).  Calls
+// that run at the same time on one device share the side stream: their
+// certificate stages then run one after the other.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::once_flag g_side_once[kMaxDevices];
+hipStream_t g_side[kMaxDevices] = {};
+hipError_t g_side_err[kMaxDevices] = {};
+
+hipError_t side_stream(hipStream_t* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_side_once[dev], [dev]() { g_side_err[dev] = hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking); });
+  if (g_side_err[dev] != hipSuccess) return g_side_err[dev];
+  *out = g_side[dev];
+  return hipSuccess;
+}
+
+// Fork of the side stream from the caller's stream; the destructor joins it
+// back (also on an early error return), so nothing of the call is left
+// unordered with the caller's later work.
+struct SideFork {
+  hipStream_t main = nullptr, side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  hipError_t open(hipStream_t caller) {
+    main = caller;
+    // per-pass event timing keeps every pass on the caller's stream, so each
+    // pass's span is its own launch (not the wait for CUs held by the other)
+    if (g_prof.on) return hipSuccess;
+    hipError_t e = side_stream(&side);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&join, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(fork, main);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side, fork, 0);
+    if (e != hipSuccess) side = nullptr;   // stay on the caller's stream
+    return e;
+  }
+  hipError_t close() {
+    hipError_t e = hipSuccess;
+    if (side != nullptr) {
+      e = hipEventRecord(join, side);
+      if (e == hipSuccess) e = hipStreamWaitEvent(main, join, 0);
+      side = nullptr;
+    }
+    if (fork) hipEventDestroy(fork);
+    if (join) hipEventDestroy(join);
+    fork = join = nullptr;
+    return e;
+  }
+  ~SideFork() { close(); }
+};
+
 int combo_of(int qd, int kd) {
   if (qd == DOSA_F32 && kd == DOSA_F32) return C_F32;
   if (qd == DOSA_BF16 && kd == DOSA_BF16) return C_BF16;
@@ -1016,6 +1078,15 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_plan(P.combo, H, d, pp, stream);
       if (e != hipSuccess) return fail_hip(e, "probe plan kernel launch");
     }
+    // With a probe, the certificate stages (steps 2-7) go to the side stream
+    // and the dense alternative (step 8) stays on the caller's stream.
+    SideFork sf;
+    hipStream_t cs = stream;
+    if (P.probe) {
+      e = sf.open(stream);
+      if (e != hipSuccess) return fail_hip(e, "side stream");
+      if (sf.side != nullptr) cs = sf.side;
+    }
     // 2. seed pass: exact scores of the seed keys into regions 0..Js-1
     ScoreLaunch sl{};
     sl.theta_share = tshare;
@@ -1036,18 +1107,18 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     sl.theta_part = tpart;
     sl.part_stride = P.n_parts;
     {
-      PassScope ps(P_SCORE_SEED, stream);
-      e = launch_score(P.combo, H, d, sl, stream);
+      PassScope ps(P_SCORE_SEED, cs);
+      e = launch_score(P.combo, H, d, sl, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "seed score kernel launch");
     // 2b. extra seed keys: the union list of each group, scored into regions
     //     Js..Js+X-1 (read by the threshold select only; compaction clears them)
     if (P.X > 0) {
-      PassScope ps(P_SEED_EXTRA, stream);
+      PassScope ps(P_SEED_EXTRA, cs);
       int32_t* xlists = reinterpret_cast<int32_t*>(ws + P.o_xlists);
       int32_t* xlen = reinterpret_cast<int32_t*>(ws + P.o_xlen);
       SeedUnionLaunch su{dg, G, cfg.seed_idx, cfg.seed_count, xlists, P.x_stride, xlen, mode, MODE_PRUNED};
-      e = launch_seed_union(su, stream);
+      e = launch_seed_union(su, cs);
       if (e == hipSuccess && !P.x_items.empty()) {
         ScoreLaunch xl{};
         xl.theta_share = tshare;
@@ -1068,7 +1139,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
         xl.scored_slot = 1;
         xl.tiled = P.tiled ? 0 : 2;
         xl.role = ROLE_SURVIVORS;
-        e = launch_score(P.combo, H, d, xl, stream);
+        e = launch_score(P.combo, H, d, xl, cs);
       }
     }
     if (e != hipSuccess) return fail_hip(e, "extra seed kernel launch");
@@ -1084,8 +1155,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ts.tau_out = tau;
     ts.tau_copy = cfg.debug_tau;
     {
-      PassScope ps(P_SELECT_SEED, stream);
-      e = launch_select(ts, stream);
+      PassScope ps(P_SELECT_SEED, cs);
+      e = launch_select(ts, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "seed select kernel launch");
     // 4. certificate plan per query
@@ -1105,8 +1176,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     pl.rows = ws + P.o_rows;
     pl.coef = coef;
     {
-      PassScope ps(P_PLAN, stream);
-      e = launch_plan(P.combo, H, d, pl, stream);
+      PassScope ps(P_PLAN, cs);
+      e = launch_plan(P.combo, H, d, pl, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "plan kernel launch");
     // 4b. per-key norms for the bound pass; the launch returns at once when the
@@ -1116,9 +1187,9 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
                   cu_dev + (batch + 1), key_blocks ? reinterpret_cast<uint8_t*>(ws + P.o_blk_code) : nullptr,
                   reinterpret_cast<float*>(ws + P.o_blk_info)};
     {
-      PassScope ps(P_NORMS, stream);
-      e = launch_key_norms(P.combo, d, nl, stream);
-      if (e == hipSuccess) e = launch_key_blocks(P.combo, d, nl, stream);
+      PassScope ps(P_NORMS, cs);
+      e = launch_key_norms(P.combo, d, nl, cs);
+      if (e == hipSuccess) e = launch_key_blocks(P.combo, d, nl, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
     // 5. bound pass -> survivor bitmasks
@@ -1149,8 +1220,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     }
     bl.stats = st;
     {
-      PassScope ps(P_BOUND, stream);
-      e = launch_bound(P.combo, H, d, bl, stream);
+      PassScope ps(P_BOUND, cs);
+      e = launch_bound(P.combo, H, d, bl, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
     // 6. compaction -> survivor key lists
@@ -1173,8 +1244,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     cl.mode = mode;
     cl.run_if = MODE_PRUNED;
     {
-      PassScope ps(P_COMPACT, stream);
-      e = launch_compact(cl, stream);
+      PassScope ps(P_COMPACT, cs);
+      e = launch_compact(cl, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
     // 7. survivors scored with all heads into regions Js..Js+J-1, threshold starts at tau:
@@ -1199,7 +1270,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     ml.tile_flags = gflags;
     ml.role = ROLE_SURVIVORS;
     {
-      PassScope ps(P_SURV_TILES, stream);
+      PassScope ps(P_SURV_TILES, cs);
       ml.items = di + off_surv;
       ml.n_items = (int)P.surv_tiled_items.size();
       ml.tiled = P.tiled ? 1 : 2;
@@ -1214,20 +1285,20 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       if (P.tiled && ml.n_items > 0 && ml.n_items <= kMaxOrderItems) {
         OrderLaunch ol{ml.items, ml.n_items, list_len, gflags, reinterpret_cast<int32_t*>(ws + P.o_order), mode,
                        MODE_PRUNED};
-        e = launch_order(ol, stream);
+        e = launch_order(ol, cs);
         ml.order = ol.order;
       }
-      if (e == hipSuccess) e = launch_score(P.combo, H, d, ml, stream);
+      if (e == hipSuccess) e = launch_score(P.combo, H, d, ml, cs);
     }
     if (e == hipSuccess) {
-      PassScope ps(P_SURV_LISTS, stream);
+      PassScope ps(P_SURV_LISTS, cs);
       ml.theta_part = nullptr;
       ml.items = di + off_list;
       ml.n_items = (int)P.surv_list_items.size();
       ml.tiled = P.tiled ? 0 : 2;
       ml.flag_mode = 2;
       ml.scored_slot2 = 8;
-      e = launch_score(P.combo, H, d, ml, stream);
+      e = launch_score(P.combo, H, d, ml, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
     // 8. the dense alternative, run only when the probe found nothing to prune
@@ -1256,6 +1327,8 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       e = launch_score(P.combo, H, d, dl, stream);
       if (e != hipSuccess) return fail_hip(e, "dense score kernel launch");
     }
+    e = sf.close();
+    if (e != hipSuccess) return fail_hip(e, "side stream join");
   }
   SelectLaunch se{};
   se.cb = cb;

@@ -22,8 +22,9 @@ typedef unsigned long long u64;
 // total order; low word: ~position.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t f2ord(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; otherwise the sign bit set (three VALU ops)
+  const uint32_t u = __float_as_uint(f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float ord2f(uint32_t o) {
   uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;

@@ -6,7 +6,8 @@
 //     x[(t,h), s] = q[t,h,:] . k[s,:]            (fp32 accumulation)
 // and each lane folds its 4 output rows -- 4 heads of one query -- into the
 // score through the identity w max(0,x) = w x/2 + w |x|/2:
-//     S(t,s) = sum_h (w_h/2) |x_h|  +  (1/2) qbar_t . k_s   (then x q_scale * k_scale)
+//     S(t,s) = sum_h (w'_h/2) |x_h|  +  (q_scale/2) qbar_t . k_s   (then x k_scale)
+// with w'_h = w_h x q_scale (the query's fp8 scale, 1 otherwise)
 // with qbar_t = sum_h w_h q_h evaluated by one more MFMA row group (its terms
 // come from prep.hip), so each head value costs one fused multiply-add with
 // a free |.| operand modifier.  After all head groups every lane holds a
@@ -151,7 +152,7 @@ struct Scorer {
   __device__ __forceinline__ int owner_lane0() const { return 16 * (qi() * (4 / QW)); }
   __device__ __forceinline__ bool qok() const { return qi() < nq; }
   __device__ __forceinline__ bool owner() const { return g() == (owner_lane0() >> 4); }
-  float qs, theta;
+  float theta;
   uint32_t count;
   u64* buf;
   uint32_t wq_lds;   // LDS byte address of this lane's query's weights / 2, then its term scales / 2
@@ -192,17 +193,19 @@ struct Scorer {
       else
         O::zero(AL);
     }
+    // the query's fp8 scale is folded into its weights here, so a score is
+    // (sum of weighted terms) x key scale with no per-score query-scale product
     for (int e = lane; write_lds && e < QW * (H + S); e += 64) {
       const int q = e / (H + S), h = e % (H + S);
       float v = 0.f;
       if (q < nq) {
-        if (h >= H) v = 0.5f * p.lsig[(int64_t)(gr.q_row0 + q) * S + (h - H)];
-        else if (h < p.in.H) v = 0.5f * p.in.w[(int64_t)(gr.q_row0 + q) * p.in.H + h];
+        const float qsc = HasQScale<C>::value ? p.in.q_scale[gr.q_row0 + q] : 1.f;
+        if (h >= H) v = (0.5f * p.lsig[(int64_t)(gr.q_row0 + q) * S + (h - H)]) * qsc;
+        else if (h < p.in.H) v = (0.5f * p.in.w[(int64_t)(gr.q_row0 + q) * p.in.H + h]) * qsc;
       }
       wl[e] = v;
     }
     wq_lds = (uint32_t)(uintptr_t)(wl + qi() * (H + S));   // low 32 bits of a generic LDS address = the LDS offset
-    qs = (HasQScale<C>::value && qok()) ? p.in.q_scale[qrow()] : 1.f;
     // lanes of absent queries get an unreachable threshold, so they never append
     theta = qok() ? (p.theta_init != nullptr ? p.theta_init[qrow()] : -INFINITY) : INFINITY;
     count = 0;
@@ -428,35 +431,48 @@ struct Scorer {
   // about to overflow.  Called by all 64 lanes of the wavefront.  CHECK: some
   // keys of the step may lie outside the range (kvalid) or after a query's
   // position; without it every key of the step is visible to every query of
-  // the group.  Lanes of absent queries hold theta = +inf and never take.  A
-  // step whose scores all stay below theta costs a few instructions.  A step
-  // adds at most 64 entries per query, so regions are checked against
-  // cap - 64 once per step.
-  template <bool CHECK>
+  // the group.  KBASE: the step's keys are kbase + 16 b + column (a key range),
+  // computed only when a score is taken; otherwise they come in key[].  Lanes
+  // of absent queries hold theta = +inf and never take.  A step whose scores
+  // all stay below theta costs a few instructions.  A step adds at most 64
+  // entries per query, so regions are checked against cap - 64 once per step.
+  template <bool CHECK, bool KBASE = false>
   __device__ __forceinline__ void append4(const ScoreLaunch& p, const GroupInfo& gr, int region, const float* o,
-                                          const float* ks, const int* key, const bool* kvalid, uint32_t* shist) {
-    const int ln = lane_fresh();
-    const int c = ln & 15, gg = ln >> 4;
-    const int q_i = (4 * gg) / S;
-    const int ol0 = 16 * (q_i * (4 / QW));
-    const bool own = (QW == 4) || (gg == (ol0 >> 4));
+                                          const float* ks, const int* key, const bool* kvalid, uint32_t* shist,
+                                          int kbase = 0) {
     float sc[4];
     bool take[4];
     bool anyt = false;
+    if constexpr (CHECK || QW < 4) {
+      const int gg = lane_fresh() >> 4;
+      const int q_i = (4 * gg) / S;
+      const bool own = (QW == 4) || (gg == ((16 * (q_i * (4 / QW))) >> 4));
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      sc[b] = o[b] * qs * ks[b];
-      bool v = own;
-      if constexpr (CHECK) {
-        v = v && kvalid[b] && key[b] <= pos0 + q_i && q_i < nq;
-        n_scored += __popcll(ballot(v));
+      for (int b = 0; b < 4; ++b) {
+        sc[b] = o[b] * ks[b];
+        bool v = own;
+        if constexpr (CHECK) {
+          v = v && kvalid[b] && key[b] <= pos0 + q_i && q_i < nq;
+          n_scored += __popcll(ballot(v));
+        }
+        take[b] = v && sc[b] >= theta;
+        anyt = anyt || take[b];
       }
-      take[b] = v && sc[b] >= theta;
-      anyt = anyt || take[b];
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        sc[b] = o[b] * ks[b];
+        take[b] = sc[b] >= theta;
+        anyt = anyt || take[b];
+      }
     }
     if constexpr (!CHECK) n_scored += 64u * (uint32_t)nq;
     if (ballot(anyt) == 0ull) return;
     dirty = true;
+    const int ln = lane_fresh();
+    const int c = ln & 15, gg = ln >> 4;
+    const int q_i = (4 * gg) / S;
+    const int ol0 = 16 * (q_i * (4 / QW));
     uint32_t so[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) so[b] = f2ord(sc[b]);
@@ -490,7 +506,10 @@ struct Scorer {
       if (take[b] && hbase != 0 && so[b] >= hbase)
         atomicAdd(&hq[min((so[b] - hbase) >> kHistShift, (uint32_t)(kHistBins - 1))], 1u);
       const uint32_t slice = (uint32_t)(m >> ol0) & 0xFFFFu;
-      if (take[b]) buf[count + __popc(slice & below)] = ((u64)so[b] << 32) | (u64)(uint32_t)(~(uint32_t)key[b]);
+      if (take[b]) {
+        const int kk = KBASE ? kbase + 16 * b + c : key[b];
+        buf[count + __popc(slice & below)] = ((u64)so[b] << 32) | (u64)(uint32_t)(~(uint32_t)kk);
+      }
       count += __popc(slice);
       n_written += __popcll(m);
     }
@@ -903,10 +922,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
   constexpr int KB = SC::KBYTES;
   constexpr int ROW = KB + 16;                       // padded LDS row: conflict-free 16-byte reads
   constexpr int CPK = KB / 16;                       // 16-byte chunks per key
-  // 64-key scoring steps per LDS tile.  One: with two (128-key tiles, half
-  // the barriers) the kernel measured slower on MI355X.
-  constexpr int TS = 1;
-  constexpr int TK = kTileKeys * TS;                 // keys per LDS tile
+  constexpr int TK = kTileKeys;                      // keys per LDS tile (one 64-key scoring step)
   constexpr int NCH = (TK * CPK + 64 * kTileWaves - 1) / (64 * kTileWaves);
   // 16-key blocks per scoring step: as many as the key fragments' registers allow
   constexpr int FB = (int)sizeof(typename O::frag) * SC::STEPS;   // bytes of one block's key fragment per lane
@@ -1011,10 +1027,26 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
       fetch_gather(t);
       return;
     }
-    const int tid = lane_fresh() + 64 * wave;
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
     const int kb = hi - TK * ((ra ? t : t - na) + 1);
+    if (!PAGED && kb >= lo && kb + TK <= hi) {
+      // every key of the tile in range: its rows are TK * KB contiguous bytes
+      // from a wavefront-uniform base, chunk ch at byte 16 ch
+      const int tid = lane_fresh() + 64 * wave;
+      const uint8_t* kt = kseq + (uint32_t)kb * (uint32_t)KB;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const int ch = tid + c * 64 * kTileWaves;
+        if ((TK * CPK) % (64 * kTileWaves) == 0 || ch < TK * CPK)
+          stage[c] = *reinterpret_cast<const v4i*>(kt + (uint32_t)ch * 16u);
+      }
+      if constexpr (HasKScale<C>::value) {
+        if (tid < TK) stage_s = sseq[(uint32_t)kb + (uint32_t)tid];
+      }
+      return;
+    }
+    const int tid = lane_fresh() + 64 * wave;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 64 * kTileWaves;
@@ -1046,9 +1078,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     wait_vmem();
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
+      // chunk ch = (slot, part) goes to slot * ROW + 16 part = 16 (ch + slot)
       const int ch = tid + c * 64 * kTileWaves;
-      const int slot = ch / CPK, part = ch % CPK;
-      if (slot < TK) *reinterpret_cast<v4i*>(&ktile[bufi][slot * ROW + part * 16]) = stage[c];
+      const int slot = ch / CPK;
+      if (slot < TK) *reinterpret_cast<v4i*>(&ktile[bufi][16 * (ch + slot)]) = stage[c];
     }
     if (tid < TK) {
       kscale[bufi][tid] = stage_s;
@@ -1068,6 +1101,24 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     commit(0);
   }
   __syncthreads();
+  auto range_epilogue = [&](const float* o4, const float* ks4, int kh, int lo, int hi) {
+    // whole step inside the range and visible to every query of the group
+    const bool full = kh >= lo && kh + kTileKeys <= hi && kh + kTileKeys - 1 <= last0;
+    if (full) {
+      // key positions kh + 16 b + column, formed only for taken scores
+      sc.template append4<false, true>(p, gr, it.region, o4, ks4, nullptr, nullptr, hist[wave], kh);
+    } else {
+      const int cl = sc.col();
+      int keys[4];
+      bool kv[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        keys[b] = kh + b * 16 + cl;
+        kv[b] = keys[b] >= lo && keys[b] < hi;
+      }
+      sc.template append4<true>(p, gr, it.region, o4, ks4, keys, kv, hist[wave]);
+    }
+  };
 #pragma unroll 1
   for (int t = 0; t < ntiles; ++t) {
     const int bufi = t & 1;
@@ -1075,60 +1126,49 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_tiled_kernel(const Scor
     const bool ra = t < na;
     const int lo = ra ? it.a0 : it.b0, hi = ra ? it.a1 : it.b1;
     const int kb = hi - TK * ((ra ? t : t - na) + 1);
-    float o[TS][4];
+    float o[4];
     if (active) {
       // one fresh lane id for every fragment address of the tile: the blocks'
       // LDS reads then differ by immediate offsets only
       const int ln = lane_fresh();
       const int fcol = ln & 15, fg = ln >> 4;
 #pragma unroll
-      for (int hh = 0; hh < TS; ++hh) {
+      for (int hb = 0; hb < 4 / NBK; ++hb) {
+        typename O::frag B[NBK][SC::STEPS];
 #pragma unroll
-        for (int hb = 0; hb < 4 / NBK; ++hb) {
-          typename O::frag B[NBK][SC::STEPS];
+        for (int b = 0; b < NBK; ++b) O::load_k(&ktile[bufi][((NBK * hb + b) * 16 + fcol) * ROW], fg, B[b]);
+        // all blocks' fragments in flight together: one LDS wait, not one per block
 #pragma unroll
-          for (int b = 0; b < NBK; ++b)
-            O::load_k(&ktile[bufi][(kTileKeys * hh + (NBK * hb + b) * 16 + fcol) * ROW], fg, B[b]);
-          // all blocks' fragments in flight together: one LDS wait, not one per block
+        for (int b = 0; b < NBK; ++b)
 #pragma unroll
-          for (int b = 0; b < NBK; ++b)
-#pragma unroll
-            for (int s = 0; s < SC::STEPS; ++s) asm volatile("" : "+v"(B[b][s]));
-          sc.template scoreN<NBK>(B, o[hh] + NBK * hb);
-        }
+          for (int s = 0; s < SC::STEPS; ++s) asm volatile("" : "+v"(B[b][s]));
+        sc.template scoreN<NBK>(B, o + NBK * hb);
       }
     }
     commit(bufi ^ 1);
     if (active) {
       const int cl = sc.col();
+      float ks[4];
 #pragma unroll
-      for (int hh = 0; hh < TS; ++hh) {
-        const int kh = kb + kTileKeys * hh;
-        float ks[4];
+      for (int b = 0; b < 4; ++b) ks[b] = HasKScale<C>::value ? kscale[bufi][b * 16 + cl] : 1.f;
+      if (kGatherRole && gather) {
         int keys[4];
         bool kv[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          ks[b] = HasKScale<C>::value ? kscale[bufi][kTileKeys * hh + b * 16 + cl] : 1.f;
-          if (kGatherRole && gather) {
-            keys[b] = kid[bufi][kTileKeys * hh + b * 16 + cl];
-            kv[b] = keys[b] >= 0;
-          } else {
-            keys[b] = kh + b * 16 + cl;
-            kv[b] = keys[b] >= lo && keys[b] < hi;
-          }
+          keys[b] = kid[bufi][b * 16 + cl];
+          kv[b] = keys[b] >= 0;
         }
-        // whole step inside the range (gather: every slot of the tile filled)
-        // and visible to every query of the group
-        const bool full = (kGatherRole && gather)
-                              ? (e1 - TK * (t + 1) >= e0)
-                              : (kh >= lo && kh + kTileKeys <= hi && kh + kTileKeys - 1 <= last0);
-        if (full)
-          sc.template append4<false>(p, gr, it.region, o[hh], ks, keys, kv, hist[wave]);
+        // every slot of the tile filled: each listed key lies before the
+        // tile's first query
+        if (e1 - TK * (t + 1) >= e0)
+          sc.template append4<false>(p, gr, it.region, o, ks, keys, kv, hist[wave]);
         else
-          sc.template append4<true>(p, gr, it.region, o[hh], ks, keys, kv, hist[wave]);
+          sc.template append4<true>(p, gr, it.region, o, ks, keys, kv, hist[wave]);
+      } else {
+        range_epilogue(o, ks, kb, lo, hi);
       }
-      if ((t & (kRefreshTiles / TS - 1)) == kRefreshTiles / TS - 1 && sc.dirty) sc.refresh_theta(p.topk);
+      if ((t & (kRefreshTiles - 1)) == kRefreshTiles - 1 && sc.dirty) sc.refresh_theta(p.topk);
     }
     __syncthreads();
   }

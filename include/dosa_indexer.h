@@ -58,11 +58,16 @@
  * Inputs must be finite.
  *
  * Ownership and synchronisation: the caller owns every buffer, including the
- * workspace (size from dosa_workspace_size).  The library allocates nothing
- * and keeps no state between calls; everything is enqueued on `stream`
+ * workspace (size from dosa_workspace_size).  The library allocates no device
+ * memory and keeps no data between calls; everything is ordered on `stream`
  * (a hipStream_t, NULL = default stream) and no call waits for the device.
+ * A pruned call that runs the probe (see DOSA_NO_PROBE) forks the certificate stages onto
+ * a side stream the library creates once per device (default priority, kept
+ * until the process ends) and joins it back into `stream` before its final
+ * selection, so `stream` order covers the whole call (graph capture too).
  * Outputs, workspace contents and stats are valid once the stream has
- * completed.  Calls on distinct workspaces/streams may run concurrently.
+ * completed.  Calls on distinct workspaces/streams may run concurrently;
+ * their certificate stages then share the device's side stream.
  *
  * Errors: 0 on success or a negative dosa_status.  On error nothing has been
  * enqueued.  No C++ exception crosses this interface.
