@@ -746,6 +746,16 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
   __shared__ __attribute__((aligned(16))) float wl[SC::QW * (H + SC::S)];
   __shared__ uint32_t qhist[SC::QW * kHistBins];
   __shared__ uint32_t anchor[SC::QW];
+  // fp8 key rows of each wavefront's next step, streamed straight into LDS:
+  // two images per wavefront (even and odd steps, separate arrays so the
+  // compiler can tell a step's reads from the next step's stores)
+  constexpr int KIMG = KeyRaw<C>::value ? kTileWaves * 64 * SC::KBYTES : 16;
+  constexpr int SIMG = KeyRaw<C>::value ? kTileWaves * 64 : 1;
+  __shared__ __attribute__((aligned(16))) uint8_t kimg0[KIMG];
+  __shared__ __attribute__((aligned(16))) uint8_t kimg1[KIMG];
+  __shared__ float simg0[SIMG];
+  __shared__ float simg1[SIMG];
+  __shared__ __attribute__((aligned(16))) v4f opend[KeyRaw<C>::value ? kTileWaves * 64 : 1];   // a step's scores, appended in the next
   if (skip_launch(p.mode, p.run_if)) return;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x) >> 6;   // wavefront-uniform
   const WorkItem it = p.items[blockIdx.x];
@@ -797,6 +807,175 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
   const int region = it.region * kTileWaves + wave;
 
   if constexpr (KeyRaw<C>::value) {
+    if (!it.gather && (p.in.page_table == nullptr || p.in.page_shift >= 6)) {
+      // Range walk with the next step's 64 key rows and scales streamed by
+      // direct global->LDS loads into this wavefront's own image while the
+      // current step is scored: a step's key bytes (8 KiB at d = 128) are in
+      // flight per wavefront without holding registers, and no barrier is
+      // needed (each wavefront reads only the rows it loaded).  Image layout:
+      // 16-byte unit u = 64 i + lane of load instruction i holds chunk
+      // (u % CPK) ^ (r % CPK) of the step's key r = u / CPK, so the 16 lanes
+      // that read one chunk column of 16 rows hit different banks.
+      constexpr int KBY = SC::KBYTES;               // bytes per key row
+      constexpr int CPK = KBY / 16;                 // 16-byte chunks per row (= load instructions per step)
+      const int na = it.a1 > it.a0 ? (it.a1 - it.a0 + 63) / 64 : 0;
+      const int ns = na + (it.b1 > it.b0 ? (it.b1 - it.b0 + 63) / 64 : 0);
+      // step s: keys [base, base + 64) of its range, those >= lo valid
+      auto step_base = [&](int s, int& lo, int& hi) -> int {
+        const bool ra = s < na;
+        lo = ra ? it.a0 : it.b0;
+        hi = ra ? it.a1 : it.b1;
+        return hi - 64 - 64 * (ra ? s : s - na);
+      };
+      const bool paged = p.in.page_table != nullptr;
+      const int sh = paged ? p.in.page_shift : 0;
+      // the page table is read-only here: read through the constant address
+      // space, so its wavefront-uniform entries come by scalar loads whose
+      // waits the compiler places where they are used
+      typedef __attribute__((address_space(4))) const int32_t cint;
+      cint* ptab = paged ? (cint*)(p.in.page_table + (int64_t)gr.seq * p.in.max_pages) : nullptr;
+      // pool pages of a step's first and last valid keys (a step spans at
+      // most two pages of >= 64 keys); wavefront-uniform
+      // (scalar loads: a vector load here would make the wait for its value
+      // also wait for the direct loads in flight)
+      auto step_pages = [&](int s, int& pg0, int& pp0, int& pg1) {
+        int lo, hi;
+        const int base = step_base(s, lo, hi);
+        pp0 = __builtin_amdgcn_readfirstlane(max(base, lo) >> sh);
+        const int pl = __builtin_amdgcn_readfirstlane((base + 63) >> sh);
+        pg0 = ptab[pp0];
+        pg1 = pl > pp0 ? ptab[pl] : pg0;
+      };
+      const uint8_t* kbase = static_cast<const uint8_t*>(p.in.k) + (paged ? 0 : (int64_t)gr.key_base * KBY);
+      const float* sbase = p.in.k_scale + (paged ? 0 : (int64_t)gr.key_base);
+      typedef __attribute__((address_space(1))) const void gvoid;
+      typedef __attribute__((address_space(3))) void lvoid;
+      // direct loads of step s's rows and scales into image `img`, scales
+      // `simg`; lane l's unit in instruction i is key (64 / CPK) i + l / CPK,
+      // chunk (l % CPK) ^ ((l / CPK) % CPK) (the same chunk for every i)
+      auto issue_as = [&](auto paged_t, int s, uint8_t* img, float* simg, int pg0, int pp0, int pg1) {
+        constexpr bool PG = decltype(paged_t)::value;
+        int lo, hi;
+        const int base = step_base(s, lo, hi);
+        const uint32_t ln = (uint32_t)lane_fresh();
+        const int rl = (int)(ln / CPK);
+        const uint32_t ch = (ln % CPK) ^ ((uint32_t)rl % CPK);
+        const uint32_t pmask = (1u << sh) - 1u;
+        auto row_of = [&](int key) -> uint32_t {
+          if constexpr (!PG) return (uint32_t)key;
+          const uint32_t pg = (uint32_t)((key >> sh) == pp0 ? pg0 : pg1);
+          return (pg << sh) | ((uint32_t)key & pmask);
+        };
+#pragma unroll
+        for (int i = 0; i < CPK; ++i) {
+          const int key = max(base + (64 / CPK) * i + rl, lo);   // rows before the range: a valid row, never read
+          const uint8_t* src = kbase + (uint64_t)row_of(key) * KBY + 16u * ch;
+          __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(img + wave * 64 * KBY + 1024 * i), 16, 0, 0);
+        }
+        const int key = max(base + (int)ln, lo);
+        __builtin_amdgcn_global_load_lds((gvoid*)(sbase + row_of(key)), (lvoid*)(simg + wave * 64), 4, 0, 0);
+      };
+      auto issue = [&](int s, uint8_t* img, float* simg, int pg0, int pp0, int pg1) {
+        if (paged) issue_as(std::true_type{}, s, img, simg, pg0, pp0, pg1);
+        else issue_as(std::false_type{}, s, img, simg, pg0, pp0, pg1);
+      };
+      // raw fragments of blocks 2j, 2j+1 (keys r = 48 - 16 b + column) from an image
+      auto read2 = [&](const uint8_t* img, const float* simg, int j, typename O::raw* rw, float* ks2) {
+        const int ln = lane_fresh();
+        const int c = ln & 15, g = ln >> 4;
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const int r = 48 - 16 * (2 * j + bb) + c;
+          const uint8_t* row = img + wave * 64 * KBY + r * KBY;
+          if constexpr (KBY == 128) {
+            const v4i lo4 = *reinterpret_cast<const v4i*>(row + 16 * ((2 * g) ^ (r % 8)));
+            const v4i hi4 = *reinterpret_cast<const v4i*>(row + 16 * ((2 * g + 1) ^ (r % 8)));
+            rw[bb] = typename O::raw{lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+          } else {
+            const v4i lo4 = *reinterpret_cast<const v4i*>(row + 16 * (g ^ (r % CPK)));
+            rw[bb] = typename O::raw{lo4[0], lo4[1], lo4[2], lo4[3], 0, 0, 0, 0};
+          }
+          ks2[bb] = HasKScale<C>::value ? simg[wave * 64 + r] : 1.f;
+        }
+      };
+      // candidates of step sp (scores saved in opend, key scales still in
+      // that step's image)
+      auto append_step = [&](int sp, const float* psimg) {
+        int lo, hi;
+        const int base = step_base(sp, lo, hi);
+        const int ln = lane_fresh();
+        const int c = ln & 15;
+        int keys[4];
+        bool v[4];
+        float ks[4], o[4];
+        const v4f o4 = opend[wave * 64 + ln];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          keys[b] = base + 48 - 16 * b + c;
+          v[b] = keys[b] >= lo;
+          ks[b] = psimg[wave * 64 + 48 - 16 * b + c];
+          o[b] = o4[b];
+        }
+        sc.template append4<true>(p, gr, region, o, ks, keys, v, shist);
+      };
+      // Step s from image (img, simg).  The previous step's candidates are
+      // appended first and the next step's loads go out after them, into the
+      // image the previous step used: the wait at the top of the following
+      // step then finds both the loads and the candidate stores a whole step
+      // old (loads and stores may complete in any order relative to each
+      // other, so that wait covers both).
+      auto do_step = [&](int s, const uint8_t* img, const float* simg, uint8_t* nimg, float* nsimg, int npg0,
+                         int npp0, int npg1) {
+        wait_vmem();   // this step's direct loads and the previous step's candidate stores
+        if (s - kTileWaves >= wave) {
+          if ((++nstep & 3) == 0) sc.refresh_theta(p.topk);
+          append_step(s - kTileWaves, nsimg);
+        }
+        if (s + kTileWaves < ns) issue(s + kTileWaves, nimg, nsimg, npg0, npp0, npg1);
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          typename O::raw rw[2];
+          float ks2[2];
+          read2(img, simg, j, rw, ks2);
+          typename O::frag B[2][SC::STEPS];
+#pragma unroll
+          for (int b = 0; b < 2; ++b) O::from_raw(rw[b], B[b]);
+          sc.template scoreN<2>(B, o + 2 * j);
+        }
+        opend[wave * 64 + lane_fresh()] = v4f{o[0], o[1], o[2], o[3]};
+      };
+      // page entries run two steps ahead of the scoring, the key rows one
+      int pa0 = 0, qa0 = 0, pa1 = 0, pb0 = 0, qb0 = 0, pb1 = 0;
+      if (wave < ns) {
+        if (paged) step_pages(wave, pa0, qa0, pa1);
+        issue(wave, kimg0, simg0, pa0, qa0, pa1);
+      }
+      if (paged && wave + kTileWaves < ns) step_pages(wave + kTileWaves, pb0, qb0, pb1);
+      int last = -1;   // the last step scored, whose candidates are still to append
+#pragma unroll 1
+      for (int s = wave; s < ns; s += 2 * kTileWaves) {
+        // even step s from image 0; step s + 8 goes to image 1
+        int pc0 = 0, qc0 = 0, pc1 = 0;
+        if (paged && s + 2 * kTileWaves < ns) step_pages(s + 2 * kTileWaves, pc0, qc0, pc1);
+        do_step(s, kimg0, simg0, kimg1, simg1, pb0, qb0, pb1);
+        last = s;
+        if (s + kTileWaves >= ns) break;
+        // odd step s + 8 from image 1; step s + 16 goes to image 0
+        int pd0 = 0, qd0 = 0, pd1 = 0;
+        if (paged && s + 3 * kTileWaves < ns) step_pages(s + 3 * kTileWaves, pd0, qd0, pd1);
+        do_step(s + kTileWaves, kimg1, simg1, kimg0, simg0, pc0, qc0, pc1);
+        last = s + kTileWaves;
+        pb0 = pd0; qb0 = qd0; pb1 = pd1;
+      }
+      if (last >= 0) {
+        wait_vmem();
+        append_step(last, ((last - wave) / kTileWaves) % 2 == 0 ? simg0 : simg1);
+      }
+      sc.close(p, gr, region, shist);
+      sc.finish(p, region);
+      return;
+    }
     if (!it.gather) {
       // range walk with the next step's key bytes in flight while the current
       // step is scored (half steps of two 16-key blocks, as the list kernel)
