@@ -149,6 +149,13 @@ struct Plan {
   std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed, tiled-survivor, list-survivor items
   std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items, probe_items,
       x_items;                       // DoSA with extra seed keys: their scoring items (regions Js..Js+X-1)
+  // DoSA in two rounds (DOSA_TWO_ROUNDS, calls with query tiles): each round's
+  // groups (bounded range: round 1 the newer half, round 2 the older half),
+  // round 2's bound items and survivor items (regions Js+X+J..Js+X+2J-1)
+  bool two_rounds = false;
+  std::vector<GroupInfo> groups_r1, groups_r2;
+  std::vector<WorkItem> bound_items2, surv_tiled_items2, surv_list_items2;
+  size_t o_groups1 = 0, o_groups2 = 0;
   bool probe = false;                // DoSA: plan the last tile first, score densely if it cannot prune
   int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0, Jp = 0;
   int bound_gpw = 1;                 // query groups per wavefront of the tiled bound kernel
@@ -534,17 +541,16 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     // A bound workgroup takes 4/QW consecutive tiles of one sequence with the
     // same first bounded key, so its wavefronts hold 4 queries each; its key
     // range runs to the longest of their bounded ranges.
-    if (P.tiled) {
-      P.bound_gpw = 4 / P.QW;
+    auto make_bound_items = [&](const std::vector<GroupInfo>& gs, std::vector<WorkItem>& out) {
       struct BlockInfo { int first, n, lo, hi; };
       std::vector<BlockInfo> blocks;
       for (size_t ti = 0; ti < tiles.size(); ++ti) {
         const TileInfo& t = tiles[ti];
-        const GroupInfo& g = P.groups[t.first];
+        const GroupInfo& g = gs[t.first];
         const int lo = g.bound_lo, hi = g.bound_lo + g.n_bounded;
         if (!blocks.empty()) {
           BlockInfo& bk = blocks.back();
-          const GroupInfo& h = P.groups[bk.first];
+          const GroupInfo& h = gs[bk.first];
           if (h.seq == g.seq && h.bound_lo == lo && bk.n + t.n <= TW * P.bound_gpw &&
               bk.first + bk.n == t.first) {
             bk.n += t.n;
@@ -558,6 +564,7 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       int64_t bsum_t = 0;
       for (const auto& bk : blocks) bsum_t += bk.hi - bk.lo;
       const int Jb = choose_splits(NB, NB ? bsum_t / NB : 0, 4 * tiled_target, 2048);
+      const size_t first = out.size();
       for (const auto& bk : blocks) {
         for (int r = 0; r < Jb; ++r) {
           int lo, hi;
@@ -568,10 +575,44 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
           it.pad = bk.n;
           it.a0 = lo; it.a1 = hi;
           it.b0 = r;
-          P.bound_items.push_back(it);
+          out.push_back(it);
         }
       }
-      longest_first(P.bound_items, 0);
+      longest_first(out, first);
+    };
+    if (P.tiled) {
+      P.bound_gpw = 4 / P.QW;
+      P.two_rounds = (cfg.flags & DOSA_TWO_ROUNDS) != 0;
+      if (!P.two_rounds) {
+        make_bound_items(P.groups, P.bound_items);
+      } else {
+        // Two rounds: round 1 bounds the newer half of each tile's bounded
+        // range with the seed threshold and scores its survivors; the K-th
+        // largest exact score of the seed and round-1 candidates then becomes
+        // the threshold of round 2 over the older half.  The split is a
+        // multiple of 64 keys from the range's start (the bound kernels'
+        // alignment); both rounds share the tile's list area.
+        P.groups_r1 = P.groups;
+        P.groups_r2 = P.groups;
+        for (int gi = 0; gi < G; ++gi) {
+          const GroupInfo& g = P.groups[gi];
+          const int half = g.n_bounded > 0 ? (g.n_bounded / 2) / 64 * 64 : 0;
+          P.groups_r1[gi].bound_lo = g.bound_lo + half;
+          P.groups_r1[gi].n_bounded = g.n_bounded - half;
+          P.groups_r2[gi].n_bounded = half;
+        }
+        make_bound_items(P.groups_r1, P.bound_items);
+        make_bound_items(P.groups_r2, P.bound_items2);
+        for (WorkItem it : P.surv_tiled_items) {
+          it.region += P.J;
+          P.surv_tiled_items2.push_back(it);
+        }
+        for (WorkItem it : P.surv_list_items) {
+          it.region += P.J;
+          P.surv_list_items2.push_back(it);
+        }
+        P.R = (Js + X + 2 * P.J) * P.RW;
+      }
     }
     // probe: with enough tiles, the last tile (longest contexts) is seeded and
     // planned first; if its certificate can prune no query, the call scores
@@ -609,6 +650,9 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
     P.items.insert(P.items.end(), P.bound_items.begin(), P.bound_items.end());
     P.items.insert(P.items.end(), P.dense_items.begin(), P.dense_items.end());
+    P.items.insert(P.items.end(), P.bound_items2.begin(), P.bound_items2.end());
+    P.items.insert(P.items.end(), P.surv_tiled_items2.begin(), P.surv_tiled_items2.end());
+    P.items.insert(P.items.end(), P.surv_list_items2.begin(), P.surv_list_items2.end());
     P.items.insert(P.items.end(), P.x_items.begin(), P.x_items.end());
     P.items.insert(P.items.end(), P.probe_items.begin(), P.probe_items.end());
     P.list_total = loff;
@@ -659,6 +703,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   P.o_groups = take(sizeof(GroupInfo) * std::max(G, 1));
   P.o_items = take(sizeof(WorkItem) * std::max<size_t>(P.items.size(), 1));
   if (!dense) P.o_seqinfo = take((size_t)2 * (batch + 1) * sizeof(int32_t));   // cu_kv, cu_blk: copied with the plan
+  if (P.two_rounds) {   // the two rounds' group tables, copied with the plan too
+    P.o_groups1 = take(sizeof(GroupInfo) * std::max(G, 1));
+    P.o_groups2 = take(sizeof(GroupInfo) * std::max(G, 1));
+  }
   P.o_cand = take((size_t)P.total_q * P.R * P.cap * sizeof(u64));
   P.o_counts = take((size_t)P.total_q * P.R * sizeof(uint32_t));
   const int LS = 16 / P.QW;   // weighted-query terms per query
@@ -942,7 +990,9 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   // so one copy at the start costs one such wait instead of one per array.
   {
     const size_t n_items = sizeof(WorkItem) * P.items.size();
-    const size_t end = dense ? P.o_items + n_items : P.o_seqinfo + (size_t)2 * (batch + 1) * sizeof(int32_t);
+    const size_t end = dense ? P.o_items + n_items
+                       : (P.two_rounds ? P.o_groups2 + sizeof(GroupInfo) * P.groups.size()
+                                       : P.o_seqinfo + (size_t)2 * (batch + 1) * sizeof(int32_t));
     std::vector<char> stage(end - P.o_groups, 0);
     std::memcpy(stage.data(), P.groups.data(), sizeof(GroupInfo) * P.groups.size());
     std::memcpy(stage.data() + (P.o_items - P.o_groups), P.items.data(), n_items);
@@ -954,6 +1004,10 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       for (int b = 0; b < batch; ++b) {
         cu[b + 1] = cu[b] + kv_lens[b];
         cub[b + 1] = cub[b] + (kv_lens[b] + kKeyBlock - 1) / kKeyBlock;
+      }
+      if (P.two_rounds) {
+        std::memcpy(stage.data() + (P.o_groups1 - P.o_groups), P.groups_r1.data(), sizeof(GroupInfo) * P.groups.size());
+        std::memcpy(stage.data() + (P.o_groups2 - P.o_groups), P.groups_r2.data(), sizeof(GroupInfo) * P.groups.size());
       }
     }
     e = hipMemcpyAsync(ws + P.o_groups, stage.data(), stage.size(), hipMemcpyHostToDevice, stream);
@@ -1020,9 +1074,13 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* list_len = reinterpret_cast<int32_t*>(ws + P.o_listlen);
     int32_t* gflags = reinterpret_cast<int32_t*>(ws + P.o_gflags);
     int32_t* prunes = reinterpret_cast<int32_t*>(ws + P.o_flag);   // cleared by the prep kernel
+    // device item order (the order of P.items): seed, tiled survivors, list survivors, bound,
+    // dense, round-2 bound, round-2 tiled survivors, round-2 list survivors, extra seed, probe
     const size_t off_surv = P.seed_items.size(), off_list = off_surv + P.surv_tiled_items.size(),
                  off_bound = off_list + P.surv_list_items.size(), off_dense = off_bound + P.bound_items.size(),
-                 off_x = off_dense + P.dense_items.size(), off_probe = off_x + P.x_items.size();
+                 off_bound2 = off_dense + P.dense_items.size(), off_surv2 = off_bound2 + P.bound_items2.size(),
+                 off_list2 = off_surv2 + P.surv_tiled_items2.size(),
+                 off_x = off_list2 + P.surv_list_items2.size(), off_probe = off_x + P.x_items.size();
     int32_t* mode = P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr;
     // 1b. probe: seed pass, threshold and plan of the last tile only, then the
     //     decision whether the call runs the certificate pipeline or dense scoring
@@ -1192,115 +1250,157 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       if (e == hipSuccess) e = launch_key_blocks(P.combo, d, nl, cs);
     }
     if (e != hipSuccess) return fail_hip(e, "key norm kernel launch");
-    // 5. bound pass -> survivor bitmasks
-    BoundLaunch bl{};
-    bl.mode = mode;
-    bl.run_if = MODE_PRUNED;
-    bl.in = in;
-    bl.groups = dg;
-    bl.n_groups = G;
-    bl.rows = ws + P.o_rows;
-    bl.coef = coef;
-    bl.norms = norms;
-    bl.masks = masks;
-    bl.mask_words = std::max(P.mask_words, 1);
-    bl.debug_ub = cfg.debug_ub;
-    bl.debug_ld = max_kv;
-    bl.debug_mask = reinterpret_cast<unsigned long long*>(cfg.debug_mask);
-    bl.debug_mask_ld = (max_kv + 63) / 64;
-    if (key_blocks) {
-      bl.blk_code = reinterpret_cast<const uint8_t*>(ws + P.o_blk_code);
-      bl.blk_info = reinterpret_cast<const float*>(ws + P.o_blk_info);
-    }
-    bl.splits = P.bound_splits;
-    if (!P.bound_items.empty()) {
-      bl.items = di + off_bound;
-      bl.n_items = (int)P.bound_items.size();
-      bl.groups_per_wave = P.bound_gpw;
-    }
-    bl.stats = st;
-    {
-      PassScope ps(P_BOUND, cs);
-      e = launch_bound(P.combo, H, d, bl, cs);
-    }
-    if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
-    // 6. compaction -> survivor key lists
-    CompactLaunch cl{};
-    cl.groups = dg;
-    cl.tiles = di;                    // the seed items: Js per tile, the first names the tile
-    cl.tile_stride = P.Js;
-    cl.n_tiles = P.n_tiles;
-    cl.allow_union = P.tiled ? 1 : 0;
-    cl.coef = coef;
-    cl.masks = masks;
-    cl.mask_words = std::max(P.mask_words, 1);
-    cl.lists = lists;
-    cl.list_len = list_len;
-    cl.list_start = list_start;
-    cl.group_flags = gflags;
-    cl.cb = cb;
-    cl.r0 = P.Js * P.RW;                       // the extra seed regions too
-    cl.r1 = (P.Js + P.X + P.J) * P.RW;
-    cl.mode = mode;
-    cl.run_if = MODE_PRUNED;
-    {
-      PassScope ps(P_COMPACT, cs);
-      e = launch_compact(cl, cs);
-    }
-    if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
-    // 7. survivors scored with all heads into regions Js..Js+J-1, threshold starts at tau:
-    //    flagged tiles take the tiled kernel over their union list (or, in calls
-    //    without tiles, over the bounded range), the other groups walk their own lists
-    ScoreLaunch ml{};
-    ml.theta_share = tshare;
-    ml.mode = mode;
-    ml.run_if = MODE_PRUNED;
-    ml.in = in;
-    ml.lrows = pr.rows;
-    ml.lsig = pr.sig;
-    ml.groups = dg;
-    ml.cb = cb;
-    ml.theta_init = tau;
-    ml.lists = lists;
-    ml.list_len = list_len;
-    ml.list_start = list_start;
-    ml.topk = topk;
-    ml.stats = st;
-    ml.scored_slot = 4;
-    ml.tile_flags = gflags;
-    ml.role = ROLE_SURVIVORS;
-    {
-      PassScope ps(P_SURV_TILES, cs);
-      ml.items = di + off_surv;
-      ml.n_items = (int)P.surv_tiled_items.size();
-      ml.tiled = P.tiled ? 1 : 2;
-      ml.flag_mode = 1;
-      if (!P.tiled) {   // survivor range items of groups scored whole: disjoint sweeps
-        ml.theta_part = tpart;
-        ml.part_stride = P.n_parts;
-        ml.part_base = P.Js;
-        ml.part_rbase = P.Js + P.X;
+    // 5.-7. bound pass, compaction and survivor scoring: one round over every
+    //    bounded key, or (two rounds) the newer half of each tile's bounded
+    //    range, a raised threshold, then the older half
+    auto round = [&](const GroupInfo* rg, size_t boff, size_t nb, size_t soff, size_t ns, size_t loff, size_t nl,
+                     int r0, int r1, bool first) -> int {
+      // 5. bound pass -> survivor bitmasks
+      BoundLaunch bl{};
+      bl.mode = mode;
+      bl.run_if = MODE_PRUNED;
+      bl.in = in;
+      bl.groups = rg;
+      bl.n_groups = G;
+      bl.rows = ws + P.o_rows;
+      bl.coef = coef;
+      bl.norms = norms;
+      bl.masks = masks;
+      bl.mask_words = std::max(P.mask_words, 1);
+      bl.debug_ub = cfg.debug_ub;
+      bl.debug_ld = max_kv;
+      bl.debug_mask = reinterpret_cast<unsigned long long*>(cfg.debug_mask);
+      bl.debug_mask_ld = (max_kv + 63) / 64;
+      if (key_blocks) {
+        bl.blk_code = reinterpret_cast<const uint8_t*>(ws + P.o_blk_code);
+        bl.blk_info = reinterpret_cast<const float*>(ws + P.o_blk_info);
       }
-      // union shares are cut on the device: launch them longest first
-      if (P.tiled && ml.n_items > 0 && ml.n_items <= kMaxOrderItems) {
-        OrderLaunch ol{ml.items, ml.n_items, list_len, gflags, reinterpret_cast<int32_t*>(ws + P.o_order), mode,
-                       MODE_PRUNED};
-        e = launch_order(ol, cs);
-        ml.order = ol.order;
+      bl.splits = P.bound_splits;
+      bl.count_skipped = first ? 1 : 0;
+      if (nb > 0) {
+        bl.items = di + boff;
+        bl.n_items = (int)nb;
+        bl.groups_per_wave = P.bound_gpw;
       }
-      if (e == hipSuccess) e = launch_score(P.combo, H, d, ml, cs);
+      bl.stats = st;
+      {
+        PassScope ps(P_BOUND, cs);
+        e = launch_bound(P.combo, H, d, bl, cs);
+      }
+      if (e != hipSuccess) return fail_hip(e, "bound kernel launch");
+      // 6. compaction -> survivor key lists
+      CompactLaunch cl{};
+      cl.groups = rg;
+      cl.tiles = di;                    // the seed items: Js per tile, the first names the tile
+      cl.tile_stride = P.Js;
+      cl.n_tiles = P.n_tiles;
+      cl.allow_union = P.tiled ? 1 : 0;
+      cl.coef = coef;
+      cl.masks = masks;
+      cl.mask_words = std::max(P.mask_words, 1);
+      cl.lists = lists;
+      cl.list_len = list_len;
+      cl.list_start = list_start;
+      cl.group_flags = gflags;
+      cl.cb = cb;
+      cl.r0 = r0;
+      cl.r1 = r1;
+      cl.mode = mode;
+      cl.run_if = MODE_PRUNED;
+      {
+        PassScope ps(P_COMPACT, cs);
+        e = launch_compact(cl, cs);
+      }
+      if (e != hipSuccess) return fail_hip(e, "compact kernel launch");
+      // 7. survivors scored with all heads into the round's regions, threshold starts at tau:
+      //    flagged tiles take the tiled kernel over their union list (or, in calls
+      //    without tiles, over the bounded range), the other groups walk their own lists
+      ScoreLaunch ml{};
+      ml.theta_share = tshare;
+      ml.mode = mode;
+      ml.run_if = MODE_PRUNED;
+      ml.in = in;
+      ml.lrows = pr.rows;
+      ml.lsig = pr.sig;
+      ml.groups = rg;
+      ml.cb = cb;
+      ml.theta_init = tau;
+      ml.lists = lists;
+      ml.list_len = list_len;
+      ml.list_start = list_start;
+      ml.topk = topk;
+      ml.stats = st;
+      ml.scored_slot = 4;
+      ml.tile_flags = gflags;
+      ml.role = ROLE_SURVIVORS;
+      {
+        PassScope ps(P_SURV_TILES, cs);
+        ml.items = di + soff;
+        ml.n_items = (int)ns;
+        ml.tiled = P.tiled ? 1 : 2;
+        ml.flag_mode = 1;
+        if (!P.tiled) {   // survivor range items of groups scored whole: disjoint sweeps
+          ml.theta_part = tpart;
+          ml.part_stride = P.n_parts;
+          ml.part_base = P.Js;
+          ml.part_rbase = P.Js + P.X;
+        }
+        // union shares are cut on the device: launch them longest first
+        if (P.tiled && ml.n_items > 0 && ml.n_items <= kMaxOrderItems) {
+          OrderLaunch ol{ml.items, ml.n_items, list_len, gflags, reinterpret_cast<int32_t*>(ws + P.o_order), mode,
+                         MODE_PRUNED};
+          e = launch_order(ol, cs);
+          ml.order = ol.order;
+        }
+        if (e == hipSuccess) e = launch_score(P.combo, H, d, ml, cs);
+      }
+      if (e == hipSuccess) {
+        PassScope ps(P_SURV_LISTS, cs);
+        ml.theta_part = nullptr;
+        ml.order = nullptr;
+        ml.items = di + loff;
+        ml.n_items = (int)nl;
+        ml.tiled = P.tiled ? 0 : 2;
+        ml.flag_mode = 2;
+        ml.scored_slot2 = 8;
+        e = launch_score(P.combo, H, d, ml, cs);
+      }
+      if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
+      return DOSA_OK;
+    };
+    if (!P.two_rounds) {
+      const int rc = round(dg, off_bound, P.bound_items.size(), off_surv, P.surv_tiled_items.size(), off_list,
+                           P.surv_list_items.size(), P.Js * P.RW, (P.Js + P.X + P.J) * P.RW, true);   // r0: the extra seed regions too
+      if (rc != DOSA_OK) return rc;
+    } else {
+      const GroupInfo* dg1 = reinterpret_cast<const GroupInfo*>(ws + P.o_groups1);
+      const GroupInfo* dg2 = reinterpret_cast<const GroupInfo*>(ws + P.o_groups2);
+      int rc = round(dg1, off_bound, P.bound_items.size(), off_surv, P.surv_tiled_items.size(), off_list,
+                     P.surv_list_items.size(), P.Js * P.RW, (P.Js + P.X + P.J) * P.RW, true);
+      if (rc != DOSA_OK) return rc;
+      // the raised threshold: K-th largest score of the seed and round-1
+      // candidates (distinct keys, each exactly scored), into tau and the
+      // plan's threshold slot of every query; the merged regions keep the
+      // K entries at or above it
+      SelectLaunch t2{};
+      t2.mode = mode;
+      t2.run_if = MODE_PRUNED;
+      t2.cb = cb;
+      t2.total_q = (int32_t)P.total_q;
+      t2.topk = topk;
+      t2.r0 = 0;
+      t2.r1 = (P.Js + P.X + P.J) * P.RW;
+      t2.tau_out = tau;
+      t2.coef_tau = coef;
+      {
+        PassScope ps(P_SELECT_SEED, cs);
+        e = launch_select(t2, cs);
+      }
+      if (e != hipSuccess) return fail_hip(e, "round threshold select kernel launch");
+      rc = round(dg2, off_bound2, P.bound_items2.size(), off_surv2, P.surv_tiled_items2.size(), off_list2,
+                 P.surv_list_items2.size(), (P.Js + P.X + P.J) * P.RW, (P.Js + P.X + 2 * P.J) * P.RW, false);
+      if (rc != DOSA_OK) return rc;
     }
-    if (e == hipSuccess) {
-      PassScope ps(P_SURV_LISTS, cs);
-      ml.theta_part = nullptr;
-      ml.items = di + off_list;
-      ml.n_items = (int)P.surv_list_items.size();
-      ml.tiled = P.tiled ? 0 : 2;
-      ml.flag_mode = 2;
-      ml.scored_slot2 = 8;
-      e = launch_score(P.combo, H, d, ml, cs);
-    }
-    if (e != hipSuccess) return fail_hip(e, "survivor score kernel launch");
     // 8. the dense alternative, run only when the probe found nothing to prune
     if (P.probe) {
       ScoreLaunch dl{};
@@ -1335,7 +1435,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   se.total_q = (int32_t)P.total_q;
   se.topk = topk;
   se.r0 = 0;
-  se.r1 = dense ? P.R : (P.Js + P.X + P.J) * P.RW;   // pruned path: seed, (cleared) extra seed, survivor regions
+  se.r1 = dense ? P.R : (P.Js + P.X + (P.two_rounds ? 2 : 1) * P.J) * P.RW;   // pruned path: seed, (cleared) extra seed, survivor regions
   se.out_idx = out_idx;
   se.out_score = out_score;
   se.tau_out = nullptr;

@@ -168,6 +168,7 @@ struct SelectLaunch {
   float* out_score;
   float* tau_out;            // K-th score per query (-inf if fewer than K), or NULL
   float* tau_copy;           // a second copy of tau_out (the caller's debug array), or NULL
+  float* coef_tau;           // plan coefficients whose threshold slot (coef[5]) takes tau too, or NULL
   int32_t sorted;
   unsigned long long* stats;
   int32_t q_first;           // rows q_first .. q_first + total_q - 1
@@ -232,6 +233,7 @@ struct BoundLaunch {
                              // pad = groups, [a0, a1) keys, b0 = share index; NULL = per-group kernel
   int32_t n_items;
   int32_t groups_per_wave;   // tiled kernel: 4 / (queries per group)
+  int32_t count_skipped;     // 1: skipped groups are counted (stats slot 7); 0 in a call's second round
   unsigned long long* stats;
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;

@@ -113,12 +113,16 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
   constexpr int VPC = 16 / KBY;               // values per chunk
   const int t = threadIdx.x;
   const int sub = t % CH;
-  const int first = blockIdx.x * KPB * kNormIter + t / CH;
 #pragma unroll 1
   for (int b = blockIdx.y; b < p.batch; b += gridDim.y) {   // grid.y is capped at 65535
   const int base = p.cu_kv[b];
   const int n = p.cu_kv[b + 1] - base;
-  if (blockIdx.x * KPB * kNormIter >= n) continue;
+  // blocks of KPB * kNormIter keys, strided over grid.x (capped, so that a
+  // batch of short and long sequences does not launch a workgroup per block
+  // of the longest one for every sequence)
+#pragma unroll 1
+  for (int bx = blockIdx.x; bx * KPB * kNormIter < n; bx += gridDim.x) {
+  const int first = bx * KPB * kNormIter + t / CH;
   uint4 v[kNormIter];
   int64_t rows[kNormIter];
 #pragma unroll
@@ -145,6 +149,7 @@ __global__ __launch_bounds__(256) void key_norm_kernel(const NormLaunch p) {
       if constexpr (HasKScale<C>::value) nv *= p.in.k_scale[rows[it]];
       p.norms[(int64_t)base + first + it * KPB] = nv * 1.0000153f;   // covers the fp32 sum/sqrt/scale rounding (<< 2^-16)
     }
+  }
   }
   }
 }
@@ -864,7 +869,7 @@ __global__ __launch_bounds__(64) void bound_kernel(const BoundLaunch p) {
       const u64 all = (u64)n_all * (u64)gr.nq;
       atomicAdd(&p.stats[2], all);
       atomicAdd(&p.stats[3], all);
-      atomicAdd(&p.stats[7], 1ull);
+      if (p.count_skipped) atomicAdd(&p.stats[7], 1ull);
     }
     if (p.debug_ub == nullptr && p.debug_mask == nullptr) return;
   }
@@ -992,7 +997,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void bound_tiled_kernel(const Boun
     const u64 all = (u64)gr.n_bounded * (u64)gr.nq;   // the group's first share counts the whole group
     atomicAdd(&p.stats[2], all);
     atomicAdd(&p.stats[3], all);
-    atomicAdd(&p.stats[7], 1ull);
+    if (p.count_skipped) atomicAdd(&p.stats[7], 1ull);
   }
   // the whole workgroup leaves if no wavefront has work (and no dump is asked for)
   const bool dump = p.debug_ub != nullptr || p.debug_mask != nullptr;
@@ -1453,7 +1458,10 @@ static hipError_t norms_t(const NormLaunch& p, hipStream_t s) {
   constexpr int per_block = 256 / (D * KBytes<C>::value / 16) * kNormIter;
   const int nb = (int)((p.max_kv + per_block - 1) / per_block);
   if (nb == 0 || p.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL((key_norm_kernel<C, D>), dim3(nb, p.batch < 65535 ? p.batch : 65535), dim3(256), 0, s, p);
+  const int gy = p.batch < 65535 ? p.batch : 65535;
+  const int gcap = 2048 / gy > 1 ? 2048 / gy : 1;
+  const int gx = nb < gcap ? nb : gcap;   // about 2048 workgroups, each striding over key blocks
+  hipLaunchKernelGGL((key_norm_kernel<C, D>), dim3(gx, gy), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

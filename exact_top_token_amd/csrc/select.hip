@@ -105,6 +105,7 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
     if (lane == 0) {
       if (p.tau_out != nullptr) p.tau_out[q] = tau;
       if (p.tau_copy != nullptr) p.tau_copy[q] = tau;
+      if (p.coef_tau != nullptr) p.coef_tau[(int64_t)q * kCoefStride + 5] = tau;
     }
     return;
   }

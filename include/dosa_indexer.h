@@ -112,6 +112,16 @@ typedef enum {
                                      (by default a call with >= 8 query tiles first seeds and plans
                                      its last tile and, if the certificate prunes no query there,
                                      scores every key densely; the result is the same either way) */
+#define DOSA_TWO_ROUNDS 0x40u     /* dosa_indexer_topk, calls with query tiles: the threshold is
+                                     refined once within the call (the DoSA transcript, Method: the
+                                     stages repeat over tiles of keys as the standings refine).
+                                     Round 1 bounds and scores the newer half of each tile's bounded
+                                     keys against the seed threshold; the K-th largest exact score
+                                     of the seed and round-1 candidates (a valid lower bound of the
+                                     K-th score: K distinct keys reach it) becomes the threshold of
+                                     round 2 over the older half.  debug_tau keeps round 1's
+                                     threshold; debug_mask bits of round-2 keys are against the
+                                     raised one */
 
 /* Knobs of dosa_indexer_topk.  None of them changes the selected set; they
  * only change how much work the certificate saves. */

@@ -26,6 +26,10 @@ Method section; the zicq.com summary, "Technical Mechanism Analysis" items
    at least tau > S), whatever the tie rule, so it is pruned.
 6. Key blocks: a block's centre, radius and largest norm give one bound that
    dominates UB for every key of the block (block_upper_bound).
+7. Refinement within a call (two_round_pruned): the stages repeat over key
+   ranges, newest first; exactly scored survivors of the first range join the
+   seed scores, and their K-th largest (K distinct keys reach it, so it still
+   lower-bounds the K-th score) is the threshold for the second range.
 
 None of the choices (seed set, proxy count, rho variant, support) affects the
 selected set as long as each bound is valid; they only change how much is
@@ -194,6 +198,37 @@ def query_certificate(q, w, k_vis, pos, K, num_proxies=3, prefix=64, window=None
     is_seed[seeds] = True
     pruned = (~is_seed) & (UB < tau)
     return {"S": S, "seeds": seeds, "tau": tau, "UB": UB, "pruned": pruned, "plan": pl}
+
+
+def two_round_pruned(cert: dict, K: int, align: int = 64):
+    """The bounded keys of one query's certificate in two rounds.
+
+    cert: a query_certificate result.  Bounded keys are the non-seed visible
+    keys, one contiguous range [lo, hi) for the seed set of seed_keys.  The
+    range splits at lo + align * floor((hi - lo) / 2 / align): round 1 takes
+    the newer keys [mid, hi) against tau and its survivors (UB >= tau) are
+    scored exactly; tau2 = K-th largest of the seed scores and those scores;
+    round 2 prunes the older keys [lo, mid) with UB < tau2.
+    Returns (pruned mask over the visible keys, tau2, mid).
+    """
+    S, UB, tau = cert["S"], cert["UB"], cert["tau"]
+    n = S.size
+    is_seed = np.zeros(n, dtype=bool)
+    is_seed[cert["seeds"]] = True
+    bounded = np.nonzero(~is_seed)[0]
+    pruned = np.zeros(n, dtype=bool)
+    if bounded.size == 0:
+        return pruned, tau, 0
+    lo, hi = int(bounded[0]), int(bounded[-1]) + 1
+    assert hi - lo == bounded.size, "bounded keys form one range"
+    mid = lo + align * (((hi - lo) // 2) // align)
+    r1 = np.arange(mid, hi)
+    pruned[r1] = UB[r1] < tau
+    surv1 = r1[~pruned[r1]]
+    tau2 = seed_threshold(np.concatenate([S[cert["seeds"]], S[surv1]]), K)
+    r2 = np.arange(lo, mid)
+    pruned[r2] = UB[r2] < tau2
+    return pruned, tau2, mid
 
 
 def filter_rate(wl, rows, **kw):

@@ -133,7 +133,7 @@ def test_survivor_shares_ragged_launch_order():
 
 
 @pytest.mark.parametrize("knob", ["p0", "p1", "p2", "w64", "w512", "cap", "noprune", "separable", "noneg",
-                                  "splits3", "frac0", "frac1", "probe", "blocks"])
+                                  "splits3", "frac0", "frac1", "probe", "blocks", "tworounds", "tworounds_probe"])
 def test_knob_invariance(knob):
     import exact_top_token_amd as E
     from exact_top_token_amd.runner import run_once
@@ -168,6 +168,10 @@ def test_knob_invariance(knob):
         cfg.neg_support_frac = 1.0
     elif knob == "blocks":
         cfg.flags |= E.DOSA_KEY_BLOCKS
+    elif knob == "tworounds":
+        cfg.flags |= E.DOSA_TWO_ROUNDS
+    elif knob == "tworounds_probe":
+        cfg.flags = (cfg.flags | E.DOSA_TWO_ROUNDS) & ~E.DOSA_NO_PROBE
     print(f"[gpu] knob {knob}", flush=True)
     pi, ps, _ = run_once(wl, "dosa", cfg=cfg, key_splits=ks)
     assert_same_selection(pi, ps, di, ds)
@@ -342,6 +346,48 @@ def test_correlated_fp8_chunked_prunes():
     idx, sc, st, ub, tau, mask = _debug_run(sub, cfg)
     assert_same_selection(idx, sc, outs["dsa"][0][c["q0"]:], outs["dsa"][1][c["q0"]:])
     assert check_debug_dumps(sub, ub, tau, mask, sample_rows(sub, 12)) > 0
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_two_rounds_raise_the_threshold_and_match(dtype):
+    """DOSA_TWO_ROUNDS: the newer half of each tile's bounded keys is bounded and scored first,
+    the K-th largest exact score so far bounds the older half.  Every chunk call equals the dense
+    path bit for bit, the same pairs are bounded as with one round and no more survive (the
+    older half is bounded against a threshold at least as high), and the oracle agrees."""
+    import torch
+
+    import exact_top_token_amd as E
+    from exact_top_token_amd.runner import Runner, slice_chunk, to_device
+
+    wl = synth.correlated_heads(L=16384, dtype=dtype, chunk=4096)
+    inp = to_device(wl)
+    outs, stats = {}, {}
+    for name, path, flags in (("dense", "dsa", 0), ("one", "dosa", 0), ("two", "dosa", E.DOSA_TWO_ROUNDS)):
+        idx = np.zeros((wl.total_q, wl.topk), np.int32)
+        sc = np.zeros((wl.total_q, wl.topk), np.float32)
+        cfg = E.default_config(wl.topk)
+        cfg.flags |= E.DOSA_NO_PROBE | flags
+        cfg.seed_window = 2048
+        tot = {}
+        for c in wl.chunk_calls():
+            print(f"[gpu] two rounds {dtype} chunk {c} {name}", flush=True)
+            r = Runner(slice_chunk(inp, c["q0"], c["q_len"], c["kv_len"]), path, cfg)
+            a, b = r()
+            torch.cuda.synchronize()
+            idx[c["q0"]:c["q0"] + c["q_len"]] = a.cpu().numpy()
+            sc[c["q0"]:c["q0"] + c["q_len"]] = b.cpu().numpy()
+            for k, v in r.stats_dict().items():
+                tot[k] = tot.get(k, 0) + v
+        outs[name] = (idx, sc)
+        stats[name] = tot
+    one, two = stats["one"], stats["two"]
+    print(f"two rounds {dtype}: one round {one}", flush=True)
+    print(f"two rounds {dtype}: two rounds {two}", flush=True)
+    assert_same_selection(*outs["one"], *outs["dense"])
+    assert_same_selection(*outs["two"], *outs["dense"])
+    assert two["pairs_bounded"] == one["pairs_bounded"] > 0
+    assert two["pairs_survived"] <= one["pairs_survived"]
+    check_vs_oracle(wl, *outs["two"], sample_rows(wl, 96), verbose=True)
 
 
 def test_correlated_decode_bf16q_fp8k_prunes():

@@ -353,6 +353,33 @@ def test_pruning_never_drops_topk_tiny_prefill():
         assert np.all(c["S"][pr] < theta[j])
 
 
+@pytest.mark.parametrize("recipe", ["tiny", "correlated"])
+def test_two_round_threshold_is_valid_and_prunes_more(recipe):
+    """Two rounds (threshold raised by round-1 survivors): tau <= tau2 <= the K-th score of a
+    full sort, every key one round prunes is pruned again, and no Top-K key is pruned."""
+    if recipe == "tiny":
+        wl = synth.tiny_prefill(L=600, topk=32)
+        rows, kw = np.arange(300, 600, 41), dict(num_proxies=3, prefix=4, window=64)
+    else:
+        wl = synth.correlated_heads(L=2048, topk=64)
+        rows, kw = np.array([1500, 1800, 2047]), dict(num_proxies=3, prefix=64, window=256)
+    idx, sc, theta = indexer.topk_rows(wl, rows)
+    seq, pos = indexer.query_positions(wl)
+    gained = 0
+    for j, r in enumerate(rows):
+        kv = indexer.seq_keys(wl, 0, pos[r] + 1)
+        c = cert.query_certificate(indexer.query_rows(wl, [r])[0], indexer.weights(wl, [r])[0], kv,
+                                   int(pos[r]), wl.topk, **kw)
+        pr2, tau2, mid = cert.two_round_pruned(c, wl.topk)
+        kth = np.sort(c["S"])[::-1][wl.topk - 1]
+        assert c["tau"] <= tau2 <= kth
+        assert np.all(pr2[c["pruned"]])                    # round 2 only adds pruned keys
+        assert not np.any(np.isin(np.nonzero(pr2)[0], idx[j]))
+        assert np.all(c["S"][pr2] < theta[j])
+        gained += int(pr2.sum() - c["pruned"].sum())
+    assert gained >= 0
+
+
 def test_seed_threshold_is_lower_bound():
     rng = np.random.default_rng(50)
     for _ in range(30):
