@@ -79,6 +79,7 @@ int fail_hip(hipError_t e, const char* what) {
 // certificate stages then run one after the other.
 // ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
+constexpr int kSideStreamMaxItems = 512;   // dense work items of a call that still takes the side stream
 std::once_flag g_side_once[kMaxDevices];
 hipStream_t g_side[kMaxDevices] = {};
 hipError_t g_side_err[kMaxDevices] = {};
@@ -1137,10 +1138,16 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       if (e != hipSuccess) return fail_hip(e, "probe plan kernel launch");
     }
     // With a probe, the certificate stages (steps 2-7) go to the side stream
-    // and the dense alternative (step 8) stays on the caller's stream.
+    // and the dense alternative (step 8) stays on the caller's stream, when
+    // the dense alternative runs in at most two workgroups per CU: its
+    // workgroups then finish together and the certificate launches (which
+    // return at once after a dense decision) run in its tail.  With more
+    // rounds of dense workgroups, the certificate launches' empty workgroups
+    // (tens of thousands at a 32K-query call) interleave with them and cost
+    // more than the serial launches (32K bf16 prefill: 11.8 against 9.1 ms).
     SideFork sf;
     hipStream_t cs = stream;
-    if (P.probe) {
+    if (P.probe && P.dense_items.size() <= (size_t)kSideStreamMaxItems) {
       e = sf.open(stream);
       if (e != hipSuccess) return fail_hip(e, "side stream");
       if (sf.side != nullptr) cs = sf.side;

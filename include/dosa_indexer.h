@@ -61,7 +61,8 @@
  * workspace (size from dosa_workspace_size).  The library allocates no device
  * memory and keeps no data between calls; everything is ordered on `stream`
  * (a hipStream_t, NULL = default stream) and no call waits for the device.
- * A pruned call that runs the probe (see DOSA_NO_PROBE) forks the certificate stages onto
+ * A pruned call that runs the probe (see DOSA_NO_PROBE) and whose dense
+ * alternative fits in two workgroups per CU forks the certificate stages onto
  * a side stream the library creates once per device (default priority, kept
  * until the process ends) and joins it back into `stream` before its final
  * selection, so `stream` order covers the whole call (graph capture too).
