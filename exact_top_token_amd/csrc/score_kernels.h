@@ -818,14 +818,18 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
       // that read one chunk column of 16 rows hit different banks.
       constexpr int KBY = SC::KBYTES;               // bytes per key row
       constexpr int CPK = KBY / 16;                 // 16-byte chunks per row (= load instructions per step)
-      const int na = it.a1 > it.a0 ? (it.a1 - it.a0 + 63) / 64 : 0;
-      const int ns = na + (it.b1 > it.b0 ? (it.b1 - it.b0 + 63) / 64 : 0);
-      // step s: keys [base, base + 64) of its range, those >= lo valid
+      // Steps are the 64-key blocks of absolute key positions that meet the
+      // range, from the top down: a step lies in one page (pages hold a
+      // power of two >= 64 keys) and its rows are consecutive.
+      auto nsteps = [](int lo, int hi) { return hi > lo ? (((hi + 63) & ~63) - (lo & ~63)) / 64 : 0; };
+      const int na = nsteps(it.a0, it.a1);
+      const int ns = na + nsteps(it.b0, it.b1);
+      // step s: keys [base, base + 64), those in [lo, hi) valid
       auto step_base = [&](int s, int& lo, int& hi) -> int {
         const bool ra = s < na;
         lo = ra ? it.a0 : it.b0;
         hi = ra ? it.a1 : it.b1;
-        return hi - 64 - 64 * (ra ? s : s - na);
+        return ((hi + 63) & ~63) - 64 - 64 * (ra ? s : s - na);
       };
       const bool paged = p.in.page_table != nullptr;
       const int sh = paged ? p.in.page_shift : 0;
@@ -834,17 +838,15 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
       // waits the compiler places where they are used
       typedef __attribute__((address_space(4))) const int32_t cint;
       cint* ptab = paged ? (cint*)(p.in.page_table + (int64_t)gr.seq * p.in.max_pages) : nullptr;
-      // pool pages of a step's first and last valid keys (a step spans at
-      // most two pages of >= 64 keys); wavefront-uniform
-      // (scalar loads: a vector load here would make the wait for its value
-      // also wait for the direct loads in flight)
+      // the pool page of a step (base < hi <= kv_len: a page of the
+      // sequence), wavefront-uniform; scalar loads: a vector load here would
+      // make the wait for its value also wait for the direct loads in flight
       auto step_pages = [&](int s, int& pg0, int& pp0, int& pg1) {
         int lo, hi;
         const int base = step_base(s, lo, hi);
-        pp0 = __builtin_amdgcn_readfirstlane(max(base, lo) >> sh);
-        const int pl = __builtin_amdgcn_readfirstlane((base + 63) >> sh);
+        pp0 = __builtin_amdgcn_readfirstlane(base >> sh);
         pg0 = ptab[pp0];
-        pg1 = pl > pp0 ? ptab[pl] : pg0;
+        pg1 = pg0;
       };
       const uint8_t* kbase = static_cast<const uint8_t*>(p.in.k) + (paged ? 0 : (int64_t)gr.key_base * KBY);
       const float* sbase = p.in.k_scale + (paged ? 0 : (int64_t)gr.key_base);
@@ -853,6 +855,10 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
       // direct loads of step s's rows and scales into image `img`, scales
       // `simg`; lane l's unit in instruction i is key (64 / CPK) i + l / CPK,
       // chunk (l % CPK) ^ ((l / CPK) % CPK) (the same chunk for every i)
+      // The step's rows are consecutive: row(base + r) = row0 + r, so
+      // instruction i reads 1 KiB at row0 * KBY + 1024 i.  Steps at a
+      // range's ends clamp their keys into [lo, hi) (rows outside it are
+      // never read; clamping keeps every address inside the sequence).
       auto issue_as = [&](auto paged_t, int s, uint8_t* img, float* simg, int pg0, int pp0, int pg1) {
         constexpr bool PG = decltype(paged_t)::value;
         int lo, hi;
@@ -860,20 +866,25 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
         const uint32_t ln = (uint32_t)lane_fresh();
         const int rl = (int)(ln / CPK);
         const uint32_t ch = (ln % CPK) ^ ((uint32_t)rl % CPK);
-        const uint32_t pmask = (1u << sh) - 1u;
-        auto row_of = [&](int key) -> uint32_t {
-          if constexpr (!PG) return (uint32_t)key;
-          const uint32_t pg = (uint32_t)((key >> sh) == pp0 ? pg0 : pg1);
-          return (pg << sh) | ((uint32_t)key & pmask);
-        };
+        // row of the step's key 0 (wavefront-uniform)
+        const int64_t row0 = PG ? ((int64_t)pg0 << sh) + (base & ((1 << sh) - 1)) : (int64_t)base;
+        uint8_t* dimg = img + wave * 64 * KBY;
+        if (base >= lo && base + 64 <= hi) {
+          const uint8_t* src = kbase + (row0 + rl) * KBY + 16u * ch;
 #pragma unroll
-        for (int i = 0; i < CPK; ++i) {
-          const int key = max(base + (64 / CPK) * i + rl, lo);   // rows before the range: a valid row, never read
-          const uint8_t* src = kbase + (uint64_t)row_of(key) * KBY + 16u * ch;
-          __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(img + wave * 64 * KBY + 1024 * i), 16, 0, 0);
+          for (int i = 0; i < CPK; ++i)
+            __builtin_amdgcn_global_load_lds((gvoid*)(src + 1024 * i), (lvoid*)(dimg + 1024 * i), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((gvoid*)(sbase + row0 + ln), (lvoid*)(simg + wave * 64), 4, 0, 0);
+        } else {
+#pragma unroll
+          for (int i = 0; i < CPK; ++i) {
+            const int r = min(max(base + (64 / CPK) * i + rl, lo), hi - 1) - base;
+            const uint8_t* src = kbase + (row0 + r) * KBY + 16u * ch;
+            __builtin_amdgcn_global_load_lds((gvoid*)src, (lvoid*)(dimg + 1024 * i), 16, 0, 0);
+          }
+          const int r = min(max(base + (int)ln, lo), hi - 1) - base;
+          __builtin_amdgcn_global_load_lds((gvoid*)(sbase + row0 + r), (lvoid*)(simg + wave * 64), 4, 0, 0);
         }
-        const int key = max(base + (int)ln, lo);
-        __builtin_amdgcn_global_load_lds((gvoid*)(sbase + row_of(key)), (lvoid*)(simg + wave * 64), 4, 0, 0);
       };
       auto issue = [&](int s, uint8_t* img, float* simg, int pg0, int pp0, int pg1) {
         if (paged) issue_as(std::true_type{}, s, img, simg, pg0, pp0, pg1);
@@ -912,7 +923,7 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           keys[b] = base + 48 - 16 * b + c;
-          v[b] = keys[b] >= lo;
+          v[b] = keys[b] >= lo && keys[b] < hi;
           ks[b] = psimg[wave * 64 + 48 - 16 * b + c];
           o[b] = o4[b];
         }

@@ -68,7 +68,7 @@ def _check_block(wl, rows, gidx, gsc, rel):
             bad = err > tol
             assert not np.any(bad), (f"row {r}: score error {err[bad][:3]} > tol {tol[bad][:3]} "
                                      f"(S {S[bad][:3]}, A {A[bad][:3]})")
-            canc = np.abs(S) < CANCEL * A
+            canc = (np.abs(S) < CANCEL * A) | (A == 0)   # A = 0: every head value is 0, S = 0 exactly
             st["n_cancel"] += int(canc.sum())
             st["pairs"] += int(gv.size)
             if np.any(~canc):
