@@ -626,13 +626,13 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       P.probe_q0 = P.groups[t.first].q_row0;
       P.probe_nq = 0;
       for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
-      // the probe tile's seed window in shares of at least 256 keys (up to 32
+      // the probe tile's seed window in shares of at least 128 keys (up to 64
       // workgroups): the probe's time is its latency, with most of the GPU
       // idle; more shares score faster but give the threshold select more
       // regions to read
       const int wlo = std::max(0, t.n_last - P.W);
       const int f = std::min(P.F, wlo);
-      P.Jp = (int)std::max<int64_t>(1, std::min<int64_t>(32, (t.n_last - wlo) / 256));
+      P.Jp = (int)std::max<int64_t>(1, std::min<int64_t>(64, (t.n_last - wlo) / 128));
       for (int r = 0; r < P.Jp; ++r) {
         int lo, hi;
         range_split(wlo, t.n_last, r, P.Jp, 64, lo, hi);

@@ -443,9 +443,9 @@ __device__ __forceinline__ uint32_t select_kth_score_staged(const Segs sg, const
   const int tid = (int)threadIdx.x;
   const int lane = lane_id();
   constexpr int B = 8;
+  int r = 0;   // a thread's indices only grow, so its segment cursor only moves forward
   for (uint32_t b = 0; b < total; b += (uint32_t)NT * B) {
     uint32_t e[B];
-    int r = 0;
 #pragma unroll
     for (int u = 0; u < B; ++u) {
       const uint32_t i = b + (uint32_t)NT * u + tid;
