@@ -30,6 +30,7 @@ DOSA_NO_NEGATIVE = 0x8
 DOSA_NO_PROBE = 0x10
 DOSA_KEY_BLOCKS = 0x20
 DOSA_TWO_ROUNDS = 0x40
+DOSA_GROUP_LISTS = 0x80
 
 STATUS = {0: "DOSA_OK", -1: "DOSA_ERR_INVALID_ARG", -2: "DOSA_ERR_UNSUPPORTED", -3: "DOSA_ERR_WORKSPACE",
           -4: "DOSA_ERR_HIP"}

@@ -465,8 +465,11 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       }
       // calls with query tiles: one list area per tile, for its union list or
       // its groups' lists one after the other (compaction takes that route only
-      // when they total fewer entries than the union)
-      if (P.tiled) loff += (wlo - f + 15) / 16 * 16 + 16 * t.n;
+      // when they total fewer entries than the union, unless DOSA_GROUP_LISTS
+      // sends every tile there: then each group has room for all its keys)
+      if (P.tiled)
+        loff += (cfg.flags & DOSA_GROUP_LISTS) ? (int64_t)t.n * ((wlo - f + 15) / 16 * 16 + 16)
+                                               : (int64_t)(wlo - f + 15) / 16 * 16 + 16 * t.n;
     }
     // survivor lists: J shares per group (one wavefront each with the list
     // kernel; with the split kernel, 8 wavefronts each, so fewer shares)
@@ -1302,6 +1305,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       cl.tile_stride = P.Js;
       cl.n_tiles = P.n_tiles;
       cl.allow_union = P.tiled ? 1 : 0;
+      cl.force_lists = (cfg.flags & DOSA_GROUP_LISTS) ? 1 : 0;
       cl.coef = coef;
       cl.masks = masks;
       cl.mask_words = std::max(P.mask_words, 1);

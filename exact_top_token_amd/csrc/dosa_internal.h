@@ -245,6 +245,7 @@ struct CompactLaunch {
   int32_t tile_stride;
   int32_t n_tiles;           // grid: one workgroup per tile
   int32_t allow_union;       // 1: tiles may be routed to the tiled kernel's union lists
+  int32_t force_lists;       // 1 (with allow_union): every tile's groups get their own lists
   const float* coef;         // plan coefficients (coef[7]: hopeless flag per query)
   const unsigned long long* masks;
   int32_t mask_words;

@@ -1408,7 +1408,7 @@ __global__ __launch_bounds__(512) void compact_kernel(const CompactLaunch p) {
     if (i < wave) ubase += part[i];
   }
   bool whole;
-  if (p.allow_union) whole = (uint64_t)tn * tu <= (uint64_t)kTileGain * ts;
+  if (p.allow_union) whole = p.force_lists == 0 && (uint64_t)tn * tu <= (uint64_t)kTileGain * ts;
   else whole = (float)ts >= kDenseFrac * (float)((uint64_t)nb * (uint64_t)tn);
   // With query tiles the tile's groups share one list area of n_bounded + 16 per
   // group entries: the union list, or the groups' own lists one after the

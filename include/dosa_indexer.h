@@ -123,6 +123,17 @@ typedef enum {
                                      round 2 over the older half.  debug_tau keeps round 1's
                                      threshold; debug_mask bits of round-2 keys are against the
                                      raised one */
+#define DOSA_GROUP_LISTS 0x80u    /* dosa_indexer_topk, calls with query tiles: every tile's survivors
+                                     go to the per-group streams (each query group's own compacted
+                                     list, scored one wavefront per group; a group holds the queries
+                                     one wavefront scores together: 4 for fp8, 2 for bf16, 1 for
+                                     fp32 at H = 64, d = 128) instead of the shared stream (the
+                                     tile's union list, whose keys serve all its queries), the two
+                                     kinds of survivor stream of the DoSA transcript (Method: GPU
+                                     kernel design).  By default compaction picks the union unless
+                                     it is 8x the groups' lists together.  The result is the same
+                                     either way; the workspace reserves one list of every bounded
+                                     key per group */
 
 /* Knobs of dosa_indexer_topk.  None of them changes the selected set; they
  * only change how much work the certificate saves. */

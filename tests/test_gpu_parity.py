@@ -133,7 +133,8 @@ def test_survivor_shares_ragged_launch_order():
 
 
 @pytest.mark.parametrize("knob", ["p0", "p1", "p2", "w64", "w512", "cap", "noprune", "separable", "noneg",
-                                  "splits3", "frac0", "frac1", "probe", "blocks", "tworounds", "tworounds_probe"])
+                                  "splits3", "frac0", "frac1", "probe", "blocks", "tworounds", "tworounds_probe",
+                                  "grouplists"])
 def test_knob_invariance(knob):
     import exact_top_token_amd as E
     from exact_top_token_amd.runner import run_once
@@ -172,6 +173,8 @@ def test_knob_invariance(knob):
         cfg.flags |= E.DOSA_TWO_ROUNDS
     elif knob == "tworounds_probe":
         cfg.flags = (cfg.flags | E.DOSA_TWO_ROUNDS) & ~E.DOSA_NO_PROBE
+    elif knob == "grouplists":
+        cfg.flags |= E.DOSA_GROUP_LISTS | E.DOSA_TWO_ROUNDS
     print(f"[gpu] knob {knob}", flush=True)
     pi, ps, _ = run_once(wl, "dosa", cfg=cfg, key_splits=ks)
     assert_same_selection(pi, ps, di, ds)
@@ -346,6 +349,35 @@ def test_correlated_fp8_chunked_prunes():
     idx, sc, st, ub, tau, mask = _debug_run(sub, cfg)
     assert_same_selection(idx, sc, outs["dsa"][0][c["q0"]:], outs["dsa"][1][c["q0"]:])
     assert check_debug_dumps(sub, ub, tau, mask, sample_rows(sub, 12)) > 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_group_lists_match_the_union_route(dtype):
+    """DOSA_GROUP_LISTS sends every tile's survivors to per-group streams (4 queries per group
+    for fp8, 2 for bf16, 1 for fp32 at H = 64, d = 128) instead of the tile's shared union
+    list: both routes return the dense path's selection bit for bit, the forced route scores
+    its survivors from the group lists, and it never scores more pairs than the union does."""
+    import exact_top_token_amd as E
+    from exact_top_token_amd.runner import run_once
+
+    wl = synth.correlated_heads(L=6144, topk=256, dtype=dtype)
+    di, ds, _ = run_once(wl, "dsa")
+    out = {}
+    for name, extra in (("union", 0), ("lists", E.DOSA_GROUP_LISTS)):
+        cfg = E.default_config(wl.topk)
+        cfg.seed_window = 1024
+        cfg.flags |= E.DOSA_NO_PROBE | extra
+        print(f"[gpu] group lists {dtype} {name}", flush=True)
+        pi, ps, pst = run_once(wl, "dosa", cfg=cfg)
+        assert_same_selection(pi, ps, di, ds)
+        out[name] = pst
+    print("union route", out["union"], "\nlist route", out["lists"], flush=True)
+    u, g = out["union"], out["lists"]
+    assert u["pairs_survived"] == g["pairs_survived"] and u["pairs_bounded"] == g["pairs_bounded"]
+    assert g["pairs_survived"] < g["pairs_bounded"], "the certificate should prune"
+    assert g["pairs_scored_list"] == g["pairs_scored"] > 0
+    assert g["pairs_scored"] <= u["pairs_scored"]
+    check_vs_oracle(wl, di, ds, sample_rows(wl, 16))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
