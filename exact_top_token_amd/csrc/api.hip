@@ -148,7 +148,7 @@ struct Plan {
   int64_t total_q = 0, total_k = 0;
   std::vector<GroupInfo> groups;
   std::vector<WorkItem> items;       // dense: scoring items; DoSA: seed, tiled-survivor, list-survivor items
-  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items, probe_items,
+  std::vector<WorkItem> seed_items, surv_tiled_items, surv_list_items, bound_items, dense_items,
       x_items;                       // DoSA with extra seed keys: their scoring items (regions Js..Js+X-1)
   // DoSA in two rounds (DOSA_TWO_ROUNDS, calls with query tiles): each round's
   // groups (bounded range: round 1 the newer half, round 2 the older half),
@@ -158,7 +158,7 @@ struct Plan {
   std::vector<WorkItem> bound_items2, surv_tiled_items2, surv_list_items2;
   size_t o_groups1 = 0, o_groups2 = 0;
   bool probe = false;                // DoSA: plan the last tile first, score densely if it cannot prune
-  int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0, Jp = 0;
+  int probe_group = 0, probe_ngroups = 0, probe_q0 = 0, probe_nq = 0, Jd = 0;
   int bound_gpw = 1;                 // query groups per wavefront of the tiled bound kernel
   bool tiled = true;
   int RW = 1;                        // candidate regions per item region: 1, or kTileWaves for the split
@@ -169,7 +169,6 @@ struct Plan {
   int n_parts = 0;                   // split-threshold slots per query (tiled dense / seed launches)
   int64_t x_stride = 0;              // entries per group of the extra seed lists
   int n_tiles = 0;                   // query tiles (seed items 0 .. n_tiles*Js-1 are Js per tile, tile order)
-  int pcap = 0;                      // probe: entries per region of its own candidate buffer
   int mask_words = 0;
   int64_t list_total = 0;
   int64_t n_blocks = 0;              // 64-key blocks of all sequences (key-block summaries)
@@ -177,7 +176,7 @@ struct Plan {
   size_t o_groups = 0, o_items = 0, o_cand = 0, o_counts = 0, o_tau = 0, o_rows = 0, o_coef = 0,
          o_norms = 0, o_masks = 0, o_lists = 0, o_listlen = 0, o_seqinfo = 0, o_gflags = 0, o_flag = 0,
          o_lrows = 0, o_lsig = 0, o_lerr = 0, o_mode = 0, o_tshare = 0, o_order = 0, o_blk_code = 0, o_blk_info = 0,
-         o_liststart = 0, o_pcand = 0, o_pcounts = 0, o_xlists = 0, o_xlen = 0, o_tpart = 0, total = 0;
+         o_liststart = 0, o_xlists = 0, o_xlen = 0, o_tpart = 0, total = 0;
   uint64_t pairs_total = 0;
 };
 
@@ -618,9 +617,9 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         P.R = (Js + X + 2 * P.J) * P.RW;
       }
     }
-    // probe: with enough tiles, the last tile (longest contexts) is seeded and
-    // planned first; if its certificate can prune no query, the call scores
-    // every tile densely with the dense path's items (regions 0..Jd-1)
+    // probe: with enough tiles, the last tile (longest contexts) is planned
+    // first; if its certificate can prune no query, the call scores every
+    // tile densely with the dense path's items (regions 0..Jd-1)
     if (P.tiled && NT >= 8 && (cfg.flags & DOSA_NO_PROBE) == 0) {
       P.probe = true;
       const TileInfo& t = tiles.back();
@@ -629,26 +628,8 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
       P.probe_q0 = P.groups[t.first].q_row0;
       P.probe_nq = 0;
       for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
-      // the probe tile's seed window in shares of at least 128 keys (up to 64
-      // workgroups): the probe's time is its latency, with most of the GPU
-      // idle; more shares score faster but give the threshold select more
-      // regions to read
-      const int wlo = std::max(0, t.n_last - P.W);
-      const int f = std::min(P.F, wlo);
-      P.Jp = (int)std::max<int64_t>(1, std::min<int64_t>(64, (t.n_last - wlo) / 128));
-      for (int r = 0; r < P.Jp; ++r) {
-        int lo, hi;
-        range_split(wlo, t.n_last, r, P.Jp, 64, lo, hi);
-        WorkItem it{};
-        it.group = t.first;
-        it.pad = t.n;
-        it.region = r;
-        it.a0 = 0; it.a1 = (r == 0) ? f : 0;
-        it.b0 = lo; it.b1 = hi;
-        P.probe_items.push_back(it);
-      }
       P.Jd = dense_tiled_items(P.dense_items);
-      P.R = std::max(P.R, P.Jd);   // the probe's regions live in a buffer of their own
+      P.R = std::max(P.R, P.Jd);
     }
     P.items.insert(P.items.end(), P.surv_tiled_items.begin(), P.surv_tiled_items.end());
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
@@ -658,7 +639,6 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.items.insert(P.items.end(), P.surv_tiled_items2.begin(), P.surv_tiled_items2.end());
     P.items.insert(P.items.end(), P.surv_list_items2.begin(), P.surv_list_items2.end());
     P.items.insert(P.items.end(), P.x_items.begin(), P.x_items.end());
-    P.items.insert(P.items.end(), P.probe_items.begin(), P.probe_items.end());
     P.list_total = loff;
     P.mask_words = (max_bounded + 63) / 64;
     int64_t bsum = 0;
@@ -669,8 +649,8 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
   // threshold receives about K (1 + ln(n / K)) entries (the expected number of
   // records among n draws); automatic sizing takes 1.3x that plus slack, so a
   // region rarely has to be compacted mid-sweep, and never more than n + 64.
-  const size_t n_main_items = P.items.size() - P.probe_items.size();   // probe items come last
-  const size_t x_end = n_main_items, x_begin = x_end - P.x_items.size();   // extra seed items before them
+  const size_t n_main_items = P.items.size();
+  const size_t x_end = n_main_items, x_begin = x_end - P.x_items.size();   // extra seed items come last
   auto est_cap = [&](int64_t max_n) {
     const double k = (double)topk;
     const double est = 1.3 * k * (1.0 + std::log(std::max((double)max_n, k) / k)) + 256.0;
@@ -678,11 +658,6 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     cap = std::max<int64_t>(cap, topk + 64);
     return (int)((cap + 63) / 64 * 64);
   };
-  if (P.probe) {
-    int64_t pn = 0;
-    for (const auto& it : P.probe_items) pn = std::max<int64_t>(pn, (int64_t)(it.a1 - it.a0) + (it.b1 - it.b0));
-    P.pcap = cfg.buffer_cap == 0 ? est_cap(pn) : (cfg.buffer_cap + 63) / 64 * 64;
-  }
   if (cfg.buffer_cap == 0) {
     int64_t max_n = 0;
     for (size_t ii = 0; ii < n_main_items; ++ii) {
@@ -733,10 +708,6 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     P.o_lists = take((size_t)std::max<int64_t>(P.list_total, 1) * sizeof(int32_t));
     P.o_listlen = take((size_t)std::max(G, 1) * sizeof(int32_t));
     P.o_liststart = take((size_t)std::max(G, 1) * sizeof(int32_t));
-    if (P.probe) {
-      P.o_pcand = take((size_t)P.probe_nq * P.Jp * P.pcap * sizeof(u64));
-      P.o_pcounts = take((size_t)P.probe_nq * P.Jp * sizeof(uint32_t));
-    }
     P.o_gflags = take((size_t)std::max(G, 1) * sizeof(int32_t));
     if (P.X > 0) {
       P.o_xlists = take((size_t)std::max(G, 1) * P.x_stride * sizeof(int32_t));
@@ -1079,46 +1050,19 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     int32_t* gflags = reinterpret_cast<int32_t*>(ws + P.o_gflags);
     int32_t* prunes = reinterpret_cast<int32_t*>(ws + P.o_flag);   // cleared by the prep kernel
     // device item order (the order of P.items): seed, tiled survivors, list survivors, bound,
-    // dense, round-2 bound, round-2 tiled survivors, round-2 list survivors, extra seed, probe
+    // dense, round-2 bound, round-2 tiled survivors, round-2 list survivors, extra seed
     const size_t off_surv = P.seed_items.size(), off_list = off_surv + P.surv_tiled_items.size(),
                  off_bound = off_list + P.surv_list_items.size(), off_dense = off_bound + P.bound_items.size(),
                  off_bound2 = off_dense + P.dense_items.size(), off_surv2 = off_bound2 + P.bound_items2.size(),
                  off_list2 = off_surv2 + P.surv_tiled_items2.size(),
-                 off_x = off_list2 + P.surv_list_items2.size(), off_probe = off_x + P.x_items.size();
+                 off_x = off_list2 + P.surv_list_items2.size();
     int32_t* mode = P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr;
-    // 1b. probe: seed pass, threshold and plan of the last tile only, then the
-    //     decision whether the call runs the certificate pipeline or dense scoring
+    // 1b. probe: plan of the last tile only, with a threshold estimated from
+    //     the plan's sample of seed-window keys, then the decision whether the
+    //     call runs the certificate pipeline or dense scoring
     int32_t* list_start = reinterpret_cast<int32_t*>(ws + P.o_liststart);
     if (P.probe) {
       PassScope ps(P_PROBE, stream);
-      // the probe tile's seed candidates: a buffer of its own (its queries only)
-      const CandBuf pcb{reinterpret_cast<u64*>(ws + P.o_pcand), reinterpret_cast<uint32_t*>(ws + P.o_pcounts), P.Jp,
-                        P.pcap, (int64_t)P.probe_nq, (int64_t)P.probe_q0};
-      ScoreLaunch pb{};
-      pb.theta_share = tshare;
-      pb.in = in;
-      pb.lrows = pr.rows;
-      pb.lsig = pr.sig;
-      pb.groups = dg;
-      pb.items = di + off_probe;
-      pb.n_items = P.Jp;
-      pb.cb = pcb;
-      pb.topk = topk;
-      pb.scored_slot = 1;
-      pb.tiled = 1;
-      pb.role = ROLE_SEED;
-      e = launch_score(P.combo, H, d, pb, stream);
-      if (e != hipSuccess) return fail_hip(e, "probe seed kernel launch");
-      SelectLaunch pt{};
-      pt.cb = pcb;
-      pt.q_first = P.probe_q0;
-      pt.total_q = P.probe_nq;
-      pt.topk = topk;
-      pt.r0 = 0;
-      pt.r1 = P.Jp;
-      pt.tau_out = tau;
-      e = launch_select_tau(pt, stream);
-      if (e != hipSuccess) return fail_hip(e, "probe select kernel launch");
       PlanLaunch pp{};
       pp.in = in;
       pp.groups = dg + P.probe_group;
@@ -1127,7 +1071,9 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       pp.seed_window = P.W;
       pp.neg_frac = cfg.neg_support_frac;
       pp.flags = cfg.flags;
-      pp.tau = tau;
+      pp.tau = nullptr;                // threshold estimated from the sampled window keys
+      pp.topk = topk;
+      pp.seed_prefix = P.F;
       pp.lerr = pr.err;
       pp.prunes = prunes;
       pp.rows = ws + P.o_rows;

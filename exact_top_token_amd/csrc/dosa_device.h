@@ -429,105 +429,6 @@ __device__ __noinline__ u64 select_kth_nt(const Segs sg, int K, uint32_t* hist) 
 
 __device__ __forceinline__ u64 select_kth(const Segs sg, int K, uint32_t* hist) { return select_kth_nt<64>(sg, K, hist); }
 
-// A score threshold for a query whose total entry count fits an LDS stage
-// (total <= stage capacity, K <= total): the score images (upper 32 bits) of
-// all segments' entries (at offsets off, LDS [nseg + 1]) are copied to the stage once, with batches of loads
-// in flight together, then a radix select on digits of up to 11 bits of the
-// image minus the smallest staged image runs on LDS.  Returns the K-th
-// largest image, or the lower edge of a digit bin that holds the remaining
-// entries whole; either way the smallest staged image >= T is the K-th
-// largest, and ord2f(T) never exceeds the K-th largest score.
-template <int NT>
-__device__ __forceinline__ uint32_t select_kth_score_staged(const Segs sg, const uint32_t* off, uint32_t total, int K,
-                                                            uint32_t* hist, uint32_t* stage) {
-  const int tid = (int)threadIdx.x;
-  const int lane = lane_id();
-  constexpr int B = 8;
-  int r = 0;   // a thread's indices only grow, so its segment cursor only moves forward
-  for (uint32_t b = 0; b < total; b += (uint32_t)NT * B) {
-    uint32_t e[B];
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const uint32_t i = b + (uint32_t)NT * u + tid;
-      e[u] = 0u;
-      if (i < total) {
-        while (off[r + 1] <= i) ++r;
-        e[u] = (uint32_t)(sg.ptr(r)[i - off[r]] >> 32);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < B; ++u) {
-      const uint32_t i = b + (uint32_t)NT * u + tid;
-      if (i < total) stage[i] = e[u];
-    }
-  }
-  // Digits are taken from d = v - lo over the staged range [lo, hi], so the
-  // first pass spreads the entries over its bins whatever their magnitude
-  // (digits of the raw image put nearly all scores of a query in a few bins,
-  // and every entry then contends for the same histogram words).
-  constexpr int NW = NT / 64;
-  uint32_t lo_l = 0xFFFFFFFFu, hi_l = 0u;
-  __syncthreads();   // the stage is written
-  for (uint32_t i = tid; i < total; i += NT) {
-    const uint32_t v = stage[i];
-    lo_l = min(lo_l, v);
-    hi_l = max(hi_l, v);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    lo_l = min(lo_l, (uint32_t)__shfl_xor((int)lo_l, off, 64));
-    hi_l = max(hi_l, (uint32_t)__shfl_xor((int)hi_l, off, 64));
-  }
-  if (lane == 0) {
-    hist[tid >> 6] = lo_l;
-    hist[NW + (tid >> 6)] = hi_l;
-  }
-  __syncthreads();
-  uint32_t lo = hist[0], hi = hist[NW];
-  for (int w = 1; w < NW; ++w) {
-    lo = min(lo, hist[w]);
-    hi = max(hi, hist[NW + w]);
-  }
-  const uint32_t range = hi - lo;
-  uint32_t prefix = 0, rem = (uint32_t)K;
-  // bits of d above `top` are fixed by the digits found so far
-  int top = range ? 32 - __clz((int)range) : 0;
-#pragma unroll 1
-  while (top > 0) {
-    const int sh = top > 11 ? top - 11 : 0;
-    const int nb = 1 << (top - sh);
-    __syncthreads();   // the previous pass's histogram (or the range words) is read
-    for (int i = tid; i < nb; i += NT) hist[i] = 0;
-    __syncthreads();
-    const uint32_t want = top >= 32 ? 0u : (prefix >> top);
-    for (uint32_t i = tid; i < total; i += NT) {
-      const uint32_t d = stage[i] - lo;
-      if (top >= 32 || (d >> top) == want) atomicAdd(&hist[(d >> sh) & (uint32_t)(nb - 1)], 1u);
-    }
-    __syncthreads();
-    const int per = (nb + 63) >> 6;
-    uint32_t sum = 0;
-    for (int t = 0; t < per; ++t) sum += (lane * per + t < nb) ? hist[lane * per + t] : 0u;
-    const uint32_t suf = wave_suffix_sum(sum);
-    const bool cross = (suf >= rem) && (suf - sum < rem);
-    const u64 cm = __ballot(cross);
-    const int L = cm ? (__ffsll((long long)cm) - 1) : 0;
-    uint32_t acc = __shfl(suf - sum, L, 64);
-    int bin = L * per;
-    uint32_t cnt_b = 0;
-    for (int t = per - 1; t >= 0; --t) {
-      const uint32_t h = (L * per + t < nb) ? hist[L * per + t] : 0u;
-      if (acc + h >= rem) { bin = L * per + t; cnt_b = h; break; }
-      acc += h;
-    }
-    rem -= acc;
-    prefix |= (uint32_t)bin << sh;
-    top = sh;
-    if (cnt_b == rem) break;   // the bin holds exactly the remaining entries
-  }
-  return lo + prefix;
-}
-
 // Copy the entries >= T of src[0..n) to dst[out..] in order (dst may equal
 // src, with out <= 0 then).  Returns the new end.  Entries are read kBatch
 // wavefront-rows at a time before any is written: in place, every write

@@ -197,7 +197,7 @@ struct PlanLaunch {
   int32_t seed_window;
   float neg_frac;
   uint32_t flags;
-  const float* tau;          // [total_q]
+  const float* tau;          // [total_q], or NULL in a probe plan (estimated threshold, below)
   const float* lerr;         // [total_q, 2] weighted-query representation error and magnitude
   void* rows;                // [total_q, 4, d] query storage type
   float* coef;               // [total_q, 8]
@@ -211,6 +211,12 @@ struct PlanLaunch {
   int32_t decide_q0, decide_nq;
   int32_t* decide_mode;
   unsigned long long* stats;
+  // probe plans (tau == NULL): the threshold is estimated from the sampled
+  // window keys instead of read, as the sample's quantile at topk over the
+  // query's seed keys (the first seed_prefix keys and its window); a cost
+  // decision only, the certificate pipeline plans every query again
+  int32_t topk;
+  int32_t seed_prefix;
 };
 
 struct BoundLaunch {
@@ -314,7 +320,6 @@ constexpr int kMaxBoundTiles = 4096;// key tiles of a bound item that the block 
 hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream_t s);
 hipError_t launch_prep(int combo, int H, int d, const PrepLaunch& p, hipStream_t s);
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s);
-hipError_t launch_select_tau(const SelectLaunch& p, hipStream_t s);
 hipError_t launch_key_norms(int combo, int d, const NormLaunch& p, hipStream_t s);
 hipError_t launch_key_blocks(int combo, int d, const NormLaunch& p, hipStream_t s);
 hipError_t launch_plan(int combo, int H, int d, const PlanLaunch& p, hipStream_t s);

@@ -400,6 +400,9 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __shared__ double red4[4];
   __shared__ float rnorm[4];                       // norms of the 4 stored certificate rows (rounded up)
   __shared__ int np_s, nsurv_s, nsep_s;
+  __shared__ float ssc[4][kSampleKeys];             // probe plan: per-wavefront partial scores of the
+  __shared__ float sfin[kSampleKeys];               // activation keys, their scores, the estimate
+  __shared__ float tau_s;
 
   // ---- 0. issue the loads
   // Heads stored per query (a multiple of 8, at most H): the head slots past
@@ -418,17 +421,19 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   if (wave * 16 + col < Hr) O::load_q(qrow_raw + (wave * 16 + col) * D * QB, g, qa);
   else O::zero(qa);
   const float wv = (t < Hr) ? p.in.w[(int64_t)qrow * Hr + t] : 0.f;
-  const float tau = p.tau[qrow];
+  const bool est = p.tau == nullptr;               // probe plan: the threshold is estimated below
+  const float tau_in = est ? -INFINITY : p.tau[qrow];
   const float qscale = HasQScale<C>::value ? p.in.q_scale[qrow] : 1.f;
   const float l_err_f = p.lerr[(int64_t)qrow * 2], l_mag_f = p.lerr[(int64_t)qrow * 2 + 1];
   const bool use_neg = (p.flags & DOSA_NO_NEGATIVE) == 0;
   const int n_last = gr.pos0 + gr.nq;
   const int wlo = max(0, n_last - p.seed_window);
   const int span = pos - wlo + 1;                   // window keys visible to this query
-  const int ns = use_neg ? min(kSampleKeys, max(span, 0)) : 0;
+  const int ns = (use_neg || est) ? min(kSampleKeys, max(span, 0)) : 0;
   const int astep = max(1, span / max(ns, 1));
   const int nb = gr.n_bounded;
-  const int nsb = ((p.flags & DOSA_NO_PRUNE) == 0 && tau > -INFINITY) ? min(kSampleKeys, nb) : 0;
+  // skip-test keys loaded (the sample size once the threshold is known)
+  const int nsb_ld = ((p.flags & DOSA_NO_PRUNE) == 0 && (est || tau_in > -INFINITY)) ? min(kSampleKeys, nb) : 0;
   const uint8_t* kbase = static_cast<const uint8_t*>(p.in.k);
   uint4 kav[NKV], ksv[NKV];
 #pragma unroll
@@ -441,15 +446,18 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
       const int64_t row = key_row(p.in, gr.key_base, gr.seq, pos - i * astep);
       kav[j] = reinterpret_cast<const uint4*>(kbase + row * D * KBY)[sub];
     }
-    if (i < nsb) {
-      const int64_t row = key_row(p.in, gr.key_base, gr.seq, gr.bound_lo + (int)(((int64_t)i * nb) / nsb));
+    if (i < nsb_ld) {
+      const int64_t row = key_row(p.in, gr.key_base, gr.seq, gr.bound_lo + (int)(((int64_t)i * nb) / nsb_ld));
       ksv[j] = reinterpret_cast<const uint4*>(kbase + row * D * KBY)[sub];
     }
   }
-  float kscale = 1.f;
-  if (t < nsb) {
-    const int key = gr.bound_lo + (int)(((int64_t)t * nb) / nsb);
+  float kscale = 1.f, kscale_a = 1.f;
+  if (t < nsb_ld) {
+    const int key = gr.bound_lo + (int)(((int64_t)t * nb) / nsb_ld);
     if constexpr (HasKScale<C>::value) kscale = p.in.k_scale[key_row(p.in, gr.key_base, gr.seq, key)];
+  }
+  if (est && t < ns) {   // the activation key's scale, for its score
+    if constexpr (HasKScale<C>::value) kscale_a = p.in.k_scale[key_row(p.in, gr.key_base, gr.seq, pos - t * astep)];
   }
 
   // ---- 1. query and activation keys (stored type) to LDS
@@ -474,6 +482,8 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     act[t] = 0;
   }
   if (t < kSampleKeys) ksc[t] = kscale;
+  ssc[wave][lane] = 0.f;
+  if (t == 0) tau_s = -INFINITY;
   __syncthreads();
 
   // ---- 2. activation counts of the negative heads on the window keys
@@ -489,6 +499,17 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
       for (int st = 0; st < O::STEPS; ++st) c = O::mma(qa[st], B[st], c);
 #pragma unroll
       for (int i = 0; i < 4; ++i) cnt[i] += (key < ns && c[i] > 0.f) ? 1 : 0;
+      if (est) {   // this wavefront's heads' part of the key's score (unscaled)
+        float sp = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int h = wave * 16 + 4 * g + i;
+          sp = fmaf(h < H ? (float)wd[h] : 0.f, fmaxf(c[i], 0.f), sp);
+        }
+        sp += __shfl_xor(sp, 16, 64);
+        sp += __shfl_xor(sp, 32, 64);
+        if (g == 0 && key < ns) ssc[wave][key] = sp;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -510,6 +531,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     if (part == 0) qn2[hh] = s2;
   }
   __syncthreads();
+  if (est && t < ns) sfin[t] = (ssc[0][t] + ssc[1][t] + ssc[2][t] + ssc[3][t]) * qscale * kscale_a;
   if (wave == 0) {
     // positive heads of largest w_h ||q_h||, lower head index on ties
     double v = (lane < H && wd[lane] > 0.0) ? wd[lane] * sqrt(qn2[lane]) : -1.0;
@@ -532,6 +554,19 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   }
   __syncthreads();
   const int np = np_s;
+  // probe plan: the estimated threshold is the sample's score of rank
+  // ceil(ns * topk / n_seed), n_seed the seed keys this query sees; none
+  // (nothing to prune) when it sees fewer than topk
+  if (est && t < ns) {
+    const int64_t n_seed = (int64_t)span + min(p.seed_prefix, wlo);
+    if (n_seed >= p.topk) {
+      const int r = (int)min<int64_t>(ns, max<int64_t>(1, ((int64_t)ns * p.topk + n_seed - 1) / n_seed));
+      const float mine = sfin[t];
+      int above = 0;
+      for (int j = 0; j < ns; ++j) above += (sfin[j] > mine || (sfin[j] == mine && j < t)) ? 1 : 0;
+      if (above == r - 1) tau_s = mine;
+    }
+  }
   for (int r = 0; r < np; ++r) {
     const int pr = prox[r] * QS + part;
     double dsum = 0.0;
@@ -602,6 +637,8 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     }
   }
   __syncthreads();   // activation keys no longer read
+  const float tau = est ? tau_s : tau_in;
+  const int nsb = tau > -INFINITY ? nsb_ld : 0;
 #pragma unroll
   for (int j = 0; j < NKV; ++j) {
     const int c = t + 256 * j;
@@ -752,7 +789,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   }
   __syncthreads();
   const bool hopeless = nsb == 0 || (float)nsurv_s >= kSkipFrac * (float)nsb;
-  const bool joint = !hopeless && (p.flags & DOSA_SEPARABLE_RHO) == 0 &&
+  const bool joint = !est && !hopeless && (p.flags & DOSA_SEPARABLE_RHO) == 0 &&
                      (nsb < 16 || (float)(nsep_s - nsurv_s) >= fmaxf(2.f, kJointGain * (float)nsb));
 
   // ---- 7. joint residual constant rho^2 = sum_{h,j in O} w_h w_j max(0, <r_h, r_j>)

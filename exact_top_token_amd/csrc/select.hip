@@ -159,66 +159,6 @@ __global__ __launch_bounds__(NT) void select_kernel(const SelectLaunch p) {
   }
 }
 
-// Threshold only: tau_out = the K-th largest score of the entries of regions
-// [r0, r1) (-inf if fewer than K), by 4 wavefronts per query and without
-// touching the regions.  For small launches whose time
-// is one query's latency.
-constexpr uint32_t kTauStage = 12288;  // score images staged in LDS (48 KiB): the seed window and prefix at defaults
-constexpr int kTauThreads = 256;       // per query (1024 measured slower)
-
-__global__ __launch_bounds__(kTauThreads) void select_tau_kernel(const SelectLaunch p) {
-  __shared__ uint32_t hist[2048];
-  __shared__ uint32_t stage[kTauStage];
-  __shared__ uint32_t segoff[kMaxMergeRegions + 1];
-  if (skip_launch(p.mode, p.run_if)) return;
-  const int q = p.q_first + blockIdx.x;
-  const int K = p.topk;
-  const Segs sg{p.cb.row(q, p.r0), p.cb.count(q, p.r0), p.cb.rows * p.cb.cap, p.cb.rows, p.r1 - p.r0,
-                (uint32_t)p.cb.cap, nullptr};
-  __shared__ u64 kth;
-  uint32_t total = 0;
-  const bool offs = sg.nseg <= kMaxMergeRegions;
-  if (offs) {
-    segment_offsets_wg<kTauThreads>(sg, segoff);
-    total = segoff[sg.nseg];
-  } else {
-    for (int r = 0; r < sg.nseg; ++r) total += sg.n(r);
-  }
-  float tau = -INFINITY;
-  if (total >= (uint32_t)K) {
-    // T: the lower edge of the radix bin that holds the K-th entry (exactly K
-    // entries at or above it); the smallest of those is the K-th largest.
-    if (threadIdx.x == 0) kth = ~0ull;
-    const int tid = (int)threadIdx.x;
-    if (total <= kTauStage && offs) {
-      const uint32_t T = select_kth_score_staged<kTauThreads>(sg, segoff, total, K, hist, stage);
-      uint32_t m = 0xFFFFFFFFu;
-      for (uint32_t i = tid; i < total; i += kTauThreads) {
-        const uint32_t v = stage[i];
-        if (v >= T && v < m) m = v;
-      }
-      atomicMin(&kth, (u64)m);
-      __syncthreads();
-      tau = ord2f((uint32_t)kth);
-    } else {
-      const u64 T = select_kth_nt<kTauThreads>(sg, K, hist);
-      u64 m = ~0ull;
-      for (int r = 0; r < sg.nseg; ++r) {
-        const u64* ptr = sg.ptr(r);
-        const uint32_t n = sg.n(r);
-        for (uint32_t i = tid; i < n; i += kTauThreads) {
-          const u64 e = ptr[i];
-          if (e >= T && e < m) m = e;
-        }
-      }
-      atomicMin(&kth, m);
-      __syncthreads();
-      tau = key_score(kth);
-    }
-  }
-  if (threadIdx.x == 0) p.tau_out[q] = tau;
-}
-
 // Same merge, rows ordered by (score desc, position asc): the kept keys are
 // gathered into LDS and bitonic-sorted (K <= 4096 -> 32 KiB).
 __global__ __launch_bounds__(64) void select_sorted_kernel(const SelectLaunch p) {
@@ -303,12 +243,6 @@ hipError_t launch_score(int combo, int H, int d, const ScoreLaunch& p, hipStream
     case C_BF16Q_FP8K: return launch_score_bf16fp8(H, d, p, s);
   }
   return hipErrorInvalidValue;
-}
-
-hipError_t launch_select_tau(const SelectLaunch& p, hipStream_t s) {
-  if (p.total_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(select_tau_kernel, dim3(p.total_q), dim3(kTauThreads), 0, s, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectLaunch& p, hipStream_t s) {

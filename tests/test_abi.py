@@ -94,8 +94,7 @@ def test_workspace_beyond_int32_list_offsets(q_len, kv_len):
 
 def test_workspace_of_long_chunks_fits_hbm():
     """The 1M-key context with 32K-query chunks: the pruned path's workspace stays a small part of
-    the 288 GB of one MI355X (one list area per query tile; the probe tile's seed regions in a
-    buffer of their own)."""
+    the 288 GB of one MI355X (one list area per query tile)."""
     n = E.workspace_size([32768], [1048576], 64, 128, 2048, "fp8", "fp8", False, False)
     assert 0 < n < 20 * 2 ** 30
 
