@@ -619,17 +619,36 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     }
     // probe: with enough tiles, the last tile (longest contexts) is planned
     // first; if its certificate can prune no query, the call scores every
-    // tile densely with the dense path's items (regions 0..Jd-1)
-    if (P.tiled && NT >= 8 && (cfg.flags & DOSA_NO_PROBE) == 0) {
+    // tile densely with the dense path's items (regions 0..Jd-1).  Calls
+    // without tiles (decode-like: every sequence a tile of its own) plan all
+    // their groups in the probe -- one launch of one workgroup per query --
+    // and score densely with the dense path's balanced split items.
+    if (NT >= 8 && (cfg.flags & DOSA_NO_PROBE) == 0) {
       P.probe = true;
-      const TileInfo& t = tiles.back();
-      P.probe_group = t.first;
-      P.probe_ngroups = t.n;
-      P.probe_q0 = P.groups[t.first].q_row0;
-      P.probe_nq = 0;
-      for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
-      P.Jd = dense_tiled_items(P.dense_items);
-      P.R = std::max(P.R, P.Jd);
+      if (P.tiled) {
+        const TileInfo& t = tiles.back();
+        P.probe_group = t.first;
+        P.probe_ngroups = t.n;
+        P.probe_q0 = P.groups[t.first].q_row0;
+        P.probe_nq = 0;
+        for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
+        P.Jd = dense_tiled_items(P.dense_items);
+      } else {
+        P.probe_group = 0;
+        P.probe_ngroups = G;
+        P.probe_q0 = 0;
+        P.probe_nq = (int)P.total_q;
+        std::vector<int64_t> lens;
+        for (const auto& g : P.groups) lens.push_back(g.pos0 + g.nq);
+        const int64_t chunk = split_chunk(lens);
+        P.Jd = 1;
+        for (int gi = 0; gi < G; ++gi) {
+          const GroupInfo& g = P.groups[gi];
+          P.Jd = std::max(P.Jd, split_range(gi, 0, g.pos0 + g.nq, 0, chunk, P.dense_items));
+        }
+        longest_first(P.dense_items, 0);
+      }
+      P.R = std::max(P.R, P.Jd * P.RW);
     }
     P.items.insert(P.items.end(), P.surv_tiled_items.begin(), P.surv_tiled_items.end());
     P.items.insert(P.items.end(), P.surv_list_items.begin(), P.surv_list_items.end());
@@ -1079,7 +1098,6 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       pp.rows = ws + P.o_rows;
       pp.coef = coef;
       pp.ticket = prunes + 1;
-      pp.decide_q0 = P.probe_q0;
       pp.decide_nq = P.probe_nq;
       pp.decide_mode = mode;
       pp.stats = st;
@@ -1096,7 +1114,11 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     // more than the serial launches (32K bf16 prefill: 11.8 against 9.1 ms).
     SideFork sf;
     hipStream_t cs = stream;
-    if (P.probe && P.dense_items.size() <= (size_t)kSideStreamMaxItems) {
+    // Calls without tiles stay on one stream too: the split kernel's
+    // workgroups each take a whole CU, and the side stream's empty workgroups
+    // (thousands, across eight launches) hold CUs it waits for (decode batch:
+    // 1.28 ms on two streams, see the measurements).
+    if (P.probe && P.tiled && P.dense_items.size() <= (size_t)kSideStreamMaxItems) {
       e = sf.open(stream);
       if (e != hipSuccess) return fail_hip(e, "side stream");
       if (sf.side != nullptr) cs = sf.side;
@@ -1375,7 +1397,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
       dl.topk = topk;
       dl.stats = st;
       dl.scored_slot = 4;
-      dl.tiled = 1;
+      dl.tiled = P.tiled ? 1 : 2;
       dl.role = ROLE_DENSE;
       dl.theta_part = tpart;
       dl.part_stride = P.n_parts;
@@ -1396,7 +1418,7 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
   se.out_idx = out_idx;
   se.out_score = out_score;
   se.tau_out = nullptr;
-  se.r1_unpruned = P.probe ? P.Jd : P.R;
+  se.r1_unpruned = P.probe ? P.Jd * P.RW : P.R;
   se.mode = dense ? nullptr : (P.probe ? reinterpret_cast<int32_t*>(ws + P.o_mode) : nullptr);
   se.run_if = -1;
   se.sorted = (cfg.flags & DOSA_SORTED) ? 1 : 0;

@@ -205,10 +205,10 @@ struct PlanLaunch {
   const int32_t* mode;       // NULL: always run; else run only if *mode == run_if (see DosaMode)
   int32_t run_if;
   // probe decision (or NULL): the last of the decide_nq planned queries (a
-  // ticket counter, zeroed by the prep kernel) sets *decide_mode from their
-  // plans, queries decide_q0 .. decide_q0 + decide_nq - 1
+  // ticket counter, zeroed by the prep kernel) sets *decide_mode from the
+  // prunes flag their plans raised (prunes must be set)
   int32_t* ticket;
-  int32_t decide_q0, decide_nq;
+  int32_t decide_nq;
   int32_t* decide_mode;
   unsigned long long* stats;
   // probe plans (tau == NULL): the threshold is estimated from the sampled

@@ -852,15 +852,12 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
     if (!hopeless && p.prunes != nullptr) atomicOr(p.prunes, 1);   // the bound pass has work: key norms are needed
     if (p.ticket != nullptr) {
       // probe: the last planned query decides whether the call runs the
-      // certificate pipeline (some probe query can prune) or dense scoring
+      // certificate pipeline (some probe query can prune: the prunes flag,
+      // cleared by the prep kernel, was raised) or dense scoring
       __threadfence();
       if (atomicAdd(p.ticket, 1) == p.decide_nq - 1) {
         __threadfence();
-        bool any = false;
-        for (int i = 0; i < p.decide_nq && !any; ++i) {
-          const uint32_t* f = reinterpret_cast<const uint32_t*>(p.coef + (int64_t)(p.decide_q0 + i) * kCoefStride + 7);
-          any = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;   // coef[7] == 0.f
-        }
+        const bool any = __hip_atomic_load(p.prunes, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
         *p.decide_mode = any ? MODE_PRUNED : MODE_UNPRUNED;
         if (!any && p.stats != nullptr) atomicAdd(&p.stats[10], 1ull);
       }
