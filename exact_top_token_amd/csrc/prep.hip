@@ -67,21 +67,36 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
   }
   __syncthreads();
   const uint8_t* qraw = qrow;
+  // lane owns the PER consecutive elements PER*lane .. PER*lane + PER - 1
+  // (d = 64: one, d = 128: a pair, decoded together: fp8 by the hardware
+  // converter, exact for every finite E4M3 code)
   double r[PER];
 #pragma unroll
-  for (int v = 0; v < PER; ++v) {
-    const int i = lane + 64 * v;
-    double acc = 0.0;
-    if (i < D) {
-      for (int h = 0; h < Hr; ++h) {
-        float x;
-        if constexpr (C == C_F32) x = reinterpret_cast<const float*>(qraw)[h * D + i];
-        else if constexpr (C == C_FP8) x = dec_fp8_p(qraw[h * D + i]);
-        else x = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qraw)[h * D + i] << 16);
-        acc += (double)wrow[h] * (double)x;
-      }
+  for (int v = 0; v < PER; ++v) r[v] = 0.0;
+  for (int h = 0; h < Hr; ++h) {
+    const double wh = (double)wrow[h];
+    float x[PER];
+    if constexpr (PER == 2 && C == C_FP8) {
+      const uint32_t two = (uint32_t)reinterpret_cast<const uint16_t*>(qraw)[(h * D) / 2 + lane];
+      const uint32_t bf = fp8x2_to_bf16x2<false>(two);
+      x[0] = __uint_as_float(bf << 16);
+      x[1] = __uint_as_float(bf & 0xFFFF0000u);
+    } else if constexpr (PER == 2 && C == C_F32) {
+      const float2 f = reinterpret_cast<const float2*>(qraw)[(h * D) / 2 + lane];
+      x[0] = f.x;
+      x[1] = f.y;
+    } else if constexpr (PER == 2) {
+      const uint32_t bf = reinterpret_cast<const uint32_t*>(qraw)[(h * D) / 2 + lane];
+      x[0] = __uint_as_float(bf << 16);
+      x[1] = __uint_as_float(bf & 0xFFFF0000u);
+    } else {
+      const int i = lane;
+      if constexpr (C == C_F32) x[0] = reinterpret_cast<const float*>(qraw)[h * D + i];
+      else if constexpr (C == C_FP8) x[0] = dec_fp8_p(qraw[h * D + i]);
+      else x[0] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(qraw)[h * D + i] << 16);
     }
-    r[v] = acc;
+#pragma unroll
+    for (int v = 0; v < PER; ++v) r[v] = fma(wh, (double)x[v], r[v]);
   }
   uint8_t* rows = static_cast<uint8_t*>(p.rows) + (int64_t)q * S * D * QB;
   float* sig = p.sig + (int64_t)q * S;
@@ -105,7 +120,7 @@ __global__ __launch_bounds__(64) void qbar_kernel(const PrepLaunch p) {
     double fn = 0.0;
 #pragma unroll
     for (int v = 0; v < PER; ++v) {
-      const int i = lane + 64 * v;
+      const int i = PER * lane + v;
       if (i >= D) continue;
       double dv;
       if constexpr (C == C_FP8) {
