@@ -524,13 +524,17 @@ struct Scorer {
 
 
   // End of the sweep: bring every region down to its final theta.
+  // Every region is cut, also one holding fewer than K entries: with many
+  // regions per query (a split kernel's eight wavefronts times its key
+  // splits) the final merge would otherwise read every appended candidate
+  // in each of its passes.
   __device__ __forceinline__ void close(const ScoreLaunch& p, const GroupInfo& gr, int region, uint32_t* shist) {
     refresh_theta(p.topk);
 #pragma unroll 1
     for (int qq = 0; qq < QW; ++qq) {
       const uint32_t cq = __shfl(count, 16 * (qq * (4 / QW)), 64);
       const float tq = __shfl(theta, 16 * (qq * (4 / QW)), 64);
-      if (cq > (uint32_t)p.topk && tq > -INFINITY) {
+      if (cq > 0u && tq > -INFINITY) {
         u64* bq = p.cb.row(gr.q_row0 + qq, region);
         const uint32_t nk = compact_ge(bq, cq, (u64)f2ord(tq) << 32, bq, 0);
         if (qi() == qq) count = nk;
