@@ -80,6 +80,7 @@ int fail_hip(hipError_t e, const char* what) {
 // ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
 constexpr int kSideStreamMaxItems = 512;   // dense work items of a call that still takes the side stream
+constexpr uint64_t kSideStreamMinPairs = uint64_t(1) << 26;   // causal pairs of a call that takes the side stream
 std::once_flag g_side_once[kMaxDevices];
 hipStream_t g_side[kMaxDevices] = {};
 hipError_t g_side_err[kMaxDevices] = {};
@@ -1118,7 +1119,12 @@ int run(bool dense, const void* q, int32_t q_dtype, const float* q_scale, const 
     // workgroups each take a whole CU, and the side stream's empty workgroups
     // (thousands, across eight launches) hold CUs it waits for (decode batch:
     // 1.28 ms on two streams, see the measurements).
-    if (P.probe && P.tiled && P.dense_items.size() <= (size_t)kSideStreamMaxItems) {
+    // Small calls (fewer than kSideStreamMinPairs causal pairs) stay on one
+    // stream as well: their launches are short, and the fork and join cost
+    // more than the overlap saves (tiny prefill: 0.5-0.9 ms on two streams
+    // from run to run, 0.49 ms on one).
+    if (P.probe && P.tiled && P.dense_items.size() <= (size_t)kSideStreamMaxItems &&
+        P.pairs_total >= kSideStreamMinPairs) {
       e = sf.open(stream);
       if (e != hipSuccess) return fail_hip(e, "side stream");
       if (sf.side != nullptr) cs = sf.side;
