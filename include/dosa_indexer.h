@@ -61,8 +61,9 @@
  * workspace (size from dosa_workspace_size).  The library allocates no device
  * memory and keeps no data between calls; everything is ordered on `stream`
  * (a hipStream_t, NULL = default stream) and no call waits for the device.
- * A pruned call that runs the probe (see DOSA_NO_PROBE) and whose dense
- * alternative fits in two workgroups per CU forks the certificate stages onto
+ * A pruned call with query tiles that runs the probe (see DOSA_NO_PROBE),
+ * has at least 2^26 causal pairs and whose dense alternative fits in two
+ * workgroups per CU forks the certificate stages onto
  * a side stream the library creates once per device (default priority, kept
  * until the process ends) and joins it back into `stream` before its final
  * selection, so `stream` order covers the whole call (graph capture too).
@@ -109,10 +110,12 @@ typedef enum {
                                      32-query bound tile is never loaded.  Off by default: on the
                                      correlated 128K recipe it skips 5.6% of the tiles and the test
                                      costs more than that saves */
-#define DOSA_NO_PROBE 0x10u       /* dosa_indexer_topk: no probe tile, always the certificate pipeline
-                                     (by default a call with >= 8 query tiles first seeds and plans
-                                     its last tile and, if the certificate prunes no query there,
-                                     scores every key densely; the result is the same either way) */
+#define DOSA_NO_PROBE 0x10u       /* dosa_indexer_topk: no probe, always the certificate pipeline
+                                     (by default a call with >= 8 query tiles first plans its last
+                                     tile -- a decode-like call with >= 8 sequences every group --
+                                     with the threshold estimated from the plan's sampled seed-window
+                                     keys and, if the certificate prunes no query there, scores every
+                                     key densely; the result is the same either way) */
 #define DOSA_TWO_ROUNDS 0x40u     /* dosa_indexer_topk, calls with query tiles: the threshold is
                                      refined once within the call (the DoSA transcript, Method: the
                                      stages repeat over tiles of keys as the standings refine).
@@ -193,7 +196,8 @@ typedef struct {
   uint64_t keys_streamed;      /* key rows the bound pass read (once per query tile or group that
                                   streamed them; skipped groups read none) */
   uint64_t calls_unpruned;     /* dosa_indexer_topk calls scored densely: the certificate could
-                                  prune no query of the call's probe tile (its last query tile) */
+                                  prune no query the probe planned (the call's last query tile, or
+                                  every group of a decode-like call) */
   uint64_t key_blocks_skipped; /* 64-key tiles the bound pass never loaded: the key-block bound
                                   (centre, radius and largest norm of the block's keys) was below
                                   tau for every query of the query tile that needed them */
