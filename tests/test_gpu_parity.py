@@ -440,6 +440,29 @@ def test_correlated_decode_bf16q_fp8k_prunes():
     assert check_debug_dumps(wl, ub, tau, mask, np.arange(wl.total_q)) > 0
 
 
+def test_decode_probe_decisions():
+    """Decode-like batches of at least 8 sequences are probed by planning every group with an
+    estimated threshold: the structured recipe (no query can prune) goes to the dense split items,
+    the correlated one keeps the certificate pipeline; both equal the dense path on every row."""
+    import exact_top_token_amd as E
+
+    wl = synth.decode_mtp(batch=10, kv_min=3000, kv_max=20000)
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 8))
+    assert pst["calls_unpruned"] == 1 and pst["pairs_bounded"] == 0 and pst["pairs_scored"] == wl.pairs()
+    cfg = E.default_config(wl.topk)
+    cfg.flags |= E.DOSA_NO_PROBE
+    pi2, ps2, pst2 = _run(wl, "dosa", cfg=cfg)
+    assert_same_selection(pi2, ps2, di, ds)
+    assert pst2["calls_unpruned"] == 0 and pst2["pairs_seed"] + pst2["pairs_bounded"] == wl.pairs()
+
+    wl = synth.correlated_decode(batch=10, kv_min=3000, kv_max=20000, topk=256)
+    cfg = E.default_config(wl.topk)
+    cfg.seed_window = 256
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 8), cfg=cfg)
+    assert pst["calls_unpruned"] == 0, "the probe sent a prunable decode batch to dense scoring"
+    assert pst["pairs_bounded"] > 0 and pst["pairs_survived"] < pst["pairs_bounded"]
+
+
 @pytest.mark.parametrize("H", [24, 40, 48, 56])
 @pytest.mark.parametrize("qd,kd", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
 def test_head_counts_padded(H, qd, kd):
