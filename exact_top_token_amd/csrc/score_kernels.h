@@ -780,8 +780,11 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
   uint32_t* shist = hist[wave];
   const uint8_t* kbytes = static_cast<const uint8_t*>(p.in.k);
   auto after_step = [&]() {
-    // every 4 steps of this wavefront: the histogram also holds the others' counts
-    if ((++nstep & 3) == 0) sc.refresh_theta(p.topk);
+    // steps 2 and 3 of this wavefront, then every 4: the histogram also holds
+    // the others' counts (the early refreshes raise the threshold from -inf
+    // once the workgroup's first steps are counted)
+    ++nstep;
+    if ((nstep & 3) == 0 || nstep == 2 || nstep == 3) sc.refresh_theta(p.topk);
   };
   auto load = [&](int key, bool kvalid, typename O::frag* B, float& ks) {
     ks = 1.f;
@@ -943,7 +946,8 @@ __global__ __launch_bounds__(64 * kTileWaves) void score_split_kernel(const Scor
                          int npp0, int npg1) {
         wait_vmem();   // this step's direct loads and the previous step's candidate stores
         if (s - kTileWaves >= wave) {
-          if ((++nstep & 3) == 0) sc.refresh_theta(p.topk);
+          ++nstep;
+          if ((nstep & 3) == 0 || nstep == 2 || nstep == 3) sc.refresh_theta(p.topk);
           append_step(s - kTileWaves, nsimg);
         }
         if (s + kTileWaves < ns) issue(s + kTileWaves, nimg, nsimg, npg0, npp0, npg1);
