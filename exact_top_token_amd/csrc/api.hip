@@ -262,6 +262,9 @@ constexpr bool kShareTheta = true;
 // workgroup per CU.
 constexpr int64_t kSplitItems = 256;
 
+// Groups planned by the probe of a call without query tiles.
+constexpr int kProbeGroups = 256;
+
 // Split choice: enough work items to fill the GPU (target items), keeping at
 // least min_keys keys per split.
 int choose_splits(int64_t n_units, int64_t avg_keys, int64_t target, int64_t min_keys) {
@@ -621,9 +624,10 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
     // probe: with enough tiles, the last tile (longest contexts) is planned
     // first; if its certificate can prune no query, the call scores every
     // tile densely with the dense path's items (regions 0..Jd-1).  Calls
-    // without tiles (decode-like: every sequence a tile of its own) plan all
-    // their groups in the probe -- one launch of one workgroup per query --
-    // and score densely with the dense path's balanced split items.
+    // without tiles (decode-like: every sequence a tile of its own) plan
+    // their groups in the probe -- up to kProbeGroups of them, one launch of
+    // one workgroup per query -- and score densely with the dense path's
+    // balanced split items.
     if (NT >= 8 && (cfg.flags & DOSA_NO_PROBE) == 0) {
       P.probe = true;
       if (P.tiled) {
@@ -635,10 +639,13 @@ void build_plan(Plan& P, int32_t batch, const int32_t* q_lens, const int32_t* kv
         for (int i = 0; i < t.n; ++i) P.probe_nq += P.groups[t.first + i].nq;
         P.Jd = dense_tiled_items(P.dense_items);
       } else {
-        P.probe_group = 0;
-        P.probe_ngroups = G;
-        P.probe_q0 = 0;
-        P.probe_nq = (int)P.total_q;
+        // at most kProbeGroups groups (the last ones): the decision needs a
+        // sample, and the plan launch's time grows with its rounds of workgroups
+        P.probe_ngroups = std::min(G, kProbeGroups);
+        P.probe_group = G - P.probe_ngroups;
+        P.probe_q0 = P.groups[P.probe_group].q_row0;
+        P.probe_nq = 0;
+        for (int gi = P.probe_group; gi < G; ++gi) P.probe_nq += P.groups[gi].nq;
         std::vector<int64_t> lens;
         for (const auto& g : P.groups) lens.push_back(g.pos0 + g.nq);
         const int64_t chunk = split_chunk(lens);

@@ -112,7 +112,8 @@ typedef enum {
                                      costs more than that saves */
 #define DOSA_NO_PROBE 0x10u       /* dosa_indexer_topk: no probe, always the certificate pipeline
                                      (by default a call with >= 8 query tiles first plans its last
-                                     tile -- a decode-like call with >= 8 sequences every group --
+                                     tile -- a decode-like call with >= 8 sequences its groups, up
+                                     to 256 of them --
                                      with the threshold estimated from the plan's sampled seed-window
                                      keys and, if the certificate prunes no query there, scores every
                                      key densely; the result is the same either way) */

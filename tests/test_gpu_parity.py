@@ -462,6 +462,11 @@ def test_decode_probe_decisions():
     assert pst["calls_unpruned"] == 0, "the probe sent a prunable decode batch to dense scoring"
     assert pst["pairs_bounded"] > 0 and pst["pairs_survived"] < pst["pairs_bounded"]
 
+    # more groups than the probe plans (it takes a sample of the last ones)
+    wl = synth.decode_mtp(batch=300, kv_min=5000, kv_max=9000)
+    (di, ds, dst), (pi, ps, pst) = _both(wl, rows=sample_rows(wl, 8))
+    assert pst["calls_unpruned"] == 1 and pst["pairs_bounded"] == 0
+
 
 @pytest.mark.parametrize("H", [24, 40, 48, 56])
 @pytest.mark.parametrize("qd,kd", [("f32", "f32"), ("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8")])
