@@ -338,15 +338,58 @@ constexpr float kSkipFrac = 0.7f;   // sampled survival above which the bound pa
 constexpr int kSampleKeys = 64;     // keys sampled for activations and for the skip test
 constexpr float kJointGain = 0.1f;  // sampled extra pruning that pays for the joint constant
 
-// Sum over the P consecutive lanes that share one head (P a power of two <= 64).
-template <int P, typename T>
-__device__ __forceinline__ T part_sum(T v) {
-#pragma unroll
-  for (int off = P / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, P);
-  return v;
+// Cross-lane exchanges without the LDS crossbar: DPP moves within a row of
+// 16 lanes, readlane across rows.  A row-local DPP move of a value that every
+// lane holds (all lanes of the wavefront active).
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_mov(T v) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+  }
 }
 template <typename T>
-__device__ __forceinline__ T wave_sum(T v) { return part_sum<64>(v); }
+__device__ __forceinline__ T lane_value(T v, int l) {
+  if constexpr (sizeof(T) == 8) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  } else {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+  }
+}
+struct OpAdd { template <typename T> __device__ T operator()(T a, T b) const { return a + b; } };
+struct OpMax { template <typename T> __device__ T operator()(T a, T b) const { return a > b ? a : b; } };
+
+// Reduction over the P consecutive lanes that share one head (P = 4, 8, 16,
+// 32 or 64): xor 1 and xor 2 by quad permutes, then the mirrored half of 8
+// and of 16 lanes, then the rows' values by readlane.  Every lane of a part
+// gets the same value (each step combines two equal-shaped partials).
+template <int P, typename T, typename Op>
+__device__ __forceinline__ T part_reduce(T v, Op op) {
+  static_assert(P == 4 || P == 8 || P == 16 || P == 32 || P == 64, "part size");
+  v = op(v, dpp_mov<0xB1>(v));                          // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_mov<0x4E>(v));                          // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (P >= 8) v = op(v, dpp_mov<0x141>(v));   // row_half_mirror: the other quad of 8
+  if constexpr (P >= 16) v = op(v, dpp_mov<0x140>(v));  // row_mirror: the other half of 16
+  if constexpr (P >= 32) {
+    const T r0 = lane_value(v, 0), r1 = lane_value(v, 16), r2 = lane_value(v, 32), r3 = lane_value(v, 48);
+    if constexpr (P == 32) v = (lane_id() < 32) ? op(r0, r1) : op(r2, r3);
+    else v = op(op(r0, r1), op(r2, r3));
+  }
+  return v;
+}
+template <int P, typename T>
+__device__ __forceinline__ T part_sum(T v) { return part_reduce<P>(v, OpAdd{}); }
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) { return part_reduce<64>(v, OpAdd{}); }
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) { return part_reduce<64>(v, OpMax{}); }
 
 // Layout: thread t works on head t / PARTS and owns that head's elements
 // part + PARTS*e (e < EL), PARTS = 256 / H; per-head dot products are lane
@@ -403,6 +446,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __shared__ float ssc[4][kSampleKeys];             // probe plan: per-wavefront partial scores of the
   __shared__ float sfin[kSampleKeys];               // activation keys, their scores, the estimate
   __shared__ float tau_s;
+  __shared__ double pvals[64];                     // proxy choice: w_h ||q_h|| (or -1) per head lane
 
   // ---- 0. issue the loads
   // Heads stored per query (a multiple of 8, at most H): the head slots past
@@ -533,23 +577,20 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
   __syncthreads();
   if (est && t < ns) sfin[t] = (ssc[0][t] + ssc[1][t] + ssc[2][t] + ssc[3][t]) * qscale * kscale_a;
   if (wave == 0) {
-    // positive heads of largest w_h ||q_h||, lower head index on ties
-    double v = (lane < H && wd[lane] > 0.0) ? wd[lane] * sqrt(qn2[lane]) : -1.0;
-    int n = 0;
-    for (int r = 0; r < p.num_proxies; ++r) {
-      double bv = v;
-      int bi = lane;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const double ov = __shfl_xor(bv, off, 64);
-        const int oi = __shfl_xor(bi, off, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      if (bv < 0.0) break;
-      if (lane == 0) prox[n] = bi;
-      if (lane == bi) v = -1.0;
-      ++n;
+    // positive heads of largest w_h ||q_h||, lower head index on ties: head
+    // h's rank in (value desc, index asc) order, counted over the staged
+    // values; the first min(num_proxies, #positive heads) ranks are proxies
+    const double v = (lane < H && wd[lane] > 0.0) ? wd[lane] * sqrt(qn2[lane]) : -1.0;
+    pvals[lane] = v;
+    wave_sync();
+    int above = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) {
+      const double o = pvals[j];
+      above += (o > v || (o == v && j < lane)) ? 1 : 0;
     }
+    const int n = min(p.num_proxies, (int)__popcll(ballot(v >= 0.0)));
+    if (v >= 0.0 && above < n) prox[above] = lane;
     if (lane == 0) np_s = n;
   }
   __syncthreads();
@@ -670,8 +711,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const PlanLaunch p) {
         double mx = 0.0;
 #pragma unroll
         for (int v = 0; v < PER; ++v) mx = fmax(mx, fabs(res[v]));
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) mx = fmax(mx, __shfl_xor(mx, off, 64));
+        mx = wave_max(mx);
         sg = (mx > 0.0) ? (float)(mx / 448.0) : 1.f;
         if (!(sg > 0.f)) sg = 1.f;   // underflow guard
       }
